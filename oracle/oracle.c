@@ -1,0 +1,331 @@
+/*
+ * CPU oracle for the DeepSeek-V4 CSA / HCA attention hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY. This file is the plain, slow, fp64 definition of what
+ * the path computes. Only the test suite, the smoke check and the benchmark's CPU
+ * baseline may load it; the GPU library never links, includes or calls it, and it
+ * shares no header, helper or table with the GPU sources.
+ *
+ * Source: "DeepSeek-V4 混合注意力：从压缩记忆到百万上下文" (brenchcc notes):
+ *   compress (ratio 4)    §4.1, equations for alpha_{i,:,j} and C^comp_{i,j}
+ *   compress (ratio 128)  §5, equations for beta_{i,:,j} and C^hca_{i,j}
+ *   index score           §4.2, equation for s_{t,i}
+ *   top-k                 §2 table (Top-k 512 / 1,024) and §4.2
+ *   sink softmax          §6, equation for p_i
+ *   shared-KV MQA         §4.2 (one compressed vector is both K and V), §7 call chain
+ *   SWA, partial RoPE     §6 (window 128, RoPE on the last 64 dims, inverse RoPE on o)
+ *   MXFP4 operands        the MXFP4 model-card page (one E8M0 scale per 32 E2M1 values)
+ *
+ * Every sum, dot product and softmax is accumulated in double precision and each
+ * logit vector is materialised before it is normalised.
+ *
+ * Readings where the pages leave a step open:
+ *  - the sum index r = 1..m of the compression equations is read as the same rows
+ *    as the softmax slice, i.e. row (i-1)m + r - 1 (0-based);
+ *  - a compression slot with no row (the b-branch of entry 0 without a carry) has
+ *    weight zero;
+ *  - a query at absolute position t sees compressed entry i iff (i+1)*ratio <= t;
+ *  - the SWA rows of a query at t are positions max(0, t-window+1) .. t;
+ *  - a RoPE pair is the interleaved pair (D-R+2p, D-R+2p+1), rotated by (cos, sin)
+ *    of the caller's table; the output is rotated back with (cos, -sin);
+ *  - top-k ties are broken by the lower entry index; -INF scores are never taken.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_OK 0
+#define OR_EINVAL 1
+
+/* ---------------------------------------------------------------------------------
+ * Compressor.  §4.1 (ratio 4, overlapped: the b-branch of block i-1 and the
+ * a-branch of block i share one per-channel softmax over 2m slots) and §5
+ * (ratio 128, non-overlapped: one softmax over the m' rows of block i).
+ *
+ * Ca, Za: [B][n][c]. Cb, Zb: [B][n][c] or NULL when overlap == 0.
+ * carry_Cb, carry_Zb: [B][ratio][c] b-branch rows of the block before row 0, or NULL.
+ * bias: [(1+overlap)*ratio][c] positional logit bias, or NULL.
+ * out:  [B][n/ratio][c].
+ * ------------------------------------------------------------------------------- */
+int oracle_compress(const double *Ca, const double *Cb, const double *Za, const double *Zb,
+                    const double *carry_Cb, const double *carry_Zb, const double *bias,
+                    int B, int64_t n, int c, int ratio, int overlap, double *out)
+{
+    if (B < 0 || n < 0 || c <= 0 || ratio <= 0 || (overlap != 0 && overlap != 1)) return OR_EINVAL;
+    if (overlap && (!Cb || !Zb)) return OR_EINVAL;
+    const int64_t E = n / ratio;           /* a trailing partial block is not compressed */
+    const int S = (1 + overlap) * ratio;   /* slots in one entry's receptive field */
+
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int b = 0; b < B; ++b) {
+        for (int64_t i = 0; i < E; ++i) {
+            double *logit = (double *)malloc(sizeof(double) * S);
+            double *val = (double *)malloc(sizeof(double) * S);
+            int *has = (int *)malloc(sizeof(int) * S);
+            for (int j = 0; j < c; ++j) {
+                /* gather the receptive field of entry i, channel j */
+                for (int s = 0; s < S; ++s) {
+                    int is_b = overlap && s < ratio;
+                    int r = is_b ? s : s - overlap * ratio;
+                    has[s] = 1;
+                    if (is_b) {
+                        if (i >= 1) {
+                            int64_t row = (i - 1) * ratio + r;
+                            logit[s] = Zb[((int64_t)b * n + row) * c + j];
+                            val[s] = Cb[((int64_t)b * n + row) * c + j];
+                        } else if (carry_Cb && carry_Zb) {
+                            logit[s] = carry_Zb[((int64_t)b * ratio + r) * c + j];
+                            val[s] = carry_Cb[((int64_t)b * ratio + r) * c + j];
+                        } else {
+                            has[s] = 0;
+                        }
+                    } else {
+                        int64_t row = i * ratio + r;
+                        logit[s] = Za[((int64_t)b * n + row) * c + j];
+                        val[s] = Ca[((int64_t)b * n + row) * c + j];
+                    }
+                    if (has[s] && bias) logit[s] += bias[(int64_t)s * c + j];
+                }
+                /* softmax over the present slots, then the weighted sum */
+                double M = -INFINITY;
+                for (int s = 0; s < S; ++s)
+                    if (has[s] && logit[s] > M) M = logit[s];
+                double den = 0.0, num = 0.0;
+                for (int s = 0; s < S; ++s) {
+                    if (!has[s]) continue;
+                    double e = exp(logit[s] - M);
+                    den += e;
+                    num += e * val[s];
+                }
+                out[((int64_t)b * E + i) * c + j] = num / den;
+            }
+            free(logit);
+            free(val);
+            free(has);
+        }
+    }
+    return OR_OK;
+}
+
+/* ---------------------------------------------------------------------------------
+ * Lightning Indexer score.  §4.2:  s_{t,i} = sum_h w_{t,h} ReLU(<q^I_{t,h}, k^I_{i,h}>).
+ *
+ * qI: [T][H][Dh]; w: [T][H]; kI: [B][N][kh][Dh] with kh = H (per-head keys) or 1.
+ * entry_ids: [N] absolute entry index of each stored key row (NULL: row i is entry i);
+ * used to check a sample of a long key store without materialising all of it.
+ * scores: [T][N]; -INF where the entry's block is not wholly before q_pos[t].
+ * ------------------------------------------------------------------------------- */
+int oracle_index_scores(const double *qI, const double *w, const double *kI,
+                        const int32_t *q_seq, const int64_t *q_pos, const int64_t *entry_ids,
+                        int T, int B, int64_t N, int H, int Dh, int kh, int ratio, double *scores)
+{
+    if (T < 0 || B <= 0 || N < 0 || H <= 0 || Dh <= 0 || (kh != H && kh != 1) || ratio <= 0)
+        return OR_EINVAL;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int t = 0; t < T; ++t) {
+        for (int64_t i = 0; i < N; ++i) {
+            const int s = q_seq[t];
+            const int64_t e = entry_ids ? entry_ids[i] : i;
+            double sc = -INFINITY;
+            if (s >= 0 && s < B && (e + 1) * (int64_t)ratio <= q_pos[t]) {
+                sc = 0.0;
+                for (int h = 0; h < H; ++h) {
+                    const double *q = qI + ((int64_t)t * H + h) * Dh;
+                    const int hk = (kh == H) ? h : 0;
+                    const double *k = kI + (((int64_t)s * N + i) * kh + hk) * Dh;
+                    double dot = 0.0;
+                    for (int d = 0; d < Dh; ++d) dot += q[d] * k[d];
+                    sc += w[(int64_t)t * H + h] * (dot > 0.0 ? dot : 0.0);
+                }
+            }
+            scores[(int64_t)t * N + i] = sc;
+        }
+    }
+    return OR_OK;
+}
+
+/* ---------------------------------------------------------------------------------
+ * MXFP4 decode (the page on DeepSeek-V4-Pro-MXFP4: E2M1 values sharing one E8M0
+ * scale per 32 elements). Value = sign * {0,.5,1,1.5,2,3,4,6}[code&7] * 2^(scale-127);
+ * element 2m sits in the low nibble of byte m; scale byte 255 is NaN.
+ * ------------------------------------------------------------------------------- */
+int oracle_mxfp4_decode(const uint8_t *codes, const uint8_t *scales, int64_t nelem, double *out)
+{
+    static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    if (nelem % 32) return OR_EINVAL;
+    for (int64_t e = 0; e < nelem; ++e) {
+        uint8_t byte = codes[e / 2];
+        int nib = (e & 1) ? (byte >> 4) : (byte & 15);
+        uint8_t sc = scales[e / 32];
+        double v = mag[nib & 7] * ldexp(1.0, (int)sc - 127);
+        if (nib & 8) v = -v;
+        out[e] = (sc == 255) ? NAN : v;
+    }
+    return OR_OK;
+}
+
+/* ---------------------------------------------------------------------------------
+ * Top-k: the k largest finite scores of each row, ties to the lower index,
+ * padded with -1 (value -INF) when fewer than k are finite.
+ * ------------------------------------------------------------------------------- */
+typedef struct {
+    double s;
+    int64_t i;
+} or_pair;
+
+static int or_pair_cmp(const void *a, const void *b)
+{
+    const or_pair *x = (const or_pair *)a, *y = (const or_pair *)b;
+    if (x->s > y->s) return -1;
+    if (x->s < y->s) return 1;
+    return (x->i < y->i) ? -1 : (x->i > y->i);
+}
+
+int oracle_topk(const double *scores, int T, int64_t N, int k, int32_t *idx, double *vals)
+{
+    if (T < 0 || N < 0 || k <= 0) return OR_EINVAL;
+#pragma omp parallel for schedule(dynamic)
+    for (int t = 0; t < T; ++t) {
+        or_pair *p = (or_pair *)malloc(sizeof(or_pair) * (N > 0 ? N : 1));
+        int64_t cnt = 0;
+        for (int64_t i = 0; i < N; ++i) {
+            double s = scores[(int64_t)t * N + i];
+            if (isfinite(s)) {
+                p[cnt].s = s;
+                p[cnt].i = i;
+                ++cnt;
+            }
+        }
+        qsort(p, (size_t)cnt, sizeof(or_pair), or_pair_cmp);
+        for (int j = 0; j < k; ++j) {
+            idx[(int64_t)t * k + j] = (j < cnt) ? (int32_t)p[j].i : -1;
+            if (vals) vals[(int64_t)t * k + j] = (j < cnt) ? p[j].s : -INFINITY;
+        }
+        free(p);
+    }
+    return OR_OK;
+}
+
+/* ---------------------------------------------------------------------------------
+ * Shared-KV MQA with a sink logit over an explicit row set (§4.2, §6).
+ *   z_j = scale <q', row_j>;  p_j = e^{z_j} / (e^{sink} + sum_l e^{z_l});  o' = sum_j p_j row_j
+ *   lse = log(e^{sink} + sum_j e^{z_j})
+ * q' is q with its last R dims rotated forward, o is o' with its last R dims rotated back.
+ * ------------------------------------------------------------------------------- */
+static void mqa_rows(const double *qrow, const double *const *rows, int64_t L, double sink,
+                     double scale, const double *cs, int R, int D, double *o, double *lse)
+{
+    double *qv = (double *)malloc(sizeof(double) * D);
+    double *z = (double *)malloc(sizeof(double) * (L > 0 ? L : 1));
+    memcpy(qv, qrow, sizeof(double) * D);
+    if (cs) {
+        for (int p = 0; p < R / 2; ++p) {
+            double c = cs[2 * p], s = cs[2 * p + 1];
+            double x0 = qv[D - R + 2 * p], x1 = qv[D - R + 2 * p + 1];
+            qv[D - R + 2 * p] = x0 * c - x1 * s;
+            qv[D - R + 2 * p + 1] = x0 * s + x1 * c;
+        }
+    }
+    double M = sink;
+    for (int64_t j = 0; j < L; ++j) {
+        double dot = 0.0;
+        for (int d = 0; d < D; ++d) dot += qv[d] * rows[j][d];
+        z[j] = scale * dot;
+        if (z[j] > M) M = z[j];
+    }
+    double den = exp(sink - M);
+    for (int d = 0; d < D; ++d) o[d] = 0.0;
+    for (int64_t j = 0; j < L; ++j) {
+        double e = exp(z[j] - M);
+        den += e;
+        for (int d = 0; d < D; ++d) o[d] += e * rows[j][d];
+    }
+    for (int d = 0; d < D; ++d) o[d] /= den;
+    if (cs) {
+        for (int p = 0; p < R / 2; ++p) {
+            double c = cs[2 * p], s = cs[2 * p + 1];
+            double x0 = o[D - R + 2 * p], x1 = o[D - R + 2 * p + 1];
+            o[D - R + 2 * p] = x0 * c + x1 * s;
+            o[D - R + 2 * p + 1] = -x0 * s + x1 * c;
+        }
+    }
+    *lse = M + log(den);
+    free(qv);
+    free(z);
+}
+
+/* SWA rows of a query at t: positions max(0, t-window+1)..t present in swa[s]. */
+static int64_t add_swa_rows(const double **rows, int64_t L, const double *swa, const int64_t *swa_pos0,
+                            int swa_rows, int window, int s, int64_t t, int D)
+{
+    if (!swa || window <= 0) return L;
+    int64_t lo = t - window + 1;
+    if (lo < 0) lo = 0;
+    for (int64_t p = lo; p <= t; ++p) {
+        int64_t r = p - swa_pos0[s];
+        if (r >= 0 && r < swa_rows) rows[L++] = swa + ((int64_t)s * swa_rows + r) * D;
+    }
+    return L;
+}
+
+/* q: [T][H][D]; kv: [B][N][D]; sink: [H]; topk_idxs: [T][k] (-1 or out of range: skipped);
+ * swa: [B][swa_rows][D], row r of sequence s holds position swa_pos0[s] + r;
+ * rope_cs: [T][R/2][2] or NULL; out: [T][H][D]; lse: [T][H] or NULL. */
+int oracle_sparse_attn(const double *q, const double *kv, const double *sink,
+                       const int32_t *topk_idxs, int k, double scale,
+                       const double *swa, const int64_t *swa_pos0, int swa_rows, int window,
+                       const int32_t *q_seq, const int64_t *q_pos, const double *rope_cs, int R,
+                       int T, int B, int64_t N, int H, int D, double *out, double *lse)
+{
+    if (T < 0 || B <= 0 || N < 0 || H <= 0 || D <= 0 || k < 0 || window < 0) return OR_EINVAL;
+    if (rope_cs && (R <= 0 || R % 2 || R > D)) return OR_EINVAL;
+#pragma omp parallel for schedule(dynamic)
+    for (int t = 0; t < T; ++t) {
+        const int s = q_seq[t];
+        const double **rows = (const double **)malloc(sizeof(double *) * ((size_t)k + window + 1));
+        int64_t L = 0;
+        for (int j = 0; j < k; ++j) {
+            int32_t id = topk_idxs[(int64_t)t * k + j];
+            if (id >= 0 && id < N) rows[L++] = kv + ((int64_t)s * N + id) * D;
+        }
+        L = add_swa_rows(rows, L, swa, swa_pos0, swa_rows, window, s, q_pos[t], D);
+        for (int g = 0; g < H; ++g) {
+            double l;
+            mqa_rows(q + ((int64_t)t * H + g) * D, rows, L, sink[g], scale,
+                     rope_cs ? rope_cs + (int64_t)t * R : NULL, R, D,
+                     out + ((int64_t)t * H + g) * D, &l);
+            if (lse) lse[(int64_t)t * H + g] = l;
+        }
+        free(rows);
+    }
+    return OR_OK;
+}
+
+/* HCA (§5): every summary i with (i+1)*ratio <= t, plus the SWA rows. summ: [B][N][D]. */
+int oracle_hca_attn(const double *q, const double *summ, const double *sink, int ratio, double scale,
+                    const double *swa, const int64_t *swa_pos0, int swa_rows, int window,
+                    const int32_t *q_seq, const int64_t *q_pos, const double *rope_cs, int R,
+                    int T, int B, int64_t N, int H, int D, double *out, double *lse)
+{
+    if (T < 0 || B <= 0 || N < 0 || H <= 0 || D <= 0 || ratio <= 0 || window < 0) return OR_EINVAL;
+    if (rope_cs && (R <= 0 || R % 2 || R > D)) return OR_EINVAL;
+#pragma omp parallel for schedule(dynamic)
+    for (int t = 0; t < T; ++t) {
+        const int s = q_seq[t];
+        const double **rows = (const double **)malloc(sizeof(double *) * ((size_t)N + window + 1));
+        int64_t L = 0;
+        for (int64_t i = 0; i < N; ++i)
+            if ((i + 1) * (int64_t)ratio <= q_pos[t]) rows[L++] = summ + ((int64_t)s * N + i) * D;
+        L = add_swa_rows(rows, L, swa, swa_pos0, swa_rows, window, s, q_pos[t], D);
+        for (int g = 0; g < H; ++g) {
+            double l;
+            mqa_rows(q + ((int64_t)t * H + g) * D, rows, L, sink[g], scale,
+                     rope_cs ? rope_cs + (int64_t)t * R : NULL, R, D,
+                     out + ((int64_t)t * H + g) * D, &l);
+            if (lse) lse[(int64_t)t * H + g] = l;
+        }
+        free(rows);
+    }
+    return OR_OK;
+}
