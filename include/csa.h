@@ -1,0 +1,171 @@
+/*
+ * csa.h - C ABI of the MI355X (gfx950) DeepSeek-V4 CSA / HCA attention hot path.
+ *
+ * The operations follow "DeepSeek-V4 混合注意力：从压缩记忆到百万上下文" (brenchcc
+ * technical note, built on the DeepSeek-V4 technical report and inference code):
+ *   csa_compress      §4.1 (ratio 4, overlapped two-branch pooling) and §5 (ratio 128)
+ *   csa_index_scores  §4.2 (Lightning Indexer score), FP4 operands per §2 and §4.2
+ *   csa_topk          §2 table and §4.2 (top-k 512 / 1,024 compressed entries per query)
+ *   csa_sparse_attn   §4.2 (shared-KV MQA over the selected entries), §6 (SWA 128,
+ *                     partial RoPE and inverse RoPE, attention sink), §7 call chain;
+ *                     argument order of the sparse_attn(q, kv, attn_sink, topk_idxs,
+ *                     softmax_scale) call on the DeepSeek-V4-Flash page
+ *   hca_attn          §5 (dense MQA over every visible 128:1 summary) plus §6
+ *
+ * Conventions for every call:
+ *  - Every tensor pointer is a DEVICE pointer (hipMalloc'd or a torch tensor's
+ *    data_ptr()). Tensors are row-major with the innermost dimension contiguous.
+ *  - The caller owns every buffer, including outputs and workspaces. The library
+ *    allocates no device memory and keeps no pointer after a call returns.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the null
+ *    stream). Results are ready when that stream is synchronised.
+ *  - Positions are 0-based absolute token positions. Compressed entry i of a
+ *    ratio-m compressor pools the block of tokens [i*m, (i+1)*m); a query at
+ *    position t sees entry i iff (i+1)*m <= t.
+ *  - Return value: CSA_OK, or an error code. Scalar/pointer arguments are validated
+ *    before anything is launched: on CSA_EINVAL / CSA_EUNSUPPORTED /
+ *    CSA_EWORKSPACE no work is enqueued. CSA_EHIP reports a HIP launch error.
+ *    csa_last_error() gives a detail string (thread-local). Nothing is printed and
+ *    nothing throws across the ABI.
+ *  - Device-resident index data (q_seq, q_pos, topk_idxs, swa_pos0) cannot be
+ *    validated without a synchronisation: out-of-range row indices are skipped,
+ *    never dereferenced; an out-of-range q_seq yields a query that sees no rows.
+ */
+#ifndef CSA_H
+#define CSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { CSA_F32 = 0, CSA_BF16 = 1, CSA_MXFP4 = 2 } csa_dtype;
+
+typedef enum {
+    CSA_OK = 0,
+    CSA_EINVAL = 1,       /* bad shape, NULL required pointer, bad combination */
+    CSA_EUNSUPPORTED = 2, /* valid request that this library does not implement */
+    CSA_EWORKSPACE = 3,   /* workspace missing or smaller than the *_workspace_bytes query */
+    CSA_EHIP = 4          /* the HIP runtime reported an error */
+} csa_status;
+
+/*
+ * csa_compress - token-level KV compressor (§4.1, §5).
+ *
+ * ratio 4, overlap 1 (CSA): for entry i and channel j, a softmax over the 8 logits
+ *   [Z_b rows 4(i-1)..4i-1 ; Z_a rows 4i..4i+3] (+ logit_bias), and
+ *   out[i][j] = sum of the weights times the matching C_b / C_a rows.
+ *   For i = 0 the b-branch rows come from carry_C_b / carry_Z_b (the b-branch of the
+ *   block just before row 0, e.g. from the previous chunk); when the carry is NULL
+ *   those slots are absent (weight 0) and entry 0 pools block 0's a-branch alone.
+ * ratio 128, overlap 0 (HCA): out[i][j] = sum_r softmax_r(Z_a[128i + r][j]) C_a[128i + r][j].
+ *
+ * C_a, Z_a:   [B][n][c]           dtype dt (F32 or BF16)
+ * C_b, Z_b:   [B][n][c]           dtype dt; required iff overlap == 1, else ignored
+ * carry_C_b, carry_Z_b: [B][ratio][c] dtype dt, or both NULL (overlap == 1 only)
+ * logit_bias: [(1+overlap)*ratio][c] fp32 added to the slot logits (b-slots first), or NULL
+ * out:        [B][n/ratio][c] dtype dt, sequence b starting at out + b*out_bstride
+ *             elements (out_bstride == 0 means (n/ratio)*c). A trailing partial block
+ *             (n % ratio rows) is not compressed.
+ * Supported: (ratio, overlap) = (4, 1) or (128, 0); any other pair is CSA_EUNSUPPORTED.
+ * Softmax and sums are fp32; the output is rounded once to dt.
+ */
+int csa_compress(const void *C_a, const void *C_b, const void *Z_a, const void *Z_b,
+                 const void *carry_C_b, const void *carry_Z_b, const float *logit_bias,
+                 int B, int64_t n, int c, int ratio, int overlap, csa_dtype dt,
+                 void *out, int64_t out_bstride, void *stream);
+
+/*
+ * csa_index_scores - Lightning Indexer (§4.2):
+ *   scores[t][i] = sum_h w[t][h] * ReLU(<q_I[t][h], k_I[q_seq[t]][i][h]>)
+ * for every stored entry i with (i+1)*ratio <= q_pos[t]; -INFINITY otherwise.
+ *
+ * q_I:  [T][H_I][D_I] in dt.  For CSA_MXFP4: [T][H_I][D_I/2] bytes of E2M1 codes (even
+ *       element in the low nibble) plus q_I_scale [T][H_I][D_I/32] E8M0 bytes (value =
+ *       code * 2^(scale-127)), as in the MXFP4 checkpoints' indexer path.
+ * w:    [T][H_I] fp32 query-dependent head weights (any sign).
+ * k_I:  [B][N][H_I][D_I] per-head keys in dt (MXFP4: [B][N][H_I][D_I/2] + k_I_scale
+ *       [B][N][H_I][D_I/32]). q_I_scale / k_I_scale are ignored unless dt == CSA_MXFP4.
+ * q_seq [T] int32 sequence of each query; q_pos [T] int64 absolute position.
+ * scores: [T][N] fp32. Products and sums are fp32 (MXFP4 products are exact).
+ * Supported: H_I == 64, D_I == 128 (the indexer of both model sizes), dt F32 | BF16 |
+ * MXFP4, ratio >= 1. T, N may be 0 (nothing is launched).
+ */
+int csa_index_scores(const void *q_I, const uint8_t *q_I_scale, const float *w,
+                     const void *k_I, const uint8_t *k_I_scale,
+                     const int32_t *q_seq, const int64_t *q_pos,
+                     int T, int B, int64_t N, int H_I, int D_I, int ratio, csa_dtype dt,
+                     float *scores, void *stream);
+
+/*
+ * csa_topk - per-query top-k selection over index scores (§4.2).
+ *
+ * scores: [T][N] fp32; -INFINITY (and NaN) entries are never selected.
+ * topk_idxs: [T][k] int32 out: the indices of the k largest scores of each row, in
+ *   ascending index order; ties at the k-th value go to the lower indices; when a row
+ *   has fewer than k finite scores the remaining slots are -1.
+ * topk_vals: [T][k] fp32 out (the scores of topk_idxs, -INFINITY for padding), or NULL.
+ * workspace: device scratch of at least csa_topk_workspace_bytes(T, N, k) bytes
+ *   (may be NULL when that query returns 0).
+ * Supported: 1 <= k <= 4096.
+ */
+size_t csa_topk_workspace_bytes(int T, int64_t N, int k);
+int csa_topk(const float *scores, int T, int64_t N, int k,
+             int32_t *topk_idxs, float *topk_vals,
+             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * csa_sparse_attn - shared-KV multi-query attention with an attention sink
+ * (§4.2, §6; the sparse_attn(q, kv, attn_sink, topk_idxs, softmax_scale) call).
+ *
+ * For query t (sequence s = q_seq[t], position p = q_pos[t]) and head g the rows are
+ *   kv[s][topk_idxs[t][j]] for every j with 0 <= topk_idxs[t][j] < N (others skipped),
+ *   then swa_kv[s][r] for every position x in [max(0, p-window+1), p] with
+ *   r = x - swa_pos0[s] in [0, swa_rows)   (the raw sliding-window rows, no dedup).
+ * q' = q[t][g] with its last rope_dim dims rotated pairwise by rope_cs[t] (pair
+ * (D-R+2i, D-R+2i+1) by (cos, sin)); z_j = softmax_scale * <q', row_j>;
+ * o' = sum_j e^{z_j} row_j / (e^{attn_sink[g]} + sum_j e^{z_j});
+ * out[t][g] = o' with its last rope_dim dims rotated back (by (cos, -sin));
+ * lse[t][g] = log(e^{attn_sink[g]} + sum_j e^{z_j}).
+ *
+ * q: [T][H][D] dt; kv: [B][N][D] dt (already RoPE-rotated as stored in the cache);
+ * attn_sink: [H] fp32 (not scaled); topk_idxs: [T][k] int32;
+ * swa_kv: [B][swa_rows][D] dt or NULL (then window is ignored); swa_pos0: [B] int64;
+ * rope_cs: [T][rope_dim/2][2] fp32 or NULL (rope_dim ignored); out: [T][H][D] dt;
+ * lse: [T][H] fp32 or NULL; workspace: csa_attn_workspace_bytes(...) bytes.
+ * Supported: dt F32 | BF16, D <= 1024, D % 64 == 0, rope_dim even and <= D.
+ */
+size_t csa_attn_workspace_bytes(int T, int H, int D, int64_t max_rows);
+int csa_sparse_attn(const void *q, const void *kv, const float *attn_sink,
+                    const int32_t *topk_idxs, int k, float softmax_scale,
+                    const void *swa_kv, const int64_t *swa_pos0, int swa_rows, int window,
+                    const int32_t *q_seq, const int64_t *q_pos,
+                    const float *rope_cs, int rope_dim,
+                    int T, int B, int64_t N, int H, int D, csa_dtype dt,
+                    void *out, float *lse, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
+/*
+ * hca_attn - HCA dense shared-KV MQA (§5, §6): csa_sparse_attn with the compressed rows
+ * replaced by every summary i < N with (i+1)*ratio <= q_pos[t] (summ: [B][N][D] dt),
+ * followed by the same SWA rows, sink, RoPE and outputs. max_rows for the workspace
+ * query is N + window.
+ */
+int hca_attn(const void *q, const void *summ, const float *attn_sink, int ratio,
+             float softmax_scale, const void *swa_kv, const int64_t *swa_pos0, int swa_rows,
+             int window, const int32_t *q_seq, const int64_t *q_pos,
+             const float *rope_cs, int rope_dim,
+             int T, int B, int64_t N, int H, int D, csa_dtype dt,
+             void *out, float *lse, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static name of a status code. */
+const char *csa_status_str(int status);
+/* Detail string of the last non-OK return on the calling thread ("" if none). */
+const char *csa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA_H */

@@ -1,0 +1,160 @@
+// C ABI of the CSA / HCA library: argument validation, then dispatch to the launchers.
+// Every check below runs before anything is enqueued; a failed check launches nothing.
+#include <cmath>
+#include <string>
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace csa {
+
+static thread_local std::string g_err;
+
+void set_error(const std::string &msg) { g_err = msg; }
+void clear_error() { g_err.clear(); }
+int fail(int status, const std::string &msg) {
+    g_err = msg;
+    return status;
+}
+int check_launch(const char *what) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(CSA_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+    return CSA_OK;
+}
+
+}  // namespace csa
+
+using namespace csa;
+
+#define REQUIRE(cond, code, msg) \
+    do {                         \
+        if (!(cond)) return fail((code), (msg)); \
+    } while (0)
+
+extern "C" {
+
+const char *csa_status_str(int status) {
+    switch (status) {
+        case CSA_OK: return "CSA_OK";
+        case CSA_EINVAL: return "CSA_EINVAL";
+        case CSA_EUNSUPPORTED: return "CSA_EUNSUPPORTED";
+        case CSA_EWORKSPACE: return "CSA_EWORKSPACE";
+        case CSA_EHIP: return "CSA_EHIP";
+        default: return "CSA_UNKNOWN";
+    }
+}
+
+const char *csa_last_error(void) { return g_err.c_str(); }
+
+int csa_compress(const void *C_a, const void *C_b, const void *Z_a, const void *Z_b,
+                 const void *carry_C_b, const void *carry_Z_b, const float *logit_bias, int B, int64_t n,
+                 int c, int ratio, int overlap, csa_dtype dt, void *out, int64_t out_bstride, void *stream) {
+    clear_error();
+    REQUIRE(B >= 0 && n >= 0 && c > 0, CSA_EINVAL, "csa_compress: need B >= 0, n >= 0, c > 0");
+    REQUIRE(ratio > 0 && (overlap == 0 || overlap == 1), CSA_EINVAL, "csa_compress: ratio > 0, overlap in {0,1}");
+    REQUIRE(dt == CSA_F32 || dt == CSA_BF16, CSA_EINVAL, "csa_compress: dt must be CSA_F32 or CSA_BF16");
+    REQUIRE((ratio == 4 && overlap == 1) || (ratio == 128 && overlap == 0), CSA_EUNSUPPORTED,
+            "csa_compress: supported (ratio, overlap) pairs are (4, 1) and (128, 0)");
+    const int64_t E = n / ratio;
+    REQUIRE((carry_C_b == nullptr) == (carry_Z_b == nullptr), CSA_EINVAL,
+            "csa_compress: carry_C_b and carry_Z_b must both be given or both be NULL");
+    REQUIRE(overlap || carry_C_b == nullptr, CSA_EINVAL, "csa_compress: a carry needs overlap == 1");
+    REQUIRE(out_bstride == 0 || out_bstride >= E * c, CSA_EINVAL, "csa_compress: out_bstride < (n/ratio)*c");
+    if (B == 0 || E == 0) return CSA_OK;
+    REQUIRE(C_a && Z_a && out, CSA_EINVAL, "csa_compress: C_a, Z_a and out are required");
+    REQUIRE(!overlap || (C_b && Z_b), CSA_EINVAL, "csa_compress: C_b and Z_b are required when overlap == 1");
+    return launch_compress(C_a, overlap ? C_b : nullptr, Z_a, overlap ? Z_b : nullptr, carry_C_b, carry_Z_b,
+                           logit_bias, B, n, c, ratio, overlap, dt, out, out_bstride, (hipStream_t)stream);
+}
+
+int csa_index_scores(const void *q_I, const uint8_t *q_I_scale, const float *w, const void *k_I,
+                     const uint8_t *k_I_scale, const int32_t *q_seq, const int64_t *q_pos, int T, int B,
+                     int64_t N, int H_I, int D_I, int ratio, csa_dtype dt, float *scores, void *stream) {
+    clear_error();
+    REQUIRE(T >= 0 && B > 0 && N >= 0 && ratio > 0, CSA_EINVAL, "csa_index_scores: need T >= 0, B > 0, N >= 0, ratio > 0");
+    REQUIRE(H_I > 0 && D_I > 0, CSA_EINVAL, "csa_index_scores: H_I and D_I must be positive");
+    REQUIRE(dt == CSA_F32 || dt == CSA_BF16 || dt == CSA_MXFP4, CSA_EINVAL, "csa_index_scores: bad dtype");
+    REQUIRE(dt != CSA_MXFP4 || D_I % 32 == 0, CSA_EINVAL, "csa_index_scores: MXFP4 needs D_I % 32 == 0");
+    REQUIRE(H_I == 64 && D_I == 128, CSA_EUNSUPPORTED, "csa_index_scores: only H_I = 64, D_I = 128 is built");
+    if (T == 0 || N == 0) return CSA_OK;
+    REQUIRE(q_I && w && k_I && q_seq && q_pos && scores, CSA_EINVAL, "csa_index_scores: NULL tensor");
+    REQUIRE(dt != CSA_MXFP4 || (q_I_scale && k_I_scale), CSA_EINVAL, "csa_index_scores: MXFP4 needs both scale tensors");
+    return launch_index_scores(q_I, q_I_scale, w, k_I, k_I_scale, q_seq, q_pos, T, B, N, ratio, dt, scores,
+                               (hipStream_t)stream);
+}
+
+size_t csa_topk_workspace_bytes(int T, int64_t N, int k) {
+    if (T <= 0 || N <= 0 || k <= 0) return 0;
+    return topk_workspace_bytes(T, N, k);
+}
+
+int csa_topk(const float *scores, int T, int64_t N, int k, int32_t *topk_idxs, float *topk_vals, void *workspace,
+             size_t workspace_bytes, void *stream) {
+    clear_error();
+    REQUIRE(T >= 0 && N >= 0, CSA_EINVAL, "csa_topk: need T >= 0 and N >= 0");
+    REQUIRE(k > 0, CSA_EINVAL, "csa_topk: k must be positive");
+    REQUIRE(k <= 4096, CSA_EUNSUPPORTED, "csa_topk: k > 4096 is not built");
+    REQUIRE(N < ((int64_t)1 << 31), CSA_EUNSUPPORTED, "csa_topk: N must fit int32 indices");
+    if (T == 0) return CSA_OK;
+    REQUIRE(topk_idxs && (scores || N == 0), CSA_EINVAL, "csa_topk: NULL tensor");
+    return launch_topk(scores, T, N, k, topk_idxs, topk_vals, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+size_t csa_attn_workspace_bytes(int T, int H, int D, int64_t max_rows) {
+    if (T <= 0 || H <= 0 || D <= 0 || max_rows <= 0) return 0;
+    return attn_workspace_bytes(T, H, D, max_rows);
+}
+
+static int check_attn_common(const void *q, const void *kv, const float *sink, const void *swa,
+                             const int64_t *swa_pos0, int swa_rows, int window, const int32_t *q_seq,
+                             const int64_t *q_pos, const float *rope_cs, int rope_dim, int T, int B, int64_t N,
+                             int H, int D, csa_dtype dt, void *out, const char *who) {
+    const std::string w(who);
+    REQUIRE(T >= 0 && B > 0 && N >= 0 && H > 0 && D > 0, CSA_EINVAL, w + ": need T >= 0, B > 0, N >= 0, H > 0, D > 0");
+    REQUIRE(window >= 0 && swa_rows >= 0, CSA_EINVAL, w + ": window and swa_rows must be >= 0");
+    REQUIRE(dt == CSA_F32 || dt == CSA_BF16, CSA_EINVAL, w + ": dt must be CSA_F32 or CSA_BF16");
+    REQUIRE(!rope_cs || (rope_dim > 0 && rope_dim % 2 == 0 && rope_dim <= D), CSA_EINVAL,
+            w + ": rope_dim must be even, positive and <= D");
+    REQUIRE(D % 64 == 0 && D <= 1024, CSA_EUNSUPPORTED, w + ": D must be a multiple of 64 and <= 1024");
+    if (T == 0) return CSA_OK;
+    REQUIRE(q && sink && q_seq && q_pos && out, CSA_EINVAL, w + ": NULL tensor");
+    REQUIRE(kv || N == 0, CSA_EINVAL, w + ": NULL key/value rows");
+    REQUIRE(!swa || swa_pos0, CSA_EINVAL, w + ": swa_kv needs swa_pos0");
+    return CSA_OK;
+}
+
+int csa_sparse_attn(const void *q, const void *kv, const float *attn_sink, const int32_t *topk_idxs, int k,
+                    float softmax_scale, const void *swa_kv, const int64_t *swa_pos0, int swa_rows, int window,
+                    const int32_t *q_seq, const int64_t *q_pos, const float *rope_cs, int rope_dim, int T, int B,
+                    int64_t N, int H, int D, csa_dtype dt, void *out, float *lse, void *workspace,
+                    size_t workspace_bytes, void *stream) {
+    clear_error();
+    int rc = check_attn_common(q, kv, attn_sink, swa_kv, swa_pos0, swa_rows, window, q_seq, q_pos, rope_cs,
+                               rope_dim, T, B, N, H, D, dt, out, "csa_sparse_attn");
+    if (rc != CSA_OK) return rc;
+    REQUIRE(k >= 0, CSA_EINVAL, "csa_sparse_attn: k must be >= 0");
+    REQUIRE(std::isfinite(softmax_scale), CSA_EINVAL, "csa_sparse_attn: softmax_scale must be finite");
+    if (T == 0) return CSA_OK;
+    REQUIRE(k == 0 || topk_idxs, CSA_EINVAL, "csa_sparse_attn: NULL topk_idxs");
+    AttnArgs a{q, kv, attn_sink, topk_idxs, k, 0, softmax_scale, swa_kv, swa_pos0, swa_rows, window, q_seq, q_pos,
+               rope_cs, rope_cs ? rope_dim : 0, T, B, N, H, D, dt, out, lse, workspace, workspace_bytes};
+    return launch_attn(a, (hipStream_t)stream);
+}
+
+int hca_attn(const void *q, const void *summ, const float *attn_sink, int ratio, float softmax_scale,
+             const void *swa_kv, const int64_t *swa_pos0, int swa_rows, int window, const int32_t *q_seq,
+             const int64_t *q_pos, const float *rope_cs, int rope_dim, int T, int B, int64_t N, int H, int D,
+             csa_dtype dt, void *out, float *lse, void *workspace, size_t workspace_bytes, void *stream) {
+    clear_error();
+    int rc = check_attn_common(q, summ, attn_sink, swa_kv, swa_pos0, swa_rows, window, q_seq, q_pos, rope_cs,
+                               rope_dim, T, B, N, H, D, dt, out, "hca_attn");
+    if (rc != CSA_OK) return rc;
+    REQUIRE(ratio > 0, CSA_EINVAL, "hca_attn: ratio must be positive");
+    REQUIRE(std::isfinite(softmax_scale), CSA_EINVAL, "hca_attn: softmax_scale must be finite");
+    if (T == 0) return CSA_OK;
+    AttnArgs a{q, summ, attn_sink, nullptr, 0, ratio, softmax_scale, swa_kv, swa_pos0, swa_rows, window, q_seq,
+               q_pos, rope_cs, rope_cs ? rope_dim : 0, T, B, N, H, D, dt, out, lse, workspace, workspace_bytes};
+    return launch_attn(a, (hipStream_t)stream);
+}
+
+}  // extern "C"

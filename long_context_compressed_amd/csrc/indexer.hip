@@ -1,0 +1,208 @@
+// Lightning Indexer scores on gfx950 ("DeepSeek-V4 混合注意力" §4.2):
+//   s[t][i] = sum_h w[t][h] * ReLU(<q_I[t][h], k_I[i][h]>),  64 heads x 128 dims.
+//
+// Decode scan (bf16 / fp32 keys). Every visible entry's 64x128 key block is read
+// once; with one query per sequence there is no reuse to feed a matrix core, so this
+// is an HBM stream:
+//  - one wavefront owns a run of consecutive entries of one query; per entry each lane
+//    issues 16-byte non-temporal loads that together cover the block contiguously
+//    (1 KiB per wave instruction), and the next entry's loads are in flight while the
+//    current one is reduced;
+//  - the query's 64x128 operand sits in VGPRs, in the same lane layout as the keys;
+//  - per-lane partial dots of the lanes sharing a head are combined by a transposed
+//    butterfly (each xor step halves the values a lane carries), after which every lane
+//    holds one head's full dot: ReLU, times w, and one 64-lane sum give the score.
+//  - entries that the query cannot see are written as -inf without being read.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace csa {
+
+namespace {
+
+template <typename KT> struct ScanTraits {
+    static constexpr int VEC = 16 / (int)sizeof(KT);  // elements per 16-byte load
+    static constexpr int G = 128 / VEC;               // lanes that share one head
+    static constexpr int J = 8192 / (64 * VEC);       // 16-byte loads per lane per entry
+    static constexpr int HPL = 64 / G;                // heads covered by one wave load
+};
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float dot16B(const u32x4 &a, const u32x4 &b, float acc, bf16_t) {
+    // components are copied to scalars first: a bit_cast of a vector-element lvalue
+    // reads element 0 whatever the component
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const uint32_t x = a[c], y = b[c];
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, x), __builtin_bit_cast(bf16x2v, y),
+                                              acc, false);
+    }
+    return acc;
+}
+
+__device__ __forceinline__ float dot16B(const u32x4 &a, const u32x4 &b, float acc, float) {
+    acc = fmaf(__uint_as_float(a.x), __uint_as_float(b.x), acc);
+    acc = fmaf(__uint_as_float(a.y), __uint_as_float(b.y), acc);
+    acc = fmaf(__uint_as_float(a.z), __uint_as_float(b.z), acc);
+    acc = fmaf(__uint_as_float(a.w), __uint_as_float(b.w), acc);
+    return acc;
+}
+
+template <typename KT>
+__device__ __forceinline__ void load_entry(u32x4 (&buf)[ScanTraits<KT>::J], const u32x4 *p, int lane) {
+#pragma unroll
+    for (int j = 0; j < ScanTraits<KT>::J; ++j) buf[j] = __builtin_nontemporal_load(p + j * 64 + lane);
+}
+
+// full score of the entry held in `buf` (wave-uniform result)
+template <typename KT>
+__device__ __forceinline__ float entry_score(const u32x4 (&buf)[ScanTraits<KT>::J],
+                                             const u32x4 (&qf)[ScanTraits<KT>::J], float wl, int lane) {
+    using TR = ScanTraits<KT>;
+    float v[TR::J];
+#pragma unroll
+    for (int j = 0; j < TR::J; ++j) v[j] = dot16B(qf[j], buf[j], 0.f, KT());
+    // transposed butterfly over the G lanes of a head: after it, lane L holds the
+    // complete dot of load slot j = L % G
+#pragma unroll
+    for (int st = 1; st < TR::G; st <<= 1) {
+        const int m = TR::G / (2 * st);
+        const int len = TR::J / (2 * st);
+        const bool up = (lane & m) != 0;
+#pragma unroll
+        for (int x = 0; x < len; ++x) {
+            const float keep = up ? v[x + len] : v[x];
+            const float send = up ? v[x] : v[x + len];
+            v[x] = keep + __shfl_xor(send, m);
+        }
+    }
+    float r = fmaxf(v[0], 0.f) * wl;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) r += __shfl_xor(r, m);
+    return r;
+}
+
+template <typename KT, int EPW>
+__global__ void __launch_bounds__(256)
+index_scan_kernel(const KT *__restrict__ qI, const float *__restrict__ w, const KT *__restrict__ kI,
+                  const int32_t *__restrict__ q_seq, const int64_t *__restrict__ q_pos, int B,
+                  int64_t N, int ratio, float *__restrict__ scores)
+{
+    using TR = ScanTraits<KT>;
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int t = blockIdx.y;
+    const int64_t e0 = ((int64_t)blockIdx.x * 4 + wv) * EPW;
+    if (e0 >= N) return;
+    const int64_t e1 = (e0 + EPW < N) ? e0 + EPW : N;
+
+    const int s = q_seq[t];
+    int64_t nvis = q_pos[t] / ratio;
+    if (nvis > N) nvis = N;
+    if (nvis < 0 || s < 0 || s >= B) nvis = 0;
+    const int64_t ev = (e1 < nvis) ? e1 : nvis;  // [e0, ev) are read, [ev, e1) masked
+
+    float my_score = -INFINITY;
+    if (e0 < ev) {
+        u32x4 qf[TR::J];
+        const u32x4 *qp = reinterpret_cast<const u32x4 *>(qI + (int64_t)t * 8192);
+#pragma unroll
+        for (int j = 0; j < TR::J; ++j) qf[j] = qp[j * 64 + lane];
+        const float wl = w[(int64_t)t * 64 + (lane % TR::G) * TR::HPL + lane / TR::G];
+
+        const u32x4 *kb = reinterpret_cast<const u32x4 *>(kI + ((int64_t)s * N) * 8192);
+        u32x4 bufA[TR::J], bufB[TR::J];
+        load_entry<KT>(bufA, kb + e0 * (8192 / TR::VEC), lane);
+        for (int64_t e = e0; e < ev; e += 2) {
+            if (e + 1 < ev) load_entry<KT>(bufB, kb + (e + 1) * (8192 / TR::VEC), lane);
+            float sc = entry_score<KT>(bufA, qf, wl, lane);
+            if (lane == (int)(e - e0)) my_score = sc;
+            if (e + 2 < ev) load_entry<KT>(bufA, kb + (e + 2) * (8192 / TR::VEC), lane);
+            if (e + 1 < ev) {
+                sc = entry_score<KT>(bufB, qf, wl, lane);
+                if (lane == (int)(e + 1 - e0)) my_score = sc;
+            }
+        }
+    }
+    if (lane < (int)(e1 - e0)) scores[(int64_t)t * N + e0 + lane] = my_score;
+}
+
+// ---- MXFP4 operands (the FP4 indexer path): value = code * 2^(scale - 127) ----------
+// Magnitudes x2 of the E2M1 codes 0..7 ({0, .5, 1, 1.5, 2, 3, 4, 6} * 2), one nibble each.
+__device__ __forceinline__ float e2m1_x2(uint32_t nib) {
+    const float m = (float)((0xC8643210u >> (4 * (nib & 7u))) & 15u);
+    return (nib & 8u) ? -m : m;
+}
+
+// One wave per entry; lane h owns head h. Block dots of 32 E2M1 products are exact in
+// fp32; each is scaled by 2^(sq + sk - 254) and the four blocks are summed in fp32.
+__global__ void __launch_bounds__(256)
+index_mxfp4_valu_kernel(const uint8_t *__restrict__ qI, const uint8_t *__restrict__ qS,
+                        const float *__restrict__ w, const uint8_t *__restrict__ kI,
+                        const uint8_t *__restrict__ kS, const int32_t *__restrict__ q_seq,
+                        const int64_t *__restrict__ q_pos, int B, int64_t N, int ratio,
+                        float *__restrict__ scores)
+{
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.y;
+    const int64_t e = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (e >= N) return;
+    const int s = q_seq[t];
+    int64_t nvis = q_pos[t] / ratio;
+    if (nvis > N) nvis = N;
+    if (nvis < 0 || s < 0 || s >= B) nvis = 0;
+    float sc = -INFINITY;
+    if (e < nvis) {
+        const uint4 *qp = reinterpret_cast<const uint4 *>(qI + ((int64_t)t * 64 + lane) * 64);
+        const uint4 *kp = reinterpret_cast<const uint4 *>(kI + (((int64_t)s * N + e) * 64 + lane) * 64);
+        const uint32_t qsc = *reinterpret_cast<const uint32_t *>(qS + ((int64_t)t * 64 + lane) * 4);
+        const uint32_t ksc = *reinterpret_cast<const uint32_t *>(kS + (((int64_t)s * N + e) * 64 + lane) * 4);
+        float dot = 0.f;
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) {
+            const uint4 qa = qp[blk], ka = kp[blk];
+            const uint32_t qw[4] = {qa.x, qa.y, qa.z, qa.w}, kw[4] = {ka.x, ka.y, ka.z, ka.w};
+            float part = 0.f;
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+#pragma unroll
+                for (int nb = 0; nb < 8; ++nb)
+                    part = fmaf(e2m1_x2((qw[x] >> (4 * nb)) & 15u), e2m1_x2((kw[x] >> (4 * nb)) & 15u), part);
+            const int ex = (int)((qsc >> (8 * blk)) & 255u) + (int)((ksc >> (8 * blk)) & 255u) - 254 - 2;
+            dot += ldexpf(part, ex);  // the -2 undoes the two x2 magnitudes
+        }
+        float r = fmaxf(dot, 0.f) * w[(int64_t)t * 64 + lane];
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) r += __shfl_xor(r, m);
+        sc = r;
+    }
+    if (lane == 0) scores[(int64_t)t * N + e] = sc;
+}
+
+}  // namespace
+
+int launch_index_scores(const void *qI, const uint8_t *qs, const float *w, const void *kI,
+                        const uint8_t *ks, const int32_t *q_seq, const int64_t *q_pos, int T,
+                        int B, int64_t N, int ratio, csa_dtype dt, float *scores, hipStream_t st)
+{
+    if (T == 0 || N == 0) return CSA_OK;
+    if (dt == CSA_MXFP4) {
+        dim3 grid((unsigned)((N + 3) / 4), (unsigned)T);
+        hipLaunchKernelGGL(index_mxfp4_valu_kernel, grid, dim3(256), 0, st, (const uint8_t *)qI, qs,
+                           w, (const uint8_t *)kI, ks, q_seq, q_pos, B, N, ratio, scores);
+        return check_launch("index_mxfp4_valu_kernel");
+    }
+    constexpr int EPW = 64;
+    dim3 grid((unsigned)((N + 4 * EPW - 1) / (4 * EPW)), (unsigned)T);
+    if (dt == CSA_BF16) {
+        hipLaunchKernelGGL((index_scan_kernel<bf16_t, EPW>), grid, dim3(256), 0, st,
+                           (const bf16_t *)qI, w, (const bf16_t *)kI, q_seq, q_pos, B, N, ratio, scores);
+    } else {
+        hipLaunchKernelGGL((index_scan_kernel<float, EPW>), grid, dim3(256), 0, st,
+                           (const float *)qI, w, (const float *)kI, q_seq, q_pos, B, N, ratio, scores);
+    }
+    return check_launch("index_scan_kernel");
+}
+
+}  // namespace csa

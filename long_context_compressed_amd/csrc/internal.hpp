@@ -1,0 +1,53 @@
+// Launchers behind the C ABI (arguments already validated by api.cpp).
+#pragma once
+
+#include "common.hpp"
+
+namespace csa {
+
+int launch_compress(const void *Ca, const void *Cb, const void *Za, const void *Zb,
+                    const void *cCb, const void *cZb, const float *bias, int B, int64_t n, int c,
+                    int ratio, int overlap, csa_dtype dt, void *out, int64_t out_bstride,
+                    hipStream_t st);
+
+int launch_index_scores(const void *qI, const uint8_t *qs, const float *w, const void *kI,
+                        const uint8_t *ks, const int32_t *q_seq, const int64_t *q_pos, int T,
+                        int B, int64_t N, int ratio, csa_dtype dt, float *scores, hipStream_t st);
+
+size_t topk_workspace_bytes(int T, int64_t N, int k);
+int launch_topk(const float *scores, int T, int64_t N, int k, int32_t *idx, float *vals,
+                void *ws, size_t ws_bytes, hipStream_t st);
+
+// Rows of one query: the first `k` slots come from topk_idxs (sparse mode) or from
+// the visible summaries 0..nvis-1 (dense mode, k < 0 selects it with ratio = -k),
+// then the SWA window rows.
+struct AttnArgs {
+    const void *q;
+    const void *kv;
+    const float *sink;
+    const int32_t *idx;
+    int k;          // sparse: slots per query from idx
+    int ratio;      // dense: visibility ratio (0 = sparse mode)
+    float scale;
+    const void *swa;
+    const int64_t *swa_pos0;
+    int swa_rows;
+    int window;
+    const int32_t *q_seq;
+    const int64_t *q_pos;
+    const float *rope_cs;
+    int rope_dim;
+    int T, B;
+    int64_t N;
+    int H, D;
+    csa_dtype dt;
+    void *out;
+    float *lse;
+    void *ws;
+    size_t ws_bytes;
+};
+
+size_t attn_workspace_bytes(int T, int H, int D, int64_t max_rows);
+int launch_attn(const AttnArgs &a, hipStream_t st);
+
+}  // namespace csa

@@ -1,0 +1,108 @@
+"""The C ABI library loads, exports every symbol include/csa.h declares, and rejects bad
+arguments synchronously. Every call here either fails validation or has nothing to
+launch (T = 0, N = 0, no complete block): none reaches a kernel, so the fake pointer
+values are never dereferenced."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"\b(csa_\w+|hca_attn)\s*\(", src)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import long_context_compressed_amd as csa
+    if not os.path.exists(csa.LIB_PATH):
+        from long_context_compressed_amd import build
+        build.build()
+    return csa.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    import long_context_compressed_amd as csa
+    names = _declared()
+    assert set(names) == set(csa.EXPORTS), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    assert L.csa_status_str(0) == b"CSA_OK"
+    assert L.csa_status_str(2) == b"CSA_EUNSUPPORTED"
+    assert L.csa_status_str(99) == b"CSA_UNKNOWN"
+
+
+def _compress(L, **kw):
+    a = dict(Ca=1, Cb=1, Za=1, Zb=1, cCb=None, cZb=None, bias=None, B=1, n=16, c=8, ratio=4, overlap=1,
+             dt=0, out=1, bstride=0)
+    a.update(kw)
+    return L.csa_compress(a["Ca"], a["Cb"], a["Za"], a["Zb"], a["cCb"], a["cZb"], a["bias"], a["B"], a["n"],
+                          a["c"], a["ratio"], a["overlap"], a["dt"], a["out"], a["bstride"], None)
+
+
+def test_compress_validation(L):
+    assert _compress(L, ratio=8) == 2          # valid but not built
+    assert _compress(L, ratio=4, overlap=0) == 2
+    assert _compress(L, c=0) == 1
+    assert _compress(L, dt=2) == 1             # MXFP4 is not a compressor dtype
+    assert _compress(L, Cb=None) == 1
+    assert _compress(L, cCb=1, cZb=None) == 1
+    assert _compress(L, ratio=128, overlap=0, cCb=1, cZb=1) == 1
+    assert _compress(L, bstride=5) == 1
+    assert b"bstride" in L.csa_last_error()
+    assert _compress(L, n=3) == 0               # no complete block: nothing to launch
+
+
+def test_index_scores_validation(L):
+    f = lambda **kw: L.csa_index_scores(*[kw.get(k, v) for k, v in (
+        ("q", 1), ("qs", None), ("w", 1), ("k", 1), ("ks", None), ("qseq", 1), ("qpos", 1), ("T", 2), ("B", 1),
+        ("N", 8), ("H", 64), ("D", 128), ("ratio", 4), ("dt", 1), ("scores", 1), ("st", None))])
+    assert f(H=32) == 2
+    assert f(D=100, dt=2) == 1
+    assert f(D=96, dt=2) == 2
+    assert f(dt=2) == 1                         # MXFP4 without scales
+    assert f(w=None) == 1
+    assert f(ratio=0) == 1
+    assert f(T=0) == 0 and f(N=0) == 0
+
+
+def test_topk_validation(L):
+    assert L.csa_topk(1, 4, 100, 0, 1, None, None, 0, None) == 1
+    assert L.csa_topk(1, 4, 100, 5000, 1, None, None, 0, None) == 2
+    assert L.csa_topk(1, 4, 100, 10, None, None, None, 0, None) == 1
+    assert L.csa_topk(1, 0, 100, 10, None, None, None, 0, None) == 0
+
+
+def test_attn_validation(L):
+    def f(**kw):
+        a = dict(q=1, kv=1, sink=1, idx=1, k=4, scale=0.1, swa=1, p0=1, rows=8, win=128, qseq=1, qpos=1,
+                 cs=None, R=0, T=2, B=1, N=8, H=8, D=128, dt=0, out=1, lse=None, ws=None, wsb=0)
+        a.update(kw)
+        return L.csa_sparse_attn(a["q"], a["kv"], a["sink"], a["idx"], a["k"], C.c_float(a["scale"]), a["swa"],
+                                 a["p0"], a["rows"], a["win"], a["qseq"], a["qpos"], a["cs"], a["R"], a["T"],
+                                 a["B"], a["N"], a["H"], a["D"], a["dt"], a["out"], a["lse"], a["ws"], a["wsb"],
+                                 None)
+    assert f(D=100) == 2
+    assert f(D=2048) == 2
+    assert f(cs=1, R=3) == 1
+    assert f(cs=1, R=256) == 1
+    assert f(sink=None) == 1
+    assert f(idx=None) == 1
+    assert f(p0=None) == 1
+    assert f(scale=float("nan")) == 1
+    assert f(k=-1) == 1
+    assert f(dt=2) == 1
+    assert f(T=0) == 0
+    g = lambda **kw: L.hca_attn(1, 1, 1, kw.get("ratio", 128), C.c_float(0.1), 1, 1, 8, 128, 1, 1, None, 0,
+                                2, 1, 8, 8, 128, 0, 1, None, None, 0, None)
+    assert g(ratio=0) == 1
