@@ -1,0 +1,275 @@
+"""Benchmark of the CSA / HCA decode hot path on one MI355X.
+
+Workload (default): Pro-shape decode at 1M context. B = 4 independent sequences, each
+with n = 2^20 cached tokens, issue one query at t = n. One step is one CSA layer plus
+one HCA layer of that decode:
+  CSA: csa_compress (the block [n-4, n) completes: new KV entry and new index-key entry)
+       -> csa_index_scores over all 262,144 entries (64 heads x 128, bf16 per-head keys)
+       -> csa_topk (k = 1,024) -> csa_sparse_attn (128 heads x 512, 1,024 + 128 SWA rows)
+  HCA: csa_compress (ratio 128: summary 8,191 completes) -> hca_attn over 8,192 summaries
+       + 128 SWA rows.
+Inputs are seeded synthetic tensors resident in HBM before the timed region.
+
+Prints one JSON line: decode queries/s (value), the index-scan kernel's achieved HBM
+bandwidth against MI355X's 8 TB/s (roofline), and the CPU oracle's rate on a bounded
+sample of the same step (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode queries/s + indexer GB/s (% HBM roofline), Pro shape, 1M ctx, 1 GPU"
+HBM_PEAK_GBS = 8000.0
+PMC_FILE = os.path.join(ROOT, "profiles", "index_scan_pro_decode_1m_pmc.json")
+SCAN_SRC = os.path.join(ROOT, "long_context_compressed_amd", "csrc", "indexer.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-entries", type=int, default=4096,
+                    help="index entries per query in the oracle's bounded sample")
+    return ap.parse_args()
+
+
+def scan_source_hash() -> str:
+    return hashlib.sha256(open(SCAN_SRC, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profile(alg_bytes):
+    """HBM bytes per index-scan launch from the committed rocprofv3 counter summary,
+    or None when it is missing or was taken on a different kernel source."""
+    try:
+        d = json.load(open(PMC_FILE))
+    except (OSError, ValueError):
+        return None
+    if d.get("indexer_hip_sha256_16") != scan_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {a.gpus}); "
+              "the multi-GPU sharding is a design, not a measured path", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import long_context_compressed_amd as csa
+    import workloads as W
+
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    csa.lib()
+    cfg = W.PRO
+    B, T, n, N, D, H, k = cfg.B, cfg.T, cfg.n, cfg.N, cfg.c, cfg.H, cfg.k
+    s = cfg.seed
+    NH = W.HCA.N  # 8192 summaries
+    bf = torch.bfloat16
+
+    # ---- inputs (HBM-resident) ------------------------------------------------------
+    inp = W.decode_inputs(cfg, dev)
+    kv, k_I = inp["kv"], inp["k_I"]
+    summ = W.normal((B, NH, D), W.HCA.seed, "summ", dtype=bf, device=dev)
+    sink_h = W.normal((H,), W.HCA.seed, "sink", device=dev)
+    # the block [n-4, n): a- and b-branch content/logits, plus the carry (block n-8..n-5)
+    blk = {nm: W.normal((B, 4, D), s, "new_" + nm, dtype=bf, device=dev) for nm in ("Ca", "Cb", "Za", "Zb")}
+    carry = {nm: W.normal((B, 4, D), s, "carry_" + nm, dtype=bf, device=dev) for nm in ("C", "Z")}
+    iblk = {nm: W.normal((B, 4, 8192), s, "inew_" + nm, dtype=bf, device=dev) for nm in ("Ca", "Cb", "Za", "Zb")}
+    icarry = {nm: W.normal((B, 4, 8192), s, "icarry_" + nm, dtype=bf, device=dev) for nm in ("C", "Z")}
+    hblk = {nm: W.normal((B, 128, D), W.HCA.seed, "hnew_" + nm, dtype=bf, device=dev) for nm in ("C", "Z")}
+
+    kv_new = kv[:, N - 1:N, :]
+    kI_new = k_I.view(B, N, 8192)[:, N - 1:N, :]
+    summ_new = summ[:, NH - 1:NH, :]
+    scores = torch.empty((T, N), dtype=torch.float32, device=dev)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    topk_ws = torch.empty(max(1, csa.topk_workspace_bytes(T, N, k)), dtype=torch.uint8, device=dev)
+    attn_ws = torch.empty(max(1, csa.attn_workspace_bytes(T, H, D, k + cfg.window)), dtype=torch.uint8, device=dev)
+    hca_ws = torch.empty(max(1, csa.attn_workspace_bytes(T, H, D, NH + cfg.window)), dtype=torch.uint8, device=dev)
+    out = torch.empty((T, H, D), dtype=bf, device=dev)
+    out_h = torch.empty((T, H, D), dtype=bf, device=dev)
+    lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    lse_h = torch.empty((T, H), dtype=torch.float32, device=dev)
+    scale = cfg.scale
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        csa.compress(blk["Ca"], blk["Za"], blk["Cb"], blk["Zb"], carry["C"], carry["Z"], ratio=4, overlap=1,
+                     out=kv_new)
+        csa.compress(iblk["Ca"], iblk["Za"], iblk["Cb"], iblk["Zb"], icarry["C"], icarry["Z"], ratio=4,
+                     overlap=1, out=kI_new)
+        if ev is not None:
+            ev[0].record()
+        csa.index_scores(inp["q_I"], inp["w"], k_I, inp["q_seq"], inp["q_pos"], scores=scores)
+        if ev is not None:
+            ev[1].record()
+        csa.topk(scores, k, idx=idx, workspace=topk_ws)
+        csa.sparse_attn(inp["q"], kv, inp["sink"], idx, scale, inp["swa"], inp["swa_pos0"], cfg.window,
+                        inp["q_seq"], inp["q_pos"], inp["rope_cs"], cfg.rope_dim, out=out, lse=lse,
+                        workspace=attn_ws)
+        csa.compress(hblk["C"], hblk["Z"], ratio=128, overlap=0, out=summ_new)
+        csa.hca_attn(inp["q"], summ, sink_h, 128, scale, inp["swa"], inp["swa_pos0"], cfg.window,
+                     inp["q_seq"], inp["q_pos"], inp["rope_cs"], cfg.rope_dim, out=out_h, lse=lse_h,
+                     workspace=hca_ws)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    scan_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+    scan_avg_s = float(np.mean(scan_ms)) / 1e3
+
+    # ---- per-stage times (separate, untimed-for-value pass) ---------------------------
+    def timed(fn, reps=10):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    stages = {
+        "compress_csa_kv_and_index_key": timed(lambda: (
+            csa.compress(blk["Ca"], blk["Za"], blk["Cb"], blk["Zb"], carry["C"], carry["Z"], out=kv_new),
+            csa.compress(iblk["Ca"], iblk["Za"], iblk["Cb"], iblk["Zb"], icarry["C"], icarry["Z"], out=kI_new))),
+        "index_scores": timed(lambda: csa.index_scores(inp["q_I"], inp["w"], k_I, inp["q_seq"], inp["q_pos"],
+                                                       scores=scores)),
+        "topk": timed(lambda: csa.topk(scores, k, idx=idx, workspace=topk_ws)),
+        "sparse_attn": timed(lambda: csa.sparse_attn(inp["q"], kv, inp["sink"], idx, scale, inp["swa"],
+                                                     inp["swa_pos0"], cfg.window, inp["q_seq"], inp["q_pos"],
+                                                     inp["rope_cs"], cfg.rope_dim, out=out, lse=lse,
+                                                     workspace=attn_ws)),
+        "compress_hca": timed(lambda: csa.compress(hblk["C"], hblk["Z"], ratio=128, overlap=0, out=summ_new)),
+        "hca_attn": timed(lambda: csa.hca_attn(inp["q"], summ, sink_h, 128, scale, inp["swa"], inp["swa_pos0"],
+                                               cfg.window, inp["q_seq"], inp["q_pos"], inp["rope_cs"],
+                                               cfg.rope_dim, out=out_h, lse=lse_h, workspace=hca_ws)),
+    }
+
+    # algorithmic bytes of one index-scan launch: every visible key block once
+    # (64 x 128 bf16 = 16 KiB per entry per sequence) + q_I + w + the fp32 scores
+    alg_bytes = B * N * 64 * 128 * 2 + T * 64 * 128 * 2 + T * 64 * 4 + T * N * 4
+    achieved = alg_bytes / scan_avg_s / 1e9
+    traffic = traffic_from_profile(alg_bytes)
+
+    res = {
+        "metric": METRIC,
+        "value": round(B * a.steps / elapsed, 2),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(elapsed / a.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), bf16)",
+        "config": {
+            "workload": "pro_decode_1m: one CSA layer + one HCA layer decode step, B=4 sequences x 1 query at "
+                        "t=2^20; 262,144 entries x 64 heads x 128 bf16 index keys per sequence, top-k 1,024, "
+                        "128 heads x 512 shared KV, SWA 128, 8,192 HCA summaries",
+            "batch": B, "context": n, "index_entries": N, "topk": k, "heads": H, "head_dim": D,
+        },
+        "roofline": {
+            "kernel": "index_scan_kernel (csa_index_scores, bf16 per-head keys)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": alg_bytes,
+            "avg_launch_ms": round(scan_avg_s * 1e3, 4),
+        },
+        "stages_ms": {kk: round(v, 4) for kk, v in stages.items()},
+    }
+    if not a.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(a, inp, kv, k_I, summ, sink_h, scores, idx, cfg, NH)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(a, inp, kv, k_I, summ, sink_h, scores, idx, cfg, NH):
+    """The fp64 oracle on a bounded sample of the same decode step, scaled to queries/s.
+
+    Sample: the index scores of all B queries over `cpu_entries` randomly chosen entries
+    (scaled by N / cpu_entries), top-k over the full 262,144 scores of every query, the
+    sparse attention of every query (1,152 rows x 128 heads), and the HCA attention of
+    one query (8,320 rows x 128 heads, scaled by B). Only the oracle's own calls are
+    timed, not the widening of the inputs to fp64.
+    """
+    import numpy as np
+    import torch
+
+    import oracle
+    import workloads as W
+
+    oracle.lib()
+    B, T, N = cfg.B, cfg.T, cfg.N
+    S = min(a.cpu_entries, N)
+    f64 = lambda x: x.detach().to("cpu", torch.float64).numpy()
+    npy = lambda x: x.detach().cpu().numpy()
+    ids = np.sort(W.distinct_sample(S, N, cfg.seed, "cpu_sample"))
+    k_s = f64(k_I.index_select(1, torch.from_numpy(ids).to(k_I.device)))
+    qI, w, qs, qp = f64(inp["q_I"]), f64(inp["w"]), npy(inp["q_seq"]), npy(inp["q_pos"])
+    q, sink, swa, p0, cs = f64(inp["q"]), f64(inp["sink"]), f64(inp["swa"]), npy(inp["swa_pos0"]), f64(inp["rope_cs"])
+    # the rows each query's sparse attention reads, gathered (query t reads sequence t)
+    idx_h = npy(idx).astype(np.int64)
+    kv_c = np.stack([f64(kv[t].index_select(0, torch.from_numpy(np.maximum(idx_h[t], 0)).to(kv.device)))
+                     for t in range(T)])
+    idx_c = np.where(idx_h >= 0, np.arange(cfg.k)[None, :], -1).astype(np.int32)
+    summ1, sinkh = f64(summ[:1]), f64(sink_h)
+    sc = scores.double().cpu().numpy()
+
+    t_idx = _time_call(lambda: oracle.index_scores(qI, w, k_s, qs, qp, entry_ids=ids)) * (N / S)
+    t_topk = _time_call(lambda: oracle.topk(sc, cfg.k))
+    t_attn = _time_call(lambda: oracle.sparse_attn(q, kv_c, sink, idx_c, cfg.scale, swa, p0, cfg.window, qs, qp,
+                                                   cs, cfg.rope_dim))
+    t_hca = _time_call(lambda: oracle.hca_attn(q[:1], summ1, sinkh, 128, cfg.scale, swa[:1], p0[:1], cfg.window,
+                                               np.zeros(1, np.int32), qp[:1], cs[:1], cfg.rope_dim)) * B
+    total = t_idx + t_topk + t_attn + t_hca
+    return {
+        "value": round(B / total, 6),
+        "unit": "queries/s",
+        "cores": oracle.threads(),
+        "kind": "oracle",
+        "sample": f"index scores of {B} queries over {S} of {N} entries (x{N / S:.0f}), full top-k, full sparse "
+                  f"attention, HCA attention of 1 of {B} queries (x{B}); oracle seconds (scaled): index "
+                  f"{t_idx:.2f}, topk {t_topk:.2f}, attn {t_attn:.2f}, hca {t_hca:.2f}; 'cores' is the OpenMP "
+                  f"thread count (attention steps use at most one thread per query)",
+    }
+
+
+def _time_call(fn):
+    """Wall seconds of one oracle call (inputs already widened to fp64 on the host)."""
+    t0 = time.perf_counter()
+    fn()
+    return time.perf_counter() - t0
+
+
+if __name__ == "__main__":
+    main()

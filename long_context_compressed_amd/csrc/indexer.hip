@@ -55,6 +55,55 @@ __device__ __forceinline__ void load_entry(u32x4 (&buf)[ScanTraits<KT>::J], cons
     for (int j = 0; j < ScanTraits<KT>::J; ++j) buf[j] = __builtin_nontemporal_load(p + j * 64 + lane);
 }
 
+// ---- cross-lane exchange ------------------------------------------------------------
+// DPP lane permutations inside a row of 16 lanes (no LDS traffic). Each is an
+// involution; row_mirror pairs lanes differing in bit 3, half_mirror in bit 2 (with
+// bit 3 equal), quad reverse in bit 1 (bits 3..2 equal), quad swap in bit 0.
+enum : int { kRowMirror = 0x140, kRowHalfMirror = 0x141, kQuadRev = 0x1B, kQuadSwap = 0xB1 };
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// partner of a lane for the butterfly step whose role bit is ROLE (8, 4, 2, 1: DPP
+// inside a row; 16, 32: across rows)
+template <int ROLE>
+__device__ __forceinline__ float partner(float x) {
+    if constexpr (ROLE == 8) return dpp<kRowMirror>(x);
+    else if constexpr (ROLE == 4) return dpp<kRowHalfMirror>(x);
+    else if constexpr (ROLE == 2) return dpp<kQuadRev>(x);
+    else if constexpr (ROLE == 1) return dpp<kQuadSwap>(x);
+    else return __shfl_xor(x, ROLE);
+}
+
+// Transposed butterfly: v[0..2*LEN) of every lane in a group of lanes that differ in the
+// role bits ROLE, ROLE/2, ..., 1. Each step keeps the half selected by the lane's role
+// bit and adds the partner's copy of the same half, so after log2(2*LEN) steps lane L
+// holds the group-sum of element j = (L's role bits read as a binary number).
+template <int ROLE, int LEN, int J>
+__device__ __forceinline__ void tbutterfly(float (&v)[J], int lane) {
+    const bool up = (lane & ROLE) != 0;
+#pragma unroll
+    for (int x = 0; x < LEN; ++x) {
+        const float keep = up ? v[x + LEN] : v[x];
+        const float send = up ? v[x] : v[x + LEN];
+        v[x] = keep + partner<ROLE>(send);
+    }
+    if constexpr (ROLE > 1) tbutterfly<ROLE / 2, LEN / 2, J>(v, lane);
+}
+
+// sum over all 64 lanes (every lane gets the total)
+__device__ __forceinline__ float wave_sum(float r) {
+    r += dpp<kRowMirror>(r);
+    r += dpp<kRowHalfMirror>(r);
+    r += dpp<kQuadRev>(r);
+    r += dpp<kQuadSwap>(r);
+    r += __shfl_xor(r, 16);
+    r += __shfl_xor(r, 32);
+    return r;
+}
+
 // full score of the entry held in `buf` (wave-uniform result)
 template <typename KT>
 __device__ __forceinline__ float entry_score(const u32x4 (&buf)[ScanTraits<KT>::J],
@@ -63,24 +112,9 @@ __device__ __forceinline__ float entry_score(const u32x4 (&buf)[ScanTraits<KT>::
     float v[TR::J];
 #pragma unroll
     for (int j = 0; j < TR::J; ++j) v[j] = dot16B(qf[j], buf[j], 0.f, KT());
-    // transposed butterfly over the G lanes of a head: after it, lane L holds the
-    // complete dot of load slot j = L % G
-#pragma unroll
-    for (int st = 1; st < TR::G; st <<= 1) {
-        const int m = TR::G / (2 * st);
-        const int len = TR::J / (2 * st);
-        const bool up = (lane & m) != 0;
-#pragma unroll
-        for (int x = 0; x < len; ++x) {
-            const float keep = up ? v[x + len] : v[x];
-            const float send = up ? v[x] : v[x + len];
-            v[x] = keep + __shfl_xor(send, m);
-        }
-    }
-    float r = fmaxf(v[0], 0.f) * wl;
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) r += __shfl_xor(r, m);
-    return r;
+    // after it, lane L holds the complete dot of load slot j = L % G
+    tbutterfly<TR::G / 2, TR::J / 2, TR::J>(v, lane);
+    return wave_sum(fmaxf(v[0], 0.f) * wl);
 }
 
 template <typename KT, int EPW>
@@ -90,6 +124,7 @@ index_scan_kernel(const KT *__restrict__ qI, const float *__restrict__ w, const 
                   int64_t N, int ratio, float *__restrict__ scores)
 {
     using TR = ScanTraits<KT>;
+    constexpr int EU = 8192 / TR::VEC;  // 16-byte units per entry
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
     const int t = blockIdx.y;
@@ -113,16 +148,27 @@ index_scan_kernel(const KT *__restrict__ qI, const float *__restrict__ w, const 
 
         const u32x4 *kb = reinterpret_cast<const u32x4 *>(kI + ((int64_t)s * N) * 8192);
         u32x4 bufA[TR::J], bufB[TR::J];
-        load_entry<KT>(bufA, kb + e0 * (8192 / TR::VEC), lane);
-        for (int64_t e = e0; e < ev; e += 2) {
-            if (e + 1 < ev) load_entry<KT>(bufB, kb + (e + 1) * (8192 / TR::VEC), lane);
+        load_entry<KT>(bufA, kb + e0 * EU, lane);
+        int64_t e = e0;
+        // steady state: both loads of an iteration are unconditional, so the wait before
+        // scoring A leaves B's loads in flight
+        for (; e + 2 < ev; e += 2) {
+            load_entry<KT>(bufB, kb + (e + 1) * EU, lane);
             float sc = entry_score<KT>(bufA, qf, wl, lane);
             if (lane == (int)(e - e0)) my_score = sc;
-            if (e + 2 < ev) load_entry<KT>(bufA, kb + (e + 2) * (8192 / TR::VEC), lane);
-            if (e + 1 < ev) {
-                sc = entry_score<KT>(bufB, qf, wl, lane);
-                if (lane == (int)(e + 1 - e0)) my_score = sc;
-            }
+            load_entry<KT>(bufA, kb + (e + 2) * EU, lane);
+            sc = entry_score<KT>(bufB, qf, wl, lane);
+            if (lane == (int)(e + 1 - e0)) my_score = sc;
+        }
+        if (e + 1 < ev) {
+            load_entry<KT>(bufB, kb + (e + 1) * EU, lane);
+            float sc = entry_score<KT>(bufA, qf, wl, lane);
+            if (lane == (int)(e - e0)) my_score = sc;
+            sc = entry_score<KT>(bufB, qf, wl, lane);
+            if (lane == (int)(e + 1 - e0)) my_score = sc;
+        } else {
+            const float sc = entry_score<KT>(bufA, qf, wl, lane);
+            if (lane == (int)(e - e0)) my_score = sc;
         }
     }
     if (lane < (int)(e1 - e0)) scores[(int64_t)t * N + e0 + lane] = my_score;
