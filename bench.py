@@ -38,8 +38,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-entries", type=int, default=4096,
+    ap.add_argument("--cpu-entries", type=int, default=16384,
                     help="index entries per query in the oracle's bounded sample")
+    ap.add_argument("--profile-copy", action="store_true",
+                    help="before the timed region, run a plain 1 GiB device copy three times (a kernel of "
+                         "known traffic that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
     return ap.parse_args()
 
 
@@ -130,6 +133,13 @@ def main():
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
+    if a.profile_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
     torch.cuda.synchronize()

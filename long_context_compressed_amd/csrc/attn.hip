@@ -447,34 +447,56 @@ attn_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, co
     }
 }
 
-// log-sum-exp merge of split partials + sink + inverse RoPE; one block per (query, head)
+// log-sum-exp merge of split partials + sink + inverse RoPE; one block per (query, head).
+// The per-split weights 2^(m_s - M) are formed once in LDS; every thread then streams
+// its two output dims over all splits with independent loads.
 template <typename ET>
 __global__ void __launch_bounds__(256)
 attn_merge_kernel(const float *__restrict__ part, const float *__restrict__ sink, int nsplit,
                   const float *__restrict__ rope_cs, int R, int T, int H, int D,
                   ET *__restrict__ out, float *__restrict__ lse)
 {
+    __shared__ float fs[256];
+    __shared__ float red[2];
     const int64_t unit = blockIdx.x;
     const int t = (int)(unit / H), g = (int)(unit % H);
     const float *pml = part;
     const float *pacc = part + (int64_t)T * nsplit * H * 2;
     const float sk = sink[g] * kLog2e;
-    float M = sk;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pml[(((int64_t)t * nsplit + s) * H + g) * 2]);
-    const float mu = (M == -INFINITY) ? 0.f : M;
-    float L = exp2f(sk - mu);
-    for (int s = 0; s < nsplit; ++s) {
-        const int64_t o = (((int64_t)t * nsplit + s) * H + g) * 2;
-        L += pml[o + 1] * exp2f(pml[o] - mu);
+    if (threadIdx.x < 64) {
+        // one wavefront forms the global max, the denominator and the split weights
+        const int lane = threadIdx.x;
+        float M = sk;
+        for (int s2 = lane; s2 < nsplit; s2 += 64) M = fmaxf(M, pml[(((int64_t)t * nsplit + s2) * H + g) * 2]);
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+        const float mu = (M == -INFINITY) ? 0.f : M;
+        float L = 0.f;
+        for (int s2 = lane; s2 < nsplit; s2 += 64) {
+            const int64_t o = (((int64_t)t * nsplit + s2) * H + g) * 2;
+            const float f = exp2f(pml[o] - mu);
+            fs[s2] = f;
+            L += pml[o + 1] * f;
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
+        L += exp2f(sk - mu);
+        if (lane == 0) {
+            red[0] = mu;
+            red[1] = L;
+        }
     }
+    __syncthreads();
+    const float mu = red[0], L = red[1];
     const float inv = L > 0.f ? 1.f / L : 0.f;
     for (int d0 = 2 * threadIdx.x; d0 < D; d0 += 2 * blockDim.x) {
         float x0 = 0.f, x1 = 0.f;
-        for (int s = 0; s < nsplit; ++s) {
-            const int64_t ps = ((int64_t)t * nsplit + s) * H + g;
-            const float f = exp2f(pml[ps * 2] - mu);
-            x0 += pacc[ps * D + d0] * f;
-            x1 += pacc[ps * D + d0 + 1] * f;
+        const float *pp = pacc + (((int64_t)t * nsplit) * H + g) * D + d0;
+#pragma unroll 8
+        for (int s2 = 0; s2 < nsplit; ++s2) {
+            const float2 v = *reinterpret_cast<const float2 *>(pp + (int64_t)s2 * H * D);
+            x0 = fmaf(v.x, fs[s2], x0);
+            x1 = fmaf(v.y, fs[s2], x1);
         }
         x0 *= inv;
         x1 *= inv;
@@ -492,13 +514,16 @@ attn_merge_kernel(const float *__restrict__ part, const float *__restrict__ sink
     if (lse != nullptr && threadIdx.x == 0) lse[(int64_t)t * H + g] = L > 0.f ? (mu + log2f(L)) * kLn2 : -INFINITY;
 }
 
+// Row splits per (query, head group): enough workgroups to cover the CUs once, at least
+// four 32-row tiles per split, at most 256 splits (the merge keeps one weight per split).
 int mfma_splits(int T, int H, int64_t max_rows) {
     const int64_t base = (int64_t)T * (H / MHG);
     const int64_t tiles = (max_rows + MTR - 1) / MTR;
-    if (base >= 512 || tiles <= 2) return 1;
-    int64_t ns = (512 + base - 1) / base;
-    const int64_t cap = (tiles + 1) / 2;  // at least two tiles per split
+    if (base >= 256 || tiles < 8) return 1;
+    int64_t ns = (256 + base - 1) / base;
+    const int64_t cap = tiles / 4;
     if (ns > cap) ns = cap;
+    if (ns > 256) ns = 256;
     return ns < 1 ? 1 : (int)ns;
 }
 

@@ -30,38 +30,56 @@ compress_kernel(const T *__restrict__ Ca, const T *__restrict__ Cb, const T *__r
     const int j = ct * CX + tx;
     const int S = (1 + overlap) * ratio;
 
+    // the slots of this thread are read in batches of 8 independent loads before any
+    // arithmetic, so a thread waits for one memory round trip per batch
     float m = -INFINITY, den = 0.f, num = 0.f;
     if (j < c) {
-        for (int s = ty; s < S; s += SG) {
-            float z, v;
-            if (overlap && s < ratio) {
-                if (i >= 1) {
-                    const int64_t o = (b * n + (i - 1) * ratio + s) * c + j;
-                    z = elem<T>::load(Zb, o);
-                    v = elem<T>::load(Cb, o);
-                } else if (cCb != nullptr) {
-                    const int64_t o = (b * ratio + s) * c + j;
-                    z = elem<T>::load(cZb, o);
-                    v = elem<T>::load(cCb, o);
+        for (int s0 = ty; s0 < S; s0 += 8 * SG) {
+            float z[8], v[8];
+            bool has[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int s = s0 + u * SG;
+                has[u] = s < S;
+                z[u] = -INFINITY;
+                v[u] = 0.f;
+                if (!has[u]) continue;
+                if (overlap && s < ratio) {
+                    if (i >= 1) {
+                        const int64_t o = (b * n + (i - 1) * ratio + s) * c + j;
+                        z[u] = elem<T>::load(Zb, o);
+                        v[u] = elem<T>::load(Cb, o);
+                    } else if (cCb != nullptr) {
+                        const int64_t o = (b * ratio + s) * c + j;
+                        z[u] = elem<T>::load(cZb, o);
+                        v[u] = elem<T>::load(cCb, o);
+                    } else {
+                        has[u] = false;  // absent slot: weight 0
+                    }
                 } else {
-                    continue;  // absent slot: weight 0
+                    const int64_t o = (b * n + i * ratio + (s - overlap * ratio)) * c + j;
+                    z[u] = elem<T>::load(Za, o);
+                    v[u] = elem<T>::load(Ca, o);
                 }
-            } else {
-                const int64_t o = (b * n + i * ratio + (s - overlap * ratio)) * c + j;
-                z = elem<T>::load(Za, o);
-                v = elem<T>::load(Ca, o);
+                if (has[u] && bias != nullptr) z[u] += bias[(int64_t)s * c + j];
             }
-            if (bias != nullptr) z += bias[(int64_t)s * c + j];
-            if (z > m) {
-                const float a = expf(m - z);
-                num = num * a + v;
-                den = den * a + 1.f;
-                m = z;
-            } else {
-                const float e = expf(z - m);
-                num += e * v;
-                den += e;
-            }
+            float bm = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (has[u]) bm = fmaxf(bm, z[u]);
+            if (bm == -INFINITY) continue;
+            const float M = fmaxf(m, bm);
+            const float a = expf(m - M);
+            num *= a;
+            den *= a;
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (has[u]) {
+                    const float e = expf(z[u] - M);
+                    num += e * v[u];
+                    den += e;
+                }
+            m = M;
         }
     }
     if (SG > 1) {
