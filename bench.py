@@ -40,6 +40,10 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-entries", type=int, default=16384,
                     help="index entries per query in the oracle's bounded sample")
+    ap.add_argument("--workload", default="pro_decode_1m",
+                    choices=["pro_decode_1m", "flash_decode_128k", "pro_prefill_chunk", "hca_prefill_4k"],
+                    help="pro_decode_1m is the benchmark line; the others print the same record for "
+                         "the other configurations' shapes (profiling aid)")
     ap.add_argument("--profile-copy", action="store_true",
                     help="before the timed region, run a plain 1 GiB device copy three times (a kernel of "
                          "known traffic that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -78,10 +82,12 @@ def main():
     dev = "cuda"
     torch.cuda.set_device(0)
     csa.lib()
-    cfg = W.PRO
+    if a.workload in ("pro_prefill_chunk", "hca_prefill_4k"):
+        return prefill_main(a)
+    cfg = W.PRO if a.workload == "pro_decode_1m" else W.FLASH
     B, T, n, N, D, H, k = cfg.B, cfg.T, cfg.n, cfg.N, cfg.c, cfg.H, cfg.k
     s = cfg.seed
-    NH = W.HCA.N  # 8192 summaries
+    NH = cfg.n // 128  # HCA summaries (8,192 at 2^20 tokens)
     bf = torch.bfloat16
 
     # ---- inputs (HBM-resident) ------------------------------------------------------
@@ -200,9 +206,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1), bf16)",
         "config": {
-            "workload": "pro_decode_1m: one CSA layer + one HCA layer decode step, B=4 sequences x 1 query at "
-                        "t=2^20; 262,144 entries x 64 heads x 128 bf16 index keys per sequence, top-k 1,024, "
-                        "128 heads x 512 shared KV, SWA 128, 8,192 HCA summaries",
+            "workload": (f"{cfg.name}: one CSA layer + one HCA layer decode step, B={B} sequences x 1 query at "
+                         f"t={n}; {N:,} entries x 64 heads x 128 bf16 index keys per sequence, top-k {k:,}, "
+                         f"{H} heads x {D} shared KV, SWA {cfg.window}, {NH:,} HCA summaries"),
             "batch": B, "context": n, "index_entries": N, "topk": k, "heads": H, "head_dim": D,
         },
         "roofline": {
@@ -218,8 +224,142 @@ def main():
         },
         "stages_ms": {kk: round(v, 4) for kk, v in stages.items()},
     }
-    if not a.no_cpu:
+    if a.workload != "pro_decode_1m":
+        res["metric"] = f"decode queries/s + indexer GB/s, {cfg.name} shape (profiling line, not the benchmark)"
+    if not a.no_cpu and a.workload == "pro_decode_1m":
         res["cpu_baseline"] = cpu_baseline(a, inp, kv, k_I, summ, sink_h, scores, idx, cfg, NH)
+    print(json.dumps(res), flush=True)
+
+
+def prefill_main(a):
+    """Prefill chunks (profiling aid): the whole CSA or HCA prefill path of one chunk.
+
+    pro_prefill_chunk: 8,192 new tokens after a 65,536-token context. csa_compress of the
+      chunk (+ the carry of block 16,383) writes KV rows 16,384..18,431; csa_index_scores
+      with MXFP4 operands (8,192 queries x 18,432 entries, causal); csa_topk (k = 1,024);
+      csa_sparse_attn (128 heads x 512, 1,024 + 128 rows per query).
+    hca_prefill_4k: the last 4,096 tokens of a 2^20 context. csa_compress (ratio 128) writes
+      summaries 8,160..8,191; hca_attn (4,096 queries, every visible summary + 128 SWA rows).
+    Dominant kernel for the roofline line: the attention (bf16 MFMA, FLOP-bound).
+    """
+    import numpy as np
+    import torch
+
+    import long_context_compressed_amd as csa
+    import workloads as W
+
+    dev, bf = "cuda", torch.bfloat16
+    if a.workload == "pro_prefill_chunk":
+        cfg = W.PRO_PREFILL
+        T, n0, D, H, k, s = cfg.T, cfg.n, cfg.c, cfg.H, cfg.k, cfg.seed
+        N = (n0 + T) // 4
+        old = n0 // 4
+        kv = W.normal((1, N, D), s, "kv", dtype=bf, device=dev)
+        C = {nm: W.normal((1, T, D), s, nm, dtype=bf, device=dev) for nm in ("Ca", "Cb", "Za", "Zb")}
+        carry = {nm: W.normal((1, 4, D), s, "carry_" + nm, dtype=bf, device=dev) for nm in ("C", "Z")}
+        qc, qsc = W.quantize_mxfp4(W.normal((T, 64, 128), s, "q_I", device=dev))
+        kc, ksc = W.quantize_mxfp4(W.normal((1, N, 64, 128), s, "k_I", device=dev))
+        w = W.normal((T, 64), s, "w", device=dev)
+        q = W.normal((T, H, D), s, "q", dtype=bf, device=dev)
+        swa_rows = T + cfg.window - 1
+        swa = W.normal((1, swa_rows, D), s, "swa", dtype=bf, device=dev)
+        p0 = torch.tensor([n0 - cfg.window + 1], dtype=torch.int64, device=dev)
+        sink = W.normal((H,), s, "sink", device=dev)
+        q_pos = torch.arange(n0, n0 + T, dtype=torch.int64, device=dev)
+        q_seq = torch.zeros(T, dtype=torch.int32, device=dev)
+        cs = W.rope_table(q_pos.cpu(), cfg.rope_dim).to(dev)
+        scores = torch.empty((T, N), dtype=torch.float32, device=dev)
+        idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        tws = torch.empty(max(1, csa.topk_workspace_bytes(T, N, k)), dtype=torch.uint8, device=dev)
+        aws = torch.empty(max(1, csa.attn_workspace_bytes(T, H, D, k + cfg.window)), dtype=torch.uint8, device=dev)
+        out = torch.empty_like(q)
+        lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+        kv_new = kv[:, old:, :]
+        stages = {
+            "compress": lambda: csa.compress(C["Ca"], C["Za"], C["Cb"], C["Zb"], carry["C"], carry["Z"], out=kv_new),
+            "index_scores_mxfp4": lambda: csa.index_scores(qc, w, kc, q_seq, q_pos, q_I_scale=qsc, k_I_scale=ksc,
+                                                           mxfp4=True, scores=scores),
+            "topk": lambda: csa.topk(scores, k, idx=idx, workspace=tws),
+            "sparse_attn": lambda: csa.sparse_attn(q, kv, sink, idx, cfg.scale, swa, p0, cfg.window, q_seq, q_pos,
+                                                   cs, cfg.rope_dim, out=out, lse=lse, workspace=aws),
+        }
+        rows = k + cfg.window
+        flops = 4.0 * T * H * rows * D
+        dominant = "sparse_attn"
+    else:
+        cfg = W.HCA
+        T, n, D, H, s = W.HCA_PREFILL_T, cfg.n, cfg.c, cfg.H, cfg.seed
+        NH = n // 128
+        summ = W.normal((1, NH, D), s, "summ", dtype=bf, device=dev)
+        Cz = W.normal((1, T, D), s, "C", dtype=bf, device=dev)
+        Zz = W.normal((1, T, D), s, "Z", dtype=bf, device=dev)
+        q = W.normal((T, H, D), s, "q", dtype=bf, device=dev)
+        swa_rows = T + cfg.window - 1
+        swa = W.normal((1, swa_rows, D), s, "swa", dtype=bf, device=dev)
+        p0 = torch.tensor([n - T - cfg.window + 1], dtype=torch.int64, device=dev)
+        sink = W.normal((H,), s, "sink", device=dev)
+        q_pos = torch.arange(n - T, n, dtype=torch.int64, device=dev)
+        q_seq = torch.zeros(T, dtype=torch.int32, device=dev)
+        cs = W.rope_table(q_pos.cpu(), cfg.rope_dim).to(dev)
+        aws = torch.empty(max(1, csa.attn_workspace_bytes(T, H, D, NH + cfg.window)), dtype=torch.uint8, device=dev)
+        out = torch.empty_like(q)
+        lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+        summ_new = summ[:, NH - T // 128:, :]
+        stages = {
+            "compress_hca": lambda: csa.compress(Cz, Zz, ratio=128, overlap=0, out=summ_new),
+            "hca_attn": lambda: csa.hca_attn(q, summ, sink, 128, cfg.scale, swa, p0, cfg.window, q_seq, q_pos, cs,
+                                             cfg.rope_dim, out=out, lse=lse, workspace=aws),
+        }
+        pos = q_pos.cpu().numpy()
+        rows = float(np.sum(np.minimum(NH, pos // 128) + cfg.window))
+        flops = 4.0 * H * rows * D
+        dominant = "hca_attn"
+    torch.cuda.synchronize()
+
+    def step():
+        for f in stages.values():
+            f()
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    dom_ms = []
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        for nm, f in stages.items():
+            if nm == dominant:
+                ev[0].record()
+                f()
+                ev[1].record()
+                ev[1].synchronize()
+                dom_ms.append(ev[0].elapsed_time(ev[1]))
+            else:
+                f()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    stage_ms = {}
+    for nm, f in stages.items():
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        stage_ms[nm] = round(e0.elapsed_time(e1) / 3, 4)
+    dom_s = float(np.mean(dom_ms)) / 1e3
+    achieved = flops / dom_s / 1e12
+    res = {
+        "metric": f"prefill tokens/s, {a.workload} (profiling line, not the benchmark)",
+        "value": round(T * a.steps / elapsed, 1), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(elapsed / a.steps * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": a.workload, "queries": T, "heads": H, "head_dim": D},
+        "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2), "peak": 2500.0,
+                     "unit": "TFLOP/s", "frac": round(achieved / 2500.0, 4), "traffic": None,
+                     "algorithmic_flops_per_launch": flops, "avg_launch_ms": round(dom_s * 1e3, 4)},
+        "stages_ms": stage_ms,
+    }
     print(json.dumps(res), flush=True)
 
 

@@ -174,58 +174,6 @@ index_scan_kernel(const KT *__restrict__ qI, const float *__restrict__ w, const 
     if (lane < (int)(e1 - e0)) scores[(int64_t)t * N + e0 + lane] = my_score;
 }
 
-// ---- MXFP4 operands (the FP4 indexer path): value = code * 2^(scale - 127) ----------
-// Magnitudes x2 of the E2M1 codes 0..7 ({0, .5, 1, 1.5, 2, 3, 4, 6} * 2), one nibble each.
-__device__ __forceinline__ float e2m1_x2(uint32_t nib) {
-    const float m = (float)((0xC8643210u >> (4 * (nib & 7u))) & 15u);
-    return (nib & 8u) ? -m : m;
-}
-
-// One wave per entry; lane h owns head h. Block dots of 32 E2M1 products are exact in
-// fp32; each is scaled by 2^(sq + sk - 254) and the four blocks are summed in fp32.
-__global__ void __launch_bounds__(256)
-index_mxfp4_valu_kernel(const uint8_t *__restrict__ qI, const uint8_t *__restrict__ qS,
-                        const float *__restrict__ w, const uint8_t *__restrict__ kI,
-                        const uint8_t *__restrict__ kS, const int32_t *__restrict__ q_seq,
-                        const int64_t *__restrict__ q_pos, int B, int64_t N, int ratio,
-                        float *__restrict__ scores)
-{
-    const int lane = threadIdx.x & 63;
-    const int t = blockIdx.y;
-    const int64_t e = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (e >= N) return;
-    const int s = q_seq[t];
-    int64_t nvis = q_pos[t] / ratio;
-    if (nvis > N) nvis = N;
-    if (nvis < 0 || s < 0 || s >= B) nvis = 0;
-    float sc = -INFINITY;
-    if (e < nvis) {
-        const uint4 *qp = reinterpret_cast<const uint4 *>(qI + ((int64_t)t * 64 + lane) * 64);
-        const uint4 *kp = reinterpret_cast<const uint4 *>(kI + (((int64_t)s * N + e) * 64 + lane) * 64);
-        const uint32_t qsc = *reinterpret_cast<const uint32_t *>(qS + ((int64_t)t * 64 + lane) * 4);
-        const uint32_t ksc = *reinterpret_cast<const uint32_t *>(kS + (((int64_t)s * N + e) * 64 + lane) * 4);
-        float dot = 0.f;
-#pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-            const uint4 qa = qp[blk], ka = kp[blk];
-            const uint32_t qw[4] = {qa.x, qa.y, qa.z, qa.w}, kw[4] = {ka.x, ka.y, ka.z, ka.w};
-            float part = 0.f;
-#pragma unroll
-            for (int x = 0; x < 4; ++x)
-#pragma unroll
-                for (int nb = 0; nb < 8; ++nb)
-                    part = fmaf(e2m1_x2((qw[x] >> (4 * nb)) & 15u), e2m1_x2((kw[x] >> (4 * nb)) & 15u), part);
-            const int ex = (int)((qsc >> (8 * blk)) & 255u) + (int)((ksc >> (8 * blk)) & 255u) - 254 - 2;
-            dot += ldexpf(part, ex);  // the -2 undoes the two x2 magnitudes
-        }
-        float r = fmaxf(dot, 0.f) * w[(int64_t)t * 64 + lane];
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) r += __shfl_xor(r, m);
-        sc = r;
-    }
-    if (lane == 0) scores[(int64_t)t * N + e] = sc;
-}
-
 }  // namespace
 
 int launch_index_scores(const void *qI, const uint8_t *qs, const float *w, const void *kI,
@@ -233,12 +181,9 @@ int launch_index_scores(const void *qI, const uint8_t *qs, const float *w, const
                         int B, int64_t N, int ratio, csa_dtype dt, float *scores, hipStream_t st)
 {
     if (T == 0 || N == 0) return CSA_OK;
-    if (dt == CSA_MXFP4) {
-        dim3 grid((unsigned)((N + 3) / 4), (unsigned)T);
-        hipLaunchKernelGGL(index_mxfp4_valu_kernel, grid, dim3(256), 0, st, (const uint8_t *)qI, qs,
-                           w, (const uint8_t *)kI, ks, q_seq, q_pos, B, N, ratio, scores);
-        return check_launch("index_mxfp4_valu_kernel");
-    }
+    if (dt == CSA_MXFP4)
+        return launch_index_mxfp4((const uint8_t *)qI, qs, w, (const uint8_t *)kI, ks, q_seq, q_pos, T, B, N,
+                                  ratio, scores, st);
     constexpr int EPW = 64;
     dim3 grid((unsigned)((N + 4 * EPW - 1) / (4 * EPW)), (unsigned)T);
     if (dt == CSA_BF16) {

@@ -1,0 +1,267 @@
+// Lightning Indexer scores with MXFP4 operands on gfx950 ("DeepSeek-V4 混合注意力" §2 and
+// §4.2: the indexer QK runs in FP4; the MXFP4 checkpoint page: E2M1 values with one E8M0
+// scale per 32 elements):
+//   s[t][i] = sum_h w[t][h] * ReLU(<q_I[t][h], k_I[i][h]>)
+//
+// Prefill: many queries share one key store, so per head the products form a dense
+// (queries x entries) contraction over 128 dims, done by v_mfma_scale_f32_16x16x128_f8f6f4
+// (one instruction = one head's full dot for a 16 x 16 tile; E2M1 products are exact and
+// the E8M0 block scales are applied inside the instruction).
+//
+// Workgroup: 8 wavefronts, a 256-query x 128-entry tile, wave (qg, eg) owns 64 queries x
+// 64 entries (4 x 4 MFMA tiles, 64 fp32 score accumulators per lane). The loop runs over
+// the 64 heads; per head the tile's q and k codes (16 + 8 KiB) and their scales are staged
+// in LDS, double buffered: head h+1 is loaded into registers while head h is computed, then
+// written to the other buffer. The epilogue of every MFMA (ReLU, times w[t][h], accumulate) is VALU work and
+// bounds the kernel. The 16-byte chunks of each 64-byte code row are XOR-swizzled in LDS so
+// the per-lane 16-byte operand reads of 8 consecutive rows hit distinct banks.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace csa {
+
+namespace {
+
+constexpr int TQ = 256;       // queries per workgroup
+constexpr int TE = 128;       // entries per workgroup
+constexpr int WPITCH = 65;    // fp32 pitch of a query's 64 head weights in LDS
+
+typedef int i32x4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 3; }
+
+__global__ void __launch_bounds__(512, 1)
+index_mxfp4_mfma_kernel(const uint8_t *__restrict__ qI, const uint8_t *__restrict__ qS,
+                        const float *__restrict__ w, const uint8_t *__restrict__ kI,
+                        const uint8_t *__restrict__ kS, const int32_t *__restrict__ q_seq,
+                        const int64_t *__restrict__ q_pos, int T, int64_t N, int ratio, int nqb, int neb,
+                        float *__restrict__ scores)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t Qs[2][TQ * 64];
+    __shared__ __attribute__((aligned(16))) uint8_t Ks[2][TE * 64];
+    __shared__ __attribute__((aligned(16))) uint32_t QSs[2][TQ];
+    __shared__ __attribute__((aligned(16))) uint32_t KSs[2][TE];
+    __shared__ float Ws[TQ * WPITCH];
+    __shared__ int64_t nvis_s[TQ];
+    __shared__ int red[2];
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int l16 = lane & 15, g4 = lane >> 4;
+    // XCD-aware order: workgroups b, b+8, ... share an XCD; one query block per XCD at a
+    // time (its q tile stays in that XCD's L2) while the entry blocks stream
+    const int b = blockIdx.x;
+    const int xcd = b & 7, r8 = b >> 3;
+    const int qb = (r8 / neb) * 8 + xcd, eb = r8 % neb;
+    if (qb >= nqb) return;
+    const int t0 = qb * TQ;
+    const int64_t i0 = (int64_t)eb * TE;
+
+    // visibility of each query of the tile (a query of another sequence sees nothing)
+    if (tid < TQ) {
+        const int t = t0 + tid;
+        int64_t nv = 0;
+        if (t < T && q_seq[t] == 0) {
+            nv = q_pos[t] / ratio;
+            nv = nv < 0 ? 0 : (nv > N ? N : nv);
+        }
+        nvis_s[tid] = nv;
+    }
+    if (tid == 0) red[0] = 0;
+    __syncthreads();
+    if (tid < TQ && nvis_s[tid] > i0) atomicOr(&red[0], 1);
+    __syncthreads();
+    const bool any_visible = red[0] != 0;
+
+    // wave (qg, eg) owns queries qg*64.. and entries eg*64.. of the tile
+    const int qg = wv & 3, eg = wv >> 2;
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int n = 0; n < 4; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    if (any_visible) {
+        // head weights of the tile's queries
+#pragma unroll 4
+        for (int x = tid; x < TQ * 64; x += 512) {
+            const int qq = x >> 6, h = x & 63;
+            const int t = t0 + qq;
+            Ws[qq * WPITCH + h] = (t < T) ? w[(int64_t)t * 64 + h] : 0.f;
+        }
+        // per-wave share of one head's operands: 32 q rows and 16 k rows (16 bytes per lane
+        // per 16-row group) and, for waves 0-5, 64 scale words (0-3: q scales, 4-5: k
+        // scales). They are loaded into registers while the previous head is computed, then
+        // written to LDS.
+        const int qrow0 = wv * 32 + (lane >> 2), qrow1 = qrow0 + 16;
+        const int krow = wv * 16 + (lane >> 2);
+        const int qpos0 = ((lane & 3) ^ swz(qrow0)) * 16, qpos1 = ((lane & 3) ^ swz(qrow1)) * 16;
+        const int kpos = ((lane & 3) ^ swz(krow)) * 16;
+        int tq0 = t0 + qrow0, tq1 = t0 + qrow1;
+        tq0 = tq0 < T ? tq0 : T - 1;
+        tq1 = tq1 < T ? tq1 : T - 1;
+        int64_t ek = i0 + krow;
+        ek = ek < N ? ek : N - 1;
+        const uint8_t *qsrc0 = qI + (int64_t)tq0 * 4096 + (lane & 3) * 16;
+        const uint8_t *qsrc1 = qI + (int64_t)tq1 * 4096 + (lane & 3) * 16;
+        const uint8_t *ksrc = kI + ek * 4096 + (lane & 3) * 16;
+        const uint8_t *ssrc = nullptr;
+        if (wv < 4) {
+            int t = t0 + wv * 64 + lane;
+            t = t < T ? t : T - 1;
+            ssrc = qS + (int64_t)t * 256;
+        } else if (wv < 6) {
+            int64_t e = i0 + (wv - 4) * 64 + lane;
+            e = e < N ? e : N - 1;
+            ssrc = kS + e * 256;
+        }
+        uint4 rq0, rq1, rk;
+        uint32_t rs = 0;
+        auto load = [&](int h) {
+            rq0 = *reinterpret_cast<const uint4 *>(qsrc0 + h * 64);
+            rq1 = *reinterpret_cast<const uint4 *>(qsrc1 + h * 64);
+            rk = *reinterpret_cast<const uint4 *>(ksrc + h * 64);
+            if (wv < 6) rs = *reinterpret_cast<const uint32_t *>(ssrc + h * 4);
+        };
+        auto store = [&](int buf) {
+            *reinterpret_cast<uint4 *>(&Qs[buf][qrow0 * 64 + qpos0]) = rq0;
+            *reinterpret_cast<uint4 *>(&Qs[buf][qrow1 * 64 + qpos1]) = rq1;
+            *reinterpret_cast<uint4 *>(&Ks[buf][krow * 64 + kpos]) = rk;
+            if (wv < 4)
+                QSs[buf][wv * 64 + lane] = rs;
+            else if (wv < 6)
+                KSs[buf][(wv - 4) * 64 + lane] = rs;
+        };
+
+        load(0);
+        store(0);
+        __syncthreads();
+        for (int h = 0; h < 64; ++h) {
+            const int buf = h & 1;
+            if (h + 1 < 64) load(h + 1);
+            // B operands (k codes of the wave's 4 entry tiles) stay in registers; A (q codes)
+            // is read per query tile
+            i32x4v Bv[4];
+            int sb[4];
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+                const int row = eg * 64 + 16 * n + l16;
+                Bv[n] = *reinterpret_cast<const i32x4v *>(&Ks[buf][row * 64 + ((g4 ^ swz(row)) * 16)]);
+                sb[n] = (int)((KSs[buf][row] >> (8 * g4)) & 0xFFu);
+            }
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int row = qg * 64 + 16 * m + l16;
+                const i32x4v av = *reinterpret_cast<const i32x4v *>(&Qs[buf][row * 64 + ((g4 ^ swz(row)) * 16)]);
+                const i32x8 A = i32x8{av[0], av[1], av[2], av[3], 0, 0, 0, 0};
+                const int sa = (int)((QSs[buf][row] >> (8 * g4)) & 0xFFu);
+                float wr[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) wr[r] = Ws[(qg * 64 + 16 * m + 4 * g4 + r) * WPITCH + h];
+#pragma unroll
+                for (int n = 0; n < 4; ++n) {
+                    const i32x8 Bn = i32x8{Bv[n][0], Bv[n][1], Bv[n][2], Bv[n][3], 0, 0, 0, 0};
+                    const f32x4 c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        A, Bn, f32x4{0.f, 0.f, 0.f, 0.f}, 4, 4, 0, sa, 0, sb[n]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[m][n][r] = fmaf(wr[r], fmaxf(c[r], 0.f), acc[m][n][r]);
+                }
+            }
+            if (h + 1 < 64) store(buf ^ 1);
+            __syncthreads();
+        }
+    }
+
+    // scores: lane holds (query 16m + 4g4 + r, entry 16n + l16) of the wave tile
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int qq = qg * 64 + 16 * m + 4 * g4 + r;
+            const int t = t0 + qq;
+            if (t >= T) continue;
+            const int64_t nv = nvis_s[qq];
+            float *srow = scores + (int64_t)t * N;
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+                const int64_t i = i0 + eg * 64 + 16 * n + l16;
+                if (i < N) srow[i] = (i < nv) ? acc[m][n][r] : -INFINITY;
+            }
+        }
+}
+
+// ---- general case (several key stores): one wavefront per (query, entry) -------------
+// value = code * 2^(scale - 127)
+// Magnitudes x2 of the E2M1 codes 0..7 ({0, .5, 1, 1.5, 2, 3, 4, 6} * 2), one nibble each.
+__device__ __forceinline__ float e2m1_x2(uint32_t nib) {
+    const float m = (float)((0xC8643210u >> (4 * (nib & 7u))) & 15u);
+    return (nib & 8u) ? -m : m;
+}
+
+// One wave per entry; lane h owns head h. Block dots of 32 E2M1 products are exact in
+// fp32; each is scaled by 2^(sq + sk - 254) and the four blocks are summed in fp32.
+__global__ void __launch_bounds__(256)
+index_mxfp4_valu_kernel(const uint8_t *__restrict__ qI, const uint8_t *__restrict__ qS,
+                        const float *__restrict__ w, const uint8_t *__restrict__ kI,
+                        const uint8_t *__restrict__ kS, const int32_t *__restrict__ q_seq,
+                        const int64_t *__restrict__ q_pos, int B, int64_t N, int ratio,
+                        float *__restrict__ scores)
+{
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.y;
+    const int64_t e = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (e >= N) return;
+    const int s = q_seq[t];
+    int64_t nvis = q_pos[t] / ratio;
+    if (nvis > N) nvis = N;
+    if (nvis < 0 || s < 0 || s >= B) nvis = 0;
+    float sc = -INFINITY;
+    if (e < nvis) {
+        const uint4 *qp = reinterpret_cast<const uint4 *>(qI + ((int64_t)t * 64 + lane) * 64);
+        const uint4 *kp = reinterpret_cast<const uint4 *>(kI + (((int64_t)s * N + e) * 64 + lane) * 64);
+        const uint32_t qsc = *reinterpret_cast<const uint32_t *>(qS + ((int64_t)t * 64 + lane) * 4);
+        const uint32_t ksc = *reinterpret_cast<const uint32_t *>(kS + (((int64_t)s * N + e) * 64 + lane) * 4);
+        float dot = 0.f;
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) {
+            const uint4 qa = qp[blk], ka = kp[blk];
+            const uint32_t qw[4] = {qa.x, qa.y, qa.z, qa.w}, kw[4] = {ka.x, ka.y, ka.z, ka.w};
+            float part = 0.f;
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+#pragma unroll
+                for (int nb = 0; nb < 8; ++nb)
+                    part = fmaf(e2m1_x2((qw[x] >> (4 * nb)) & 15u), e2m1_x2((kw[x] >> (4 * nb)) & 15u), part);
+            const int ex = (int)((qsc >> (8 * blk)) & 255u) + (int)((ksc >> (8 * blk)) & 255u) - 254 - 2;
+            dot += ldexpf(part, ex);  // the -2 undoes the two x2 magnitudes
+        }
+        float r = fmaxf(dot, 0.f) * w[(int64_t)t * 64 + lane];
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) r += __shfl_xor(r, m);
+        sc = r;
+    }
+    if (lane == 0) scores[(int64_t)t * N + e] = sc;
+}
+
+}  // namespace
+
+// MXFP4 scores: the matrix-core tile kernel when every query reads the one key store
+// (B == 1); otherwise one wavefront per (query, entry).
+int launch_index_mxfp4(const uint8_t *qI, const uint8_t *qs, const float *w, const uint8_t *kI,
+                       const uint8_t *ks, const int32_t *q_seq, const int64_t *q_pos, int T, int B, int64_t N,
+                       int ratio, float *scores, hipStream_t st)
+{
+    if (B == 1) {
+        const int nqb = (T + TQ - 1) / TQ;
+        const int neb = (int)((N + TE - 1) / TE);
+        const int64_t blocks = (int64_t)((nqb + 7) / 8) * 8 * neb;
+        hipLaunchKernelGGL(index_mxfp4_mfma_kernel, dim3((unsigned)blocks), dim3(512), 0, st, qI, qs, w, kI, ks,
+                           q_seq, q_pos, T, N, ratio, nqb, neb, scores);
+        return check_launch("index_mxfp4_mfma_kernel");
+    }
+    dim3 grid((unsigned)((N + 3) / 4), (unsigned)T);
+    hipLaunchKernelGGL(index_mxfp4_valu_kernel, grid, dim3(256), 0, st, qI, qs, w, kI, ks, q_seq, q_pos, B, N,
+                       ratio, scores);
+    return check_launch("index_mxfp4_valu_kernel");
+}
+
+}  // namespace csa

@@ -14,6 +14,10 @@ int launch_index_scores(const void *qI, const uint8_t *qs, const float *w, const
                         const uint8_t *ks, const int32_t *q_seq, const int64_t *q_pos, int T,
                         int B, int64_t N, int ratio, csa_dtype dt, float *scores, hipStream_t st);
 
+int launch_index_mxfp4(const uint8_t *qI, const uint8_t *qs, const float *w, const uint8_t *kI,
+                       const uint8_t *ks, const int32_t *q_seq, const int64_t *q_pos, int T, int B, int64_t N,
+                       int ratio, float *scores, hipStream_t st);
+
 size_t topk_workspace_bytes(int T, int64_t N, int k);
 int launch_topk(const float *scores, int T, int64_t N, int k, int32_t *idx, float *vals,
                 void *ws, size_t ws_bytes, hipStream_t st);

@@ -105,17 +105,22 @@ def test_index_bf16_decode(csa, orc, T, B, N):
     assert_rel(sc, ref, TOL_F32, "index bf16")
 
 
-def test_index_mxfp4(csa, orc):
-    """MXFP4 operands (E2M1 + E8M0 per 32), causal prefill positions."""
-    T, N = 70, 300
-    s = 4242
+@pytest.mark.parametrize("T,N,B,p_lo,p_hi", [
+    (70, 300, 1, 600, 669),      # one workgroup tile, ragged in both directions (matrix cores)
+    (520, 650, 1, 1000, 3000),   # 3 x 6 tiles, causal: partly and fully masked tiles
+    (10, 90, 2, 100, 400),       # two key stores: the per-(query, entry) path
+])
+def test_index_mxfp4(csa, orc, T, N, B, p_lo, p_hi):
+    """MXFP4 operands (E2M1 + one E8M0 scale per 32), causal prefill positions."""
+    say("index_mxfp4", T, N, B)
+    s = 4242 + T
     q32 = W.normal((T, 64, 128), s, "q", device=DEV)
-    k32 = W.normal((1, N, 64, 128), s, "k", device=DEV)
+    k32 = W.normal((B, N, 64, 128), s, "k", device=DEV)
     qc, qs = W.quantize_mxfp4(q32)
     kc, ks = W.quantize_mxfp4(k32)
     w = W.normal((T, 64), s, "w", device=DEV)
-    q_seq = torch.zeros(T, dtype=torch.int32, device=DEV)
-    q_pos = torch.arange(1100, 1100 + T, dtype=torch.int64, device=DEV) - 500
+    q_seq = (torch.arange(T, dtype=torch.int32, device=DEV) % B)
+    q_pos = torch.linspace(p_lo, p_hi, T, device=DEV).to(torch.int64)
     sc = csa.index_scores(qc, w, kc, q_seq, q_pos, q_I_scale=qs, k_I_scale=ks, mxfp4=True)
     torch.cuda.synchronize()
     qd = orc.mxfp4_decode(qc, qs)
