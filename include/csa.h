@@ -135,7 +135,7 @@ int csa_topk(const float *scores, int T, int64_t N, int k,
  * swa_kv: [B][swa_rows][D] dt or NULL (then window is ignored); swa_pos0: [B] int64;
  * rope_cs: [T][rope_dim/2][2] fp32 or NULL (rope_dim ignored); out: [T][H][D] dt;
  * lse: [T][H] fp32 or NULL; workspace: csa_attn_workspace_bytes(...) bytes.
- * Supported: dt F32 | BF16, D <= 1024, D % 64 == 0, rope_dim even and <= D.
+ * Supported: dt F32 | BF16, D <= 1024, D % 64 == 0, rope_dim even and <= D, 0 <= k <= 4096.
  */
 size_t csa_attn_workspace_bytes(int T, int H, int D, int64_t max_rows);
 int csa_sparse_attn(const void *q, const void *kv, const float *attn_sink,

@@ -133,6 +133,7 @@ int csa_sparse_attn(const void *q, const void *kv, const float *attn_sink, const
                                rope_dim, T, B, N, H, D, dt, out, "csa_sparse_attn");
     if (rc != CSA_OK) return rc;
     REQUIRE(k >= 0, CSA_EINVAL, "csa_sparse_attn: k must be >= 0");
+    REQUIRE(k <= 4096, CSA_EUNSUPPORTED, "csa_sparse_attn: k > 4096 is not built");
     REQUIRE(std::isfinite(softmax_scale), CSA_EINVAL, "csa_sparse_attn: softmax_scale must be finite");
     if (T == 0) return CSA_OK;
     REQUIRE(k == 0 || topk_idxs, CSA_EINVAL, "csa_sparse_attn: NULL topk_idxs");

@@ -25,62 +25,13 @@
 //
 // Any other shape/dtype: attn_valu_kernel, one wavefront per (query, head), rows one by
 // one with a wave-wide dot product and the same online softmax.
+#include "attn_rows.hpp"
 #include "common.hpp"
 #include "internal.hpp"
 
 namespace csa {
 
 namespace {
-
-struct RowCtx {
-    int64_t nmain;    // main slots
-    int64_t nslots;   // main + window slots
-    int64_t lo;       // first SWA position
-    int s;
-    int64_t pos;
-};
-
-__device__ __forceinline__ RowCtx row_ctx(int t, const int32_t *q_seq, const int64_t *q_pos, int B,
-                                          int64_t N, int k, int ratio, const void *swa, int window) {
-    RowCtx c;
-    c.s = q_seq[t];
-    c.pos = q_pos[t];
-    if (c.s < 0 || c.s >= B || c.pos < 0) {
-        c.nmain = c.nslots = 0;
-        c.lo = 0;
-        return c;
-    }
-    if (ratio > 0) {
-        int64_t nv = c.pos / ratio;
-        c.nmain = nv < N ? nv : N;
-    } else {
-        c.nmain = k;
-    }
-    c.lo = c.pos - window + 1;
-    if (c.lo < 0) c.lo = 0;
-    const int64_t nwin = (swa != nullptr && window > 0) ? (c.pos - c.lo + 1) : 0;
-    c.nslots = c.nmain + nwin;
-    return c;
-}
-
-template <typename ET>
-__device__ __forceinline__ const ET *row_ptr(const RowCtx &c, int64_t j, int t, const ET *kv,
-                                            const int32_t *idx, int k, int ratio, int64_t N,
-                                            const ET *swa, const int64_t *swa_pos0, int swa_rows, int D) {
-    if (j < 0 || j >= c.nslots) return nullptr;
-    if (j < c.nmain) {
-        int64_t id = j;
-        if (ratio <= 0) {
-            id = idx[(int64_t)t * k + j];
-            if (id < 0 || id >= N) return nullptr;
-        }
-        return kv + ((int64_t)c.s * N + id) * D;
-    }
-    const int64_t x = c.lo + (j - c.nmain);
-    const int64_t r = x - swa_pos0[c.s];
-    if (r < 0 || r >= swa_rows) return nullptr;
-    return swa + ((int64_t)c.s * swa_rows + r) * D;
-}
 
 // ======================================================================================
 // generic kernel: one wavefront per (query, head); lane l holds dims [l*VPL, (l+1)*VPL)
@@ -101,7 +52,7 @@ attn_valu_kernel(const ET *__restrict__ q, const ET *__restrict__ kv, const floa
     const bool active = unit0 < (int64_t)T * H;  // inactive waves still reach the barrier
     const int64_t unit = active ? unit0 : 0;
     const int t = (int)(unit / H), g = (int)(unit % H);
-    RowCtx c = row_ctx(t, q_seq, q_pos, B, N, k, ratio, swa, window);
+    RowCtx c = row_ctx(t, q_seq, q_pos, B, N, k, ratio, swa, swa_pos0, window);
     if (!active) c.nslots = 0;
 
     float qv[VPL], acc[VPL];
@@ -212,7 +163,7 @@ attn_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, co
     if (uu >= per_xcd || u >= U) return;
     const int t = (int)(u / nsplit), sp = (int)(u % nsplit);
 
-    const RowCtx c = row_ctx(t, q_seq, q_pos, B, N, k, ratio, swa, window);
+    const RowCtx c = row_ctx(t, q_seq, q_pos, B, N, k, ratio, swa, swa_pos0, window);
     const int64_t j0 = (int64_t)sp * split_slots;
     int64_t j1 = j0 + split_slots;
     if (j1 > c.nslots) j1 = c.nslots;
@@ -573,13 +524,22 @@ int launch_attn(const AttnArgs &a, hipStream_t st) {
         return fail(CSA_EWORKSPACE, "attention: workspace smaller than csa_attn_workspace_bytes()");
     const int64_t tiles = (max_rows + MTR - 1) / MTR;
     const int64_t split_slots = ((tiles + ns - 1) / ns) * MTR;
+    int rc;
+    if (wide_attn_ok(a.dt, a.H, a.D)) {
+        rc = launch_attn_wide(a, sl2, ns, split_slots, st);
+        if (rc != CSA_OK || ns == 1) return rc;
+        hipLaunchKernelGGL(attn_merge_kernel<bf16_t>, dim3((unsigned)((int64_t)a.T * a.H)), dim3(256), 0, st,
+                           (const float *)a.ws, a.sink, ns, a.rope_cs, a.rope_dim, a.T, a.H, a.D,
+                           (bf16_t *)a.out, a.lse);
+        return check_launch("attn_merge_kernel");
+    }
     const int64_t U = (int64_t)a.T * ns;
     const int64_t blocks = ((U + 7) / 8) * 8 * (a.H / MHG);
     hipLaunchKernelGGL(attn_mfma_kernel, dim3((unsigned)blocks), dim3(256), 0, st, (const bf16_t *)a.q,
                        (const bf16_t *)a.kv, a.sink, a.idx, a.k, a.ratio, sl2, (const bf16_t *)a.swa,
                        a.swa_pos0, a.swa_rows, a.window, a.q_seq, a.q_pos, a.rope_cs, a.rope_dim, a.T, a.B,
                        a.N, a.H, (bf16_t *)a.out, a.lse, (float *)a.ws, ns, split_slots);
-    int rc = check_launch("attn_mfma_kernel");
+    rc = check_launch("attn_mfma_kernel");
     if (rc != CSA_OK || ns == 1) return rc;
     hipLaunchKernelGGL(attn_merge_kernel<bf16_t>, dim3((unsigned)((int64_t)a.T * a.H)), dim3(256), 0, st,
                        (const float *)a.ws, a.sink, ns, a.rope_cs, a.rope_dim, a.T, a.H, a.D, (bf16_t *)a.out,
