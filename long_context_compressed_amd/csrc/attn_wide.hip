@@ -30,12 +30,21 @@ constexpr int WD = 512;     // head dim
 constexpr int WR = 32;      // rows per tile
 constexpr int WH = 64;      // heads per workgroup (16 per wavefront)
 constexpr float kLazy = 8.f; // log2 headroom of the reference maximum
+#ifndef SD_AHEAD
+#define SD_AHEAD 3  // K-fragment chunks read ahead of the score matrix ops
+#endif
+#ifndef PV_AHEAD
+#define PV_AHEAD 4  // V-fragment chunks read ahead of the output matrix ops
+#endif
 constexpr int kIdxCache = 4096; // top-k indices of one split kept in LDS (k <= 4096)
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef unsigned int u32x4w __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const u32x4w gu32x4;
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2w __attribute__((ext_vector_type(2)));  // converts with v_cvt_pk_bf16_f32 (RNE)
 
 // LDS pitch of a tile row: 512 bf16 + 16 bf16 of padding. With the 32-byte pad both the
 // 16-byte row-fragment reads of 16 rows and the transposing reads of 16 rows x 32 bytes
@@ -132,87 +141,95 @@ attn_wide_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, co
     if (ratio <= 0)
         for (int64_t x = threadIdx.x; x < jm - j0; x += 256) sidx[x] = idx[(int64_t)t * k + j0 + x];
     __syncthreads();
-    // rows of a tile: lane r < 32 resolves slot jt + r; validity is a 32-bit mask. Rows
-    // without data read a valid stand-in address (this wave's own q rows) and are zeroed, so
-    // every load is issued unconditionally and the wait counts stay static.
+    // Rows without data read a valid stand-in address (this wave's own q rows) and are
+    // masked out of the softmax, so every load is issued unconditionally and the wait
+    // counts stay static.
     const bf16_t *standin = q + ((int64_t)t * H + head0) * WD;
-    // a row is named by (base, element offset) with base 0 = kv, 1 = swa, 2 = the stand-in;
-    // loads rebuild the address from the kernel arguments, so they stay global-memory loads
-    auto tile_ptrs = [&](int64_t jt, int64_t &myoff, int &mybase) -> uint32_t {
+    // Row addresses of the tile at slot jt: lane r < 32 resolves slot jt + r to a byte
+    // address (the stand-in when the slot has no row) and the tile's 32-bit validity mask
+    // comes from a ballot.
+    auto tile_rows = [&](int64_t jt, uint64_t &addr) -> uint32_t {
         const int64_t j = jt + (lane & 31);
-        int64_t off = 0;
-        int base = 2;
+        const bf16_t *p = standin;
         if (j < j1) {
             if (j < c.nmain) {
                 const int64_t id = (ratio <= 0) ? (int64_t)sidx[j - j0] : j;
-                if (id >= 0 && id < N) {
-                    off = ((int64_t)c.s * N + id) * WD;
-                    base = 0;
-                }
+                if (id >= 0 && id < N) p = kv + ((int64_t)c.s * N + id) * WD;
             } else {
                 const int64_t r = c.lo + (j - c.nmain) - c.swa0;
-                if (r >= 0 && r < swa_rows) {
-                    off = ((int64_t)c.s * swa_rows + r) * WD;
-                    base = 1;
-                }
+                if (r >= 0 && r < swa_rows) p = swa + ((int64_t)c.s * swa_rows + r) * WD;
             }
         }
-        myoff = off;
-        mybase = base;
-        return (uint32_t)(__ballot(base != 2) & 0xffffffffull);
+        addr = (uint64_t)(uintptr_t)p;
+        return (uint32_t)(__ballot(p != standin) & 0xffffffffull);
     };
-    // wave w stages rows 8w..8w+7 of a tile (16 bytes of each per lane) in eight named
-    // registers; the per-row steps are macros so nothing is an array the compiler could keep
-    // in memory
+    // Wave w stages rows 8w..8w+7 of a tile, 16 bytes of each per lane, in eight named
+    // registers (macros, so nothing is an array the compiler could keep in memory). A
+    // load's row is the same for the whole wave: its address is read out of the
+    // resolving lane into scalar registers.
+    const int wu = __builtin_amdgcn_readfirstlane(w);
     uint4 st0, st1, st2, st3, st4, st5, st6, st7;
-#define CSA_LD1(I, OFF, BASE)                                                         \
+#define CSA_LD1(I, ADDR)                                                              \
     {                                                                                 \
-        const int64_t off_ = __shfl((long long)(OFF), 8 * w + (I));                   \
-        const int bs_ = __shfl((BASE), 8 * w + (I));                                  \
-        const bf16_t *bp_ = (bs_ == 0) ? kv : ((bs_ == 1) ? swa : standin);          \
-        st##I = reinterpret_cast<const uint4 *>(bp_ + off_)[lane];                    \
+        const uint32_t lo_ = __builtin_amdgcn_readlane((uint32_t)(ADDR), 8 * wu + (I)); \
+        const uint32_t hi_ = __builtin_amdgcn_readlane((uint32_t)((ADDR) >> 32), 8 * wu + (I)); \
+        const gu32x4 *rp_ = (const gu32x4 *)(((uint64_t)hi_ << 32) | lo_);           \
+        st##I = __builtin_bit_cast(uint4, rp_[lane]);                                 \
     }
-#define CSA_TILE_LOAD(OFF, BASE)                                                      \
-    CSA_LD1(0, OFF, BASE) CSA_LD1(1, OFF, BASE) CSA_LD1(2, OFF, BASE) CSA_LD1(3, OFF, BASE) \
-    CSA_LD1(4, OFF, BASE) CSA_LD1(5, OFF, BASE) CSA_LD1(6, OFF, BASE) CSA_LD1(7, OFF, BASE)
-    // rows without data hold the stand-in's finite values: their logits are masked to -inf,
-    // so they enter the products only with weight 0
-#define CSA_ST1(I, BUF) *reinterpret_cast<uint4 *>(&KV[(BUF)][(8 * w + (I)) * WP + lane * 8]) = st##I;
+#define CSA_TILE_LOAD(A)                                                              \
+    CSA_LD1(0, A) CSA_LD1(1, A) CSA_LD1(2, A) CSA_LD1(3, A)                           \
+    CSA_LD1(4, A) CSA_LD1(5, A) CSA_LD1(6, A) CSA_LD1(7, A)
+#define CSA_ST1(I, BUF) *reinterpret_cast<uint4 *>(&KV[(BUF)][(8 * wu + (I)) * WP + lane * 8]) = st##I;
 #define CSA_TILE_STORE(BUF)                                                           \
     CSA_ST1(0, BUF) CSA_ST1(1, BUF) CSA_ST1(2, BUF) CSA_ST1(3, BUF)                   \
     CSA_ST1(4, BUF) CSA_ST1(5, BUF) CSA_ST1(6, BUF) CSA_ST1(7, BUF)
 
     uint32_t valid = 0u, valid_next = 0u;
     if (j0 < j1) {
-        int64_t myoff;
-        int mybase;
-        valid = tile_ptrs(j0, myoff, mybase);
-        CSA_TILE_LOAD(myoff, mybase)
+        uint64_t ra;
+        valid = tile_rows(j0, ra);
+        CSA_TILE_LOAD(ra)
         CSA_TILE_STORE(0)
     }
     __syncthreads();
+    // Every prologue load (Q fragments, first tile) has landed: without this the
+    // loop's wait counters start pessimistic and stall the first matrix ops.
+    __builtin_amdgcn_s_waitcnt(0);
 
     int it = 0;
     for (int64_t jt = j0; jt < j1; jt += WR, ++it) {
         const int buf = it & 1;
         const bool has_next = jt + WR < j1;
         if (has_next) {  // the next tile's rows load while this one is computed
-            int64_t myoff;
-            int mybase;
-            valid_next = tile_ptrs(jt + WR, myoff, mybase);
-            CSA_TILE_LOAD(myoff, mybase)
+            uint64_t ra;
+            valid_next = tile_rows(jt + WR, ra);
+            CSA_TILE_LOAD(ra)
         }
         const bf16_t *tile = KV[buf];
     {
         f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        {
+            // Register ring of K fragments: chunk kk (rows of both 16-row halves) is
+            // read SD_AHEAD chunks before its two matrix ops issue.
+            bf16x8 ring[SD_AHEAD + 1][2];
+            const bf16_t *kb = tile + l16 * WP + g4 * 8;
 #pragma unroll
-        for (int kk = 0; kk < 16; ++kk)
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                const int row = 16 * m + l16;
-                const bf16x8 a = ld_bf16x8(tile + row * WP + (4 * kk + g4) * 8);
-                sacc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[kk], sacc[m], 0, 0, 0);
+            for (int c = 0; c < SD_AHEAD; ++c) {
+                ring[c][0] = ld_bf16x8(kb + 32 * c);
+                ring[c][1] = ld_bf16x8(kb + 16 * WP + 32 * c);
             }
+#pragma unroll
+            for (int kk = 0; kk < 16; ++kk) {
+                if (kk + SD_AHEAD < 16) {
+                    ring[(kk + SD_AHEAD) % (SD_AHEAD + 1)][0] = ld_bf16x8(kb + 32 * (kk + SD_AHEAD));
+                    ring[(kk + SD_AHEAD) % (SD_AHEAD + 1)][1] = ld_bf16x8(kb + 16 * WP + 32 * (kk + SD_AHEAD));
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ring[kk % (SD_AHEAD + 1)][0], qf[kk], sacc[0], 0, 0, 0);
+                sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ring[kk % (SD_AHEAD + 1)][1], qf[kk], sacc[1], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
 
         float z[2][4], tmax = -INFINITY;
 #pragma unroll
@@ -248,7 +265,7 @@ attn_wide_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, co
                 for (int r = 0; r < 4; r += 2) {
                     const float p0 = exp2f(z[m][r] - mu), p1 = exp2f(z[m][r + 1] - mu);
                     rs += p0 + p1;
-                    pk[2 * m + r / 2] = (uint32_t)f32_to_bf16(p0) | ((uint32_t)f32_to_bf16(p1) << 16);
+                    pk[2 * m + r / 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{p0, p1}, bf16x2w));
                 }
             rs += __shfl_xor(rs, 16);
             rs += __shfl_xor(rs, 32);
@@ -260,13 +277,24 @@ attn_wide_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, co
             const int s4 = l16 >> 2, sc = l16 & 3;
         const bf16_t *v0 = tile + (4 * g4 + s4) * WP + 4 * sc;
         const bf16_t *v1 = v0 + 16 * WP;
+        // V fragments ride a register ring PV_AHEAD matrix ops ahead.
+        bf16x4v vr[PV_AHEAD + 1][2];
+#pragma unroll
+        for (int c = 0; c < PV_AHEAD; ++c) {
+            vr[c][0] = __builtin_bit_cast(bf16x4v, ld_tr(v0 + 16 * c));
+            vr[c][1] = __builtin_bit_cast(bf16x4v, ld_tr(v1 + 16 * c));
+        }
 #pragma unroll
         for (int nd = 0; nd < 32; ++nd) {
-            const bf16x4v va = __builtin_bit_cast(bf16x4v, ld_tr(v0 + 16 * nd));
-            const bf16x4v vb = __builtin_bit_cast(bf16x4v, ld_tr(v1 + 16 * nd));
-            const bf16x8 vf = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
-            acc[nd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf, vf, acc[nd], 0, 0, 0);
+            if (nd + PV_AHEAD < 32) {
+                vr[(nd + PV_AHEAD) % (PV_AHEAD + 1)][0] = __builtin_bit_cast(bf16x4v, ld_tr(v0 + 16 * (nd + PV_AHEAD)));
+                vr[(nd + PV_AHEAD) % (PV_AHEAD + 1)][1] = __builtin_bit_cast(bf16x4v, ld_tr(v1 + 16 * (nd + PV_AHEAD)));
             }
+            __builtin_amdgcn_sched_barrier(0);
+            const bf16x8 vf = __builtin_shufflevector(vr[nd % (PV_AHEAD + 1)][0], vr[nd % (PV_AHEAD + 1)][1], 0, 1, 2, 3, 4, 5, 6, 7);
+            acc[nd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf, vf, acc[nd], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         }
     }
 
