@@ -218,6 +218,31 @@ def test_sparse_attn(csa, orc, case):
     assert_rel(lse, rlse, TOL_F32 if c["dt"] == torch.float32 else 2e-3, "sparse attn lse")
 
 
+@pytest.mark.parametrize("T,H", [(256, 64), (2, 128), (3, 64)])
+def test_sparse_attn_growing_logits(csa, orc, T, H):
+    """Rows whose magnitude grows with the index, visited in index order: the running
+    maximum keeps jumping by far more than the lazy headroom, so the rescaling of the
+    accumulators runs many times (single pass for T=256, split otherwise)."""
+    say("sparse_attn growing", T, H)
+    D, B, N, k = 512, 1, 700, 512
+    pos = [8 * N + t for t in range(T)]
+    # no RoPE here: the kernel rounds the rotated q to bf16 (as a model applying RoPE in
+    # bf16 would), and with keys this large that rounding alone moves the logits by a few
+    # percent of a unit, which is not what this test is about
+    q, kv, swa, sink, q_seq, q_pos, idx, p0, rope = _attn_inputs(900 + T, T, H, D, B, N, k, 128,
+                                                              torch.bfloat16, pos, with_rope=False,
+                                                              bad_idx=False)
+    grow = (1.0 + 0.05 * torch.arange(N, dtype=torch.float32, device=DEV)).view(1, N, 1)
+    kv = (kv.float() * grow).to(torch.bfloat16)
+    idx = torch.sort(idx, dim=1).values.contiguous()
+    scale = 1.0 / np.sqrt(D)
+    out, lse = csa.sparse_attn(q, kv, sink, idx, scale, swa, p0, 128, q_seq, q_pos, rope, 64)
+    torch.cuda.synchronize()
+    ref, rlse = orc.sparse_attn(q, kv, sink, idx, scale, swa, p0, 128, q_seq, q_pos, rope, 64)
+    assert_rel(out, ref, TOL_BF16, "growing-logit attn out")
+    assert_rel(lse, rlse, 2e-3, "growing-logit attn lse")
+
+
 @pytest.mark.parametrize("case", [
     dict(T=4, H=128, N=300, B=4, pos=[300 * 128, 300 * 128 + 5, 200 * 128 - 1, 127]),   # decode, split
     dict(T=256, H=128, N=64, B=1, pos=None),                                          # causal prefill
