@@ -77,6 +77,7 @@ def main():
     import torch
 
     import long_context_compressed_amd as csa
+    from long_context_compressed_amd import pipeline
     import workloads as W
 
     dev = "cuda"
@@ -86,55 +87,12 @@ def main():
         return prefill_main(a)
     cfg = W.PRO if a.workload == "pro_decode_1m" else W.FLASH
     B, T, n, N, D, H, k = cfg.B, cfg.T, cfg.n, cfg.N, cfg.c, cfg.H, cfg.k
-    s = cfg.seed
     NH = cfg.n // 128  # HCA summaries (8,192 at 2^20 tokens)
-    bf = torch.bfloat16
 
-    # ---- inputs (HBM-resident) ------------------------------------------------------
-    inp = W.decode_inputs(cfg, dev)
-    kv, k_I = inp["kv"], inp["k_I"]
-    summ = W.normal((B, NH, D), W.HCA.seed, "summ", dtype=bf, device=dev)
-    sink_h = W.normal((H,), W.HCA.seed, "sink", device=dev)
-    # the block [n-4, n): a- and b-branch content/logits, plus the carry (block n-8..n-5)
-    blk = {nm: W.normal((B, 4, D), s, "new_" + nm, dtype=bf, device=dev) for nm in ("Ca", "Cb", "Za", "Zb")}
-    carry = {nm: W.normal((B, 4, D), s, "carry_" + nm, dtype=bf, device=dev) for nm in ("C", "Z")}
-    iblk = {nm: W.normal((B, 4, 8192), s, "inew_" + nm, dtype=bf, device=dev) for nm in ("Ca", "Cb", "Za", "Zb")}
-    icarry = {nm: W.normal((B, 4, 8192), s, "icarry_" + nm, dtype=bf, device=dev) for nm in ("C", "Z")}
-    hblk = {nm: W.normal((B, 128, D), W.HCA.seed, "hnew_" + nm, dtype=bf, device=dev) for nm in ("C", "Z")}
-
-    kv_new = kv[:, N - 1:N, :]
-    kI_new = k_I.view(B, N, 8192)[:, N - 1:N, :]
-    summ_new = summ[:, NH - 1:NH, :]
-    scores = torch.empty((T, N), dtype=torch.float32, device=dev)
-    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
-    topk_ws = torch.empty(max(1, csa.topk_workspace_bytes(T, N, k)), dtype=torch.uint8, device=dev)
-    attn_ws = torch.empty(max(1, csa.attn_workspace_bytes(T, H, D, k + cfg.window)), dtype=torch.uint8, device=dev)
-    hca_ws = torch.empty(max(1, csa.attn_workspace_bytes(T, H, D, NH + cfg.window)), dtype=torch.uint8, device=dev)
-    out = torch.empty((T, H, D), dtype=bf, device=dev)
-    out_h = torch.empty((T, H, D), dtype=bf, device=dev)
-    lse = torch.empty((T, H), dtype=torch.float32, device=dev)
-    lse_h = torch.empty((T, H), dtype=torch.float32, device=dev)
-    scale = cfg.scale
+    # ---- inputs (HBM-resident) and the step's buffers -----------------------------------
+    inp = W.decode_step_inputs(cfg, dev)
+    step = pipeline.DecodeStep(inp, k, cfg.window, cfg.rope_dim, cfg.scale)
     torch.cuda.synchronize()
-
-    def step(ev=None):
-        csa.compress(blk["Ca"], blk["Za"], blk["Cb"], blk["Zb"], carry["C"], carry["Z"], ratio=4, overlap=1,
-                     out=kv_new)
-        csa.compress(iblk["Ca"], iblk["Za"], iblk["Cb"], iblk["Zb"], icarry["C"], icarry["Z"], ratio=4,
-                     overlap=1, out=kI_new)
-        if ev is not None:
-            ev[0].record()
-        csa.index_scores(inp["q_I"], inp["w"], k_I, inp["q_seq"], inp["q_pos"], scores=scores)
-        if ev is not None:
-            ev[1].record()
-        csa.topk(scores, k, idx=idx, workspace=topk_ws)
-        csa.sparse_attn(inp["q"], kv, inp["sink"], idx, scale, inp["swa"], inp["swa_pos0"], cfg.window,
-                        inp["q_seq"], inp["q_pos"], inp["rope_cs"], cfg.rope_dim, out=out, lse=lse,
-                        workspace=attn_ws)
-        csa.compress(hblk["C"], hblk["Z"], ratio=128, overlap=0, out=summ_new)
-        csa.hca_attn(inp["q"], summ, sink_h, 128, scale, inp["swa"], inp["swa_pos0"], cfg.window,
-                     inp["q_seq"], inp["q_pos"], inp["rope_cs"], cfg.rope_dim, out=out_h, lse=lse_h,
-                     workspace=hca_ws)
 
     for _ in range(a.warmup):
         step()
@@ -147,6 +105,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    # the events sit on the stream the library launches on (torch's current stream)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -158,7 +117,7 @@ def main():
     scan_avg_s = float(np.mean(scan_ms)) / 1e3
 
     # ---- per-stage times (separate, untimed-for-value pass) ---------------------------
-    def timed(fn, reps=10):
+    def timed(fn, reps=50):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         fn()
         torch.cuda.synchronize()
@@ -170,21 +129,14 @@ def main():
         return e0.elapsed_time(e1) / reps
 
     stages = {
-        "compress_csa_kv_and_index_key": timed(lambda: (
-            csa.compress(blk["Ca"], blk["Za"], blk["Cb"], blk["Zb"], carry["C"], carry["Z"], out=kv_new),
-            csa.compress(iblk["Ca"], iblk["Za"], iblk["Cb"], iblk["Zb"], icarry["C"], icarry["Z"], out=kI_new))),
-        "index_scores": timed(lambda: csa.index_scores(inp["q_I"], inp["w"], k_I, inp["q_seq"], inp["q_pos"],
-                                                       scores=scores)),
-        "topk": timed(lambda: csa.topk(scores, k, idx=idx, workspace=topk_ws)),
-        "sparse_attn": timed(lambda: csa.sparse_attn(inp["q"], kv, inp["sink"], idx, scale, inp["swa"],
-                                                     inp["swa_pos0"], cfg.window, inp["q_seq"], inp["q_pos"],
-                                                     inp["rope_cs"], cfg.rope_dim, out=out, lse=lse,
-                                                     workspace=attn_ws)),
-        "compress_hca": timed(lambda: csa.compress(hblk["C"], hblk["Z"], ratio=128, overlap=0, out=summ_new)),
-        "hca_attn": timed(lambda: csa.hca_attn(inp["q"], summ, sink_h, 128, scale, inp["swa"], inp["swa_pos0"],
-                                               cfg.window, inp["q_seq"], inp["q_pos"], inp["rope_cs"],
-                                               cfg.rope_dim, out=out_h, lse=lse_h, workspace=hca_ws)),
+        "compress_csa_kv_and_index_key": timed(step.compress),
+        "index_scores": timed(step.index, reps=10),
+        "topk": timed(step.select),
+        "sparse_attn": timed(step.attend),
+        "compress_hca": timed(step.hca_compress),
+        "hca_attn": timed(step.hca),
     }
+    kv, k_I, summ, sink_h, scores, idx = inp["kv"], inp["k_I"], inp["summ"], inp["sink_h"], step.scores, step.idx
 
     # algorithmic bytes of one index-scan launch: every visible key block once
     # (64 x 128 bf16 = 16 KiB per entry per sequence) + q_I + w + the fp32 scores
@@ -221,6 +173,8 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": alg_bytes,
             "avg_launch_ms": round(scan_avg_s * 1e3, 4),
+            "median_launch_ms": round(float(np.median(scan_ms)), 4),
+            "min_launch_ms": round(float(np.min(scan_ms)), 4),
         },
         "stages_ms": {kk: round(v, 4) for kk, v in stages.items()},
     }
@@ -245,75 +199,24 @@ def prefill_main(a):
     import numpy as np
     import torch
 
-    import long_context_compressed_amd as csa
+    from long_context_compressed_amd import pipeline
     import workloads as W
 
-    dev, bf = "cuda", torch.bfloat16
+    dev = "cuda"
+    inp = W.prefill_inputs(a.workload, dev)
+    cfg, T, D, H = inp["cfg"], inp["T"], inp["D"], inp["H"]
     if a.workload == "pro_prefill_chunk":
-        cfg = W.PRO_PREFILL
-        T, n0, D, H, k, s = cfg.T, cfg.n, cfg.c, cfg.H, cfg.k, cfg.seed
-        N = (n0 + T) // 4
-        old = n0 // 4
-        kv = W.normal((1, N, D), s, "kv", dtype=bf, device=dev)
-        C = {nm: W.normal((1, T, D), s, nm, dtype=bf, device=dev) for nm in ("Ca", "Cb", "Za", "Zb")}
-        carry = {nm: W.normal((1, 4, D), s, "carry_" + nm, dtype=bf, device=dev) for nm in ("C", "Z")}
-        qc, qsc = W.quantize_mxfp4(W.normal((T, 64, 128), s, "q_I", device=dev))
-        kc, ksc = W.quantize_mxfp4(W.normal((1, N, 64, 128), s, "k_I", device=dev))
-        w = W.normal((T, 64), s, "w", device=dev)
-        q = W.normal((T, H, D), s, "q", dtype=bf, device=dev)
-        swa_rows = T + cfg.window - 1
-        swa = W.normal((1, swa_rows, D), s, "swa", dtype=bf, device=dev)
-        p0 = torch.tensor([n0 - cfg.window + 1], dtype=torch.int64, device=dev)
-        sink = W.normal((H,), s, "sink", device=dev)
-        q_pos = torch.arange(n0, n0 + T, dtype=torch.int64, device=dev)
-        q_seq = torch.zeros(T, dtype=torch.int32, device=dev)
-        cs = W.rope_table(q_pos.cpu(), cfg.rope_dim).to(dev)
-        scores = torch.empty((T, N), dtype=torch.float32, device=dev)
-        idx = torch.empty((T, k), dtype=torch.int32, device=dev)
-        tws = torch.empty(max(1, csa.topk_workspace_bytes(T, N, k)), dtype=torch.uint8, device=dev)
-        aws = torch.empty(max(1, csa.attn_workspace_bytes(T, H, D, k + cfg.window)), dtype=torch.uint8, device=dev)
-        out = torch.empty_like(q)
-        lse = torch.empty((T, H), dtype=torch.float32, device=dev)
-        kv_new = kv[:, old:, :]
-        stages = {
-            "compress": lambda: csa.compress(C["Ca"], C["Za"], C["Cb"], C["Zb"], carry["C"], carry["Z"], out=kv_new),
-            "index_scores_mxfp4": lambda: csa.index_scores(qc, w, kc, q_seq, q_pos, q_I_scale=qsc, k_I_scale=ksc,
-                                                           mxfp4=True, scores=scores),
-            "topk": lambda: csa.topk(scores, k, idx=idx, workspace=tws),
-            "sparse_attn": lambda: csa.sparse_attn(q, kv, sink, idx, cfg.scale, swa, p0, cfg.window, q_seq, q_pos,
-                                                   cs, cfg.rope_dim, out=out, lse=lse, workspace=aws),
-        }
-        rows = k + cfg.window
+        chunk = pipeline.ProPrefillChunk(inp, inp["k"], cfg.window, cfg.rope_dim, cfg.scale)
+        rows = inp["k"] + cfg.window
         flops = 4.0 * T * H * rows * D
         dominant = "sparse_attn"
     else:
-        cfg = W.HCA
-        T, n, D, H, s = W.HCA_PREFILL_T, cfg.n, cfg.c, cfg.H, cfg.seed
-        NH = n // 128
-        summ = W.normal((1, NH, D), s, "summ", dtype=bf, device=dev)
-        Cz = W.normal((1, T, D), s, "C", dtype=bf, device=dev)
-        Zz = W.normal((1, T, D), s, "Z", dtype=bf, device=dev)
-        q = W.normal((T, H, D), s, "q", dtype=bf, device=dev)
-        swa_rows = T + cfg.window - 1
-        swa = W.normal((1, swa_rows, D), s, "swa", dtype=bf, device=dev)
-        p0 = torch.tensor([n - T - cfg.window + 1], dtype=torch.int64, device=dev)
-        sink = W.normal((H,), s, "sink", device=dev)
-        q_pos = torch.arange(n - T, n, dtype=torch.int64, device=dev)
-        q_seq = torch.zeros(T, dtype=torch.int32, device=dev)
-        cs = W.rope_table(q_pos.cpu(), cfg.rope_dim).to(dev)
-        aws = torch.empty(max(1, csa.attn_workspace_bytes(T, H, D, NH + cfg.window)), dtype=torch.uint8, device=dev)
-        out = torch.empty_like(q)
-        lse = torch.empty((T, H), dtype=torch.float32, device=dev)
-        summ_new = summ[:, NH - T // 128:, :]
-        stages = {
-            "compress_hca": lambda: csa.compress(Cz, Zz, ratio=128, overlap=0, out=summ_new),
-            "hca_attn": lambda: csa.hca_attn(q, summ, sink, 128, cfg.scale, swa, p0, cfg.window, q_seq, q_pos, cs,
-                                             cfg.rope_dim, out=out, lse=lse, workspace=aws),
-        }
-        pos = q_pos.cpu().numpy()
-        rows = float(np.sum(np.minimum(NH, pos // 128) + cfg.window))
+        chunk = pipeline.HcaPrefillChunk(inp, cfg.window, cfg.rope_dim, cfg.scale)
+        pos = inp["q_pos"].cpu().numpy()
+        rows = float(np.sum(np.minimum(inp["NH"], pos // 128) + cfg.window))
         flops = 4.0 * H * rows * D
         dominant = "hca_attn"
+    stages = chunk.stages()
     torch.cuda.synchronize()
 
     def step():
@@ -357,7 +260,9 @@ def prefill_main(a):
         "config": {"workload": a.workload, "queries": T, "heads": H, "head_dim": D},
         "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2), "peak": 2500.0,
                      "unit": "TFLOP/s", "frac": round(achieved / 2500.0, 4), "traffic": None,
-                     "algorithmic_flops_per_launch": flops, "avg_launch_ms": round(dom_s * 1e3, 4)},
+                     "algorithmic_flops_per_launch": flops, "avg_launch_ms": round(dom_s * 1e3, 4),
+                     "median_launch_ms": round(float(np.median(dom_ms)), 4),
+                     "min_launch_ms": round(float(np.min(dom_ms)), 4)},
         "stages_ms": stage_ms,
     }
     print(json.dumps(res), flush=True)

@@ -1,0 +1,168 @@
+"""The hot path strung together: a decode step and the two prefill chunks.
+
+Each object allocates its outputs and workspaces once and then only launches the
+library's calls (every step runs in libcsa.so), on torch's current stream. The call
+chain is the one of "DeepSeek-V4 混合注意力" §7 (CSA: compress -> indexer -> top-k ->
+sparse attention; HCA: compress -> dense attention over the summaries).
+"""
+from __future__ import annotations
+
+import torch
+
+from . import (attn_workspace_bytes, compress, hca_attn, index_scores, sparse_attn, topk,
+               topk_workspace_bytes)
+
+
+def _ws(nbytes, dev):
+    return torch.empty(max(1, nbytes), dtype=torch.uint8, device=dev)
+
+
+class DecodeStep:
+    """One decode step of a CSA layer and an HCA layer for B sequences, one query each.
+
+    `inp` holds: q [T][H][D], kv [B][N][D], swa [B][window][D], swa_pos0 [B], sink [H],
+    q_seq [T], q_pos [T], rope_cs [T][R/2][2], q_I [T][64][128], w [T][64],
+    k_I [B][N][64][128], summ [B][n/128][D], sink_h [H], and the completing blocks:
+    blk / carry (KV compressor, ratio 4), iblk / icarry (index-key compressor, ratio 4),
+    hblk (HCA compressor, ratio 128). The step writes the block's new KV row, index key
+    and summary into the last row of kv, k_I and summ, then scores, selects and attends.
+    """
+
+    def __init__(self, inp: dict, k: int, window: int, rope_dim: int, scale: float):
+        self.inp, self.k, self.window, self.rope_dim, self.scale = inp, k, window, rope_dim, scale
+        q, kv, k_I, summ = inp["q"], inp["kv"], inp["k_I"], inp["summ"]
+        T, H, D = q.shape
+        B, N = kv.shape[0], kv.shape[1]
+        NH = summ.shape[1]
+        dev = q.device
+        self.kv_new = kv[:, N - 1:N, :]
+        self.kI_new = k_I.view(B, N, -1)[:, N - 1:N, :]
+        self.summ_new = summ[:, NH - 1:NH, :]
+        self.scores = torch.empty((T, N), dtype=torch.float32, device=dev)
+        self.idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.topk_ws = _ws(topk_workspace_bytes(T, N, k), dev)
+        self.attn_ws = _ws(attn_workspace_bytes(T, H, D, k + window), dev)
+        self.hca_ws = _ws(attn_workspace_bytes(T, H, D, NH + window), dev)
+        self.out = torch.empty((T, H, D), dtype=q.dtype, device=dev)
+        self.lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+        self.out_h = torch.empty((T, H, D), dtype=q.dtype, device=dev)
+        self.lse_h = torch.empty((T, H), dtype=torch.float32, device=dev)
+
+    def compress(self):
+        i = self.inp
+        b, c, ib, ic = i["blk"], i["carry"], i["iblk"], i["icarry"]
+        compress(b["Ca"], b["Za"], b["Cb"], b["Zb"], c["C"], c["Z"], ratio=4, overlap=1, out=self.kv_new)
+        compress(ib["Ca"], ib["Za"], ib["Cb"], ib["Zb"], ic["C"], ic["Z"], ratio=4, overlap=1, out=self.kI_new)
+
+    def index(self):
+        i = self.inp
+        index_scores(i["q_I"], i["w"], i["k_I"], i["q_seq"], i["q_pos"], scores=self.scores)
+
+    def select(self):
+        topk(self.scores, self.k, idx=self.idx, workspace=self.topk_ws)
+
+    def attend(self):
+        i = self.inp
+        sparse_attn(i["q"], i["kv"], i["sink"], self.idx, self.scale, i["swa"], i["swa_pos0"], self.window,
+                    i["q_seq"], i["q_pos"], i["rope_cs"], self.rope_dim, out=self.out, lse=self.lse,
+                    workspace=self.attn_ws)
+
+    def hca_compress(self):
+        h = self.inp["hblk"]
+        compress(h["C"], h["Z"], ratio=128, overlap=0, out=self.summ_new)
+
+    def hca(self):
+        i = self.inp
+        hca_attn(i["q"], i["summ"], i["sink_h"], 128, self.scale, i["swa"], i["swa_pos0"], self.window,
+                 i["q_seq"], i["q_pos"], i["rope_cs"], self.rope_dim, out=self.out_h, lse=self.lse_h,
+                 workspace=self.hca_ws)
+
+    def __call__(self, index_events=None):
+        """The whole step; `index_events` = (start, end) events recorded around the scan."""
+        self.compress()
+        if index_events is not None:
+            index_events[0].record()
+        self.index()
+        if index_events is not None:
+            index_events[1].record()
+        self.select()
+        self.attend()
+        self.hca_compress()
+        self.hca()
+
+
+class ProPrefillChunk:
+    """A CSA prefill chunk: compress the chunk's blocks into the KV cache, MXFP4 index scores
+    of every query against every entry (causal), top-k, sparse attention.
+
+    `inp`: kv [1][N][D] (rows from `old` on are rewritten), C = {Ca, Cb, Za, Zb} [1][T][D],
+    carry = {C, Z} [1][4][D], q_I / q_I_scale, k_I / k_I_scale (MXFP4), w [T][64],
+    q [T][H][D], swa, swa_pos0, sink, q_pos, q_seq, rope_cs.
+    """
+
+    def __init__(self, inp: dict, k: int, window: int, rope_dim: int, scale: float):
+        self.inp, self.k, self.window, self.rope_dim, self.scale = inp, k, window, rope_dim, scale
+        q, kv = inp["q"], inp["kv"]
+        T, H, D = q.shape
+        N = kv.shape[1]
+        dev = q.device
+        self.kv_new = kv[:, inp["old"]:, :]
+        self.scores = torch.empty((T, N), dtype=torch.float32, device=dev)
+        self.idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.topk_ws = _ws(topk_workspace_bytes(T, N, k), dev)
+        self.attn_ws = _ws(attn_workspace_bytes(T, H, D, k + window), dev)
+        self.out = torch.empty_like(q)
+        self.lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+
+    def compress(self):
+        C, c = self.inp["C"], self.inp["carry"]
+        compress(C["Ca"], C["Za"], C["Cb"], C["Zb"], c["C"], c["Z"], out=self.kv_new)
+
+    def index(self):
+        i = self.inp
+        index_scores(i["q_I"], i["w"], i["k_I"], i["q_seq"], i["q_pos"], q_I_scale=i["q_I_scale"],
+                     k_I_scale=i["k_I_scale"], mxfp4=True, scores=self.scores)
+
+    def select(self):
+        topk(self.scores, self.k, idx=self.idx, workspace=self.topk_ws)
+
+    def attend(self):
+        i = self.inp
+        sparse_attn(i["q"], i["kv"], i["sink"], self.idx, self.scale, i["swa"], i["swa_pos0"], self.window,
+                    i["q_seq"], i["q_pos"], i["rope_cs"], self.rope_dim, out=self.out, lse=self.lse,
+                    workspace=self.attn_ws)
+
+    def stages(self):
+        return {"compress": self.compress, "index_scores_mxfp4": self.index, "topk": self.select,
+                "sparse_attn": self.attend}
+
+
+class HcaPrefillChunk:
+    """An HCA prefill chunk: compress the chunk's 128-token blocks into the last summaries,
+    then dense attention of every query over its visible summaries and SWA rows.
+
+    `inp`: summ [1][NH][D] (the last T/128 rows are rewritten), C, Z [1][T][D], q, swa,
+    swa_pos0, sink, q_pos, q_seq, rope_cs.
+    """
+
+    def __init__(self, inp: dict, window: int, rope_dim: int, scale: float):
+        self.inp, self.window, self.rope_dim, self.scale = inp, window, rope_dim, scale
+        q, summ = inp["q"], inp["summ"]
+        T, H, D = q.shape
+        NH = summ.shape[1]
+        self.summ_new = summ[:, NH - T // 128:, :]
+        self.attn_ws = _ws(attn_workspace_bytes(T, H, D, NH + window), q.device)
+        self.out = torch.empty_like(q)
+        self.lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+
+    def compress(self):
+        compress(self.inp["C"], self.inp["Z"], ratio=128, overlap=0, out=self.summ_new)
+
+    def attend(self):
+        i = self.inp
+        hca_attn(i["q"], i["summ"], i["sink"], 128, self.scale, i["swa"], i["swa_pos0"], self.window,
+                 i["q_seq"], i["q_pos"], i["rope_cs"], self.rope_dim, out=self.out, lse=self.lse,
+                 workspace=self.attn_ws)
+
+    def stages(self):
+        return {"compress_hca": self.compress, "hca_attn": self.attend}

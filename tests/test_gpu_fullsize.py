@@ -1,0 +1,188 @@
+"""Parity at the full configuration sizes, in the launch configuration bench.py times.
+
+Each test builds the configuration's inputs on the GPU, runs the same pipeline object
+bench.py times (long_context_compressed_amd.pipeline) and checks sampled outputs against
+the fp64 oracle, stage by stage and fed: every stage's oracle call gets the same inputs as
+the GPU stage (the GPU's upstream outputs, once those have passed). The oracle sees only
+the sampled rows, gathered on the GPU, so no full-size tensor is widened on the host.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from tests.helpers import TOL_BF16, TOL_F32, assert_rel
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def csa():
+    import long_context_compressed_amd as m
+    m.lib()
+    return m
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def _free():
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _check_index_sample(orc, scores, q_I, w, k_I, q_seq, q_pos, ids, mxfp4_scales=None):
+    """Oracle scores of the sampled entries `ids` (shared by every sequence) for every query."""
+    idt = torch.from_numpy(ids).to(k_I.device)
+    if mxfp4_scales is None:
+        k_s = k_I.index_select(1, idt)
+        q_o = q_I
+    else:
+        qs, ks = mxfp4_scales
+        k_s = orc.mxfp4_decode(k_I.index_select(1, idt), ks.index_select(1, idt))
+        q_o = orc.mxfp4_decode(q_I, qs)
+    ref = orc.index_scores(q_o, w, k_s, q_seq, q_pos, entry_ids=ids)
+    gpu = scores.index_select(1, idt).cpu().double().numpy()
+    fin = np.isfinite(ref)
+    assert np.array_equal(fin, np.isfinite(gpu)), "masked (causal) entries differ"
+    assert np.all(gpu[~fin] == -np.inf)
+    assert_rel(gpu[fin], ref[fin], TOL_F32, "index scores (sampled entries)")
+
+
+def _check_topk_fed(orc, scores, idx, k):
+    """Top-k of the GPU scores: identical fp32 inputs give identical sets."""
+    ridx, _ = orc.topk(scores.cpu(), k)
+    gi = idx.cpu().numpy()
+    for t in range(gi.shape[0]):
+        g = gi[t][gi[t] >= 0]
+        r = ridx[t][ridx[t] >= 0]
+        assert sorted(g.tolist()) == sorted(r.tolist()), f"top-k set of query {t}"
+        assert np.all(gi[t, len(g):] == -1)
+
+
+def _gathered_rows(kv, seqs, idx):
+    """kv rows each query selected, as [1][T*k][D] with the matching slot indices."""
+    T, k = idx.shape
+    rows = []
+    for t in range(T):
+        rows.append(kv[int(seqs[t])].index_select(0, idx[t].clamp(min=0).long()))
+    kv_c = torch.cat(rows, 0)[None]
+    slot = torch.arange(T * k, dtype=torch.int32, device=idx.device).view(T, k)
+    idx_c = torch.where(idx >= 0, slot, torch.full_like(slot, -1))
+    return kv_c, idx_c
+
+
+@pytest.mark.parametrize("name", ["flash_decode_128k", "pro_decode_1m"])
+def test_decode_step_full_size(csa, orc, name):
+    from long_context_compressed_amd import pipeline
+
+    cfg = W.CONFIGS[name]
+    say("full-size decode step", name)
+    inp = W.decode_step_inputs(cfg, DEV)
+    step = pipeline.DecodeStep(inp, cfg.k, cfg.window, cfg.rope_dim, cfg.scale)
+    step()
+    torch.cuda.synchronize()
+    B, T, N = cfg.B, cfg.T, cfg.N
+
+    # compressors: the completing block of every sequence (KV entry, index key, summary)
+    b, c, ib, ic, hb = inp["blk"], inp["carry"], inp["iblk"], inp["icarry"], inp["hblk"]
+    assert_rel(step.kv_new, orc.compress(b["Ca"], b["Za"], b["Cb"], b["Zb"], c["C"], c["Z"]), TOL_BF16,
+               "new KV entry")
+    assert_rel(step.kI_new, orc.compress(ib["Ca"], ib["Za"], ib["Cb"], ib["Zb"], ic["C"], ic["Z"]), TOL_BF16,
+               "new index key")
+    assert_rel(step.summ_new, orc.compress(hb["C"], hb["Z"], ratio=128, overlap=0), TOL_BF16, "new summary")
+
+    # index scores: 1,024 sampled entries (both ends included) of every sequence
+    ids = np.unique(np.concatenate([[0, 1, N - 2, N - 1], W.distinct_sample(1020, N, cfg.seed, "fullsize_ids")]))
+    _check_index_sample(orc, step.scores, inp["q_I"], inp["w"], inp["k_I"], inp["q_seq"], inp["q_pos"], ids)
+
+    # top-k over the full 262,144 / 32,768 scores of every query
+    _check_topk_fed(orc, step.scores, step.idx, cfg.k)
+
+    # sparse attention of every query over its selected rows + SWA
+    kv_c, idx_c = _gathered_rows(inp["kv"], inp["q_seq"].cpu().numpy(), step.idx)
+    seq = torch.zeros(T, dtype=torch.int32)
+    swa = inp["swa"].index_select(0, inp["q_seq"].long())
+    p0 = inp["swa_pos0"].index_select(0, inp["q_seq"].long())
+    outs = []
+    for t in range(T):  # one sequence per call: the query's own SWA rows
+        outs.append(orc.sparse_attn(inp["q"][t:t + 1], kv_c, inp["sink"], idx_c[t:t + 1], cfg.scale,
+                                    swa[t:t + 1], p0[t:t + 1], cfg.window, seq[:1], inp["q_pos"][t:t + 1],
+                                    inp["rope_cs"][t:t + 1], cfg.rope_dim))
+    assert_rel(step.out, np.concatenate([o for o, _ in outs]), TOL_BF16, "sparse attention out")
+    assert_rel(step.lse, np.concatenate([l for _, l in outs]), 2e-3, "sparse attention lse")
+
+    # HCA attention of every query over all its visible summaries + SWA
+    ref, rlse = orc.hca_attn(inp["q"], inp["summ"], inp["sink_h"], 128, cfg.scale, inp["swa"], inp["swa_pos0"],
+                             cfg.window, inp["q_seq"], inp["q_pos"], inp["rope_cs"], cfg.rope_dim)
+    assert_rel(step.out_h, ref, TOL_BF16, "hca attention out")
+    assert_rel(step.lse_h, rlse, 2e-3, "hca attention lse")
+    del inp, step, kv_c
+    _free()
+
+
+def test_pro_prefill_chunk_full_size(csa, orc):
+    from long_context_compressed_amd import pipeline
+
+    say("full-size Pro prefill chunk")
+    inp = W.prefill_inputs("pro_prefill_chunk", DEV)
+    cfg, T, N, k = inp["cfg"], inp["T"], inp["N"], inp["k"]
+    ch = pipeline.ProPrefillChunk(inp, k, cfg.window, cfg.rope_dim, cfg.scale)
+    for f in ch.stages().values():
+        f()
+    torch.cuda.synchronize()
+
+    # compressor over the whole chunk (with the carry of the block before it)
+    C, cr = inp["C"], inp["carry"]
+    assert_rel(ch.kv_new, orc.compress(C["Ca"], C["Za"], C["Cb"], C["Zb"], cr["C"], cr["Z"]), TOL_BF16,
+               "chunk KV entries")
+
+    # 16 sampled queries (both ends of the chunk included)
+    sel = np.unique(np.concatenate([[0, 1, T // 2, T - 2, T - 1], W.distinct_sample(11, T, cfg.seed, "fs_q")]))
+    st = torch.from_numpy(sel).to(DEV)
+    pos = inp["q_pos"].index_select(0, st)
+    # index scores: 2,048 sampled entries, including each sampled query's causal boundary
+    edge = np.concatenate([[p // 4 - 1, p // 4, p // 4 + 1] for p in pos.cpu().numpy()])
+    ids = np.unique(np.clip(np.concatenate([[0, N - 1], edge, W.distinct_sample(1980, N, cfg.seed, "fs_e")]),
+                            0, N - 1))
+    _check_index_sample(orc, ch.scores.index_select(0, st), inp["q_I"].index_select(0, st),
+                        inp["w"].index_select(0, st), inp["k_I"], inp["q_seq"].index_select(0, st), pos, ids,
+                        mxfp4_scales=(inp["q_I_scale"].index_select(0, st), inp["k_I_scale"]))
+    # top-k of the sampled queries' full score rows
+    _check_topk_fed(orc, ch.scores.index_select(0, st), ch.idx.index_select(0, st), k)
+    # sparse attention of the sampled queries
+    idx_s = ch.idx.index_select(0, st)
+    kv_c, idx_c = _gathered_rows(inp["kv"], np.zeros(len(sel), np.int64), idx_s)
+    ref, rlse = orc.sparse_attn(inp["q"].index_select(0, st), kv_c, inp["sink"], idx_c, cfg.scale, inp["swa"],
+                                inp["swa_pos0"], cfg.window, inp["q_seq"].index_select(0, st), pos,
+                                inp["rope_cs"].index_select(0, st), cfg.rope_dim)
+    assert_rel(ch.out.index_select(0, st), ref, TOL_BF16, "prefill sparse attention out")
+    assert_rel(ch.lse.index_select(0, st), rlse, 2e-3, "prefill sparse attention lse")
+    del inp, ch, kv_c
+    _free()
+
+
+def test_hca_prefill_chunk_full_size(csa, orc):
+    from long_context_compressed_amd import pipeline
+
+    say("full-size HCA prefill chunk")
+    inp = W.prefill_inputs("hca_prefill_4k", DEV)
+    cfg, T = inp["cfg"], inp["T"]
+    ch = pipeline.HcaPrefillChunk(inp, cfg.window, cfg.rope_dim, cfg.scale)
+    for f in ch.stages().values():
+        f()
+    torch.cuda.synchronize()
+    assert_rel(ch.summ_new, orc.compress(inp["C"], inp["Z"], ratio=128, overlap=0), TOL_BF16, "chunk summaries")
+    sel = np.unique(np.concatenate([[0, 127, 128, T - 1], W.distinct_sample(4, T, cfg.seed, "fs_h")]))
+    st = torch.from_numpy(sel).to(DEV)
+    ref, rlse = orc.hca_attn(inp["q"].index_select(0, st), inp["summ"], inp["sink"], 128, cfg.scale, inp["swa"],
+                             inp["swa_pos0"], cfg.window, inp["q_seq"].index_select(0, st),
+                             inp["q_pos"].index_select(0, st), inp["rope_cs"].index_select(0, st), cfg.rope_dim)
+    assert_rel(ch.out.index_select(0, st), ref, TOL_BF16, "HCA prefill attention out")
+    assert_rel(ch.lse.index_select(0, st), rlse, 2e-3, "HCA prefill attention lse")
+    del inp, ch
+    _free()

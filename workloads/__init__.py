@@ -231,3 +231,82 @@ def decode_inputs(cfg: Config, device="cpu", with_index=True) -> dict:
         inp["w"] = normal((cfg.T, cfg.H_I), s, "w", scale=wscale, device=device)
         inp["k_I"] = normal((B, N, cfg.H_I, cfg.D_I), s, "k_I", dtype=dt, device=device)
     return inp
+
+
+def decode_step_inputs(cfg: Config, device="cpu") -> dict:
+    """Everything one decode step of a CSA layer plus an HCA layer reads, for B sequences.
+
+    On top of decode_inputs: the block [n-4, n) that completes with the step (a- and
+    b-branch contents/logits for the attention KV and for the index keys, and the carry
+    block [n-8, n-4)), the HCA summaries [B][n/128][D] with their own sinks, and the
+    ratio-128 block that completes the last summary. All N(0,1) bf16 (sinks fp32).
+    """
+    s, B, D, bf = cfg.seed, cfg.B, cfg.c, torch.bfloat16
+    NH = cfg.n // 128
+    inp = decode_inputs(cfg, device)
+    inp["summ"] = normal((B, NH, D), HCA.seed, "summ", dtype=bf, device=device)
+    inp["sink_h"] = normal((cfg.H,), HCA.seed, "sink", device=device)
+    inp["blk"] = {nm: normal((B, 4, D), s, "new_" + nm, dtype=bf, device=device) for nm in ("Ca", "Cb", "Za", "Zb")}
+    inp["carry"] = {nm: normal((B, 4, D), s, "carry_" + nm, dtype=bf, device=device) for nm in ("C", "Z")}
+    KW = cfg.H_I * cfg.D_I
+    inp["iblk"] = {nm: normal((B, 4, KW), s, "inew_" + nm, dtype=bf, device=device) for nm in ("Ca", "Cb", "Za", "Zb")}
+    inp["icarry"] = {nm: normal((B, 4, KW), s, "icarry_" + nm, dtype=bf, device=device) for nm in ("C", "Z")}
+    inp["hblk"] = {nm: normal((B, 128, D), HCA.seed, "hnew_" + nm, dtype=bf, device=device) for nm in ("C", "Z")}
+    return inp
+
+
+def prefill_inputs(name: str, device="cpu") -> dict:
+    """The tensors of one prefill chunk.
+
+    "pro_prefill_chunk": 8,192 new tokens at positions 65,536..73,727 of one sequence.
+      kv [1][18432][512] (rows 0..16,383 are the old cache, 16,384.. are rewritten by the
+      compressor from Ca/Cb/Za/Zb [1][8192][512] and the carry of block 16,383);
+      MXFP4 index operands q_I [8192][64][128] and k_I [1][18432][64][128] (encoded from
+      N(0,1)); w [8192][64] N(0,1); q [8192][128][512]; SWA rows for positions
+      65,409..73,727; sinks [128]; RoPE tables at each query's position.
+    "hca_prefill_4k": the last 4,096 tokens of a 2^20 context. summaries [1][8192][512]
+      (the last 32 rewritten from C/Z [1][4096][512]); q [4096][128][512]; SWA rows for
+      positions 2^20 - 4,223 .. 2^20 - 1; sinks [128].
+    """
+    bf = torch.bfloat16
+    if name == "pro_prefill_chunk":
+        cfg = PRO_PREFILL
+        T, n0, D, H, s = cfg.T, cfg.n, cfg.c, cfg.H, cfg.seed
+        N = (n0 + T) // 4
+        qc, qsc = quantize_mxfp4(normal((T, 64, 128), s, "q_I", device=device))
+        kc, ksc = quantize_mxfp4(normal((1, N, 64, 128), s, "k_I", device=device))
+        q_pos = torch.arange(n0, n0 + T, dtype=torch.int64, device=device)
+        return dict(
+            cfg=cfg, T=T, N=N, old=n0 // 4, D=D, H=H, k=cfg.k,
+            kv=normal((1, N, D), s, "kv", dtype=bf, device=device),
+            C={nm: normal((1, T, D), s, nm, dtype=bf, device=device) for nm in ("Ca", "Cb", "Za", "Zb")},
+            carry={nm: normal((1, 4, D), s, "carry_" + nm, dtype=bf, device=device) for nm in ("C", "Z")},
+            q_I=qc, q_I_scale=qsc, k_I=kc, k_I_scale=ksc,
+            w=normal((T, 64), s, "w", device=device),
+            q=normal((T, H, D), s, "q", dtype=bf, device=device),
+            swa=normal((1, T + cfg.window - 1, D), s, "swa", dtype=bf, device=device),
+            swa_pos0=torch.tensor([n0 - cfg.window + 1], dtype=torch.int64, device=device),
+            sink=normal((H,), s, "sink", device=device),
+            q_pos=q_pos,
+            q_seq=torch.zeros(T, dtype=torch.int32, device=device),
+            rope_cs=rope_table(q_pos.cpu(), cfg.rope_dim).to(device),
+        )
+    if name == "hca_prefill_4k":
+        cfg = HCA
+        T, n, D, H, s = HCA_PREFILL_T, cfg.n, cfg.c, cfg.H, cfg.seed
+        NH = n // 128
+        q_pos = torch.arange(n - T, n, dtype=torch.int64, device=device)
+        return dict(
+            cfg=cfg, T=T, NH=NH, D=D, H=H,
+            summ=normal((1, NH, D), s, "summ", dtype=bf, device=device),
+            C=normal((1, T, D), s, "C", dtype=bf, device=device),
+            Z=normal((1, T, D), s, "Z", dtype=bf, device=device),
+            q=normal((T, H, D), s, "q", dtype=bf, device=device),
+            swa=normal((1, T + cfg.window - 1, D), s, "swa", dtype=bf, device=device),
+            swa_pos0=torch.tensor([n - T - cfg.window + 1], dtype=torch.int64, device=device),
+            sink=normal((H,), s, "sink", device=device),
+            q_pos=q_pos,
+            q_seq=torch.zeros(T, dtype=torch.int32, device=device),
+            rope_cs=rope_table(q_pos.cpu(), cfg.rope_dim).to(device),
+        )
+    raise ValueError(f"unknown prefill workload {name!r}")
