@@ -41,7 +41,8 @@ def parse():
     ap.add_argument("--cpu-entries", type=int, default=16384,
                     help="index entries per query in the oracle's bounded sample")
     ap.add_argument("--workload", default="pro_decode_1m",
-                    choices=["pro_decode_1m", "flash_decode_128k", "pro_prefill_chunk", "hca_prefill_4k"],
+                    choices=["pro_decode_1m", "flash_decode_128k", "pro_decode_1m_shared_keys", "pro_prefill_chunk",
+                             "hca_prefill_4k"],
                     help="pro_decode_1m is the benchmark line; the others print the same record for "
                          "the other configurations' shapes (profiling aid)")
     ap.add_argument("--profile-copy", action="store_true",
@@ -85,12 +86,13 @@ def main():
     csa.lib()
     if a.workload in ("pro_prefill_chunk", "hca_prefill_4k"):
         return prefill_main(a)
-    cfg = W.PRO if a.workload == "pro_decode_1m" else W.FLASH
+    cfg = W.FLASH if a.workload == "flash_decode_128k" else W.PRO
+    shared = a.workload == "pro_decode_1m_shared_keys"
     B, T, n, N, D, H, k = cfg.B, cfg.T, cfg.n, cfg.N, cfg.c, cfg.H, cfg.k
     NH = cfg.n // 128  # HCA summaries (8,192 at 2^20 tokens)
 
     # ---- inputs (HBM-resident) and the step's buffers -----------------------------------
-    inp = W.decode_step_inputs(cfg, dev)
+    inp = W.decode_step_inputs(cfg, dev, shared_keys=shared)
     step = pipeline.DecodeStep(inp, k, cfg.window, cfg.rope_dim, cfg.scale)
     torch.cuda.synchronize()
 
@@ -140,9 +142,9 @@ def main():
 
     # algorithmic bytes of one index-scan launch: every visible key block once
     # (64 x 128 bf16 = 16 KiB per entry per sequence) + q_I + w + the fp32 scores
-    alg_bytes = B * N * 64 * 128 * 2 + T * 64 * 128 * 2 + T * 64 * 4 + T * N * 4
+    alg_bytes = B * N * (1 if shared else 64) * 128 * 2 + T * 64 * 128 * 2 + T * 64 * 4 + T * N * 4
     achieved = alg_bytes / scan_avg_s / 1e9
-    traffic = traffic_from_profile(alg_bytes)
+    traffic = None if shared or a.workload != "pro_decode_1m" else traffic_from_profile(alg_bytes)
 
     res = {
         "metric": METRIC,
@@ -158,13 +160,15 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1), bf16)",
         "config": {
-            "workload": (f"{cfg.name}: one CSA layer + one HCA layer decode step, B={B} sequences x 1 query at "
-                         f"t={n}; {N:,} entries x 64 heads x 128 bf16 index keys per sequence, top-k {k:,}, "
+            "workload": (f"{a.workload}: one CSA layer + one HCA layer decode step, B={B} sequences x 1 query at "
+                         f"t={n}; {N:,} entries x {'1 shared' if shared else '64 per-head'} x 128 bf16 index keys "
+                         f"per sequence, top-k {k:,}, "
                          f"{H} heads x {D} shared KV, SWA {cfg.window}, {NH:,} HCA summaries"),
             "batch": B, "context": n, "index_entries": N, "topk": k, "heads": H, "head_dim": D,
         },
         "roofline": {
-            "kernel": "index_scan_kernel (csa_index_scores, bf16 per-head keys)",
+            "kernel": ("index_shared_kernel (csa_index_scores, bf16 keys shared by the 64 heads)" if shared
+                       else "index_scan_kernel (csa_index_scores, bf16 per-head keys)"),
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
@@ -179,7 +183,7 @@ def main():
         "stages_ms": {kk: round(v, 4) for kk, v in stages.items()},
     }
     if a.workload != "pro_decode_1m":
-        res["metric"] = f"decode queries/s + indexer GB/s, {cfg.name} shape (profiling line, not the benchmark)"
+        res["metric"] = f"decode queries/s + indexer GB/s, {a.workload} (profiling line, not the benchmark)"
     if not a.no_cpu and a.workload == "pro_decode_1m":
         res["cpu_baseline"] = cpu_baseline(a, inp, kv, k_I, summ, sink_h, scores, idx, cfg, NH)
     print(json.dumps(res), flush=True)

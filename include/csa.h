@@ -86,18 +86,22 @@ int csa_compress(const void *C_a, const void *C_b, const void *Z_a, const void *
  *       element in the low nibble) plus q_I_scale [T][H_I][D_I/32] E8M0 bytes (value =
  *       code * 2^(scale-127)), as in the MXFP4 checkpoints' indexer path.
  * w:    [T][H_I] fp32 query-dependent head weights (any sign).
- * k_I:  [B][N][H_I][D_I] per-head keys in dt (MXFP4: [B][N][H_I][D_I/2] + k_I_scale
- *       [B][N][H_I][D_I/32]). q_I_scale / k_I_scale are ignored unless dt == CSA_MXFP4.
+ * k_I:  [B][N][k_heads][D_I] keys in dt (MXFP4: [B][N][k_heads][D_I/2] + k_I_scale
+ *       [B][N][k_heads][D_I/32]). k_heads = H_I: one key per head (the formula's k_{i,h});
+ *       k_heads = 1: one key shared by every head. q_I_scale / k_I_scale are ignored unless
+ *       dt == CSA_MXFP4.
  * q_seq [T] int32 sequence of each query; q_pos [T] int64 absolute position.
  * scores: [T][N] fp32. Products and sums are fp32 (MXFP4 products are exact).
- * Supported: H_I == 64, D_I == 128 (the indexer of both model sizes), dt F32 | BF16 |
- * MXFP4, ratio >= 1. T, N may be 0 (nothing is launched).
+ * Supported: H_I == 64, D_I == 128 (the indexer of both model sizes), ratio >= 1; per-head
+ * keys in F32 | BF16 | MXFP4, shared keys in BF16 (k_heads other than H_I or 1 is
+ * CSA_EINVAL, a shared-key dtype other than BF16 CSA_EUNSUPPORTED). T, N may be 0 (nothing
+ * is launched).
  */
 int csa_index_scores(const void *q_I, const uint8_t *q_I_scale, const float *w,
                      const void *k_I, const uint8_t *k_I_scale,
                      const int32_t *q_seq, const int64_t *q_pos,
-                     int T, int B, int64_t N, int H_I, int D_I, int ratio, csa_dtype dt,
-                     float *scores, void *stream);
+                     int T, int B, int64_t N, int H_I, int D_I, int k_heads, int ratio,
+                     csa_dtype dt, float *scores, void *stream);
 
 /*
  * csa_topk - per-query top-k selection over index scores (§4.2).

@@ -41,7 +41,7 @@ def lib() -> C.CDLL:
         L = C.CDLL(LIB_PATH)
         P, i32, i64, f32, sz = C.c_void_p, C.c_int, C.c_int64, C.c_float, C.c_size_t
         L.csa_compress.argtypes = [P, P, P, P, P, P, P, i32, i64, i32, i32, i32, i32, P, i64, P]
-        L.csa_index_scores.argtypes = [P, P, P, P, P, P, P, i32, i32, i64, i32, i32, i32, i32, P, P]
+        L.csa_index_scores.argtypes = [P, P, P, P, P, P, P, i32, i32, i64, i32, i32, i32, i32, i32, P, P]
         L.csa_topk_workspace_bytes.argtypes = [i32, i64, i32]
         L.csa_topk_workspace_bytes.restype = sz
         L.csa_topk.argtypes = [P, i32, i64, i32, P, P, P, sz, P]
@@ -107,17 +107,18 @@ def compress(C_a, Z_a, C_b=None, Z_b=None, carry_C_b=None, carry_Z_b=None, logit
 
 def index_scores(q_I, w, k_I, q_seq, q_pos, ratio=4, q_I_scale=None, k_I_scale=None,
                  mxfp4=False, scores=None, stream=None):
-    """csa_index_scores -> scores [T][N] fp32. For MXFP4 pass the uint8 code tensors
-    q_I [T][64][64], k_I [B][N][64][64] and their E8M0 scale tensors."""
+    """csa_index_scores -> scores [T][N] fp32. k_I is [B][N][k_heads][D_I] (k_heads = 64
+    per-head keys, 1 shared key). For MXFP4 pass the uint8 code tensors q_I [T][64][64],
+    k_I [B][N][64][64] and their E8M0 scale tensors."""
     T = q_I.shape[0]
-    B, N = k_I.shape[0], k_I.shape[1]
+    B, N, k_heads = k_I.shape[0], k_I.shape[1], k_I.shape[2]
     H_I = q_I.shape[1]
     D_I = q_I.shape[2] * (2 if mxfp4 else 1)
     dt = MXFP4 if mxfp4 else _dt(q_I)
     if scores is None:
         scores = torch.empty((T, N), dtype=torch.float32, device=q_I.device)
     rc = lib().csa_index_scores(_ptr(q_I), _ptr(q_I_scale), _ptr(w), _ptr(k_I), _ptr(k_I_scale),
-                                _ptr(q_seq), _ptr(q_pos), T, B, N, H_I, D_I, ratio, dt,
+                                _ptr(q_seq), _ptr(q_pos), T, B, N, H_I, D_I, k_heads, ratio, dt,
                                 _ptr(scores), _stream(stream))
     _check("csa_index_scores", rc)
     return scores

@@ -69,18 +69,22 @@ int csa_compress(const void *C_a, const void *C_b, const void *Z_a, const void *
 
 int csa_index_scores(const void *q_I, const uint8_t *q_I_scale, const float *w, const void *k_I,
                      const uint8_t *k_I_scale, const int32_t *q_seq, const int64_t *q_pos, int T, int B,
-                     int64_t N, int H_I, int D_I, int ratio, csa_dtype dt, float *scores, void *stream) {
+                     int64_t N, int H_I, int D_I, int k_heads, int ratio, csa_dtype dt, float *scores,
+                     void *stream) {
     clear_error();
     REQUIRE(T >= 0 && B > 0 && N >= 0 && ratio > 0, CSA_EINVAL, "csa_index_scores: need T >= 0, B > 0, N >= 0, ratio > 0");
     REQUIRE(H_I > 0 && D_I > 0, CSA_EINVAL, "csa_index_scores: H_I and D_I must be positive");
     REQUIRE(dt == CSA_F32 || dt == CSA_BF16 || dt == CSA_MXFP4, CSA_EINVAL, "csa_index_scores: bad dtype");
     REQUIRE(dt != CSA_MXFP4 || D_I % 32 == 0, CSA_EINVAL, "csa_index_scores: MXFP4 needs D_I % 32 == 0");
+    REQUIRE(k_heads == H_I || k_heads == 1, CSA_EINVAL, "csa_index_scores: k_heads must be H_I or 1");
     REQUIRE(H_I == 64 && D_I == 128, CSA_EUNSUPPORTED, "csa_index_scores: only H_I = 64, D_I = 128 is built");
+    REQUIRE(k_heads == H_I || dt == CSA_BF16, CSA_EUNSUPPORTED,
+            "csa_index_scores: shared keys (k_heads = 1) are built for CSA_BF16 only");
     if (T == 0 || N == 0) return CSA_OK;
     REQUIRE(q_I && w && k_I && q_seq && q_pos && scores, CSA_EINVAL, "csa_index_scores: NULL tensor");
     REQUIRE(dt != CSA_MXFP4 || (q_I_scale && k_I_scale), CSA_EINVAL, "csa_index_scores: MXFP4 needs both scale tensors");
-    return launch_index_scores(q_I, q_I_scale, w, k_I, k_I_scale, q_seq, q_pos, T, B, N, ratio, dt, scores,
-                               (hipStream_t)stream);
+    return launch_index_scores(q_I, q_I_scale, w, k_I, k_I_scale, q_seq, q_pos, T, B, N, k_heads, ratio, dt,
+                               scores, (hipStream_t)stream);
 }
 
 size_t csa_topk_workspace_bytes(int T, int64_t N, int k) {

@@ -13,6 +13,7 @@
 //    butterfly (each xor step halves the values a lane carries), after which every lane
 //    holds one head's full dot: ReLU, times w, and one 64-lane sum give the score.
 //  - entries that the query cannot see are written as -inf without being read.
+// Shared keys (one key per entry for all heads) run on the matrix cores instead (below).
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -174,13 +175,105 @@ index_scan_kernel(const KT *__restrict__ qI, const float *__restrict__ w, const 
     if (lane < (int)(e1 - e0)) scores[(int64_t)t * N + e0 + lane] = my_score;
 }
 
+// ---- shared keys: one 128-dim key per entry for all 64 heads ----------------------------
+// Per query the scores are a 64 x 128 by 128 x N contraction, so they run on the matrix
+// cores: per 16-entry tile S^T = K Q^T (4 k-chunks x 4 head tiles of MFMA 16x16x32 bf16;
+// A = 16-byte fragments of the 16 keys straight from memory, B = the query's q^T fragments
+// in registers), then ReLU, times w, summed over the 4 head tiles in registers and over
+// the 16 lanes of a row (the 16 heads of a tile) by DPP. A 16-entry tile is 4 KiB of
+// contiguous keys, read by the wavefront's four 16-byte loads per lane.
+constexpr int SH_TPW = 8;  // 16-entry tiles per wavefront
+
+__device__ __forceinline__ float row_sum16(float r) {
+    r += dpp<kRowMirror>(r);
+    r += dpp<kRowHalfMirror>(r);
+    r += dpp<kQuadRev>(r);
+    r += dpp<kQuadSwap>(r);
+    return r;
+}
+
+__global__ void __launch_bounds__(256)
+index_shared_kernel(const bf16_t *__restrict__ qI, const float *__restrict__ w, const bf16_t *__restrict__ kI,
+                    const int32_t *__restrict__ q_seq, const int64_t *__restrict__ q_pos, int B, int64_t N,
+                    int ratio, float *__restrict__ scores)
+{
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int l16 = lane & 15, g = lane >> 4;
+    const int t = blockIdx.y;
+    const int64_t e0 = ((int64_t)blockIdx.x * 4 + wv) * (16 * SH_TPW);
+    if (e0 >= N) return;
+    const int64_t e1 = (e0 + 16 * SH_TPW < N) ? e0 + 16 * SH_TPW : N;
+    const int s = q_seq[t];
+    int64_t nvis = q_pos[t] / ratio;
+    if (nvis > N) nvis = N;
+    if (nvis < 0 || s < 0 || s >= B) nvis = 0;
+    const int64_t ev = (e1 < nvis) ? e1 : nvis;  // [e0, ev) are read, [ev, e1) masked
+
+    if (e0 < ev) {
+        // q^T fragments: head 16ht + l16, dims 32kk + 8g .. +7; w of the same heads
+        bf16x8 qf[4][4];
+        float wl[4];
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht) {
+            const bf16_t *qrow = qI + ((int64_t)t * 64 + 16 * ht + l16) * 128 + 8 * g;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) qf[ht][kk] = *reinterpret_cast<const bf16x8 *>(qrow + 32 * kk);
+            wl[ht] = w[(int64_t)t * 64 + 16 * ht + l16];
+        }
+        const bf16_t *kb = kI + (int64_t)s * N * 128 + 8 * g;
+        // lane l16 reads entry tb + l16 (the ragged tail re-reads the last visible entry;
+        // those results are not written)
+        auto load_tile = [&](int64_t tb, bf16x8 (&a)[4]) {
+            const int64_t er = (tb + l16 < ev) ? tb + l16 : ev - 1;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) a[kk] = *reinterpret_cast<const bf16x8 *>(kb + er * 128 + 32 * kk);
+        };
+        bf16x8 cur[4], nxt[4];
+        load_tile(e0, cur);
+        for (int64_t tb = e0; tb < ev; tb += 16) {
+            if (tb + 16 < ev) load_tile(tb + 16, nxt);
+            f32x4 acc[4];
+#pragma unroll
+            for (int ht = 0; ht < 4; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int ht = 0; ht < 4; ++ht)
+                    acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur[kk], qf[ht][kk], acc[ht], 0, 0, 0);
+            // acc[ht][r] = dot of head 16ht + l16 with entry tb + 4g + r
+            float v[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float x = 0.f;
+#pragma unroll
+                for (int ht = 0; ht < 4; ++ht) x = fmaf(wl[ht], fmaxf(acc[ht][r], 0.f), x);
+                v[r] = row_sum16(x);
+            }
+            const int64_t e = tb + 4 * g + l16;
+            if (l16 < 4 && e < ev) {
+                const float o = l16 == 0 ? v[0] : (l16 == 1 ? v[1] : (l16 == 2 ? v[2] : v[3]));
+                scores[(int64_t)t * N + e] = o;
+            }
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) cur[kk] = nxt[kk];
+        }
+    }
+    for (int64_t e = (e0 > ev ? e0 : ev) + lane; e < e1; e += 64) scores[(int64_t)t * N + e] = -INFINITY;
+}
+
 }  // namespace
 
 int launch_index_scores(const void *qI, const uint8_t *qs, const float *w, const void *kI,
                         const uint8_t *ks, const int32_t *q_seq, const int64_t *q_pos, int T,
-                        int B, int64_t N, int ratio, csa_dtype dt, float *scores, hipStream_t st)
+                        int B, int64_t N, int k_heads, int ratio, csa_dtype dt, float *scores, hipStream_t st)
 {
     if (T == 0 || N == 0) return CSA_OK;
+    if (k_heads == 1) {  // shared keys (bf16; checked by the caller)
+        dim3 grid((unsigned)((N + 4 * 16 * SH_TPW - 1) / (4 * 16 * SH_TPW)), (unsigned)T);
+        hipLaunchKernelGGL(index_shared_kernel, grid, dim3(256), 0, st, (const bf16_t *)qI, w, (const bf16_t *)kI,
+                           q_seq, q_pos, B, N, ratio, scores);
+        return check_launch("index_shared_kernel");
+    }
     if (dt == CSA_MXFP4)
         return launch_index_mxfp4((const uint8_t *)qI, qs, w, (const uint8_t *)kI, ks, q_seq, q_pos, T, B, N,
                                   ratio, scores, st);

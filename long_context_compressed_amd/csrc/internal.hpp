@@ -12,7 +12,8 @@ int launch_compress(const void *Ca, const void *Cb, const void *Za, const void *
 
 int launch_index_scores(const void *qI, const uint8_t *qs, const float *w, const void *kI,
                         const uint8_t *ks, const int32_t *q_seq, const int64_t *q_pos, int T,
-                        int B, int64_t N, int ratio, csa_dtype dt, float *scores, hipStream_t st);
+                        int B, int64_t N, int k_heads, int ratio, csa_dtype dt, float *scores,
+                        hipStream_t st);
 
 int launch_index_mxfp4(const uint8_t *qI, const uint8_t *qs, const float *w, const uint8_t *kI,
                        const uint8_t *ks, const int32_t *q_seq, const int64_t *q_pos, int T, int B, int64_t N,

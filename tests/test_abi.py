@@ -66,8 +66,12 @@ def test_compress_validation(L):
 def test_index_scores_validation(L):
     f = lambda **kw: L.csa_index_scores(*[kw.get(k, v) for k, v in (
         ("q", 1), ("qs", None), ("w", 1), ("k", 1), ("ks", None), ("qseq", 1), ("qpos", 1), ("T", 2), ("B", 1),
-        ("N", 8), ("H", 64), ("D", 128), ("ratio", 4), ("dt", 1), ("scores", 1), ("st", None))])
-    assert f(H=32) == 2
+        ("N", 8), ("H", 64), ("D", 128), ("kh", 64), ("ratio", 4), ("dt", 1), ("scores", 1), ("st", None))])
+    assert f(H=32, kh=32) == 2
+    assert f(kh=5) == 1                         # k_heads is H_I or 1
+    assert f(kh=1, dt=0) == 2                   # shared keys are built for bf16 only
+    assert f(kh=1, dt=2) == 2
+    assert f(kh=1, T=0) == 0
     assert f(D=100, dt=2) == 1
     assert f(D=96, dt=2) == 2
     assert f(dt=2) == 1                         # MXFP4 without scales

@@ -76,13 +76,15 @@ def _gathered_rows(kv, seqs, idx):
     return kv_c, idx_c
 
 
-@pytest.mark.parametrize("name", ["flash_decode_128k", "pro_decode_1m"])
-def test_decode_step_full_size(csa, orc, name):
+@pytest.mark.parametrize("name,shared", [("flash_decode_128k", False), ("pro_decode_1m", False),
+                                         ("pro_decode_1m", True)])
+def test_decode_step_full_size(csa, orc, name, shared):
+    """shared=True: the side line with one 128-dim index key per entry for all heads."""
     from long_context_compressed_amd import pipeline
 
     cfg = W.CONFIGS[name]
-    say("full-size decode step", name)
-    inp = W.decode_step_inputs(cfg, DEV)
+    say("full-size decode step", name, "shared keys" if shared else "")
+    inp = W.decode_step_inputs(cfg, DEV, shared_keys=shared)
     step = pipeline.DecodeStep(inp, cfg.k, cfg.window, cfg.rope_dim, cfg.scale)
     step()
     torch.cuda.synchronize()

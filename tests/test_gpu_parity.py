@@ -105,6 +105,25 @@ def test_index_bf16_decode(csa, orc, T, B, N):
     assert_rel(sc, ref, TOL_F32, "index bf16")
 
 
+@pytest.mark.parametrize("T,B,N", [(3, 3, 1000), (6, 2, 4133), (40, 1, 257)])
+def test_index_bf16_shared_keys(csa, orc, T, B, N):
+    """One 128-dim key per entry shared by all 64 heads (matrix-core path): N ragged against
+    the 16-entry tile and the 128-entry wavefront span, partly and fully masked queries."""
+    say("index shared keys", T, B, N)
+    s = 700 + N
+    qI = W.normal((T, 64, 128), s, "q", dtype=torch.bfloat16, device=DEV)
+    w = W.normal((T, 64), s, "w", device=DEV)
+    kI = W.normal((B, N, 1, 128), s, "k", dtype=torch.bfloat16, device=DEV)
+    q_seq = torch.tensor([t % B for t in range(T)], dtype=torch.int32, device=DEV)
+    pos = [4 * N, 4 * N + 3, 1501, 2, 4 * N - 1, 61]
+    q_pos = torch.tensor([pos[t % len(pos)] + (t // len(pos)) * 97 for t in range(T)], dtype=torch.int64,
+                         device=DEV)
+    sc = csa.index_scores(qI, w, kI, q_seq, q_pos)
+    torch.cuda.synchronize()
+    ref = orc.index_scores(qI, w, kI, q_seq, q_pos)
+    assert_rel(sc, ref, TOL_F32, "index shared keys")
+
+
 @pytest.mark.parametrize("T,N,B,p_lo,p_hi", [
     (70, 300, 1, 600, 669),      # one workgroup tile, ragged in both directions (matrix cores)
     (520, 650, 1, 1000, 3000),   # 3 x 6 tiles, causal: partly and fully masked tiles

@@ -206,7 +206,7 @@ def tiny_inputs(device="cpu", cfg: Config = TINY) -> dict:
     return inp
 
 
-def decode_inputs(cfg: Config, device="cpu", with_index=True) -> dict:
+def decode_inputs(cfg: Config, device="cpu", with_index=True, shared_keys=False) -> dict:
     """Decode-step tensors for B independent sequences, one query each at t = n.
 
     Index keys, compressed KV, SWA rows, queries and sinks are N(0,1); the indexer
@@ -229,26 +229,30 @@ def decode_inputs(cfg: Config, device="cpu", with_index=True) -> dict:
     if with_index:
         inp["q_I"] = normal((cfg.T, cfg.H_I, cfg.D_I), s, "q_I", dtype=dt, device=device)
         inp["w"] = normal((cfg.T, cfg.H_I), s, "w", scale=wscale, device=device)
-        inp["k_I"] = normal((B, N, cfg.H_I, cfg.D_I), s, "k_I", dtype=dt, device=device)
+        if shared_keys:  # one 128-dim key per entry for every head
+            inp["k_I"] = normal((B, N, 1, cfg.D_I), s, "k_I_shared", dtype=dt, device=device)
+        else:
+            inp["k_I"] = normal((B, N, cfg.H_I, cfg.D_I), s, "k_I", dtype=dt, device=device)
     return inp
 
 
-def decode_step_inputs(cfg: Config, device="cpu") -> dict:
+def decode_step_inputs(cfg: Config, device="cpu", shared_keys=False) -> dict:
     """Everything one decode step of a CSA layer plus an HCA layer reads, for B sequences.
 
     On top of decode_inputs: the block [n-4, n) that completes with the step (a- and
     b-branch contents/logits for the attention KV and for the index keys, and the carry
     block [n-8, n-4)), the HCA summaries [B][n/128][D] with their own sinks, and the
     ratio-128 block that completes the last summary. All N(0,1) bf16 (sinks fp32).
+    shared_keys: the index keys are one 128-dim key per entry for all heads.
     """
     s, B, D, bf = cfg.seed, cfg.B, cfg.c, torch.bfloat16
     NH = cfg.n // 128
-    inp = decode_inputs(cfg, device)
+    inp = decode_inputs(cfg, device, shared_keys=shared_keys)
     inp["summ"] = normal((B, NH, D), HCA.seed, "summ", dtype=bf, device=device)
     inp["sink_h"] = normal((cfg.H,), HCA.seed, "sink", device=device)
     inp["blk"] = {nm: normal((B, 4, D), s, "new_" + nm, dtype=bf, device=device) for nm in ("Ca", "Cb", "Za", "Zb")}
     inp["carry"] = {nm: normal((B, 4, D), s, "carry_" + nm, dtype=bf, device=device) for nm in ("C", "Z")}
-    KW = cfg.H_I * cfg.D_I
+    KW = cfg.D_I if shared_keys else cfg.H_I * cfg.D_I
     inp["iblk"] = {nm: normal((B, 4, KW), s, "inew_" + nm, dtype=bf, device=device) for nm in ("Ca", "Cb", "Za", "Zb")}
     inp["icarry"] = {nm: normal((B, 4, KW), s, "icarry_" + nm, dtype=bf, device=device) for nm in ("C", "Z")}
     inp["hblk"] = {nm: normal((B, 128, D), HCA.seed, "hnew_" + nm, dtype=bf, device=device) for nm in ("C", "Z")}
