@@ -3,9 +3,11 @@
 //
 // A workgroup (1024 lanes) owns one chunk of at most `cap` scores of one row and keeps
 // it in LDS as order-preserving 32-bit keys (-inf / NaN map to 0 and are never taken):
-//   1. four 8-bit radix passes over LDS find the exact key tau of the k-th largest
-//      element and how many elements equal to tau are to be taken (ties go to the lower
-//      index); histogram increments are aggregated per wavefront for the common case
+//   1. three radix passes (digits of 11, 11 and 10 bits from the top) find the exact key
+//      tau of the k-th largest element and how many elements equal to tau are to be
+//      taken (ties go to the lower index); after the first pass the keys of the leading
+//      bin are copied to a short LDS list when they fit, so the later passes scan only
+//      that list; histogram increments are aggregated per wavefront for the common case
 //      of a wave whose active lanes share one digit;
 //   2. an ordered compaction (block scans over contiguous per-lane segments) writes the
 //      selected (value, index) pairs in ascending index order.
