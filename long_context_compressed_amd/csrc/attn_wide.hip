@@ -4,9 +4,10 @@
 // §5 (HCA: every visible summary), §6 (SWA rows, sink softmax, partial RoPE / inverse RoPE).
 //
 // One workgroup = one query x 64 heads (x a range of row slots when split); wavefront w
-// owns heads 16w..16w+15 over the full head dim D = 512. Two workgroups share a CU (256
-// registers and 78 KiB of LDS each), so one's softmax and barriers overlap the other's
-// matrix and LDS work. Per 32-row tile:
+// owns heads 16w..16w+15 over the full head dim D = 512. With 4 wavefronts (64 heads) two
+// workgroups share a CU (256 registers and 78 KiB of LDS each), so one's softmax and
+// barriers overlap the other's matrix and LDS work; with 8 (128 heads) a gathered row is
+// fetched once for all heads of the query. Per 32-row tile:
 //   - the rows (bf16, 1 KiB each) go from memory straight into LDS by buffer loads with
 //     the LDS destination (one row per wave instruction, its address resolved in scalar
 //     registers), into the other of two tile buffers while this tile is computed; rows are
@@ -32,10 +33,9 @@ namespace {
 
 constexpr int WD = 512;     // head dim
 constexpr int WR = 32;      // rows per tile
-constexpr int WH = 64;      // heads per workgroup (16 per wavefront)
+constexpr int HPW = 16;     // heads per wavefront
 constexpr int KKN = WD / 32;  // k-chunks of S^T (q^T fragments)
 constexpr int NDN = WD / 16;  // 16-dim output tiles
-constexpr int RPW = WR / 4;   // tile rows loaded per wavefront
 constexpr float kLazy = 16.f; // log2 headroom of the reference maximum
 // fragment chunks read ahead of the matrix ops (two workgroups per CU hide most of the
 // LDS latency; deeper rings would not fit the 256 registers)
@@ -84,7 +84,10 @@ __device__ __forceinline__ v4i16 ld_tr(const bf16_t *p) {
         (lds_v4i16 *)((__attribute__((address_space(3))) bf16_t *)p));
 }
 
-__global__ void __launch_bounds__(256, 2)
+// NWV wavefronts per workgroup: 4 (64 heads; two workgroups share a CU) or 8 (128 heads,
+// one workgroup per CU: every gathered row is loaded once for all 128 heads).
+template <int NWV>
+__global__ void __launch_bounds__(64 * NWV, 8 / NWV)
 attn_wide_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, const float *__restrict__ sink,
                  const int32_t *__restrict__ idx, int k, int ratio, float scale_log2,
                  const bf16_t *__restrict__ swa, const int64_t *__restrict__ swa_pos0, int swa_rows,
@@ -93,6 +96,8 @@ attn_wide_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, co
                  bf16_t *__restrict__ out, float *__restrict__ lse, float *__restrict__ part,
                  int nsplit, int64_t split_slots)
 {
+    constexpr int WH = HPW * NWV;  // heads per workgroup
+    constexpr int RPW = WR / NWV;  // tile rows loaded per wavefront
     __shared__ __attribute__((aligned(16))) bf16_t KV0[WR * WP];  // tile buffers (separate arrays,
     __shared__ __attribute__((aligned(16))) bf16_t KV1[WR * WP];  // see the row loads below)
     __shared__ int32_t sidx[kIdxCache];
@@ -112,7 +117,7 @@ attn_wide_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, co
     const int hg = (int)(u % HGN);
     const int64_t tu = u / HGN;
     const int t = (int)(tu / nsplit), sp = (int)(tu % nsplit);
-    const int head0 = hg * WH + 16 * w;  // first head of this wave
+    const int head0 = hg * WH + HPW * w;  // first head of this wave
 
     const RowCtx c = row_ctx(t, q_seq, q_pos, B, N, k, ratio, swa, swa_pos0, window);
     const int64_t j0 = (int64_t)sp * split_slots;
@@ -169,7 +174,7 @@ attn_wide_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, co
     const int64_t jm = (j1 < c.nmain) ? j1 : c.nmain;  // main slots of this split: [j0, jm)
     const int64_t ncache = (jm - j0 < kIdxCache) ? jm - j0 : kIdxCache;
     if (ratio <= 0)
-        for (int64_t x = threadIdx.x; x < ncache; x += 256) sidx[x] = idx[(int64_t)t * k + j0 + x];
+        for (int64_t x = threadIdx.x; x < ncache; x += 64 * NWV) sidx[x] = idx[(int64_t)t * k + j0 + x];
     __syncthreads();
     // Rows without data read a valid stand-in address (this wave's own q rows) and are
     // masked out of the softmax, so every load is issued unconditionally.
@@ -406,15 +411,28 @@ attn_wide_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, co
 
 }  // namespace
 
-bool wide_attn_ok(csa_dtype dt, int H, int D) { return dt == CSA_BF16 && D == WD && H % WH == 0; }
+bool wide_attn_ok(csa_dtype dt, int H, int D) { return dt == CSA_BF16 && D == WD && H % 64 == 0; }
 
 int launch_attn_wide(const AttnArgs &a, float sl2, int nsplit, int64_t split_slots, hipStream_t st) {
+    // many queries with gathered rows (sparse, 128-head multiples, no row split): one 8-wave
+    // workgroup per 128 heads, so a row is fetched once per query (measured 5 % faster at
+    // the Pro prefill chunk); otherwise 4-wave workgroups, two per CU (summaries sit in L2,
+    // and few-query decode needs the extra workgroups)
+    const bool wide8 = (a.ratio <= 0 && a.H % 128 == 0 && nsplit == 1);
+    const int WH = wide8 ? 128 : 64;
     const int64_t U = (int64_t)a.T * nsplit * (a.H / WH);
     const int64_t blocks = ((U + 7) / 8) * 8;
-    hipLaunchKernelGGL(attn_wide_kernel, dim3((unsigned)blocks), dim3(256), 0, st, (const bf16_t *)a.q,
-                       (const bf16_t *)a.kv, a.sink, a.idx, a.k, a.ratio, sl2, (const bf16_t *)a.swa, a.swa_pos0,
-                       a.swa_rows, a.window, a.q_seq, a.q_pos, a.rope_cs, a.rope_dim, a.T, a.B, a.N, a.H,
+#define CSA_WIDE_LAUNCH(NWV_)                                                                                  \
+    hipLaunchKernelGGL(attn_wide_kernel<NWV_>, dim3((unsigned)blocks), dim3(64 * NWV_), 0, st, (const bf16_t *)a.q, \
+                       (const bf16_t *)a.kv, a.sink, a.idx, a.k, a.ratio, sl2, (const bf16_t *)a.swa, a.swa_pos0, \
+                       a.swa_rows, a.window, a.q_seq, a.q_pos, a.rope_cs, a.rope_dim, a.T, a.B, a.N, a.H,        \
                        (bf16_t *)a.out, a.lse, (float *)a.ws, nsplit, split_slots);
+    if (wide8) {
+        CSA_WIDE_LAUNCH(8)
+    } else {
+        CSA_WIDE_LAUNCH(4)
+    }
+#undef CSA_WIDE_LAUNCH
     return check_launch("attn_wide_kernel");
 }
 
