@@ -10,9 +10,11 @@
 //
 // Workgroup: 8 wavefronts, a 256-query x 128-entry tile, wave (qg, eg) owns 64 queries x
 // 64 entries (4 x 4 MFMA tiles, 64 fp32 score accumulators per lane). The loop runs over
-// the 64 heads; per head the tile's q and k codes (16 + 8 KiB) and their scales are staged
-// in LDS, double buffered: head h+1 is loaded into registers while head h is computed, then
-// written to the other buffer. The epilogue of every MFMA (ReLU, times w[t][h], accumulate) is VALU work and
+// the 64 heads; per head the tile's q and k codes (16 + 8 KiB) are staged in LDS, double
+// buffered: head h+2 is loaded into registers while head h is computed, and head h+1 is
+// written to the other buffer. The E8M0 scales are staged 8 heads at a time (32 bytes of
+// each row per load, not 4), since the scattered 4-byte loads of one head's scales cost
+// more address-unit cycles than its codes. The epilogue of every MFMA (ReLU, times w[t][h], accumulate) is VALU work and
 // bounds the kernel. The 16-byte chunks of each 64-byte code row are XOR-swizzled in LDS so
 // the per-lane 16-byte operand reads of 8 consecutive rows hit distinct banks.
 #include "common.hpp"
@@ -39,8 +41,9 @@ index_mxfp4_mfma_kernel(const uint8_t *__restrict__ qI, const uint8_t *__restric
 {
     __shared__ __attribute__((aligned(16))) uint8_t Qs[2][TQ * 64];
     __shared__ __attribute__((aligned(16))) uint8_t Ks[2][TE * 64];
-    __shared__ __attribute__((aligned(16))) uint32_t QSs[2][TQ];
-    __shared__ __attribute__((aligned(16))) uint32_t KSs[2][TE];
+    // scale words of 8 heads at a time, head-major ([head % 8][row]), double buffered
+    __shared__ __attribute__((aligned(16))) uint32_t QSs[2][8][TQ];
+    __shared__ __attribute__((aligned(16))) uint32_t KSs[2][8][TE];
     __shared__ float Ws[TQ * WPITCH];
     __shared__ int64_t nvis_s[TQ];
     __shared__ int red[2];
@@ -88,10 +91,9 @@ index_mxfp4_mfma_kernel(const uint8_t *__restrict__ qI, const uint8_t *__restric
             const int t = t0 + qq;
             Ws[qq * WPITCH + h] = (t < T) ? w[(int64_t)t * 64 + h] : 0.f;
         }
-        // per-wave share of one head's operands: 32 q rows and 16 k rows (16 bytes per lane
-        // per 16-row group) and, for waves 0-5, 64 scale words (0-3: q scales, 4-5: k
-        // scales). They are loaded into registers while the previous head is computed, then
-        // written to LDS.
+        // per-wave share of one head's codes: 32 q rows and 16 k rows (16 bytes per lane per
+        // 16-row group), loaded into registers while the previous head is computed, then
+        // written to LDS
         const int qrow0 = wv * 32 + (lane >> 2), qrow1 = qrow0 + 16;
         const int krow = wv * 16 + (lane >> 2);
         const int qpos0 = ((lane & 3) ^ swz(qrow0)) * 16, qpos1 = ((lane & 3) ^ swz(qrow1)) * 16;
@@ -104,40 +106,63 @@ index_mxfp4_mfma_kernel(const uint8_t *__restrict__ qI, const uint8_t *__restric
         const uint8_t *qsrc0 = qI + (int64_t)tq0 * 4096 + (lane & 3) * 16;
         const uint8_t *qsrc1 = qI + (int64_t)tq1 * 4096 + (lane & 3) * 16;
         const uint8_t *ksrc = kI + ek * 4096 + (lane & 3) * 16;
-        const uint8_t *ssrc = nullptr;
-        if (wv < 4) {
-            int t = t0 + wv * 64 + lane;
-            t = t < T ? t : T - 1;
-            ssrc = qS + (int64_t)t * 256;
-        } else if (wv < 6) {
-            int64_t e = i0 + (wv - 4) * 64 + lane;
-            e = e < N ? e : N - 1;
-            ssrc = kS + e * 256;
-        }
-        uint4 rq0, rq1, rk;
-        uint32_t rs = 0;
-        auto load = [&](int h) {
-            rq0 = *reinterpret_cast<const uint4 *>(qsrc0 + h * 64);
-            rq1 = *reinterpret_cast<const uint4 *>(qsrc1 + h * 64);
-            rk = *reinterpret_cast<const uint4 *>(ksrc + h * 64);
-            if (wv < 6) rs = *reinterpret_cast<const uint32_t *>(ssrc + h * 4);
-        };
-        auto store = [&](int buf) {
-            *reinterpret_cast<uint4 *>(&Qs[buf][qrow0 * 64 + qpos0]) = rq0;
-            *reinterpret_cast<uint4 *>(&Qs[buf][qrow1 * 64 + qpos1]) = rq1;
-            *reinterpret_cast<uint4 *>(&Ks[buf][krow * 64 + kpos]) = rk;
-            if (wv < 4)
-                QSs[buf][wv * 64 + lane] = rs;
-            else if (wv < 6)
-                KSs[buf][(wv - 4) * 64 + lane] = rs;
-        };
+        // scales, 8 heads (32 bytes of a row) at a time: thread i loads 16 bytes of q row
+        // i / 2 and, for i < 256, of k row i / 2 (half i % 2 of the row's 8 heads); a block's
+        // scales are loaded at its predecessor's first head and stored at its last
+        const int srow = tid >> 1, shalf = tid & 1;
+        int tsq = t0 + srow;
+        tsq = tsq < T ? tsq : T - 1;
+        int64_t esk = i0 + (srow & (TE - 1));
+        esk = esk < N ? esk : N - 1;
+        const uint8_t *sqsrc = qS + (int64_t)tsq * 256 + shalf * 16;
+        const uint8_t *sksrc = kS + esk * 256 + shalf * 16;
+        uint4 rsq, rsk = uint4{0u, 0u, 0u, 0u};
+#define FP4_SLOAD(BLK)                                                                   \
+    {                                                                                   \
+        rsq = *reinterpret_cast<const uint4 *>(sqsrc + (BLK) * 32);                     \
+        if (tid < 2 * TE) rsk = *reinterpret_cast<const uint4 *>(sksrc + (BLK) * 32);   \
+    }
+#define FP4_SSTORE(SB)                                                                   \
+    {                                                                                   \
+        QSs[SB][shalf * 4 + 0][srow] = rsq.x;                                           \
+        QSs[SB][shalf * 4 + 1][srow] = rsq.y;                                           \
+        QSs[SB][shalf * 4 + 2][srow] = rsq.z;                                           \
+        QSs[SB][shalf * 4 + 3][srow] = rsq.w;                                           \
+        if (tid < 2 * TE) {                                                             \
+            KSs[SB][shalf * 4 + 0][srow] = rsk.x;                                       \
+            KSs[SB][shalf * 4 + 1][srow] = rsk.y;                                       \
+            KSs[SB][shalf * 4 + 2][srow] = rsk.z;                                       \
+            KSs[SB][shalf * 4 + 3][srow] = rsk.w;                                       \
+        }                                                                               \
+    }
+        // two register sets (A: even heads, B: odd heads): head h+2 is loaded while head h
+        // is computed, and head h+1 (loaded one head earlier) is written to LDS after it
+        uint4 rq0A, rq1A, rkA, rq0B, rq1B, rkB;
+#define FP4_LOAD(S, HH)                                                                  \
+    {                                                                                   \
+        rq0##S = *reinterpret_cast<const uint4 *>(qsrc0 + (HH) * 64);                   \
+        rq1##S = *reinterpret_cast<const uint4 *>(qsrc1 + (HH) * 64);                   \
+        rk##S = *reinterpret_cast<const uint4 *>(ksrc + (HH) * 64);                     \
+    }
+#define FP4_STORE(S, BUF)                                                                \
+    {                                                                                   \
+        *reinterpret_cast<uint4 *>(&Qs[BUF][qrow0 * 64 + qpos0]) = rq0##S;              \
+        *reinterpret_cast<uint4 *>(&Qs[BUF][qrow1 * 64 + qpos1]) = rq1##S;              \
+        *reinterpret_cast<uint4 *>(&Ks[BUF][krow * 64 + kpos]) = rk##S;                 \
+    }
 
-        load(0);
-        store(0);
+        FP4_SLOAD(0)
+        FP4_LOAD(A, 0)
+        FP4_LOAD(B, 1)
+        FP4_SSTORE(0)
+        FP4_STORE(A, 0)
         __syncthreads();
         for (int h = 0; h < 64; ++h) {
-            const int buf = h & 1;
-            if (h + 1 < 64) load(h + 1);
+            const int buf = h & 1, sbuf = (h >> 3) & 1, hs = h & 7;
+            if (hs == 0 && h + 8 < 64) FP4_SLOAD((h >> 3) + 1)
+            if (h + 2 < 64) {
+                if (buf == 0) FP4_LOAD(A, h + 2) else FP4_LOAD(B, h + 2)
+            }
             // B operands (k codes of the wave's 4 entry tiles) stay in registers; A (q codes)
             // is read per query tile
             i32x4v Bv[4];
@@ -146,14 +171,14 @@ index_mxfp4_mfma_kernel(const uint8_t *__restrict__ qI, const uint8_t *__restric
             for (int n = 0; n < 4; ++n) {
                 const int row = eg * 64 + 16 * n + l16;
                 Bv[n] = *reinterpret_cast<const i32x4v *>(&Ks[buf][row * 64 + ((g4 ^ swz(row)) * 16)]);
-                sb[n] = (int)((KSs[buf][row] >> (8 * g4)) & 0xFFu);
+                sb[n] = (int)((KSs[sbuf][hs][row] >> (8 * g4)) & 0xFFu);
             }
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const int row = qg * 64 + 16 * m + l16;
                 const i32x4v av = *reinterpret_cast<const i32x4v *>(&Qs[buf][row * 64 + ((g4 ^ swz(row)) * 16)]);
                 const i32x8 A = i32x8{av[0], av[1], av[2], av[3], 0, 0, 0, 0};
-                const int sa = (int)((QSs[buf][row] >> (8 * g4)) & 0xFFu);
+                const int sa = (int)((QSs[sbuf][hs][row] >> (8 * g4)) & 0xFFu);
                 float wr[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) wr[r] = Ws[(qg * 64 + 16 * m + 4 * g4 + r) * WPITCH + h];
@@ -162,13 +187,23 @@ index_mxfp4_mfma_kernel(const uint8_t *__restrict__ qI, const uint8_t *__restric
                     const i32x8 Bn = i32x8{Bv[n][0], Bv[n][1], Bv[n][2], Bv[n][3], 0, 0, 0, 0};
                     const f32x4 c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                         A, Bn, f32x4{0.f, 0.f, 0.f, 0.f}, 4, 4, 0, sa, 0, sb[n]);
+                    // ReLU as an integer max on the bits (negative floats are negative
+                    // integers): one instruction, where fmaxf also quiets NaNs
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[m][n][r] = fmaf(wr[r], fmaxf(c[r], 0.f), acc[m][n][r]);
+                    for (int r = 0; r < 4; ++r)
+                        acc[m][n][r] = fmaf(wr[r], __int_as_float(max(__float_as_int(c[r]), 0)), acc[m][n][r]);
                 }
             }
-            if (h + 1 < 64) store(buf ^ 1);
+            if (h + 1 < 64) {
+                if (buf == 0) FP4_STORE(B, 1) else FP4_STORE(A, 0)
+            }
+            if (hs == 7 && h + 1 < 64) FP4_SSTORE(sbuf ^ 1)
             __syncthreads();
         }
+#undef FP4_LOAD
+#undef FP4_STORE
+#undef FP4_SLOAD
+#undef FP4_SSTORE
     }
 
     // scores: lane holds (query 16m + 4g4 + r, entry 16n + l16) of the wave tile
