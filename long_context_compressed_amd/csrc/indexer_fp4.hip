@@ -151,59 +151,68 @@ index_mxfp4_mfma_kernel(const uint8_t *__restrict__ qI, const uint8_t *__restric
         *reinterpret_cast<uint4 *>(&Ks[BUF][krow * 64 + kpos]) = rk##S;                 \
     }
 
+        // one head's contraction over LDS buffer BUF: the k codes of the wave's 4 entry tiles
+        // stay in registers, the q codes are read per query tile
+#define FP4_COMPUTE(HH, BUF, HS)                                                         \
+    {                                                                                   \
+        i32x4v Bv[4];                                                                   \
+        int sb[4];                                                                      \
+        _Pragma("unroll") for (int n = 0; n < 4; ++n) {                                 \
+            const int row = eg * 64 + 16 * n + l16;                                     \
+            Bv[n] = *reinterpret_cast<const i32x4v *>(&Ks[BUF][row * 64 + ((g4 ^ swz(row)) * 16)]); \
+            sb[n] = (int)((KSs[sbuf][HS][row] >> (8 * g4)) & 0xFFu);                    \
+        }                                                                               \
+        _Pragma("unroll") for (int m = 0; m < 4; ++m) {                                 \
+            const int row = qg * 64 + 16 * m + l16;                                     \
+            const i32x4v av = *reinterpret_cast<const i32x4v *>(&Qs[BUF][row * 64 + ((g4 ^ swz(row)) * 16)]); \
+            const i32x8 A = i32x8{av[0], av[1], av[2], av[3], 0, 0, 0, 0};              \
+            const int sa = (int)((QSs[sbuf][HS][row] >> (8 * g4)) & 0xFFu);             \
+            float wr[4];                                                                \
+            _Pragma("unroll") for (int r = 0; r < 4; ++r)                               \
+                wr[r] = Ws[(qg * 64 + 16 * m + 4 * g4 + r) * WPITCH + (HH)];            \
+            _Pragma("unroll") for (int n = 0; n < 4; ++n) {                             \
+                const i32x8 Bn = i32x8{Bv[n][0], Bv[n][1], Bv[n][2], Bv[n][3], 0, 0, 0, 0}; \
+                const f32x4 c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(       \
+                    A, Bn, f32x4{0.f, 0.f, 0.f, 0.f}, 4, 4, 0, sa, 0, sb[n]);           \
+                _Pragma("unroll") for (int r = 0; r < 4; ++r)                           \
+                    acc[m][n][r] = fmaf(wr[r], __int_as_float(max(__float_as_int(c[r]), 0)), acc[m][n][r]); \
+            }                                                                           \
+        }                                                                               \
+    }
+
+        // ReLU is an integer max on the bits (negative floats are negative integers): one
+        // instruction, where fmaxf also quiets NaNs. Loads past the last head or block re-read
+        // the last one and their stores go to a buffer nobody reads again, so every load and
+        // store is unconditional and the waits stay exact.
         FP4_SLOAD(0)
         FP4_LOAD(A, 0)
         FP4_LOAD(B, 1)
         FP4_SSTORE(0)
         FP4_STORE(A, 0)
         __syncthreads();
-        for (int h = 0; h < 64; ++h) {
-            const int buf = h & 1, sbuf = (h >> 3) & 1, hs = h & 7;
-            if (hs == 0 && h + 8 < 64) FP4_SLOAD((h >> 3) + 1)
-            if (h + 2 < 64) {
-                if (buf == 0) FP4_LOAD(A, h + 2) else FP4_LOAD(B, h + 2)
+#pragma unroll 1
+        for (int hb = 0; hb < 64; hb += 8) {
+            const int sbuf = (hb >> 3) & 1;
+            FP4_SLOAD(hb + 8 < 64 ? (hb >> 3) + 1 : 7)
+#pragma unroll 1
+            for (int hs = 0; hs < 8; hs += 2) {
+                const int h = hb + hs;
+                FP4_LOAD(A, h + 2 < 64 ? h + 2 : 63)
+                FP4_COMPUTE(h, 0, hs)
+                FP4_STORE(B, 1)
+                __syncthreads();
+                FP4_LOAD(B, h + 3 < 64 ? h + 3 : 63)
+                FP4_COMPUTE(h + 1, 1, hs + 1)
+                if (hs == 6) FP4_SSTORE(sbuf ^ 1)
+                FP4_STORE(A, 0)
+                __syncthreads();
             }
-            // B operands (k codes of the wave's 4 entry tiles) stay in registers; A (q codes)
-            // is read per query tile
-            i32x4v Bv[4];
-            int sb[4];
-#pragma unroll
-            for (int n = 0; n < 4; ++n) {
-                const int row = eg * 64 + 16 * n + l16;
-                Bv[n] = *reinterpret_cast<const i32x4v *>(&Ks[buf][row * 64 + ((g4 ^ swz(row)) * 16)]);
-                sb[n] = (int)((KSs[sbuf][hs][row] >> (8 * g4)) & 0xFFu);
-            }
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int row = qg * 64 + 16 * m + l16;
-                const i32x4v av = *reinterpret_cast<const i32x4v *>(&Qs[buf][row * 64 + ((g4 ^ swz(row)) * 16)]);
-                const i32x8 A = i32x8{av[0], av[1], av[2], av[3], 0, 0, 0, 0};
-                const int sa = (int)((QSs[sbuf][hs][row] >> (8 * g4)) & 0xFFu);
-                float wr[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) wr[r] = Ws[(qg * 64 + 16 * m + 4 * g4 + r) * WPITCH + h];
-#pragma unroll
-                for (int n = 0; n < 4; ++n) {
-                    const i32x8 Bn = i32x8{Bv[n][0], Bv[n][1], Bv[n][2], Bv[n][3], 0, 0, 0, 0};
-                    const f32x4 c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        A, Bn, f32x4{0.f, 0.f, 0.f, 0.f}, 4, 4, 0, sa, 0, sb[n]);
-                    // ReLU as an integer max on the bits (negative floats are negative
-                    // integers): one instruction, where fmaxf also quiets NaNs
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        acc[m][n][r] = fmaf(wr[r], __int_as_float(max(__float_as_int(c[r]), 0)), acc[m][n][r]);
-                }
-            }
-            if (h + 1 < 64) {
-                if (buf == 0) FP4_STORE(B, 1) else FP4_STORE(A, 0)
-            }
-            if (hs == 7 && h + 1 < 64) FP4_SSTORE(sbuf ^ 1)
-            __syncthreads();
         }
 #undef FP4_LOAD
 #undef FP4_STORE
 #undef FP4_SLOAD
 #undef FP4_SSTORE
+#undef FP4_COMPUTE
     }
 
     // scores: lane holds (query 16m + 4g4 + r, entry 16n + l16) of the wave tile
