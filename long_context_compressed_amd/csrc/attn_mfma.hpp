@@ -1,0 +1,103 @@
+// Fragment helpers shared by the matrix-core attention kernels (bf16, head dim 512).
+#pragma once
+
+#include "attn_rows.hpp"
+#include "common.hpp"
+
+namespace csa {
+namespace amfma {
+
+constexpr int WD = 512;         // head dim
+constexpr int WR = 32;          // rows per tile
+constexpr int KKN = WD / 32;    // k-chunks of S^T (q^T fragments)
+constexpr int NDN = WD / 16;    // 16-dim output tiles
+constexpr float kLazy = 16.f;   // log2 headroom of the reference maximum
+constexpr int kIdxCache = 3072; // top-k indices of one split kept in LDS (more are read from memory)
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef unsigned int u32x4w __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
+// word 3 of a raw buffer resource on gfx9-class parts (32-bit data format, no swizzle)
+constexpr int kBufDword3 = 0x00020000;
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2w __attribute__((ext_vector_type(2)));  // converts with v_cvt_pk_bf16_f32 (RNE)
+// B operand of ones (bf16 1.0 = 0x3f80): P x ones gives every head's row sum of P
+__device__ __forceinline__ bf16x8 ones_bf16x8() {
+    return __builtin_bit_cast(bf16x8, u32x4w{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+}
+
+// Row scaling of a 16x16 fp32 accumulator tile on the matrix cores: row i (head 4g + r of
+// the C layout) times alpha_i. With A_r[i][k] = alpha_i if i == 4k + r (else 0) and
+// B_r[k][n] = C[4k + r][n] (component r of every lane), sum_r A_r B_r = diag(alpha) C,
+// four 16x16x4 fp32 products, each exact to one fp32 rounding. ar[r] is alpha_i on the lane
+// with l % 16 == 4 (l / 16) + r and 0 elsewhere.
+__device__ __forceinline__ f32x4 scale_rows(const f32x4 c, const float ar[4]) {
+    f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) z = __builtin_amdgcn_mfma_f32_16x16x4f32(ar[r], c[r], z, 0, 0, 0);
+    return z;
+}
+
+// LDS pitch of a tile row: 512 bf16 + 16 bf16 of padding. With the 32-byte pad both the
+// 16-byte row-fragment reads of 16 rows and the transposing reads of 16 rows x 32 bytes
+// are spread over all banks (measured ~190-205 B/clk/CU, against ~117 for an unpadded
+// XOR-swizzled row).
+constexpr int WP = WD + 16;
+
+__device__ __forceinline__ bf16x8 ld_bf16x8(const bf16_t *p) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4w *>(p));
+}
+
+__device__ __forceinline__ v4i16 ld_tr(const bf16_t *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16 *)((__attribute__((address_space(3))) bf16_t *)p));
+}
+
+// Row of slot j of a query (a top-k row, a summary or an SWA row), or `standin` when the
+// slot holds no row. Slots [j0, j0 + kIdxCache) of the top-k list are read from `sidx`.
+__device__ __forceinline__ const bf16_t *slot_row(const RowCtx &c, int64_t j, int64_t j0, int64_t j1, int ratio,
+                                                  const int32_t *sidx, const int32_t *idx_t, int64_t N,
+                                                  const bf16_t *kv, const bf16_t *swa, int swa_rows,
+                                                  const bf16_t *standin) {
+    const bf16_t *p = standin;
+    if (j < j1) {
+        if (j < c.nmain) {
+            const int64_t id = (ratio > 0) ? j : (j - j0 < kIdxCache ? (int64_t)sidx[j - j0] : (int64_t)idx_t[j]);
+            if (id >= 0 && id < N) p = kv + ((int64_t)c.s * N + id) * WD;
+        } else {
+            const int64_t r = c.lo + (j - c.nmain) - c.swa0;
+            if (r >= 0 && r < swa_rows) p = swa + ((int64_t)c.s * swa_rows + r) * WD;
+        }
+    }
+    return p;
+}
+
+// q^T fragment (B operand of S^T = K Q^T) of one head: dims 32kk + 8g .. +7 of row `qrow`,
+// with the rotation of the last R dims applied in fp32 and rounded once to bf16.
+__device__ __forceinline__ bf16x8 q_fragment(const bf16_t *qrow, int kk, int g, const float *rope_t, int R) {
+    const int d0 = 32 * kk + 8 * g;
+    uint4 raw = *reinterpret_cast<const uint4 *>(qrow + d0);
+    if (rope_t != nullptr && d0 + 8 > WD - R) {
+        const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float x0 = lo_bf16(wd[e]), x1 = hi_bf16(wd[e]);
+            const int d = d0 + 2 * e;
+            if (d >= WD - R) {
+                const int p = (d - (WD - R)) >> 1;
+                const float cs = rope_t[2 * p], sn = rope_t[2 * p + 1];
+                const float y0 = x0 * cs - x1 * sn, y1 = x0 * sn + x1 * cs;
+                x0 = y0;
+                x1 = y1;
+            }
+            o[e] = (uint32_t)f32_to_bf16(x0) | ((uint32_t)f32_to_bf16(x1) << 16);
+        }
+        raw = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+    return __builtin_bit_cast(bf16x8, raw);
+}
+
+}  // namespace amfma
+}  // namespace csa

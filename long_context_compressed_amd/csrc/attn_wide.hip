@@ -23,66 +23,20 @@
 //   - online softmax with a lazy reference maximum: O and the denominators are rescaled
 //     only when a head's running maximum grows by more than 2^16 (exponentials stay below
 //     2^16), and the rescale itself runs on the matrix cores.
-#include "attn_rows.hpp"
-#include "common.hpp"
+#include "attn_mfma.hpp"
 #include "internal.hpp"
 
 namespace csa {
 
 namespace {
 
-constexpr int WD = 512;     // head dim
-constexpr int WR = 32;      // rows per tile
+using namespace amfma;
+
 constexpr int HPW = 16;     // heads per wavefront
-constexpr int KKN = WD / 32;  // k-chunks of S^T (q^T fragments)
-constexpr int NDN = WD / 16;  // 16-dim output tiles
-constexpr float kLazy = 16.f; // log2 headroom of the reference maximum
 // fragment chunks read ahead of the matrix ops (two workgroups per CU hide most of the
 // LDS latency; deeper rings would not fit the 256 registers)
 constexpr int SDA = 0;  // K fragments
 constexpr int PVA = 2;  // V fragments
-constexpr int kIdxCache = 3072; // top-k indices of one split kept in LDS (more are read from memory)
-
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-typedef unsigned int u32x4w __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(1))) const u32x4w gu32x4;
-// word 3 of a raw buffer resource on gfx9-class parts (32-bit data format, no swizzle)
-constexpr int kBufDword3 = 0x00020000;
-typedef float f32x2v __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2w __attribute__((ext_vector_type(2)));  // converts with v_cvt_pk_bf16_f32 (RNE)
-// B operand of ones (bf16 1.0 = 0x3f80): P x ones gives every head's row sum of P
-__device__ __forceinline__ bf16x8 ones_bf16x8() {
-    return __builtin_bit_cast(bf16x8, u32x4w{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
-}
-
-// Row scaling of a 16x16 fp32 accumulator tile on the matrix cores: row i (head 4g + r of
-// the C layout) times alpha_i. With A_r[i][k] = alpha_i if i == 4k + r (else 0) and
-// B_r[k][n] = C[4k + r][n] (component r of every lane), sum_r A_r B_r = diag(alpha) C,
-// four 16x16x4 fp32 products, each exact to one fp32 rounding. ar[r] is alpha_i on the lane
-// with l % 16 == 4 (l / 16) + r and 0 elsewhere.
-__device__ __forceinline__ f32x4 scale_rows(const f32x4 c, const float ar[4]) {
-    f32x4 z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int r = 0; r < 4; ++r) z = __builtin_amdgcn_mfma_f32_16x16x4f32(ar[r], c[r], z, 0, 0, 0);
-    return z;
-}
-
-// LDS pitch of a tile row: 512 bf16 + 16 bf16 of padding. With the 32-byte pad both the
-// 16-byte row-fragment reads of 16 rows and the transposing reads of 16 rows x 32 bytes
-// are spread over all banks (measured ~190-205 B/clk/CU, against ~117 for an unpadded
-// XOR-swizzled row).
-constexpr int WP = WD + 16;
-
-__device__ __forceinline__ bf16x8 ld_bf16x8(const bf16_t *p) {
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4w *>(p));
-}
-
-__device__ __forceinline__ v4i16 ld_tr(const bf16_t *p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_v4i16 *)((__attribute__((address_space(3))) bf16_t *)p));
-}
 
 // NWV wavefronts per workgroup: 4 (64 heads; two workgroups share a CU) or 8 (128 heads,
 // one workgroup per CU: every gathered row is loaded once for all 128 heads).
@@ -129,31 +83,9 @@ attn_wide_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, co
     bf16x8 qf[KKN];
     {
         const bf16_t *qrow = q + ((int64_t)t * H + head0 + l16) * WD;
+        const float *rope_t = rope_cs ? rope_cs + (int64_t)t * R : nullptr;
 #pragma unroll
-        for (int kk = 0; kk < KKN; ++kk) {
-            const int d0 = 32 * kk + 8 * g4;
-            uint4 raw = *reinterpret_cast<const uint4 *>(qrow + d0);
-            if (rope_cs != nullptr && d0 + 8 > WD - R) {
-                const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
-                uint32_t o[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float x0 = lo_bf16(wd[e]), x1 = hi_bf16(wd[e]);
-                    const int d = d0 + 2 * e;
-                    if (d >= WD - R) {
-                        const int p = (d - (WD - R)) >> 1;
-                        const float cs = rope_cs[((int64_t)t * (R / 2) + p) * 2];
-                        const float sn = rope_cs[((int64_t)t * (R / 2) + p) * 2 + 1];
-                        const float y0 = x0 * cs - x1 * sn, y1 = x0 * sn + x1 * cs;
-                        x0 = y0;
-                        x1 = y1;
-                    }
-                    o[e] = (uint32_t)f32_to_bf16(x0) | ((uint32_t)f32_to_bf16(x1) << 16);
-                }
-                raw = make_uint4(o[0], o[1], o[2], o[3]);
-            }
-            qf[kk] = __builtin_bit_cast(bf16x8, raw);
-        }
+        for (int kk = 0; kk < KKN; ++kk) qf[kk] = q_fragment(qrow, kk, g4, rope_t, R);
     }
 
     // softmax state: m_ref of head head0 + l16 (replicated over the 4 lane groups); the
@@ -179,22 +111,12 @@ attn_wide_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, co
     // Rows without data read a valid stand-in address (this wave's own q rows) and are
     // masked out of the softmax, so every load is issued unconditionally.
     const bf16_t *standin = q + ((int64_t)t * H + head0) * WD;
+    const int32_t *idx_t = (ratio > 0) ? nullptr : idx + (int64_t)t * k;
     // Row addresses of the tile at slot jt: lane r < 32 resolves slot jt + r to a byte
     // address (the stand-in when the slot has no row) and the tile's 32-bit validity mask
     // comes from a ballot.
     auto tile_rows = [&](int64_t jt, uint64_t &addr) -> uint32_t {
-        const int64_t j = jt + (lane & 31);
-        const bf16_t *p = standin;
-        if (j < j1) {
-            if (j < c.nmain) {
-                const int64_t id = (ratio > 0) ? j
-                                   : (j - j0 < kIdxCache ? (int64_t)sidx[j - j0] : (int64_t)idx[(int64_t)t * k + j]);
-                if (id >= 0 && id < N) p = kv + ((int64_t)c.s * N + id) * WD;
-            } else {
-                const int64_t r = c.lo + (j - c.nmain) - c.swa0;
-                if (r >= 0 && r < swa_rows) p = swa + ((int64_t)c.s * swa_rows + r) * WD;
-            }
-        }
+        const bf16_t *p = slot_row(c, jt + (lane & 31), j0, j1, ratio, sidx, idx_t, N, kv, swa, swa_rows, standin);
         addr = (uint64_t)(uintptr_t)p;
         return (uint32_t)(__ballot(p != standin) & 0xffffffffull);
     };
@@ -414,6 +336,12 @@ attn_wide_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, co
 bool wide_attn_ok(csa_dtype dt, int H, int D) { return dt == CSA_BF16 && D == WD && H % 64 == 0; }
 
 int launch_attn_wide(const AttnArgs &a, float sl2, int nsplit, int64_t split_slots, hipStream_t st) {
+    // dense (HCA) attention of many queries, one split each: 32 heads per wavefront, so
+    // every LDS fragment read feeds two matrix ops (measured 7 % faster at the 4,096-query
+    // HCA prefill chunk; slower on gathered top-k rows, whose per-query overhead the single
+    // workgroup per CU cannot hide)
+    if (a.ratio > 0 && w32_attn_ok(a.dt, a.H, a.D) && nsplit == 1 && (int64_t)a.T * (a.H / 128) >= 256)
+        return launch_attn_w32(a, sl2, nsplit, split_slots, st);
     // many queries with gathered rows (sparse, 128-head multiples, no row split): one 8-wave
     // workgroup per 128 heads, so a row is fetched once per query (measured 5 % faster at
     // the Pro prefill chunk); otherwise 4-wave workgroups, two per CU (summaries sit in L2,

@@ -237,11 +237,13 @@ def test_sparse_attn(csa, orc, case):
     assert_rel(lse, rlse, TOL_F32 if c["dt"] == torch.float32 else 2e-3, "sparse attn lse")
 
 
-@pytest.mark.parametrize("T,H", [(256, 64), (2, 128), (3, 64)])
+@pytest.mark.parametrize("T,H", [(256, 64), (256, 128), (2, 128), (3, 64)])
 def test_sparse_attn_growing_logits(csa, orc, T, H):
     """Rows whose magnitude grows with the index, visited in index order: the running
     maximum keeps jumping by far more than the lazy headroom, so the rescaling of the
-    accumulators runs many times (single pass for T=256, split otherwise)."""
+    accumulators runs many times (single pass for T=256, split otherwise); with 128 heads
+    and 256 queries the 32-heads-per-wavefront kernel abandons its tile loop and takes its
+    two-pass fallback."""
     say("sparse_attn growing", T, H)
     D, B, N, k = 512, 1, 700, 512
     pos = [8 * N + t for t in range(T)]
@@ -281,6 +283,27 @@ def test_hca_attn(csa, orc, case):
     ref, rlse = orc.hca_attn(q, summ, sink, 128, scale, swa, p0, 128, q_seq, q_pos, rope, 64)
     assert_rel(out, ref, TOL_F32 if dt == torch.float32 else TOL_BF16, "hca out")
     assert_rel(lse, rlse, TOL_F32 if dt == torch.float32 else 2e-3, "hca lse")
+
+
+@pytest.mark.parametrize("T,H", [(256, 128), (4, 128)])
+def test_hca_attn_growing_logits(csa, orc, T, H):
+    """Summaries whose magnitude grows with the index: the running maximum keeps jumping
+    past the headroom. With 256 queries x 128 heads the 32-heads-per-wavefront kernel
+    abandons its tile loop and takes its two-pass fallback; with 4 queries the split path
+    rescales its accumulators."""
+    say("hca_attn growing", T, H)
+    D, B, N = 512, 1, 96
+    pos = [int(p) for p in np.linspace(N * 128 - 500, N * 128 + 50, T).astype(np.int64)]
+    q, summ, swa, sink, q_seq, q_pos, _, p0, rope = _attn_inputs(700 + T, T, H, D, B, N, 0, 300,
+                                                                 torch.bfloat16, pos, with_rope=False)
+    grow = (1.0 + 0.2 * torch.arange(N, dtype=torch.float32, device=DEV)).view(1, N, 1)
+    summ = (summ.float() * grow).to(torch.bfloat16)
+    scale = 1.0 / np.sqrt(D)
+    out, lse = csa.hca_attn(q, summ, sink, 128, scale, swa, p0, 128, q_seq, q_pos, rope, 64)
+    torch.cuda.synchronize()
+    ref, rlse = orc.hca_attn(q, summ, sink, 128, scale, swa, p0, 128, q_seq, q_pos, rope, 64)
+    assert_rel(out, ref, TOL_BF16, "growing-logit hca out")
+    assert_rel(lse, rlse, 2e-3, "growing-logit hca lse")
 
 
 def test_working_set_sizes_on_gpu(csa):
