@@ -22,6 +22,11 @@ typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
 constexpr int kBufDword3 = 0x00020000;
 typedef float f32x2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2w __attribute__((ext_vector_type(2)));  // converts with v_cvt_pk_bf16_f32 (RNE)
+// two fp32 values rounded to nearest-even bf16 and packed (low = a) by v_cvt_pk_bf16_f32
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{a, b}, bf16x2w));
+}
+
 // B operand of ones (bf16 1.0 = 0x3f80): P x ones gives every head's row sum of P
 __device__ __forceinline__ bf16x8 ones_bf16x8() {
     return __builtin_bit_cast(bf16x8, u32x4w{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
@@ -73,30 +78,33 @@ __device__ __forceinline__ const bf16_t *slot_row(const RowCtx &c, int64_t j, in
     return p;
 }
 
-// q^T fragment (B operand of S^T = K Q^T) of one head: dims 32kk + 8g .. +7 of row `qrow`,
-// with the rotation of the last R dims applied in fp32 and rounded once to bf16.
-__device__ __forceinline__ bf16x8 q_fragment(const bf16_t *qrow, int kk, int g, const float *rope_t, int R) {
+// Rotation of the last R dims of a q^T fragment (dims 32kk + 8g .. +7), in fp32, rounded
+// once to bf16; fragments below the rotated dims pass through.
+__device__ __forceinline__ bf16x8 rope_fragment(bf16x8 v, int kk, int g, const float *rope_t, int R) {
     const int d0 = 32 * kk + 8 * g;
-    uint4 raw = *reinterpret_cast<const uint4 *>(qrow + d0);
-    if (rope_t != nullptr && d0 + 8 > WD - R) {
-        const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
-        uint32_t o[4];
+    if (rope_t == nullptr || d0 + 8 <= WD - R) return v;
+    const u32x4w raw = __builtin_bit_cast(u32x4w, v);
+    uint32_t o[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            float x0 = lo_bf16(wd[e]), x1 = hi_bf16(wd[e]);
-            const int d = d0 + 2 * e;
-            if (d >= WD - R) {
-                const int p = (d - (WD - R)) >> 1;
-                const float cs = rope_t[2 * p], sn = rope_t[2 * p + 1];
-                const float y0 = x0 * cs - x1 * sn, y1 = x0 * sn + x1 * cs;
-                x0 = y0;
-                x1 = y1;
-            }
-            o[e] = (uint32_t)f32_to_bf16(x0) | ((uint32_t)f32_to_bf16(x1) << 16);
+    for (int e = 0; e < 4; ++e) {
+        float x0 = lo_bf16(raw[e]), x1 = hi_bf16(raw[e]);
+        const int d = d0 + 2 * e;
+        if (d >= WD - R) {
+            const int p = (d - (WD - R)) >> 1;
+            const float cs = rope_t[2 * p], sn = rope_t[2 * p + 1];
+            const float y0 = x0 * cs - x1 * sn, y1 = x0 * sn + x1 * cs;
+            x0 = y0;
+            x1 = y1;
         }
-        raw = make_uint4(o[0], o[1], o[2], o[3]);
+        o[e] = pack_bf16x2(x0, x1);
     }
-    return __builtin_bit_cast(bf16x8, raw);
+    return __builtin_bit_cast(bf16x8, u32x4w{o[0], o[1], o[2], o[3]});
+}
+
+// q^T fragment (B operand of S^T = K Q^T) of one head: dims 32kk + 8g .. +7 of row `qrow`,
+// with the rotation of the last R dims applied.
+__device__ __forceinline__ bf16x8 q_fragment(const bf16_t *qrow, int kk, int g, const float *rope_t, int R) {
+    return rope_fragment(ld_bf16x8(qrow + 32 * kk + 8 * g), kk, g, rope_t, R);
 }
 
 }  // namespace amfma

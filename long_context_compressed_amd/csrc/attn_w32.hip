@@ -38,6 +38,7 @@ constexpr int NWV = 4;            // wavefronts per workgroup
 constexpr int HB = 2;             // 16-head blocks per wavefront
 constexpr int WH = 16 * HB * NWV; // heads per workgroup
 constexpr int RPW = WR / NWV;     // tile rows loaded per wavefront
+static_assert(RPW == 4 * HB, "the row loads are spread over the softmax of the head blocks");
 constexpr int SDA = 1;            // K fragment chunks read ahead
 constexpr int PVA = 2;            // V fragment chunks read ahead
 constexpr float kHeadroom = 24.f; // log2 growth of a head's maximum the tile loop absorbs
@@ -54,11 +55,11 @@ __device__ __forceinline__ void pv_mfma(f32x4 &acc, const bf16x8 a, const bf16x8
 }
 // the first products of a tile, both head blocks in one statement behind the wait states
 // for P's VALU writes
-__device__ __forceinline__ void pv_mfma2_after_valu(f32x4 &acc0, f32x4 &acc1, const bf16x8 a0, const bf16x8 a1,
-                                                    const bf16x8 b) {
-    asm volatile("s_nop 4\n\tv_mfma_f32_16x16x32_bf16 %0, %2, %4, %0\n\tv_mfma_f32_16x16x32_bf16 %1, %3, %4, %1"
+__device__ __forceinline__ void pv_mfma2_after_valu(f32x4 &acc0, f32x4 &acc1, const bf16x8 a, const bf16x8 b0,
+                                                    const bf16x8 b1) {
+    asm volatile("s_nop 4\n\tv_mfma_f32_16x16x32_bf16 %0, %2, %3, %0\n\tv_mfma_f32_16x16x32_bf16 %1, %2, %4, %1"
                  : "+a"(acc0), "+a"(acc1)
-                 : "v"(a0), "v"(a1), "v"(b));
+                 : "v"(a), "v"(b0), "v"(b1));
 }
 __device__ __forceinline__ void pv_fence() { asm volatile("s_nop 15\n\ts_nop 15" ::: "memory"); }
 
@@ -205,12 +206,17 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
     bf16x8 qf[HB][KKN];
     {
         const float *rope_t = rope_cs ? rope_cs + (int64_t)t * R : nullptr;
+        // every load first (they overlap), then the rotation of the fragments that need it
 #pragma unroll
         for (int b = 0; b < HB; ++b) {
             const bf16_t *qrow = q + ((int64_t)t * H + head0 + 16 * b + l16) * WD;
 #pragma unroll
-            for (int kk = 0; kk < KKN; ++kk) qf[b][kk] = q_fragment(qrow, kk, g4, rope_t, R);
+            for (int kk = 0; kk < KKN; ++kk) qf[b][kk] = ld_bf16x8(qrow + 32 * kk + 8 * g4);
         }
+#pragma unroll
+        for (int b = 0; b < HB; ++b)
+#pragma unroll
+            for (int kk = 0; kk < KKN; ++kk) qf[b][kk] = rope_fragment(qf[b][kk], kk, g4, rope_t, R);
     }
 
     // softmax state per head block: m_ref of head 16b + l16 (replicated over the 4 lane
@@ -269,6 +275,24 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(buf + row * WP), 16,
                                                  lane * 16, 0, 0, 0);
     };
+    // Dense attention walks the summaries in order, so a tile whose 32 slots are all
+    // summaries is 32 consecutive rows: one buffer resource covers it and no address leaves
+    // a lane (the per-row read-out above costs the wave more than the load itself).
+    const int64_t jc = (j1 < c.nmain) ? j1 : c.nmain;  // slots before jc are summaries
+    auto contig = [&](int64_t jn) __attribute__((always_inline)) { return ratio > 0 && jn + WR <= jc; };
+    // buffer resource over the 32 rows from slot jn (the address is read out of lane 0 so
+    // the compiler knows it is uniform)
+    auto contig_rsrc = [&](int64_t jn) __attribute__((always_inline)) {
+        const uint64_t a = (uint64_t)(uintptr_t)(kv + ((int64_t)c.s * N + jn) * WD);
+        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+        return __builtin_amdgcn_make_buffer_rsrc((void *)(((uint64_t)hi << 32) | lo), 0, WR * WD * 2, kBufDword3);
+    };
+    auto dma_row_contig = [&](bf16_t *buf, int i, __amdgpu_buffer_rsrc_t rs) __attribute__((always_inline)) {
+        const int row = RPW * wu + i;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(buf + row * WP), 16,
+                                                 lane * 16, row * WD * 2, 0, 0);
+    };
 
     uint32_t valid = 0u, valid_next = 0u;
     uint64_t ra;  // row addresses of the next tile, resolved one tile ahead
@@ -279,11 +303,17 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
     // never rescaled (so it is only ever touched by the products into it); a later tile
     // whose maximum exceeds the reference by more than 2^kHeadroom raises `redo`.
     auto tile_step = [&](const bf16_t *tile, bf16_t *nxt, int64_t jt, bool first) __attribute__((always_inline)) {
-        uint64_t ra2;
+        uint64_t ra2 = 0;
         uint32_t valid_next2;
-
+        const bool cn = contig(jt + WR);  // the tile loaded during this one
+        const __amdgpu_buffer_rsrc_t crs = contig_rsrc(cn ? jt + WR : j0);
+        if (cn) {
 #pragma unroll
-        for (int i = 0; i < RPW; ++i) dma_row(nxt, i, ra);
+            for (int i = 0; i < RPW; ++i) dma_row_contig(nxt, i, crs);
+        } else {
+#pragma unroll
+            for (int i = 0; i < RPW; ++i) dma_row(nxt, i, ra);
+        }
 
         // ---- S^T = K Q^T: each K fragment feeds both head blocks
         f32x4 sacc[2][HB];
@@ -317,7 +347,7 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
         }
         // rows of the tile after next: the index read and the address arithmetic overlap
         // the matrix ops still in flight
-        valid_next2 = tile_rows(jt + 2 * WR, ra2);
+        valid_next2 = contig(jt + 2 * WR) ? 0xffffffffu : tile_rows(jt + 2 * WR, ra2);
 
         // rows without data are masked to -inf; full tiles skip the mask
         if (valid != 0xffffffffu) {
@@ -333,6 +363,10 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
         bf16x8 pf[HB];
 #pragma unroll
         for (int b = 0; b < HB; ++b) {
+            // the next tile's row loads ride the softmax (VALU work, LDS idle): issued among
+            // it they queue in the address unit while the wave computes, where one burst at
+            // the start of the tile stalls every wavefront behind the others' loads
+
             // the scale is positive, so the max of the raw scores gives the max logit
             float smax = fmaxf(fmaxf(fmaxf(sacc[0][b][0], sacc[0][b][1]), fmaxf(sacc[0][b][2], sacc[0][b][3])),
                                fmaxf(fmaxf(sacc[1][b][0], sacc[1][b][1]), fmaxf(sacc[1][b][2], sacc[1][b][3])));
@@ -353,6 +387,7 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
             // p = 2^(s * scale - m_ref), packed to bf16 in the A-operand layout of P.
             // v_exp_f32 flushes results below 2^-126 to zero, which only drops weights that
             // no bf16 sum could hold.
+
             const float nmu = (m_ref[b] == -INFINITY) ? 0.f : -m_ref[b];
             uint32_t pk[4];
 #pragma unroll
@@ -361,11 +396,10 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
                 for (int r = 0; r < 4; r += 2) {
                     const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[m][b][r], scale_log2, nmu));
                     const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[m][b][r + 1], scale_log2, nmu));
-                    pk[2 * m + r / 2] =
-                        __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{p0, p1}, bf16x2w));
+                    pk[2 * m + r / 2] = pack_bf16x2(p0, p1);
                 }
             pf[b] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-            lacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[b], ones_bf16x8(), lacc[b], 0, 0, 0);
+            lacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_bf16x8(), pf[b], lacc[b], 0, 0, 0);
         }
 
         {
@@ -391,10 +425,10 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
                 const bf16x8 vf = __builtin_shufflevector(vr[nd % (PVA + 1)][0], vr[nd % (PVA + 1)][1], 0, 1, 2, 3,
                                                           4, 5, 6, 7);
                 if (nd == 0) {
-                    pv_mfma2_after_valu(acc[0][0], acc[1][0], pf[0], pf[1], vf);
+                    pv_mfma2_after_valu(acc[0][0], acc[1][0], vf, pf[0], pf[1]);
                 } else {
 #pragma unroll
-                    for (int b = 0; b < HB; ++b) pv_mfma(acc[b][nd], pf[b], vf);
+                    for (int b = 0; b < HB; ++b) pv_mfma(acc[b][nd], vf, pf[b]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -410,11 +444,17 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
     };
 
     if (j0 < j1) {
-        valid = tile_rows(j0, ra);
+        if (contig(j0)) {
+            valid = 0xffffffffu;
 #pragma unroll
-        for (int i = 0; i < RPW; ++i) dma_row(KV0, i, ra);
+            for (int i = 0; i < RPW; ++i) dma_row_contig(KV0, i, contig_rsrc(j0));
+        } else {
+            valid = tile_rows(j0, ra);
+#pragma unroll
+            for (int i = 0; i < RPW; ++i) dma_row(KV0, i, ra);
+        }
     }
-    valid_next = tile_rows(j0 + WR, ra);
+    valid_next = contig(j0 + WR) ? 0xffffffffu : tile_rows(j0 + WR, ra);
     // every prologue load has landed before the loop (the loop's wait counters then start
     // from a clean state)
     __builtin_amdgcn_s_waitcnt(0);
@@ -437,51 +477,55 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
     }
 
     pv_fence();
-    // ---- epilogue: O rows are heads head0 + 16b + 4g4 + r, columns dim 16nd + l16
+    // ---- epilogue. The products computed O^T: lane (l16, g4) holds dims 16nd + 4g4 + r
+    // (r = 0..3, four consecutive dims) of head 16b + l16, and the denominator of that head
+    // in every component of lacc[b], so each lane normalises, rotates back the last R dims
+    // (pairs sit in one lane) and stores 8 bytes per dim block.
 #pragma unroll
     for (int b = 0; b < HB; ++b) {
+        const int h = head0 + 16 * b + l16;
         if (single) {
+            const float sk = sink[h] * kLog2e;
+            const float mr = m_ref[b];
+            const float lv = lacc[b][0] + ((sk == -INFINITY) ? 0.f : exp2f(sk - mr));
+            if (lse != nullptr && g4 == 0) {
+                const float mu = (mr == -INFINITY) ? 0.f : mr;
+                lse[(int64_t)t * H + h] = (lv > 0.f) ? (mu + log2f(lv)) * kLn2 : -INFINITY;
+            }
+            const float inv = lv > 0.f ? 1.f / lv : 0.f;
+            bf16_t *orow = out + ((int64_t)t * H + h) * WD;
+            const float *rope_t = rope_cs ? rope_cs + (int64_t)t * R : nullptr;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int h = head0 + 16 * b + 4 * g4 + r;
-                const float mr = __shfl(m_ref[b], 4 * g4 + r);
-                const float sk = sink[h] * kLog2e;
-                const float lv = lacc[b][r] + ((sk == -INFINITY) ? 0.f : exp2f(sk - mr));
-                if (lse != nullptr && l16 == 0) {
-                    const float mu = (mr == -INFINITY) ? 0.f : mr;
-                    lse[(int64_t)t * H + h] = (lv > 0.f) ? (mu + log2f(lv)) * kLn2 : -INFINITY;
-                }
-                const float inv = lv > 0.f ? 1.f / lv : 0.f;
-                bf16_t *orow = out + ((int64_t)t * H + h) * WD;
+            for (int nd = 0; nd < NDN; ++nd) {
+                const int d0 = 16 * nd + 4 * g4;
+                float x[4];
 #pragma unroll
-                for (int nd = 0; nd < NDN; ++nd) {
-                    const int d = 16 * nd + l16;
-                    float x = acc[b][nd][r] * inv;
-                    const float y = __shfl_xor(x, 1);
-                    if (rope_cs != nullptr && d >= WD - R) {
-                        const int p = (d - (WD - R)) >> 1;
-                        const float cs = rope_cs[((int64_t)t * (R / 2) + p) * 2];
-                        const float sn = rope_cs[((int64_t)t * (R / 2) + p) * 2 + 1];
-                        x = (d & 1) ? (x * cs - y * sn) : (x * cs + y * sn);
+                for (int r = 0; r < 4; ++r) x[r] = acc[b][nd][r] * inv;
+                if (rope_t != nullptr && d0 >= WD - R) {
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const int p = (d0 + 2 * e - (WD - R)) >> 1;
+                        const float cs = rope_t[2 * p], sn = rope_t[2 * p + 1];
+                        const float x0 = x[2 * e], x1 = x[2 * e + 1];
+                        x[2 * e] = x0 * cs + x1 * sn;
+                        x[2 * e + 1] = x1 * cs - x0 * sn;
                     }
-                    orow[d] = f32_to_bf16(x);
                 }
+                const uint32_t w0 = pack_bf16x2(x[0], x[1]), w1 = pack_bf16x2(x[2], x[3]);
+                *reinterpret_cast<uint2 *>(orow + d0) = make_uint2(w0, w1);
             }
         } else {
-            const int64_t pu = ((int64_t)t * nsplit + sp) * H + head0 + 16 * b;
+            const int64_t pu = ((int64_t)t * nsplit + sp) * H + h;
             float *pml = part;                                 // [T][nsplit][H][2]
             float *pacc = part + (int64_t)T * nsplit * H * 2;  // [T][nsplit][H][D]
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float mr = __shfl(m_ref[b], 4 * g4 + r);
-                if (l16 == 0) {
-                    pml[(pu + 4 * g4 + r) * 2] = mr;
-                    pml[(pu + 4 * g4 + r) * 2 + 1] = lacc[b][r];
-                }
-                float *prow = pacc + (pu + 4 * g4 + r) * WD;
-#pragma unroll
-                for (int nd = 0; nd < NDN; ++nd) prow[16 * nd + l16] = acc[b][nd][r];
+            if (g4 == 0) {
+                pml[pu * 2] = m_ref[b];
+                pml[pu * 2 + 1] = lacc[b][0];
             }
+#pragma unroll
+            for (int nd = 0; nd < NDN; ++nd)
+                *reinterpret_cast<float4 *>(pacc + pu * WD + 16 * nd + 4 * g4) =
+                    make_float4(acc[b][nd][0], acc[b][nd][1], acc[b][nd][2], acc[b][nd][3]);
         }
     }
     if (abandoned) {
