@@ -101,6 +101,33 @@ __device__ __forceinline__ bf16x8 rope_fragment(bf16x8 v, int kk, int g, const f
     return __builtin_bit_cast(bf16x8, u32x4w{o[0], o[1], o[2], o[3]});
 }
 
+// The same rotation with the fragment's four (cos, sin) pairs already in registers.
+__device__ __forceinline__ bf16x8 rope_fragment_cs(bf16x8 v, int kk, int g, const float cs[4], const float sn[4],
+                                                   int R) {
+    const int d0 = 32 * kk + 8 * g;
+    if (d0 + 8 <= WD - R) return v;
+    const u32x4w raw = __builtin_bit_cast(u32x4w, v);
+    uint32_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        float x0 = lo_bf16(raw[e]), x1 = hi_bf16(raw[e]);
+        if (d0 + 2 * e >= WD - R) {
+            const float y0 = x0 * cs[e] - x1 * sn[e], y1 = x0 * sn[e] + x1 * cs[e];
+            x0 = y0;
+            x1 = y1;
+        }
+        o[e] = pack_bf16x2(x0, x1);
+    }
+    return __builtin_bit_cast(bf16x8, u32x4w{o[0], o[1], o[2], o[3]});
+}
+
+// (cos, sin) of the pair holding dim d, or of pair 0 when d is not rotated (the caller
+// ignores it then); always a valid table entry, so a batch of these loads needs no branch
+__device__ __forceinline__ float2 rope_pair(const float *rope_t, int d, int R) {
+    const int p = d >= WD - R ? (d - (WD - R)) >> 1 : 0;
+    return *reinterpret_cast<const float2 *>(rope_t + 2 * p);
+}
+
 // q^T fragment (B operand of S^T = K Q^T) of one head: dims 32kk + 8g .. +7 of row `qrow`,
 // with the rotation of the last R dims applied.
 __device__ __forceinline__ bf16x8 q_fragment(const bf16_t *qrow, int kk, int g, const float *rope_t, int R) {

@@ -61,6 +61,13 @@ __device__ __forceinline__ void pv_mfma2_after_valu(f32x4 &acc0, f32x4 &acc1, co
                  : "+a"(acc0), "+a"(acc1)
                  : "v"(a), "v"(b0), "v"(b1));
 }
+// one accumulator read out of its AGPR where it is used (left to itself the compiler copies
+// every accumulator to VGPRs at the loop exit, more than there are)
+__device__ __forceinline__ float agpr_read(float a) {
+    float v;
+    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+    return v;
+}
 __device__ __forceinline__ void pv_fence() { asm volatile("s_nop 15\n\ts_nop 15" ::: "memory"); }
 
 
@@ -68,7 +75,7 @@ __device__ __forceinline__ void pv_fence() { asm volatile("s_nop 15\n\ts_nop 15"
 // scratch with plain VALU arithmetic and two passes over the rows (exact maximum, then the
 // weighted sums in fp32). It backs the tile loop when a head's maximum grows past the
 // loop's headroom; lane l holds dims 8l .. 8l+7.
-__device__ __attribute__((noinline)) void unit_fallback(
+__device__ __forceinline__ void unit_fallback(
     const bf16_t *q, const float *sink, const RowCtx c, int64_t j0, int64_t j1, int ratio, const int32_t *sidx,
     const int32_t *idx_t, int64_t N, const bf16_t *kv, const bf16_t *swa, int swa_rows, const float *rope_t, int R,
     float scale_log2, int t, int T, int H, int head0, int nsplit, int sp, bf16_t *out, float *lse, float *part)
@@ -202,21 +209,38 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
     int64_t j1 = j0 + split_slots;
     if (j1 > c.nslots) j1 = c.nslots;
 
-    // q^T fragments of both head blocks, for the whole query
+    // q^T fragments of both head blocks, for the whole query. Every load is issued first
+    // (they overlap; the (cos, sin) pairs of the last 64 dims included), then the fragments
+    // that hold rotated dims are rotated.
+    const float *rope_t = rope_cs ? rope_cs + (int64_t)t * R : nullptr;
     bf16x8 qf[HB][KKN];
     {
-        const float *rope_t = rope_cs ? rope_cs + (int64_t)t * R : nullptr;
-        // every load first (they overlap), then the rotation of the fragments that need it
+        float2 qr[2][4];
+        if (rope_t != nullptr) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) qr[j][e] = rope_pair(rope_t, 32 * (KKN - 2 + j) + 8 * g4 + 2 * e, R);
+        }
 #pragma unroll
         for (int b = 0; b < HB; ++b) {
             const bf16_t *qrow = q + ((int64_t)t * H + head0 + 16 * b + l16) * WD;
 #pragma unroll
             for (int kk = 0; kk < KKN; ++kk) qf[b][kk] = ld_bf16x8(qrow + 32 * kk + 8 * g4);
         }
+        if (rope_t != nullptr) {
 #pragma unroll
-        for (int b = 0; b < HB; ++b)
+            for (int b = 0; b < HB; ++b) {
 #pragma unroll
-            for (int kk = 0; kk < KKN; ++kk) qf[b][kk] = rope_fragment(qf[b][kk], kk, g4, rope_t, R);
+                for (int kk = 0; kk < KKN - 2; ++kk) qf[b][kk] = rope_fragment(qf[b][kk], kk, g4, rope_t, R);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const float cs[4] = {qr[j][0].x, qr[j][1].x, qr[j][2].x, qr[j][3].x};
+                    const float sn[4] = {qr[j][0].y, qr[j][1].y, qr[j][2].y, qr[j][3].y};
+                    qf[b][KKN - 2 + j] = rope_fragment_cs(qf[b][KKN - 2 + j], KKN - 2 + j, g4, cs, sn, R);
+                }
+            }
+        }
     }
 
     // softmax state per head block: m_ref of head 16b + l16 (replicated over the 4 lane
@@ -459,23 +483,23 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
     // from a clean state)
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    bool abandoned = false;
-    for (int64_t jt = j0; jt < j1;) {
+    // Tiles go in pairs (one per buffer) and the loop has a single exit: an odd count ends
+    // with a tile past j1, whose slots are all masked (no weight). An abandoned loop still
+    // runs to the end; its results are replaced below.
+    for (int64_t jt = j0; jt < j1; jt += 2 * WR) {
         tile_step(KV0, KV1, jt, jt == j0);
-        jt += WR;
-        if (redo) {
-            abandoned = true;
-            break;
-        }
-        if (jt >= j1) break;
-        tile_step(KV1, KV0, jt, false);
-        jt += WR;
-        if (redo) {
-            abandoned = true;
-            break;
-        }
+        tile_step(KV1, KV0, jt + WR, false);
     }
+    const bool abandoned = redo != 0;
 
+    // (cos, sin) pairs of the lane's last 64 output dims, loaded in one batch
+    float2 orp[4][2];
+    if (rope_t != nullptr) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) orp[j][e] = rope_pair(rope_t, 16 * (NDN - 4 + j) + 4 * g4 + 2 * e, R);
+    }
     pv_fence();
     // ---- epilogue. The products computed O^T: lane (l16, g4) holds dims 16nd + 4g4 + r
     // (r = 0..3, four consecutive dims) of head 16b + l16, and the denominator of that head
@@ -494,18 +518,17 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
             }
             const float inv = lv > 0.f ? 1.f / lv : 0.f;
             bf16_t *orow = out + ((int64_t)t * H + h) * WD;
-            const float *rope_t = rope_cs ? rope_cs + (int64_t)t * R : nullptr;
 #pragma unroll
             for (int nd = 0; nd < NDN; ++nd) {
                 const int d0 = 16 * nd + 4 * g4;
                 float x[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) x[r] = acc[b][nd][r] * inv;
+                for (int r = 0; r < 4; ++r) x[r] = agpr_read(acc[b][nd][r]) * inv;
                 if (rope_t != nullptr && d0 >= WD - R) {
 #pragma unroll
                     for (int e = 0; e < 2; ++e) {
-                        const int p = (d0 + 2 * e - (WD - R)) >> 1;
-                        const float cs = rope_t[2 * p], sn = rope_t[2 * p + 1];
+                        const float2 cp = (nd >= NDN - 4) ? orp[nd >= NDN - 4 ? nd - (NDN - 4) : 0][e] : rope_pair(rope_t, d0 + 2 * e, R);
+                        const float cs = cp.x, sn = cp.y;
                         const float x0 = x[2 * e], x1 = x[2 * e + 1];
                         x[2 * e] = x0 * cs + x1 * sn;
                         x[2 * e + 1] = x1 * cs - x0 * sn;
@@ -513,6 +536,9 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
                 }
                 const uint32_t w0 = pack_bf16x2(x[0], x[1]), w1 = pack_bf16x2(x[2], x[3]);
                 *reinterpret_cast<uint2 *>(orow + d0) = make_uint2(w0, w1);
+                // one block at a time: hoisted reads of later blocks would need registers
+                // the accumulators still hold
+                __builtin_amdgcn_sched_barrier(0);
             }
         } else {
             const int64_t pu = ((int64_t)t * nsplit + sp) * H + h;
@@ -523,9 +549,12 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
                 pml[pu * 2 + 1] = lacc[b][0];
             }
 #pragma unroll
-            for (int nd = 0; nd < NDN; ++nd)
+            for (int nd = 0; nd < NDN; ++nd) {
                 *reinterpret_cast<float4 *>(pacc + pu * WD + 16 * nd + 4 * g4) =
-                    make_float4(acc[b][nd][0], acc[b][nd][1], acc[b][nd][2], acc[b][nd][3]);
+                    make_float4(agpr_read(acc[b][nd][0]), agpr_read(acc[b][nd][1]), agpr_read(acc[b][nd][2]),
+                                agpr_read(acc[b][nd][3]));
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     }
     if (abandoned) {
