@@ -518,20 +518,25 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
             }
             const float inv = lv > 0.f ? 1.f / lv : 0.f;
             bf16_t *orow = out + ((int64_t)t * H + h) * WD;
+            const int nd_r = (WD - R) >> 4;
 #pragma unroll
             for (int nd = 0; nd < NDN; ++nd) {
                 const int d0 = 16 * nd + 4 * g4;
                 float x[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) x[r] = agpr_read(acc[b][nd][r]) * inv;
-                if (rope_t != nullptr && d0 >= WD - R) {
+                // blocks before nd_r hold no rotated dim (a uniform test); within a block
+                // each pair is checked
+                if (rope_t != nullptr && nd >= nd_r) {
 #pragma unroll
                     for (int e = 0; e < 2; ++e) {
-                        const float2 cp = (nd >= NDN - 4) ? orp[nd >= NDN - 4 ? nd - (NDN - 4) : 0][e] : rope_pair(rope_t, d0 + 2 * e, R);
-                        const float cs = cp.x, sn = cp.y;
-                        const float x0 = x[2 * e], x1 = x[2 * e + 1];
-                        x[2 * e] = x0 * cs + x1 * sn;
-                        x[2 * e + 1] = x1 * cs - x0 * sn;
+                        const float2 cp =
+                            (nd >= NDN - 4) ? orp[nd >= NDN - 4 ? nd - (NDN - 4) : 0][e] : rope_pair(rope_t, d0 + 2 * e, R);
+                        if (d0 + 2 * e >= WD - R) {
+                            const float x0 = x[2 * e], x1 = x[2 * e + 1];
+                            x[2 * e] = x0 * cp.x + x1 * cp.y;
+                            x[2 * e + 1] = x1 * cp.x - x0 * cp.y;
+                        }
                     }
                 }
                 const uint32_t w0 = pack_bf16x2(x[0], x[1]), w1 = pack_bf16x2(x[2], x[3]);

@@ -191,7 +191,7 @@ def test_topk_distinct_full_sort(csa):
 # attention
 # ------------------------------------------------------------------------------------
 
-def _attn_inputs(seed, T, H, D, B, N, k, swa_rows, dt, pos, with_rope=True, bad_idx=True):
+def _attn_inputs(seed, T, H, D, B, N, k, swa_rows, dt, pos, with_rope=True, bad_idx=True, rope_dim=64):
     q = W.normal((T, H, D), seed, "q", dtype=dt, device=DEV)
     kv = W.normal((B, N, D), seed, "kv", dtype=dt, device=DEV)
     swa = W.normal((B, swa_rows, D), seed, "swa", dtype=dt, device=DEV)
@@ -208,7 +208,7 @@ def _attn_inputs(seed, T, H, D, B, N, k, swa_rows, dt, pos, with_rope=True, bad_
         idx = idx.to(DEV)
     swa_pos0 = torch.tensor([max(0, max(pos) - swa_rows + 1 - 3 * b) for b in range(B)], dtype=torch.int64,
                             device=DEV)
-    rope = W.rope_table(q_pos.cpu(), 64).to(DEV) if with_rope else None
+    rope = W.rope_table(q_pos.cpu(), rope_dim).to(DEV) if with_rope else None
     return q, kv, swa, sink, q_seq, q_pos, idx, swa_pos0, rope
 
 
@@ -304,6 +304,34 @@ def test_hca_attn_growing_logits(csa, orc, T, H):
     ref, rlse = orc.hca_attn(q, summ, sink, 128, scale, swa, p0, 128, q_seq, q_pos, rope, 64)
     assert_rel(out, ref, TOL_BF16, "growing-logit hca out")
     assert_rel(lse, rlse, 2e-3, "growing-logit hca lse")
+
+
+@pytest.mark.parametrize("R", [18, 96])
+@pytest.mark.parametrize("mode", ["sparse", "hca"])
+def test_attn_rope_dims(csa, orc, mode, R):
+    """RoPE widths whose rotated dims start inside a 4-dim output group (18) or reach past
+    the last 64 dims (96), on the many-query kernel (256 queries x 128 heads)."""
+    say("attn rope dims", mode, R)
+    T, H, D = 256, 128, 512
+    scale = 1.0 / np.sqrt(D)
+    if mode == "sparse":
+        B, N, k = 1, 600, 64
+        pos = [int(p) for p in np.linspace(5, 1023, T).astype(np.int64)]
+        q, kv, swa, sink, q_seq, q_pos, idx, p0, rope = _attn_inputs(40 + R, T, H, D, B, N, k, 400, torch.bfloat16,
+                                                                     pos, rope_dim=R)
+        out, lse = csa.sparse_attn(q, kv, sink, idx, scale, swa, p0, 128, q_seq, q_pos, rope, R)
+        torch.cuda.synchronize()
+        ref, rlse = orc.sparse_attn(q, kv, sink, idx, scale, swa, p0, 128, q_seq, q_pos, rope, R)
+    else:
+        B, N = 1, 64
+        pos = [int(p) for p in np.linspace(60 * 128 - 40, 64 * 128 + 200, T).astype(np.int64)]
+        q, summ, swa, sink, q_seq, q_pos, _, p0, rope = _attn_inputs(50 + R, T, H, D, B, N, 0, 700, torch.bfloat16,
+                                                                     pos, rope_dim=R)
+        out, lse = csa.hca_attn(q, summ, sink, 128, scale, swa, p0, 128, q_seq, q_pos, rope, R)
+        torch.cuda.synchronize()
+        ref, rlse = orc.hca_attn(q, summ, sink, 128, scale, swa, p0, 128, q_seq, q_pos, rope, R)
+    assert_rel(out, ref, TOL_BF16, f"{mode} attn out, R={R}")
+    assert_rel(lse, rlse, 2e-3, f"{mode} attn lse, R={R}")
 
 
 def test_working_set_sizes_on_gpu(csa):
