@@ -38,7 +38,7 @@ constexpr int NWV = 4;            // wavefronts per workgroup
 constexpr int HB = 2;             // 16-head blocks per wavefront
 constexpr int WH = 16 * HB * NWV; // heads per workgroup
 constexpr int RPW = WR / NWV;     // tile rows loaded per wavefront
-static_assert(RPW == 4 * HB, "the row loads are spread over the softmax of the head blocks");
+static_assert(kIdxCache % (64 * NWV) == 0, "the index cache splits evenly over the threads");
 constexpr int SDA = 1;            // K fragment chunks read ahead
 constexpr int PVA = 2;            // V fragment chunks read ahead
 constexpr float kHeadroom = 24.f; // log2 growth of a head's maximum the tile loop absorbs
@@ -204,10 +204,22 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
     const int t = (int)(tu / nsplit), sp = (int)(tu % nsplit);
     const int head0 = hg * WH + 16 * HB * w;  // first head of this wave; block b = head0 + 16b ..
 
-    const RowCtx c = row_ctx(t, q_seq, q_pos, B, N, k, ratio, swa, swa_pos0, window);
+    // The loads that depend only on the unit (q, its RoPE pairs, the sinks, the split's
+    // top-k indices) are all issued before anything waits on the row context.
     const int64_t j0 = (int64_t)sp * split_slots;
-    int64_t j1 = j0 + split_slots;
-    if (j1 > c.nslots) j1 = c.nslots;
+    constexpr int IPT = kIdxCache / (64 * NWV);  // top-k indices per thread
+    int32_t ir[IPT];
+    {
+        const int64_t nc0 = (ratio <= 0) ? (k - j0 < kIdxCache ? k - j0 : kIdxCache) : 0;
+#pragma unroll
+        for (int m = 0; m < IPT; ++m) {
+            const int x = threadIdx.x + 64 * NWV * m;
+            ir[m] = (x < nc0) ? idx[(int64_t)t * k + j0 + x] : 0;
+        }
+    }
+    float sk[HB];
+#pragma unroll
+    for (int b = 0; b < HB; ++b) sk[b] = sink[head0 + 16 * b + l16];
 
     // q^T fragments of both head blocks, for the whole query. Every load is issued first
     // (they overlap; the (cos, sin) pairs of the last 64 dims included), then the fragments
@@ -243,6 +255,10 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
         }
     }
 
+    const RowCtx c = row_ctx(t, q_seq, q_pos, B, N, k, ratio, swa, swa_pos0, window);
+    int64_t j1 = j0 + split_slots;
+    if (j1 > c.nslots) j1 = c.nslots;
+
     // softmax state per head block: m_ref of head 16b + l16 (replicated over the 4 lane
     // groups); the denominators live in the output layout (head 16b + 4g4 + r in component
     // r of lacc[b]) and are accumulated by a matrix op against a ones operand, so they sum
@@ -264,15 +280,20 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
     };
 #pragma unroll
     for (int b = 0; b < HB; ++b) {
-        m_ref[b] = single ? sink[head0 + 16 * b + l16] * kLog2e : -INFINITY;
+        m_ref[b] = single ? sk[b] * kLog2e : -INFINITY;
     }
     reset_sums();
 
     // The split's top-k indices (up to kIdxCache of them) are read once into LDS.
     const int64_t jm = (j1 < c.nmain) ? j1 : c.nmain;  // main slots of this split: [j0, jm)
     const int64_t ncache = (jm - j0 < kIdxCache) ? jm - j0 : kIdxCache;
-    if (ratio <= 0)
-        for (int64_t x = threadIdx.x; x < ncache; x += 64 * NWV) sidx[x] = idx[(int64_t)t * k + j0 + x];
+    if (ratio <= 0) {
+#pragma unroll
+        for (int m = 0; m < IPT; ++m) {
+            const int x = threadIdx.x + 64 * NWV * m;
+            if (x < ncache) sidx[x] = ir[m];
+        }
+    }
     if (threadIdx.x == 0) redo = 0;
     __syncthreads();
     // Rows without data read a valid stand-in address (this wave's own q rows) and are
