@@ -522,7 +522,12 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
             for (int e = 0; e < 2; ++e) orp[j][e] = rope_pair(rope_t, 16 * (NDN - 4 + j) + 4 * g4 + 2 * e, R);
     }
     pv_fence();
-    // ---- epilogue. The products computed O^T: lane (l16, g4) holds dims 16nd + 4g4 + r
+    // ---- epilogue. Each wavefront stages one 16-head block of bf16 output rows in its own
+    // part of the (now idle) tile buffers, so no other wavefront's data is touched.
+    constexpr int OSP = WD + 16;  // staged row pitch (bf16): 1056 bytes spread the banks
+    static_assert(2 * 16 * OSP <= WR * WP, "two wavefronts' staging fits one tile buffer");
+    bf16_t *const ostage = (wu < 2 ? KV0 : KV1) + (wu & 1) * 16 * OSP;
+    // The products computed O^T: lane (l16, g4) holds dims 16nd + 4g4 + r
     // (r = 0..3, four consecutive dims) of head 16b + l16, and the denominator of that head
     // in every component of lacc[b], so each lane normalises, rotates back the last R dims
     // (pairs sit in one lane) and stores 8 bytes per dim block.
@@ -538,34 +543,50 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
                 lse[(int64_t)t * H + h] = (lv > 0.f) ? (mu + log2f(lv)) * kLn2 : -INFINITY;
             }
             const float inv = lv > 0.f ? 1.f / lv : 0.f;
-            bf16_t *orow = out + ((int64_t)t * H + h) * WD;
             const int nd_r = (WD - R) >> 4;
+            // groups of 8 blocks: all 8 are packed before the 8 stores go out, so a store's
+            // data registers are not rewritten while it is still in flight (one block at a
+            // time, every store waited for the one before)
+            constexpr int EG = 8;
 #pragma unroll
-            for (int nd = 0; nd < NDN; ++nd) {
-                const int d0 = 16 * nd + 4 * g4;
-                float x[4];
+            for (int ng = 0; ng < NDN; ng += EG) {
+                uint2 pk[EG];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) x[r] = agpr_read(acc[b][nd][r]) * inv;
-                // blocks before nd_r hold no rotated dim (a uniform test); within a block
-                // each pair is checked
-                if (rope_t != nullptr && nd >= nd_r) {
+                for (int q8 = 0; q8 < EG; ++q8) {
+                    const int nd = ng + q8;
+                    const int d0 = 16 * nd + 4 * g4;
+                    float x[4];
 #pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        const float2 cp =
-                            (nd >= NDN - 4) ? orp[nd >= NDN - 4 ? nd - (NDN - 4) : 0][e] : rope_pair(rope_t, d0 + 2 * e, R);
-                        if (d0 + 2 * e >= WD - R) {
-                            const float x0 = x[2 * e], x1 = x[2 * e + 1];
-                            x[2 * e] = x0 * cp.x + x1 * cp.y;
-                            x[2 * e + 1] = x1 * cp.x - x0 * cp.y;
+                    for (int r = 0; r < 4; ++r) x[r] = agpr_read(acc[b][nd][r]) * inv;
+                    // blocks before nd_r hold no rotated dim (a uniform test); within a
+                    // block each pair is checked
+                    if (rope_t != nullptr && nd >= nd_r) {
+#pragma unroll
+                        for (int e = 0; e < 2; ++e) {
+                            const float2 cp = (nd >= NDN - 4) ? orp[nd >= NDN - 4 ? nd - (NDN - 4) : 0][e]
+                                                              : rope_pair(rope_t, d0 + 2 * e, R);
+                            if (d0 + 2 * e >= WD - R) {
+                                const float x0 = x[2 * e], x1 = x[2 * e + 1];
+                                x[2 * e] = x0 * cp.x + x1 * cp.y;
+                                x[2 * e + 1] = x1 * cp.x - x0 * cp.y;
+                            }
                         }
                     }
+                    pk[q8] = make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
                 }
-                const uint32_t w0 = pack_bf16x2(x[0], x[1]), w1 = pack_bf16x2(x[2], x[3]);
-                *reinterpret_cast<uint2 *>(orow + d0) = make_uint2(w0, w1);
-                // one block at a time: hoisted reads of later blocks would need registers
+#pragma unroll
+                for (int q8 = 0; q8 < EG; ++q8)
+                    *reinterpret_cast<uint2 *>(ostage + l16 * OSP + 16 * (ng + q8) + 4 * g4) = pk[q8];
+                // one group at a time: hoisted reads of later groups would need registers
                 // the accumulators still hold
                 __builtin_amdgcn_sched_barrier(0);
             }
+            // the block's 16 head rows go out whole: one 1 KiB row per store instruction (a
+            // lane's 8-byte pieces of 16 rows would be 16 partial-line writes per store)
+#pragma unroll
+            for (int hr = 0; hr < 16; ++hr)
+                *reinterpret_cast<uint4 *>(out + ((int64_t)t * H + head0 + 16 * b + hr) * WD + 8 * lane) =
+                    *reinterpret_cast<const uint4 *>(ostage + hr * OSP + 8 * lane);
         } else {
             const int64_t pu = ((int64_t)t * nsplit + sp) * H + h;
             float *pml = part;                                 // [T][nsplit][H][2]
@@ -575,10 +596,15 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
                 pml[pu * 2 + 1] = lacc[b][0];
             }
 #pragma unroll
-            for (int nd = 0; nd < NDN; ++nd) {
-                *reinterpret_cast<float4 *>(pacc + pu * WD + 16 * nd + 4 * g4) =
-                    make_float4(agpr_read(acc[b][nd][0]), agpr_read(acc[b][nd][1]), agpr_read(acc[b][nd][2]),
-                                agpr_read(acc[b][nd][3]));
+            for (int ng = 0; ng < NDN; ng += 4) {
+                float4 v[4];
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+                    v[q4] = make_float4(agpr_read(acc[b][ng + q4][0]), agpr_read(acc[b][ng + q4][1]),
+                                        agpr_read(acc[b][ng + q4][2]), agpr_read(acc[b][ng + q4][3]));
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+                    *reinterpret_cast<float4 *>(pacc + pu * WD + 16 * (ng + q4) + 4 * g4) = v[q4];
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
