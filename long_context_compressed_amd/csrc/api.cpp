@@ -1,5 +1,6 @@
 // C ABI of the CSA / HCA library: argument validation, then dispatch to the launchers.
 // Every check below runs before anything is enqueued; a failed check launches nothing.
+#include <atomic>
 #include <cmath>
 #include <string>
 
@@ -20,6 +21,22 @@ int check_launch(const char *what) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(CSA_EHIP, std::string(what) + ": " + hipGetErrorString(e));
     return CSA_OK;
+}
+
+// compute units of the current device, queried once per device (the library's only
+// global state)
+int device_cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+    if (dev < 64) {
+        const int v = cache[dev].load(std::memory_order_relaxed);
+        if (v > 0) return v;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return -1;
+    if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
 }
 
 }  // namespace csa
