@@ -128,6 +128,15 @@ __device__ __forceinline__ float2 rope_pair(const float *rope_t, int d, int R) {
     return *reinterpret_cast<const float2 *>(rope_t + 2 * p);
 }
 
+// raw buffer resource over `bytes` bytes from p, with the address read out of lane 0 (the
+// caller passes a wave-uniform pointer) so the resource sits in scalar registers
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void *p, uint32_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    return __builtin_amdgcn_make_buffer_rsrc((void *)(((uint64_t)hi << 32) | lo), 0, (int)bytes, kBufDword3);
+}
+
 // q^T fragment (B operand of S^T = K Q^T) of one head: dims 32kk + 8g .. +7 of row `qrow`,
 // with the rotation of the last R dims applied.
 __device__ __forceinline__ bf16x8 q_fragment(const bf16_t *qrow, int kk, int g, const float *rope_t, int R) {

@@ -296,29 +296,44 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
     }
     if (threadIdx.x == 0) redo = 0;
     __syncthreads();
-    // Rows without data read a valid stand-in address (this wave's own q rows) and are
-    // masked out of the softmax, so every load is issued unconditionally.
-    const bf16_t *standin = q + ((int64_t)t * H + head0) * WD;
+    // Every row of the query lives in one of two regions: its sequence's compressed rows
+    // (kv) or its SWA rows. Each gets one buffer resource for the whole unit, and a row is
+    // named by a 32-bit code (region bit | row), so a row load only needs that code in a
+    // scalar register (the row's byte offset goes in the load's scalar offset). Rows
+    // without data are masked out of the softmax and load row 0 (a buffer load past the
+    // region's end returns zeros, so nothing outside it is ever touched).
     const int32_t *idx_t = (ratio > 0) ? nullptr : idx + (int64_t)t * k;
-    // Row addresses of the tile at slot jt: lane r < 32 resolves slot jt + r; the tile's
-    // 32-bit validity mask comes from a ballot.
-    auto tile_rows = [&](int64_t jt, uint64_t &addr) __attribute__((always_inline)) -> uint32_t {
-        const bf16_t *p = slot_row(c, jt + (lane & 31), j0, j1, ratio, sidx, idx_t, N, kv, swa, swa_rows, standin);
-        addr = (uint64_t)(uintptr_t)p;
-        return (uint32_t)(__ballot(p != standin) & 0xffffffffull);
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    const int s_u = __builtin_amdgcn_readfirstlane(c.s);
+    const __amdgpu_buffer_rsrc_t kv_rs = uniform_rsrc(kv + (int64_t)s_u * N * WD, (uint32_t)(N * WD * 2));
+    const __amdgpu_buffer_rsrc_t swa_rs =
+        uniform_rsrc(swa != nullptr ? swa + (int64_t)s_u * swa_rows * WD : kv, swa != nullptr ? (uint32_t)swa_rows * WD * 2 : 0u);
+    constexpr int32_t kSwaBit = 0x40000000;
+    // Row codes of the tile at slot jt: lane r < 32 codes slot jt + r (-1: no row); the
+    // tile's 32-bit validity mask comes from a ballot.
+    auto tile_rows = [&](int64_t jt, int32_t &code) __attribute__((always_inline)) -> uint32_t {
+        const int64_t j = jt + (lane & 31);
+        int32_t cd = -1;
+        if (j < j1) {
+            if (j < c.nmain) {
+                const int64_t id = (ratio > 0) ? j : (j - j0 < kIdxCache ? (int64_t)sidx[j - j0] : (int64_t)idx_t[j]);
+                if (id >= 0 && id < N) cd = (int32_t)id;
+            } else {
+                const int64_t r = c.lo + (j - c.nmain) - c.swa0;
+                if (r >= 0 && r < swa_rows) cd = kSwaBit | (int32_t)r;
+            }
+        }
+        code = cd;
+        return (uint32_t)(__ballot(cd >= 0) & 0xffffffffull);
     };
     // Wavefront w loads rows RPW*w .. RPW*w + RPW-1 of a tile, one 1 KiB row per
-    // buffer-load instruction (16 bytes per lane, LDS destination); the row's address is
-    // read out of the resolving lane into scalar registers and wrapped in a buffer resource.
-    const int wu = __builtin_amdgcn_readfirstlane(w);
-    auto dma_row = [&](bf16_t *buf, int i, uint64_t addr) __attribute__((always_inline)) {
+    // buffer-load instruction (16 bytes per lane, LDS destination).
+    auto dma_row = [&](bf16_t *buf, int i, int32_t cd) __attribute__((always_inline)) {
         const int row = RPW * wu + i;
-        const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)addr, row);
-        const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(addr >> 32), row);
-        const __amdgpu_buffer_rsrc_t rs =
-            __builtin_amdgcn_make_buffer_rsrc((void *)(((uint64_t)hi << 32) | lo), 0, WD * 2, kBufDword3);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(buf + row * WP), 16,
-                                                 lane * 16, 0, 0, 0);
+        const uint32_t off = cd < 0 ? 0u : (uint32_t)(cd & (kSwaBit - 1)) * (WD * 2);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds((cd >= 0 && (cd & kSwaBit)) ? swa_rs : kv_rs,
+                                                 (__attribute__((address_space(3))) void *)(buf + row * WP), 16,
+                                                 lane * 16, off, 0, 0);
     };
     // Dense attention walks the summaries in order, so a tile whose 32 slots are all
     // summaries is 32 consecutive rows: one buffer resource covers it and no address leaves
@@ -340,7 +355,7 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
     };
 
     uint32_t valid = 0u, valid_next = 0u;
-    uint64_t ra;  // row addresses of the next tile, resolved one tile ahead
+    int32_t ra;  // row codes of the next tile, resolved one tile ahead
 
     // One 32-row tile: compute from `tile`, load the next tile's rows into `nxt`. Past the
     // last tile every slot of the next tile resolves to the stand-in, so the loads need no
@@ -348,8 +363,9 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
     // never rescaled (so it is only ever touched by the products into it); a later tile
     // whose maximum exceeds the reference by more than 2^kHeadroom raises `redo`.
     auto tile_step = [&](const bf16_t *tile, bf16_t *nxt, int64_t jt, bool first) __attribute__((always_inline)) {
-        uint64_t ra2 = 0;
+        int32_t ra2 = -1;
         uint32_t valid_next2;
+        int32_t dma_rows_code[RPW];
         const bool cn = contig(jt + WR);  // the tile loaded during this one
         const __amdgpu_buffer_rsrc_t crs = contig_rsrc(cn ? jt + WR : j0);
         if (cn) {
@@ -357,7 +373,11 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
             for (int i = 0; i < RPW; ++i) dma_row_contig(nxt, i, crs);
         } else {
 #pragma unroll
-            for (int i = 0; i < RPW; ++i) dma_row(nxt, i, ra);
+            for (int i = 0; i < RPW; ++i) dma_rows_code[i] = __builtin_amdgcn_readlane(ra, RPW * wu + i);
+            // all codes are in scalar registers before the first load goes out
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < RPW; ++i) dma_row(nxt, i, dma_rows_code[i]);
         }
 
         // ---- S^T = K Q^T: each K fragment feeds both head blocks
@@ -496,7 +516,7 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
         } else {
             valid = tile_rows(j0, ra);
 #pragma unroll
-            for (int i = 0; i < RPW; ++i) dma_row(KV0, i, ra);
+            for (int i = 0; i < RPW; ++i) dma_row(KV0, i, __builtin_amdgcn_readlane(ra, RPW * wu + i));
         }
     }
     valid_next = contig(j0 + WR) ? 0xffffffffu : tile_rows(j0 + WR, ra);
@@ -621,7 +641,11 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
 
 }  // namespace
 
-bool w32_attn_ok(csa_dtype dt, int H, int D) { return dt == CSA_BF16 && D == WD && H % WH == 0; }
+// bf16, D = 512, whole 128-head groups, and rows addressable by a 32-bit byte offset within
+// a sequence's region (2^21 rows of 1 KiB)
+bool w32_attn_ok(csa_dtype dt, int H, int D, int64_t N, int swa_rows) {
+    return dt == CSA_BF16 && D == WD && H % WH == 0 && N <= (int64_t{1} << 21) && swa_rows <= (1 << 21);
+}
 
 int launch_attn_w32(const AttnArgs &a, float sl2, int nsplit, int64_t split_slots, hipStream_t st) {
     const int64_t U = (int64_t)a.T * nsplit * (a.H / WH);

@@ -339,7 +339,7 @@ int launch_attn_wide(const AttnArgs &a, float sl2, int nsplit, int64_t split_slo
     // many queries, one split each: 32 heads per wavefront, so every LDS fragment read
     // feeds two matrix ops (measured 16 % faster at the 4,096-query HCA prefill chunk and
     // 7 % at the 8,192-query sparse prefill chunk)
-    if (w32_attn_ok(a.dt, a.H, a.D) && nsplit == 1 && (int64_t)a.T * (a.H / 128) >= 256)
+    if (w32_attn_ok(a.dt, a.H, a.D, a.N, a.swa_rows) && nsplit == 1 && (int64_t)a.T * (a.H / 128) >= 256)
         return launch_attn_w32(a, sl2, nsplit, split_slots, st);
     // many queries with gathered rows (sparse, 128-head multiples, no row split): one 8-wave
     // workgroup per 128 heads, so a row is fetched once per query (measured 5 % faster at
