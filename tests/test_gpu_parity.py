@@ -153,7 +153,9 @@ def test_index_mxfp4(csa, orc, T, N, B, p_lo, p_hi):
 # ------------------------------------------------------------------------------------
 
 @pytest.mark.parametrize("T,N,k", [(7, 256, 64), (5, 5000, 512), (3, 40000, 1024), (4, 262144, 1024),
-                                   (6, 18432, 1024), (2, 100, 1024)])
+                                   (6, 18432, 1024), (2, 100, 1024),
+                                   # grids of >= 4 workgroups per compute unit (the 256-lane kernel)
+                                   (1100, 5000, 512), (1030, 40000, 1024)])
 def test_topk(csa, orc, T, N, k):
     say("topk", T, N, k)
     s = 31 + N
