@@ -27,6 +27,7 @@ namespace csa {
 namespace {
 
 constexpr int kCap = 32768;  // longest chunk: 128 key registers per lane at 256 lanes
+constexpr int kList = 4096;  // LDS list of the keys that share the k-th key's leading digit
 
 __device__ __forceinline__ uint32_t order_key(float s) {
     if (!(s > -INFINITY)) return 0u;
@@ -46,13 +47,16 @@ __device__ __forceinline__ T fresh(T v) {
     return v;
 }
 
+// inclusive scan over the 64 lanes of a wavefront with DPP moves: shifts of 1, 2, 4 and 8
+// within each row of 16 lanes (a lane whose source falls outside the row adds 0), then
+// lane 15 of rows 0 and 2 into rows 1 and 3, then lane 31 into rows 2 and 3
 __device__ __forceinline__ int wave_incl_scan(int x) {
-    const int lane = fresh((int)(threadIdx.x & 63));
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
     return x;
 }
 
@@ -76,33 +80,38 @@ __device__ __forceinline__ int block_excl_scan(int v, int *ws, int &total) {
     return before + x - v;
 }
 
-// One radix pass: histogram of digit (key >> shift) & dmask over the active keys (bits
-// above the digit equal to prefix under pmask), then the digit holding the kr-th largest
-// active key; returns it and sets kr to how many keys of that digit are still to be kept.
-// hist is zero on entry and is zero again on return. Zero keys (not selectable) are not
-// filtered out: every selectable key is at least order_key(-FLT_MAX) = 0x00800000, so in
-// the first pass they only fill bin 0, which is never picked (kr <= #selectable), and the
-// later passes' prefixes exclude them.
-template <int RT, int J>
-__device__ __forceinline__ uint32_t radix_pass(const uint32_t (&key)[J], uint32_t prefix, uint32_t pmask, int shift,
-                                               int nbins, int &kr, int *hist, int *ws, int *sel) {
-    const int tid = threadIdx.x, lane = tid & 63;
-    const uint32_t dmask = (uint32_t)nbins - 1u;
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-        const uint32_t kk = key[j];
-        const bool act = (kk & pmask) == prefix;
-        const int d = (int)((kk >> shift) & dmask);
-        const uint64_t am = __ballot(act);
-        if (am) {
-            const int lead = __ffsll((unsigned long long)am) - 1;
-            const int dl = __builtin_amdgcn_readlane(d, lead);
-            const uint64_t same = __ballot(act && d == dl);
-            if (lane == lead) atomicAdd(&hist[dl], (int)__popcll(same));
-            if (act && d != dl) atomicAdd(&hist[d], 1);
-        }
+// Buffer resource over n 4-byte elements at p (a read at byte offset >= 4n returns 0;
+// the bounds check covers the per-lane offset operand only, so callers pass the whole
+// offset there).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const void *p, int n) {
+    const uint64_t a = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    return __builtin_amdgcn_make_buffer_rsrc((void *)(((uint64_t)hi << 32) | lo), 0, 4 * n, 0x00020000);
+}
+
+// Histogram increment of one key per lane (act: the key takes part, d: its digit).
+// Increments of the lanes of a wavefront that share the first active lane's digit are
+// merged into one LDS atomic (scores concentrate in a few leading-digit bins).
+__device__ __forceinline__ void hist_add(bool act, int d, int *hist) {
+    const int lane = threadIdx.x & 63;
+    const uint64_t am = __ballot(act);
+    if (am) {
+        const int lead = __ffsll((unsigned long long)am) - 1;
+        const int dl = __builtin_amdgcn_readlane(d, lead);
+        const uint64_t same = __ballot(act && d == dl);
+        if (lane == lead) atomicAdd(&hist[dl], (int)__popcll(same));
+        if (act && d != dl) atomicAdd(&hist[d], 1);
     }
-    __syncthreads();
+}
+
+// Given the histogram of nbins digits (complete: the caller has synchronized) and kr (how
+// many of the counted keys to keep, from the top), returns the digit holding the kr-th
+// largest, sets kr to how many keys of that digit are still to be kept and bin to that
+// digit's count. hist is zero again on return.
+template <int RT>
+__device__ __forceinline__ uint32_t pick_digit(int nbins, int &kr, int &bin, int *hist, int *ws, int *sel) {
+    const int tid = threadIdx.x;
     // bins per lane, top first: lane tid owns [nbins - bpt * (tid + 1), nbins - bpt * tid)
     const int bpt = nbins / RT;
     const int lo = nbins - bpt * (tid + 1);
@@ -125,13 +134,30 @@ __device__ __forceinline__ uint32_t radix_pass(const uint32_t (&key)[J], uint32_
             if (above < kr && above + h[i] >= kr) {
                 sel[0] = lo + i;
                 sel[1] = kr - above;
+                sel[2] = h[i];
             }
             above += h[i];
         }
     }
     __syncthreads();
     kr = sel[1];
+    bin = sel[2];
     return (uint32_t)sel[0];
+}
+
+// v[l] = x for one lane l (x and l wavefront-uniform)
+__device__ __forceinline__ void lane_put(int &v, int x, int l) {
+    asm("v_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(x), "i"(l));
+}
+
+template <bool B>
+struct BoolTag {
+    static constexpr bool value = B;
+};
+
+// wavefront-exclusive count of the set bits of m below this lane
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
 // vals_in/idx_in: rows of length L (row stride L); idx_in == nullptr means the index of
@@ -147,8 +173,9 @@ topk_select_kernel(const float *__restrict__ vals_in, const int32_t *__restrict_
 {
     constexpr int RW = RT / 64;
     __shared__ __attribute__((aligned(16))) int hist[2048];
-    __shared__ int ws[6][RW];
-    __shared__ int sel[2];
+    __shared__ int ws[7][RW];
+    __shared__ int sel[3];
+    __shared__ uint32_t list[kList];  // keys of the leading bin
     __shared__ int cgt[J * RW], ceq[J * RW];  // per (slot, wavefront), in position order
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -163,21 +190,18 @@ topk_select_kernel(const float *__restrict__ vals_in, const int32_t *__restrict_
     for (int i = tid; i < 2048; i += RT) hist[i] = 0;
 
     // 1. keys into registers: buffer reads bounded to the chunk (a read past it returns 0,
-    //    and its key is set to 0; the whole offset is in the per-lane operand, which is the
-    //    part the bounds check covers)
+    //    and its key is set to 0; the whole offset goes in the per-lane operand, which the
+    //    bounds check covers), all issued before the first is converted
     uint32_t key[J];
     int nvalid = 0;
     {
-        const uint64_t a = (uint64_t)(uintptr_t)vrow;
-        const uint32_t alo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-        const uint32_t ahi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(((uint64_t)ahi << 32) | alo), 0, 4 * n, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rs = chunk_rsrc(vrow, n);
+#pragma unroll
+        for (int j = 0; j < J; ++j) key[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, fresh(4 * (j * RT + tid)), 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < J; ++j) {
-            const int p = j * RT + tid;
-            const float x = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, 4 * p, 0, 0));
-            key[j] = order_key(x) & (0u - (uint32_t)(p < n));
+            key[j] = order_key(__uint_as_float(key[j])) & (0u - (uint32_t)(j * RT + tid < n));
             nvalid += key[j] != 0u;
         }
     }
@@ -187,75 +211,180 @@ topk_select_kernel(const float *__restrict__ vals_in, const int32_t *__restrict_
 
     if (keff > 0) {
         // 2. radix select: tau = key of the keff-th largest, need_eq = how many keys equal
-        //    to tau are kept (the lowest positions)
-        int kr = keff;
-        uint32_t prefix = radix_pass<RT, J>(key, 0u, 0u, 21, 2048, kr, hist, ws[1], sel) << 21;
-        prefix |= radix_pass<RT, J>(key, prefix, 0xffe00000u, 10, 2048, kr, hist, ws[2], sel) << 10;
-        prefix |= radix_pass<RT, J>(key, prefix, 0xfffffc00u, 0, 1024, kr, hist, ws[3], sel);
+        //    to tau are kept (the lowest positions). Zero keys (not selectable) are not
+        //    filtered out: every selectable key is at least order_key(-FLT_MAX) =
+        //    0x00800000, so in the first pass they only fill bin 0, which is never picked
+        //    (kr <= #selectable), and the later prefixes exclude them.
+        int kr = keff, bin;
+#pragma unroll
+        for (int j = 0; j < J; ++j) hist_add(true, (int)(key[j] >> 21), hist);
+        __syncthreads();
+        const uint32_t d0 = pick_digit<RT>(2048, kr, bin, hist, ws[1], sel);
+        uint32_t prefix = d0 << 21;
+        if (bin <= kList) {
+            // the leading bin's keys fit the LDS list: the later passes read only those.
+            // Each lane counts its keys of the bin; a scan of the counts gives every lane
+            // its own range of the list (no atomics). The two sweeps compare with opaque
+            // copies of the prefix, so the compiler keeps no per-key result between them.
+            const uint32_t pa = fresh(prefix), pb = fresh(prefix);
+            int mine = 0;
+#pragma unroll
+            for (int j = 0; j < J; ++j) mine += (key[j] ^ pa) < 0x00200000u;
+            int off = wave_incl_scan(mine);
+            if (lane == 63) ws[6][wv] = off;
+            off -= mine;
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < RW; ++i) off += (i < wv) ? ws[6][i] : 0;
+#pragma unroll
+            for (int j = 0; j < J; ++j)
+                if ((key[j] ^ pb) < 0x00200000u) list[off++] = key[j];
+            __syncthreads();
+            const int nl = bin;  // list length
+            for (int i = tid; i < nl; i += RT) hist_add(true, (int)((list[i] >> 10) & 2047u), hist);
+            __syncthreads();
+            prefix |= pick_digit<RT>(2048, kr, bin, hist, ws[2], sel) << 10;
+            for (int i = tid; i < nl; i += RT) {
+                const uint32_t kk = list[i];
+                hist_add((kk & 0xfffffc00u) == prefix, (int)(kk & 1023u), hist);
+            }
+            __syncthreads();
+            prefix |= pick_digit<RT>(1024, kr, bin, hist, ws[3], sel);
+        } else {
+            const uint32_t p1 = fresh(prefix);  // (keeps the compares of the two branches apart)
+#pragma unroll
+            for (int j = 0; j < J; ++j) hist_add((key[j] & 0xffe00000u) == p1, (int)((key[j] >> 10) & 2047u), hist);
+            __syncthreads();
+            prefix |= pick_digit<RT>(2048, kr, bin, hist, ws[2], sel) << 10;
+#pragma unroll
+            for (int j = 0; j < J; ++j) hist_add((key[j] & 0xfffffc00u) == prefix, (int)(key[j] & 1023u), hist);
+            __syncthreads();
+            prefix |= pick_digit<RT>(1024, kr, bin, hist, ws[3], sel);
+        }
         const uint32_t tau = prefix;
-        const int need_eq = kr;
+        const int need_eq = kr;  // of the `bin` keys equal to tau
 
-        // 3. counts of keys above / equal to tau per (slot, wavefront), then their
-        //    exclusive scan in position order (slot-major, then wavefront)
-        const uint32_t tau3 = fresh(tau);
+        // 3-4. Output. When every key equal to tau is taken (the usual case) the selected
+        //    keys are those >= tau; otherwise keys above tau and the first need_eq keys
+        //    equal to it, counted separately.
+        auto emit = [&](auto split_tag) __attribute__((always_inline)) {
+            constexpr bool kSplit = decltype(split_tag)::value;
+            // 3. counts per (slot, wavefront), gathered into lane j % 64 of (g|e)(A|B),
+            //    then scanned in position order (slot-major, then wavefront)
+            const uint32_t tau3 = fresh(tau);
+            int gA = 0, gB = 0, eA = 0, eB = 0;
 #pragma unroll
-        for (int j = 0; j < J; ++j) {
-            const int a = (int)__popcll(__ballot(key[j] > tau3));
-            const int e = (int)__popcll(__ballot(key[j] == tau3));
-            if (lane == 0) {
-                cgt[j * RW + wv] = a;
-                ceq[j * RW + wv] = e;
-            }
-        }
-        __syncthreads();
-        {
-            constexpr int EPT = (J * RW + RT - 1) / RT;  // entries per lane
-            int a[EPT], e[EPT], sa = 0, se = 0;
-#pragma unroll
-            for (int i = 0; i < EPT; ++i) {
-                const int x = EPT * tid + i;
-                a[i] = x < J * RW ? cgt[x] : 0;
-                e[i] = x < J * RW ? ceq[x] : 0;
-                sa += a[i];
-                se += e[i];
-            }
-            int ta, te;
-            int pa = block_excl_scan<RT>(sa, ws[4], ta);
-            int pe = block_excl_scan<RT>(se, ws[5], te);
-#pragma unroll
-            for (int i = 0; i < EPT; ++i) {
-                const int x = EPT * tid + i;
-                if (x < J * RW) {
-                    cgt[x] = pa;
-                    ceq[x] = pe;
+            for (int j = 0; j < J; ++j) {
+                const int a = (int)__popcll(__ballot(kSplit ? key[j] > tau3 : key[j] >= tau3));
+                if (j < 64) lane_put(gA, a, j);
+                else lane_put(gB, a, j - 64);
+                if (kSplit) {
+                    const int e = (int)__popcll(__ballot(key[j] == tau3));
+                    if (j < 64) lane_put(eA, e, j);
+                    else lane_put(eB, e, j - 64);
                 }
-                pa += a[i];
-                pe += e[i];
             }
-        }
-        __syncthreads();
-        // the wavefront's scanned counts of slot j sit in lane j % 64 of (g|e)(j < 64 ? A : B)
-        const int gA = lane < J ? cgt[lane * RW + wv] : 0, eA = lane < J ? ceq[lane * RW + wv] : 0;
-        const int gB = lane + 64 < J ? cgt[(lane + 64) * RW + wv] : 0;
-        const int eB = lane + 64 < J ? ceq[(lane + 64) * RW + wv] : 0;
-        // 4. ordered output: the taken keys of a slot are consecutive output slots
-        const uint64_t lt = (1ull << lane) - 1ull;
-        const uint32_t tau4 = fresh(tau);
-        const int tid4 = fresh(tid);  // positions recomputed here, not kept live from step 1
+            if (lane < J) {
+                cgt[lane * RW + wv] = gA;
+                if (kSplit) ceq[lane * RW + wv] = eA;
+            }
+            if (lane + 64 < J) {
+                cgt[(lane + 64) * RW + wv] = gB;
+                if (kSplit) ceq[(lane + 64) * RW + wv] = eB;
+            }
+            __syncthreads();
+            {
+                constexpr int EPT = (J * RW + RT - 1) / RT;  // entries per lane
+                int ca[EPT], ce[EPT], sa = 0, se = 0;
 #pragma unroll
-        for (int j = 0; j < J; ++j) {
-            const bool gt = key[j] > tau4, eq = key[j] == tau4;
-            const uint64_t bg = __ballot(gt), be = __ballot(eq);
-            if ((bg | be) == 0ull) continue;
-            const int gtb = __builtin_amdgcn_readlane(j < 64 ? gA : gB, j & 63) + (int)__popcll(bg & lt);
-            const int eqb = __builtin_amdgcn_readlane(j < 64 ? eA : eB, j & 63) + (int)__popcll(be & lt);
-            if (gt || (eq && eqb < need_eq)) {
-                const int pos = gtb + (eqb < need_eq ? eqb : need_eq);
-                const int p = j * RT + tid4;
-                io[pos] = irow ? irow[p] : (int32_t)(c0 + p);
-                if (vo) vo[pos] = key_value(key[j]);
+                for (int i = 0; i < EPT; ++i) {
+                    const int x = EPT * tid + i;
+                    ca[i] = x < J * RW ? cgt[x] : 0;
+                    ce[i] = (kSplit && x < J * RW) ? ceq[x] : 0;
+                    sa += ca[i];
+                    se += ce[i];
+                }
+                int ta, te;
+                int pa = block_excl_scan<RT>(sa, ws[4], ta);
+                int pe = kSplit ? block_excl_scan<RT>(se, ws[5], te) : 0;
+#pragma unroll
+                for (int i = 0; i < EPT; ++i) {
+                    const int x = EPT * tid + i;
+                    if (x < J * RW) {
+                        cgt[x] = pa;
+                        if (kSplit) ceq[x] = pe;
+                    }
+                    pa += ca[i];
+                    pe += ce[i];
+                }
             }
-        }
+            __syncthreads();
+            gA = lane < J ? cgt[lane * RW + wv] : 0;
+            gB = lane + 64 < J ? cgt[(lane + 64) * RW + wv] : 0;
+            if (kSplit) {
+                eA = lane < J ? ceq[lane * RW + wv] : 0;
+                eB = lane + 64 < J ? ceq[(lane + 64) * RW + wv] : 0;
+            }
+            // 4. ordered output: the taken keys of a slot are consecutive output slots,
+            //    written with bounded buffer stores (a missing value output is a
+            //    zero-length resource, whose stores are dropped). With input indices, the
+            //    index reads of 8 slots are issued before their stores (a store waits for
+            //    every older read and store of the wavefront).
+            const __amdgpu_buffer_rsrc_t rso = chunk_rsrc(io, out_slots);
+            const __amdgpu_buffer_rsrc_t rsv = chunk_rsrc(vo, vo ? out_slots : 0);
+            const uint32_t tau4 = fresh(tau);
+            const int tid4 = fresh(tid);  // positions recomputed here, not kept live from step 1
+            auto slot = [&](int j, int &pos) __attribute__((always_inline)) -> bool {
+                if (!kSplit) {
+                    const bool ge = key[j] >= tau4;
+                    const uint64_t bg = __ballot(ge);
+                    if (bg == 0ull) return false;
+                    pos = __builtin_amdgcn_readlane(j < 64 ? gA : gB, j & 63) + lanes_below(bg);
+                    return ge;
+                }
+                const bool gt = key[j] > tau4, eq = key[j] == tau4;
+                const uint64_t bg = __ballot(gt), be = __ballot(eq);
+                if ((bg | be) == 0ull) return false;
+                const int gtb = __builtin_amdgcn_readlane(j < 64 ? gA : gB, j & 63) + lanes_below(bg);
+                const int eqb = __builtin_amdgcn_readlane(j < 64 ? eA : eB, j & 63) + lanes_below(be);
+                pos = gtb + (eqb < need_eq ? eqb : need_eq);
+                return gt || (eq && eqb < need_eq);
+            };
+            auto put = [&](int pos, uint32_t ix, uint32_t kk) __attribute__((always_inline)) {
+                __builtin_amdgcn_raw_buffer_store_b32(ix, rso, 4 * pos, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(key_value(kk)), rsv, 4 * pos, 0, 0);
+            };
+            if (irow == nullptr) {
+#pragma unroll
+                for (int j = 0; j < J; ++j) {
+                    int pos;
+                    if (slot(j, pos)) put(pos, (uint32_t)(c0 + j * RT + tid4), key[j]);
+                }
+            } else {
+                const __amdgpu_buffer_rsrc_t rsi = chunk_rsrc(irow, n);
+#pragma unroll
+                for (int j0 = 0; j0 < J; j0 += 8) {
+                    int pos[8];
+                    uint32_t ix[8];
+                    bool take[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        // unconditional (bounded) reads, so their waits stay exact
+                        ix[u] = j0 + u < J
+                                    ? __builtin_amdgcn_raw_buffer_load_b32(rsi, fresh(4 * ((j0 + u) * RT + tid4)), 0, 0)
+                                    : 0u;
+                        take[u] = j0 + u < J && slot(j0 + u, pos[u]);
+                    }
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        if (take[u]) put(pos[u], ix[u], key[j0 + u]);
+                }
+            }
+        };
+        if (need_eq == bin)
+            emit(BoolTag<false>{});
+        else
+            emit(BoolTag<true>{});
     }
     for (int i = keff + tid; i < out_slots; i += RT) {
         io[i] = -1;
