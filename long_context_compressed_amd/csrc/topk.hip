@@ -27,7 +27,8 @@ namespace csa {
 namespace {
 
 constexpr int kCap = 32768;  // longest chunk: 128 key registers per lane at 256 lanes
-constexpr int kList = 4096;  // LDS list of the keys that share the k-th key's leading digit
+constexpr int kList = 4096;      // LDS list of the keys that share the k-th key's leading digit
+constexpr int kHistBins = 2048;  // bins of the widest digit; 64 words past them absorb idle adds
 
 __device__ __forceinline__ uint32_t order_key(float s) {
     if (!(s > -INFINITY)) return 0u;
@@ -92,17 +93,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const void *p, int 
 
 // Histogram increment of one key per lane (act: the key takes part, d: its digit).
 // Increments of the lanes of a wavefront that share the first active lane's digit are
-// merged into one LDS atomic (scores concentrate in a few leading-digit bins).
+// merged into one (scores concentrate in a few leading-digit bins). Branch-free, so the
+// compiler can interleave the keys of a lane: every lane issues one LDS add, and lanes
+// with nothing to add (inactive, or merged into the leading lane's add) target a private
+// word past the bins.
 __device__ __forceinline__ void hist_add(bool act, int d, int *hist) {
     const int lane = threadIdx.x & 63;
     const uint64_t am = __ballot(act);
-    if (am) {
-        const int lead = __ffsll((unsigned long long)am) - 1;
-        const int dl = __builtin_amdgcn_readlane(d, lead);
-        const uint64_t same = __ballot(act && d == dl);
-        if (lane == lead) atomicAdd(&hist[dl], (int)__popcll(same));
-        if (act && d != dl) atomicAdd(&hist[d], 1);
-    }
+    const int lead = am ? __ffsll((unsigned long long)am) - 1 : 0;
+    const int dl = __builtin_amdgcn_readlane(d, lead);
+    const bool merged = act && d == dl;
+    const uint64_t same = __ballot(merged);
+    const bool own = act && !merged;
+    const bool head = merged && lane == lead;
+    const int addr = (own || head) ? (head ? dl : d) : kHistBins + lane;
+    atomicAdd(&hist[addr], head ? (int)__popcll(same) : 1);
 }
 
 // Given the histogram of nbins digits (complete: the caller has synchronized) and kr (how
@@ -172,7 +177,7 @@ topk_select_kernel(const float *__restrict__ vals_in, const int32_t *__restrict_
                    int64_t out_ld, int out_slots)
 {
     constexpr int RW = RT / 64;
-    __shared__ __attribute__((aligned(16))) int hist[2048];
+    __shared__ __attribute__((aligned(16))) int hist[kHistBins + 64];
     __shared__ int ws[7][RW];
     __shared__ int sel[3];
     __shared__ uint32_t list[kList];  // keys of the leading bin
@@ -325,11 +330,12 @@ topk_select_kernel(const float *__restrict__ vals_in, const int32_t *__restrict_
                 eA = lane < J ? ceq[lane * RW + wv] : 0;
                 eB = lane + 64 < J ? ceq[(lane + 64) * RW + wv] : 0;
             }
-            // 4. ordered output: the taken keys of a slot are consecutive output slots,
-            //    written with bounded buffer stores (a missing value output is a
-            //    zero-length resource, whose stores are dropped). With input indices, the
-            //    index reads of 8 slots are issued before their stores (a store waits for
-            //    every older read and store of the wavefront).
+            // 4. ordered output: the taken keys of a slot are consecutive output slots.
+            //    Unstaged (k > 2,048), they are written with bounded buffer stores (a
+            //    missing value output is a zero-length resource, whose stores are
+            //    dropped); with input indices, the index reads of 8 slots are issued before
+            //    their stores (a store waits for every older read and store of the
+            //    wavefront).
             const __amdgpu_buffer_rsrc_t rso = chunk_rsrc(io, out_slots);
             const __amdgpu_buffer_rsrc_t rsv = chunk_rsrc(vo, vo ? out_slots : 0);
             const uint32_t tau4 = fresh(tau);
@@ -354,7 +360,37 @@ topk_select_kernel(const float *__restrict__ vals_in, const int32_t *__restrict_
                 __builtin_amdgcn_raw_buffer_store_b32(ix, rso, 4 * pos, 0, 0);
                 __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(key_value(kk)), rsv, 4 * pos, 0, 0);
             };
-            if (irow == nullptr) {
+            if (keff <= kList / 2) {
+                // staged: (position, key) of every taken key into the LDS list (idle since
+                // the last radix pass), then written out in order with coalesced stores
+                uint32_t *sp = list, *sk = list + kList / 2;
+#pragma unroll
+                for (int j = 0; j < J; ++j) {
+                    int pos;
+                    if (slot(j, pos)) {
+                        sp[pos] = (uint32_t)(j * RT + tid4);
+                        sk[pos] = key[j];
+                    }
+                }
+                __syncthreads();
+                for (int i0 = 0; i0 < keff; i0 += 4 * RT) {
+                    int ix[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int i = i0 + u * RT + tid;
+                        const int p = i < keff ? (int)sp[i] : 0;
+                        ix[u] = irow ? irow[p] : (int)(c0 + p);
+                    }
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int i = i0 + u * RT + tid;
+                        if (i < keff) {
+                            io[i] = ix[u];
+                            if (vo) vo[i] = key_value(sk[i]);
+                        }
+                    }
+                }
+            } else if (irow == nullptr) {
 #pragma unroll
                 for (int j = 0; j < J; ++j) {
                     int pos;
