@@ -42,12 +42,15 @@ def lib():
         L.oracle_compress.argtypes = [P, P, P, P, P, P, P, i32, i64, i32, i32, i32, P]
         L.oracle_index_scores.argtypes = [P, P, P, P, P, P, i32, i32, i64, i32, i32, i32, i32, P]
         L.oracle_mxfp4_decode.argtypes = [P, P, i64, P]
+        L.oracle_mxfp4_encode.argtypes = [P, i64, i32, i32, P, P]
+        L.oracle_hadamard.argtypes = [P, i64, i32, P]
         L.oracle_topk.argtypes = [P, i32, i64, i32, P, P]
         L.oracle_sparse_attn.argtypes = [P, P, P, P, i32, f64, P, P, i32, i32, P, P, P, i32,
                                          i32, i32, i64, i32, i32, P, P]
         L.oracle_hca_attn.argtypes = [P, P, P, i32, f64, P, P, i32, i32, P, P, P, i32,
                                       i32, i32, i64, i32, i32, P, P]
-        for f in ("oracle_compress", "oracle_index_scores", "oracle_mxfp4_decode", "oracle_topk",
+        for f in ("oracle_compress", "oracle_index_scores", "oracle_mxfp4_decode", "oracle_mxfp4_encode",
+                  "oracle_hadamard", "oracle_topk",
                   "oracle_sparse_attn", "oracle_hca_attn"):
             getattr(L, f).restype = C.c_int
         _lib = L
@@ -113,6 +116,34 @@ def mxfp4_decode(codes, scales):
     D = cd.shape[-1] * 2
     out = np.empty(cd.shape[:-1] + (D,), dtype=np.float64)
     _check(lib().oracle_mxfp4_decode(_p(cd), _p(sc), out.size, _p(out)), "mxfp4_decode")
+    return out
+
+
+def mxfp4_encode(x, hadamard=False):
+    """MXFP4 codes [..., D/2] and E8M0 scales [..., D/32] (uint8) of x [..., D] taken as
+    float32 (bf16 and fp32 inputs widen exactly), after the single-precision Hadamard
+    rotation when `hadamard`."""
+    if hasattr(x, "detach"):  # torch tensor: widen on the host (exact for bf16)
+        import torch
+        x = x.detach().to("cpu", torch.float32).numpy()
+    xf = np.ascontiguousarray(x, dtype=np.float32)
+    D = xf.shape[-1]
+    rows = xf.size // D
+    codes = np.empty(xf.shape[:-1] + (D // 2,), dtype=np.uint8)
+    scales = np.empty(xf.shape[:-1] + (D // 32,), dtype=np.uint8)
+    _check(lib().oracle_mxfp4_encode(_p(xf), rows, D, int(bool(hadamard)), _p(codes), _p(scales)), "mxfp4_encode")
+    return codes, scales
+
+
+def hadamard(x):
+    """The single-precision Hadamard rotation of the rows of x [..., D] (float32 out)."""
+    if hasattr(x, "detach"):
+        import torch
+        x = x.detach().to("cpu", torch.float32).numpy()
+    xf = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty_like(xf)
+    D = xf.shape[-1]
+    _check(lib().oracle_hadamard(_p(xf), xf.size // D, D, _p(out)), "hadamard")
     return out
 
 

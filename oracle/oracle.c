@@ -15,6 +15,7 @@
  *   shared-KV MQA         §4.2 (one compressed vector is both K and V), §7 call chain
  *   SWA, partial RoPE     §6 (window 128, RoPE on the last 64 dims, inverse RoPE on o)
  *   MXFP4 operands        the MXFP4 model-card page (one E8M0 scale per 32 E2M1 values)
+ *   Hadamard rotation     the same page's Indexer section (q rotated before FP4 scoring)
  *
  * Every sum, dot product and softmax is accumulated in double precision and each
  * logit vector is materialised before it is normalised.
@@ -162,6 +163,83 @@ int oracle_mxfp4_decode(const uint8_t *codes, const uint8_t *scales, int64_t nel
         if (nib & 8) v = -v;
         out[e] = (sc == 255) ? NAN : v;
     }
+    return OR_OK;
+}
+
+/* ---------------------------------------------------------------------------------
+ * MXFP4 encode, with the optional Hadamard rotation in front (the DeepSeek-V4-Pro-MXFP4
+ * page, Indexer: the query goes through RoPE and a Hadamard rotation before it is scored
+ * in FP4).
+ *
+ * Rotation: y = H x with H = the Sylvester-ordered D x D Walsh-Hadamard matrix over
+ * sqrt(D), taken as the textbook fast transform in single precision: stages h = 1, 2,
+ * .., D/2 replace each pair (i, i + h) with bit h of i clear by (a + b, a - b); then
+ * every element is multiplied by (float)(1/sqrt(D)). Which FP4 code a value gets
+ * depends on its float rounding, so this side rounds at exactly these steps.
+ *
+ * Encoding (OCP Microscaling v1.0, E2M1 elements, one E8M0 scale per 32): block
+ * exponent e = floor(log2(amax)) - 2 (2 = the largest E2M1 exponent), clamped to
+ * [-127, 127], -127 for an all-zero block; each element becomes the E2M1 value nearest
+ * to |y| / 2^e (ties to the even code; everything above 6 becomes 6) with the sign of
+ * y unless the code is 0. Codes pack two per byte, element 2m in the low nibble.
+ * ------------------------------------------------------------------------------- */
+static void or_hadamard_row(float *y, int D)
+{
+    const float norm = (float)(1.0 / sqrt((double)D));
+    for (int h = 1; h < D; h *= 2)
+        for (int i = 0; i < D; ++i)
+            if (!(i & h)) {
+                const float a = y[i], b = y[i + h];
+                y[i] = a + b;
+                y[i + h] = a - b;
+            }
+    for (int i = 0; i < D; ++i) y[i] = y[i] * norm;
+}
+
+/* the rotation alone, row by row (D a power of two) */
+int oracle_hadamard(const float *x, int64_t rows, int D, float *out)
+{
+    if (D <= 0 || (D & (D - 1))) return OR_EINVAL;
+    for (int64_t r = 0; r < rows; ++r) {
+        memcpy(out + r * D, x + r * D, (size_t)D * sizeof(float));
+        or_hadamard_row(out + r * D, D);
+    }
+    return OR_OK;
+}
+
+int oracle_mxfp4_encode(const float *x, int64_t rows, int D, int hadamard, uint8_t *codes, uint8_t *scales)
+{
+    static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    if (D <= 0 || D % 32) return OR_EINVAL;
+    if (hadamard && (D & (D - 1))) return OR_EINVAL;
+    float *y = (float *)malloc((size_t)D * sizeof(float));
+    if (!y) return OR_EINVAL;
+    for (int64_t r = 0; r < rows; ++r) {
+        memcpy(y, x + r * D, (size_t)D * sizeof(float));
+        if (hadamard) or_hadamard_row(y, D);
+        memset(codes + r * (D / 2), 0, (size_t)(D / 2));
+        for (int b = 0; b < D / 32; ++b) {
+            double amax = 0.0;
+            for (int i = 32 * b; i < 32 * b + 32; ++i)
+                if (fabs((double)y[i]) > amax) amax = fabs((double)y[i]);
+            int e = (amax > 0.0) ? (int)floor(log2(amax)) - 2 : -127;
+            if (e < -127) e = -127;
+            if (e > 127) e = 127;
+            scales[r * (D / 32) + b] = (uint8_t)(e + 127);
+            for (int i = 32 * b; i < 32 * b + 32; ++i) {
+                const double m = fabs((double)y[i]) / ldexp(1.0, e);
+                int best = 0;
+                for (int c = 1; c < 8; ++c) {
+                    const double dc = fabs(m - mag[c]), db = fabs(m - mag[best]);
+                    if (dc < db || (dc == db && (c % 2 == 0) && (best % 2 != 0))) best = c;
+                }
+                int nib = best;
+                if (y[i] < 0.0f && best != 0) nib |= 8;
+                codes[r * (D / 2) + i / 2] |= (uint8_t)((i & 1) ? (nib << 4) : nib);
+            }
+        }
+    }
+    free(y);
     return OR_OK;
 }
 

@@ -267,6 +267,86 @@ def test_mxfp4_quantiser_roundtrip(orc):
 
 
 # ------------------------------------------------------------------------------------
+# Hadamard rotation and MXFP4 encoding (the DeepSeek-V4-Pro-MXFP4 page, Indexer: the
+# query is rotated by a Hadamard transform before the FP4 dot products; OCP MX v1.0)
+# ------------------------------------------------------------------------------------
+
+def _popcount(v):
+    return bin(int(v)).count("1")
+
+
+@pytest.mark.parametrize("D", [32, 128, 512])
+def test_hadamard_closed_form(orc, D):
+    """The rotation of unit vector e_i is column i of the Sylvester matrix over sqrt(D):
+    H[j][i] = (-1)^popcount(i & j) / sqrt(D), exactly (one nonzero term per output)."""
+    out = orc.hadamard(np.eye(D, dtype=np.float32))  # row i = H e_i
+    norm = np.float32(1.0 / np.sqrt(D))
+    ref = np.array([[(-1.0) ** _popcount(i & j) for j in range(D)] for i in range(D)], dtype=np.float32) * norm
+    np.testing.assert_array_equal(out, ref)
+
+
+def test_hadamard_orthonormal(orc):
+    """H H^T = I, H (H x) = x, and dot products survive the rotation (fp32 rounding)."""
+    D = 128
+    Hm = orc.hadamard(np.eye(D, dtype=np.float32)).astype(np.float64)
+    np.testing.assert_allclose(Hm @ Hm.T, np.eye(D), atol=1e-6)
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((16, D)).astype(np.float32)
+    y = rng.standard_normal((16, D)).astype(np.float32)
+    np.testing.assert_allclose(orc.hadamard(orc.hadamard(x)), x, atol=2e-6)
+    hx, hy = orc.hadamard(x).astype(np.float64), orc.hadamard(y).astype(np.float64)
+    np.testing.assert_allclose((hx * hy).sum(-1), (x.astype(np.float64) * y).sum(-1), rtol=1e-5, atol=1e-4)
+
+
+def test_mxfp4_encode_worked_block(orc):
+    """A hand-encoded block (tests/golden/mxfp4_encode_block.json): every midpoint of the
+    E2M1 grid (ties to the even code), saturation above 6, -0 and small negatives, and
+    the block exponent floor(log2(amax)) - 2."""
+    g = json.load(open(os.path.join(GOLD, "mxfp4_encode_block.json")))
+    x = np.array(g["x"], dtype=np.float32).reshape(1, 32)
+    codes, scales = orc.mxfp4_encode(x)
+    nib = np.stack([codes[0] & 15, codes[0] >> 4], axis=-1).reshape(-1)
+    assert scales[0].tolist() == [g["scale"]]
+    assert nib.tolist() == g["nibbles"]
+
+
+def test_mxfp4_encode_exact_and_zero(orc):
+    """Blocks of grid values whose largest code is 6 or 7 encode exactly (decode gives them
+    back); an all-zero block gets scale 2^-127 and zero codes."""
+    grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    rng = np.random.default_rng(5)
+    rows = []
+    for e in (-3, 0, 5):
+        v = rng.choice(grid, size=32) * rng.choice([-1.0, 1.0], size=32)
+        v[rng.integers(32)] = rng.choice([4.0, 6.0])
+        rows.append(v * 2.0 ** e)
+    x = np.array(rows, dtype=np.float32)
+    codes, scales = orc.mxfp4_encode(x)
+    np.testing.assert_array_equal(orc.mxfp4_decode(codes, scales), x.astype(np.float64))
+    c0, s0 = orc.mxfp4_encode(np.zeros((1, 64), dtype=np.float32))
+    assert s0.tolist() == [[0, 0]] and not c0.any()
+
+
+def test_mxfp4_encode_matches_generator(orc):
+    """The oracle's encoder and the input generator's (written separately, in torch)
+    agree code for code on random blocks."""
+    y = torch.randn(200, 128, generator=torch.Generator().manual_seed(3)) * 3.0
+    c1, s1 = orc.mxfp4_encode(y)
+    c2, s2 = workloads.quantize_mxfp4(y)
+    np.testing.assert_array_equal(c1, c2.numpy())
+    np.testing.assert_array_equal(s1, s2.numpy())
+
+
+def test_mxfp4_encode_hadamard_composes(orc):
+    """Encoding with the rotation is encoding of the rotated rows."""
+    x = np.random.default_rng(9).standard_normal((8, 256)).astype(np.float32)
+    a = orc.mxfp4_encode(x, hadamard=True)
+    b = orc.mxfp4_encode(orc.hadamard(x))
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+# ------------------------------------------------------------------------------------
 # Top-k
 # ------------------------------------------------------------------------------------
 
