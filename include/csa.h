@@ -104,6 +104,30 @@ int csa_index_scores(const void *q_I, const uint8_t *q_I_scale, const float *w,
                      csa_dtype dt, float *scores, void *stream);
 
 /*
+ * csa_quantize_mxfp4 - MXFP4 encoding of indexer operands, with the optional Hadamard
+ * rotation that the DeepSeek-V4-Pro-MXFP4 page puts in front of the FP4 index dot
+ * products (its Indexer section: the query goes through RoPE and a Hadamard rotation
+ * before it is scored against the compressed keys). The rotation is orthonormal, so
+ * rotating both q_I and k_I leaves every exact dot product unchanged; it spreads outlying
+ * channels before the coarse FP4 grid sees them.
+ *
+ * x:      [rows][D] in dt (CSA_F32 or CSA_BF16).
+ * hadamard != 0: y = H x with H the Sylvester-ordered Walsh-Hadamard matrix scaled by
+ *         1/sqrt(D) (H[i][j] = (-1)^popcount(i & j) / sqrt(D)), computed in fp32 as
+ *         log2(D) butterfly stages (a + b, a - b) on pairs (i, i + h), h = 1, 2, ..,
+ *         D/2, then one multiply by the fp32 value of 1/sqrt(D). hadamard == 0: y = x.
+ * codes:  [rows][D/2] out, E2M1 nibbles, even element in the low nibble.
+ * scales: [rows][D/32] out, E8M0 (value = code * 2^(scale - 127)).
+ * Encoding (OCP Microscaling v1.0): per block of 32, scale exponent
+ *   E = floor(log2(max |y|)) - 2 clamped to [-127, 127] (-127 for an all-zero block);
+ *   each y / 2^E rounds to the nearest of {0, .5, 1, 1.5, 2, 3, 4, 6} (ties to the even
+ *   code), saturating at 6, with the sign bit set for negative nonzero codes.
+ * Supported: D in {128, 256, 512}. rows may be 0 (nothing is launched).
+ */
+int csa_quantize_mxfp4(const void *x, int64_t rows, int D, csa_dtype dt, int hadamard,
+                       uint8_t *codes, uint8_t *scales, void *stream);
+
+/*
  * csa_topk - per-query top-k selection over index scores (§4.2).
  *
  * scores: [T][N] fp32; -INFINITY (and NaN) entries are never selected.

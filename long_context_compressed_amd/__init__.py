@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libcsa.so")
 
 F32, BF16, MXFP4 = 0, 1, 2
 STATUS = {0: "CSA_OK", 1: "CSA_EINVAL", 2: "CSA_EUNSUPPORTED", 3: "CSA_EWORKSPACE", 4: "CSA_EHIP"}
-EXPORTS = ("csa_compress", "csa_index_scores", "csa_topk_workspace_bytes", "csa_topk",
+EXPORTS = ("csa_compress", "csa_index_scores", "csa_quantize_mxfp4", "csa_topk_workspace_bytes", "csa_topk",
            "csa_attn_workspace_bytes", "csa_sparse_attn", "hca_attn", "csa_status_str",
            "csa_last_error")
 
@@ -42,6 +42,7 @@ def lib() -> C.CDLL:
         P, i32, i64, f32, sz = C.c_void_p, C.c_int, C.c_int64, C.c_float, C.c_size_t
         L.csa_compress.argtypes = [P, P, P, P, P, P, P, i32, i64, i32, i32, i32, i32, P, i64, P]
         L.csa_index_scores.argtypes = [P, P, P, P, P, P, P, i32, i32, i64, i32, i32, i32, i32, i32, P, P]
+        L.csa_quantize_mxfp4.argtypes = [P, i64, i32, i32, i32, P, P, P]
         L.csa_topk_workspace_bytes.argtypes = [i32, i64, i32]
         L.csa_topk_workspace_bytes.restype = sz
         L.csa_topk.argtypes = [P, i32, i64, i32, P, P, P, sz, P]
@@ -51,7 +52,8 @@ def lib() -> C.CDLL:
                                       i32, i32, i64, i32, i32, i32, P, P, P, sz, P]
         L.hca_attn.argtypes = [P, P, P, i32, f32, P, P, i32, i32, P, P, P, i32,
                                i32, i32, i64, i32, i32, i32, P, P, P, sz, P]
-        for f in ("csa_compress", "csa_index_scores", "csa_topk", "csa_sparse_attn", "hca_attn"):
+        for f in ("csa_compress", "csa_index_scores", "csa_quantize_mxfp4", "csa_topk", "csa_sparse_attn",
+                  "hca_attn"):
             getattr(L, f).restype = C.c_int
         L.csa_status_str.argtypes = [C.c_int]
         L.csa_status_str.restype = C.c_char_p
@@ -122,6 +124,21 @@ def index_scores(q_I, w, k_I, q_seq, q_pos, ratio=4, q_I_scale=None, k_I_scale=N
                                 _ptr(scores), _stream(stream))
     _check("csa_index_scores", rc)
     return scores
+
+
+def quantize_mxfp4(x, hadamard=False, codes=None, scales=None, stream=None):
+    """csa_quantize_mxfp4 -> (codes [..., D/2] uint8, scales [..., D/32] uint8) of x [..., D]
+    (fp32 or bf16), after the Hadamard rotation when `hadamard`."""
+    D = x.shape[-1]
+    rows = x.numel() // D if D else 0
+    if codes is None:
+        codes = torch.empty(x.shape[:-1] + (D // 2,), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(x.shape[:-1] + (D // 32,), dtype=torch.uint8, device=x.device)
+    rc = lib().csa_quantize_mxfp4(_ptr(x), rows, D, _dt(x), int(bool(hadamard)), _ptr(codes), _ptr(scales),
+                                  _stream(stream))
+    _check("csa_quantize_mxfp4", rc)
+    return codes, scales
 
 
 def topk_workspace_bytes(T, N, k) -> int:

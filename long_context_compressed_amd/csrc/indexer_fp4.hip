@@ -233,68 +233,112 @@ index_mxfp4_mfma_kernel(const uint8_t *__restrict__ qI, const uint8_t *__restric
         }
 }
 
-// ---- general case (several key stores): one wavefront per (query, entry) -------------
-// value = code * 2^(scale - 127)
-// Magnitudes x2 of the E2M1 codes 0..7 ({0, .5, 1, 1.5, 2, 3, 4, 6} * 2), one nibble each.
-__device__ __forceinline__ float e2m1_x2(uint32_t nib) {
-    const float m = (float)((0xC8643210u >> (4 * (nib & 7u))) & 15u);
-    return (nib & 8u) ? -m : m;
+// ---- few queries per key store (decode): an HBM stream of each query's keys --------
+// One wavefront per run of SE entries of one query. Per entry, the 64 heads' codes
+// (4 KiB) arrive as four coalesced 1 KiB loads already in the A-operand layout of the FP4
+// matrix op (row = head 16hb + l16, 16-byte k-chunk g4 of its 64 bytes); the query's codes
+// for the same 16 heads are the B operand (column = head). The product's diagonal
+// C[h][h] is then the 16 heads' dot products (exact E2M1 products, E8M0 block scales
+// applied inside the instruction); lane (l16, g4) holds C[4g4 + r][l16], so the diagonal
+// sits in the lanes with l16 / 4 == g4, component l16 % 4. The entry's 256 bytes of key
+// scales come in as one 4-byte load per lane (head `lane`'s four blocks) and reach the
+// lanes that need them by a permute. SP entries are in flight per wavefront.
+constexpr int SE = 64;  // entries per wavefront
+constexpr int SP = 4;   // entries loaded ahead
+
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xF, 0xF, false)); // row_ror:4
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false)); // row_ror:8
+    // every lane now holds its row's sum; the four row sums come out of lanes 0, 16, 32, 48
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)) +
+           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16)) +
+           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)) +
+           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
 }
 
-// One wave per entry; lane h owns head h. Block dots of 32 E2M1 products are exact in
-// fp32; each is scaled by 2^(sq + sk - 254) and the four blocks are summed in fp32.
 __global__ void __launch_bounds__(256)
-index_mxfp4_valu_kernel(const uint8_t *__restrict__ qI, const uint8_t *__restrict__ qS,
+index_mxfp4_scan_kernel(const uint8_t *__restrict__ qI, const uint8_t *__restrict__ qS,
                         const float *__restrict__ w, const uint8_t *__restrict__ kI,
                         const uint8_t *__restrict__ kS, const int32_t *__restrict__ q_seq,
-                        const int64_t *__restrict__ q_pos, int B, int64_t N, int ratio,
+                        const int64_t *__restrict__ q_pos, int T, int B, int64_t N, int ratio,
                         float *__restrict__ scores)
 {
-    const int lane = threadIdx.x & 63;
-    const int t = blockIdx.y;
-    const int64_t e = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (e >= N) return;
-    const int s = q_seq[t];
-    int64_t nvis = q_pos[t] / ratio;
-    if (nvis > N) nvis = N;
-    if (nvis < 0 || s < 0 || s >= B) nvis = 0;
-    float sc = -INFINITY;
-    if (e < nvis) {
-        const uint4 *qp = reinterpret_cast<const uint4 *>(qI + ((int64_t)t * 64 + lane) * 64);
-        const uint4 *kp = reinterpret_cast<const uint4 *>(kI + (((int64_t)s * N + e) * 64 + lane) * 64);
-        const uint32_t qsc = *reinterpret_cast<const uint32_t *>(qS + ((int64_t)t * 64 + lane) * 4);
-        const uint32_t ksc = *reinterpret_cast<const uint32_t *>(kS + (((int64_t)s * N + e) * 64 + lane) * 4);
-        float dot = 0.f;
+    const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
+    const int64_t e0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * SE;
+    if (e0 >= N) return;
+    const int64_t e1 = e0 + SE < N ? e0 + SE : N;
+    const bool diag = (l16 >> 2) == g4;
+    const int r = lane & 3;
+    for (int t = blockIdx.y; t < T; t += gridDim.y) {
+        const int s = q_seq[t];
+        int64_t nv = (s >= 0 && s < B) ? q_pos[t] / ratio : 0;
+        nv = nv < 0 ? 0 : (nv > N ? N : nv);
+        const int64_t ev = e1 < nv ? e1 : nv;  // visible entries of the run: [e0, ev)
+        float out = -INFINITY;                 // lane j: the score of entry e0 + j
+        if (ev > e0) {
+            i32x8 qb[4];
+            int sb[4];
+            float wd[4];
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-            const uint4 qa = qp[blk], ka = kp[blk];
-            const uint32_t qw[4] = {qa.x, qa.y, qa.z, qa.w}, kw[4] = {ka.x, ka.y, ka.z, ka.w};
-            float part = 0.f;
+            for (int hb = 0; hb < 4; ++hb) {
+                const int64_t qh = (int64_t)t * 64 + 16 * hb + l16;
+                const uint4 v = *reinterpret_cast<const uint4 *>(qI + qh * 64 + 16 * g4);
+                qb[hb] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+                sb[hb] = (int)qS[qh * 4 + g4];
+                wd[hb] = w[qh];
+            }
+            const uint8_t *kb = kI + (int64_t)s * N * 4096 + l16 * 64 + 16 * g4;
+            const uint32_t *ksb = reinterpret_cast<const uint32_t *>(kS + (int64_t)s * N * 256) + lane;
+            uint4 kc[SP][4];
+            uint32_t kw[SP];
+            // entries past the run re-read its last visible entry (cache hits), so every load
+            // is unconditional and the waits stay exact
+            auto load = [&](int u, int64_t e) __attribute__((always_inline)) {
+                e = e < ev ? e : ev - 1;
 #pragma unroll
-            for (int x = 0; x < 4; ++x)
+                for (int hb = 0; hb < 4; ++hb) kc[u][hb] = *reinterpret_cast<const uint4 *>(kb + e * 4096 + hb * 1024);
+                kw[u] = ksb[e * 64];
+            };
 #pragma unroll
-                for (int nb = 0; nb < 8; ++nb)
-                    part = fmaf(e2m1_x2((qw[x] >> (4 * nb)) & 15u), e2m1_x2((kw[x] >> (4 * nb)) & 15u), part);
-            const int ex = (int)((qsc >> (8 * blk)) & 255u) + (int)((ksc >> (8 * blk)) & 255u) - 254 - 2;
-            dot += ldexpf(part, ex);  // the -2 undoes the two x2 magnitudes
+            for (int u = 0; u < SP; ++u) load(u, e0 + u);
+            for (int64_t eb = e0; eb < ev; eb += SP) {
+#pragma unroll
+                for (int u = 0; u < SP; ++u) {
+                    const int64_t e = eb + u;
+                    if (e < ev) {
+                        float acc = 0.f;
+#pragma unroll
+                        for (int hb = 0; hb < 4; ++hb) {
+                            const int sa = (__builtin_amdgcn_ds_bpermute(4 * (16 * hb + l16), (int)kw[u]) >> (8 * g4)) & 0xFF;
+                            const i32x8 A = i32x8{(int)kc[u][hb].x, (int)kc[u][hb].y, (int)kc[u][hb].z,
+                                                  (int)kc[u][hb].w, 0, 0, 0, 0};
+                            const f32x4 c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                A, qb[hb], f32x4{0.f, 0.f, 0.f, 0.f}, 4, 4, 0, sa, 0, sb[hb]);
+                            const float x = r == 0 ? c[0] : (r == 1 ? c[1] : (r == 2 ? c[2] : c[3]));
+                            acc = fmaf(wd[hb], __int_as_float(max(__float_as_int(x), 0)), acc);
+                        }
+                        const float tot = wave_sum_dpp(diag ? acc : 0.f);
+                        out = (lane == (int)(e - e0)) ? tot : out;
+                    }
+                    load(u, eb + SP + u);
+                }
+            }
         }
-        float r = fmaxf(dot, 0.f) * w[(int64_t)t * 64 + lane];
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) r += __shfl_xor(r, m);
-        sc = r;
+        if (e0 + lane < e1) scores[(int64_t)t * N + e0 + lane] = out;
     }
-    if (lane == 0) scores[(int64_t)t * N + e] = sc;
 }
 
 }  // namespace
 
-// MXFP4 scores: the matrix-core tile kernel when every query reads the one key store
-// (B == 1); otherwise one wavefront per (query, entry).
+// MXFP4 scores: the matrix-core tile kernel when many queries read the one key store
+// (B == 1, prefill); otherwise (decode, several key stores) each query streams its keys.
 int launch_index_mxfp4(const uint8_t *qI, const uint8_t *qs, const float *w, const uint8_t *kI,
                        const uint8_t *ks, const int32_t *q_seq, const int64_t *q_pos, int T, int B, int64_t N,
                        int ratio, float *scores, hipStream_t st)
 {
-    if (B == 1) {
+    if (B == 1 && T > 16) {
         const int nqb = (T + TQ - 1) / TQ;
         const int neb = (int)((N + TE - 1) / TE);
         const int64_t blocks = (int64_t)((nqb + 7) / 8) * 8 * neb;
@@ -302,10 +346,10 @@ int launch_index_mxfp4(const uint8_t *qI, const uint8_t *qs, const float *w, con
                            q_seq, q_pos, T, N, ratio, nqb, neb, scores);
         return check_launch("index_mxfp4_mfma_kernel");
     }
-    dim3 grid((unsigned)((N + 3) / 4), (unsigned)T);
-    hipLaunchKernelGGL(index_mxfp4_valu_kernel, grid, dim3(256), 0, st, qI, qs, w, kI, ks, q_seq, q_pos, B, N,
+    const dim3 grid((unsigned)((N + 4 * SE - 1) / (4 * SE)), (unsigned)(T < 65535 ? T : 65535));
+    hipLaunchKernelGGL(index_mxfp4_scan_kernel, grid, dim3(256), 0, st, qI, qs, w, kI, ks, q_seq, q_pos, T, B, N,
                        ratio, scores);
-    return check_launch("index_mxfp4_valu_kernel");
+    return check_launch("index_mxfp4_scan_kernel");
 }
 
 }  // namespace csa

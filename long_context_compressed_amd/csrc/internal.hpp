@@ -19,6 +19,9 @@ int launch_index_mxfp4(const uint8_t *qI, const uint8_t *qs, const float *w, con
                        const uint8_t *ks, const int32_t *q_seq, const int64_t *q_pos, int T, int B, int64_t N,
                        int ratio, float *scores, hipStream_t st);
 
+int launch_quantize_mxfp4(const void *x, int64_t rows, int D, csa_dtype dt, bool hadamard, uint8_t *codes,
+                          uint8_t *scales, hipStream_t st);
+
 size_t topk_workspace_bytes(int T, int64_t N, int k);
 int launch_topk(const float *scores, int T, int64_t N, int k, int32_t *idx, float *vals,
                 void *ws, size_t ws_bytes, hipStream_t st);

@@ -127,7 +127,9 @@ def test_index_bf16_shared_keys(csa, orc, T, B, N):
 @pytest.mark.parametrize("T,N,B,p_lo,p_hi", [
     (70, 300, 1, 600, 669),      # one workgroup tile, ragged in both directions (matrix cores)
     (520, 650, 1, 1000, 3000),   # 3 x 6 tiles, causal: partly and fully masked tiles
-    (10, 90, 2, 100, 400),       # two key stores: the per-(query, entry) path
+    (10, 90, 2, 100, 400),       # two key stores: the per-query key stream
+    (4, 1000, 4, 4001, 4001),    # decode shape: one query per store, every entry visible
+    (6, 333, 1, 500, 1400),      # few queries on one store: the key stream, causal, ragged run
 ])
 def test_index_mxfp4(csa, orc, T, N, B, p_lo, p_hi):
     """MXFP4 operands (E2M1 + one E8M0 scale per 32), causal prefill positions."""
@@ -146,6 +148,30 @@ def test_index_mxfp4(csa, orc, T, N, B, p_lo, p_hi):
     kd = orc.mxfp4_decode(kc, ks)
     ref = orc.index_scores(qd, w, kd, q_seq, q_pos)
     assert_rel(sc, ref, TOL_F32, "index mxfp4")
+
+
+@pytest.mark.parametrize("D,dt,had", [(128, torch.float32, False), (128, torch.float32, True),
+                                      (128, torch.bfloat16, True), (256, torch.float32, True),
+                                      (512, torch.bfloat16, False), (512, torch.float32, True)])
+def test_quantize_mxfp4(csa, orc, D, dt, had):
+    """MXFP4 encoding with and without the Hadamard rotation: codes and scales bit-exact
+    against the oracle (1,001 rows: random rows at block exponents from -40 to 40, a zero
+    row, rows of grid midpoints, an outlier row)."""
+    say("quantize_mxfp4", D, dt, had)
+    rows = 1001
+    x = W.normal((rows, D), 777 + D, "x", device=DEV)
+    x = x * torch.pow(2.0, torch.linspace(-40, 40, rows, device=DEV)).unsqueeze(1)
+    x[0] = 0.0
+    mids = torch.tensor([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0], device=DEV)
+    x[1] = mids.repeat(D // 8) * torch.where(torch.arange(D, device=DEV) % 3 == 0, -1.0, 1.0)
+    x[2, :] = 0.01
+    x[2, 5] = 1.0e4
+    x = x.to(dt)
+    codes, scales = csa.quantize_mxfp4(x, hadamard=had)
+    torch.cuda.synchronize()
+    rc, rs = orc.mxfp4_encode(x, hadamard=had)
+    np.testing.assert_array_equal(scales.cpu().numpy(), rs)
+    np.testing.assert_array_equal(codes.cpu().numpy(), rc)
 
 
 # ------------------------------------------------------------------------------------
