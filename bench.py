@@ -41,7 +41,8 @@ def parse():
     ap.add_argument("--cpu-entries", type=int, default=16384,
                     help="index entries per query in the oracle's bounded sample")
     ap.add_argument("--workload", default="pro_decode_1m",
-                    choices=["pro_decode_1m", "flash_decode_128k", "pro_decode_1m_shared_keys", "pro_prefill_chunk",
+                    choices=["pro_decode_1m", "flash_decode_128k", "pro_decode_1m_shared_keys", "pro_decode_1m_mxfp4",
+                             "pro_prefill_chunk",
                              "hca_prefill_4k"],
                     help="pro_decode_1m is the benchmark line; the others print the same record for "
                          "the other configurations' shapes (profiling aid)")
@@ -88,11 +89,12 @@ def main():
         return prefill_main(a)
     cfg = W.FLASH if a.workload == "flash_decode_128k" else W.PRO
     shared = a.workload == "pro_decode_1m_shared_keys"
+    fp4 = a.workload == "pro_decode_1m_mxfp4"
     B, T, n, N, D, H, k = cfg.B, cfg.T, cfg.n, cfg.N, cfg.c, cfg.H, cfg.k
     NH = cfg.n // 128  # HCA summaries (8,192 at 2^20 tokens)
 
     # ---- inputs (HBM-resident) and the step's buffers -----------------------------------
-    inp = W.decode_step_inputs(cfg, dev, shared_keys=shared)
+    inp = W.decode_step_inputs(cfg, dev, shared_keys=shared, mxfp4=fp4)
     step = pipeline.DecodeStep(inp, k, cfg.window, cfg.rope_dim, cfg.scale)
     torch.cuda.synchronize()
 
@@ -132,6 +134,7 @@ def main():
 
     stages = {
         "compress_csa_kv_and_index_key": timed(step.compress),
+        **({"quantize_q_mxfp4": timed(step.index_prep)} if fp4 else {}),
         "index_scores": timed(step.index, reps=10),
         "topk": timed(step.select),
         "sparse_attn": timed(step.attend),
@@ -142,7 +145,11 @@ def main():
 
     # algorithmic bytes of one index-scan launch: every visible key block once
     # (64 x 128 bf16 = 16 KiB per entry per sequence) + q_I + w + the fp32 scores
-    alg_bytes = B * N * (1 if shared else 64) * 128 * 2 + T * 64 * 128 * 2 + T * 64 * 4 + T * N * 4
+    # (MXFP4: 64 x 64 bytes of codes + 64 x 4 E8M0 scales = 4,352 B per entry, same for q_I)
+    if fp4:
+        alg_bytes = B * N * 4352 + T * 4352 + T * 64 * 4 + T * N * 4
+    else:
+        alg_bytes = B * N * (1 if shared else 64) * 128 * 2 + T * 64 * 128 * 2 + T * 64 * 4 + T * N * 4
     achieved = alg_bytes / scan_avg_s / 1e9
     traffic = None if shared or a.workload != "pro_decode_1m" else traffic_from_profile(alg_bytes)
 
@@ -161,13 +168,15 @@ def main():
         "data": "synthetic (seeded N(0,1), bf16)",
         "config": {
             "workload": (f"{a.workload}: one CSA layer + one HCA layer decode step, B={B} sequences x 1 query at "
-                         f"t={n}; {N:,} entries x {'1 shared' if shared else '64 per-head'} x 128 bf16 index keys "
+                         f"t={n}; {N:,} entries x {'1 shared' if shared else '64 per-head'} x 128 "
+                         f"{'MXFP4 (Hadamard-rotated)' if fp4 else 'bf16'} index keys "
                          f"per sequence, top-k {k:,}, "
                          f"{H} heads x {D} shared KV, SWA {cfg.window}, {NH:,} HCA summaries"),
             "batch": B, "context": n, "index_entries": N, "topk": k, "heads": H, "head_dim": D,
         },
         "roofline": {
             "kernel": ("index_shared_kernel (csa_index_scores, bf16 keys shared by the 64 heads)" if shared
+                       else "index_mxfp4_scan_kernel (csa_index_scores, MXFP4 per-head keys)" if fp4
                        else "index_scan_kernel (csa_index_scores, bf16 per-head keys)"),
             "bound": "hbm",
             "achieved": round(achieved, 1),

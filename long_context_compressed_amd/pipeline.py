@@ -9,7 +9,7 @@ from __future__ import annotations
 
 import torch
 
-from . import (attn_workspace_bytes, compress, hca_attn, index_scores, sparse_attn, topk,
+from . import (attn_workspace_bytes, compress, hca_attn, index_scores, quantize_mxfp4, sparse_attn, topk,
                topk_workspace_bytes)
 
 
@@ -26,6 +26,9 @@ class DecodeStep:
     blk / carry (KV compressor, ratio 4), iblk / icarry (index-key compressor, ratio 4),
     hblk (HCA compressor, ratio 128). The step writes the block's new KV row, index key
     and summary into the last row of kv, k_I and summ, then scores, selects and attends.
+    With MXFP4 index keys (k_I codes [B][N][64][64] and k_I_scale [B][N][64][4] in `inp`)
+    the new index key is compressed to bf16, rotated by the Hadamard transform and encoded
+    into the last entry, and each step's q_I is rotated and encoded before the scan.
     """
 
     def __init__(self, inp: dict, k: int, window: int, rope_dim: int, scale: float):
@@ -36,7 +39,14 @@ class DecodeStep:
         NH = summ.shape[1]
         dev = q.device
         self.kv_new = kv[:, N - 1:N, :]
-        self.kI_new = k_I.view(B, N, -1)[:, N - 1:N, :]
+        self.mxfp4 = inp.get("k_I_scale") is not None
+        if self.mxfp4:
+            qI = inp["q_I"]
+            self.kI_new = torch.empty((B, 1, 64 * 128), dtype=torch.bfloat16, device=dev)
+            self.qc = torch.empty(qI.shape[:-1] + (qI.shape[-1] // 2,), dtype=torch.uint8, device=dev)
+            self.qs = torch.empty(qI.shape[:-1] + (qI.shape[-1] // 32,), dtype=torch.uint8, device=dev)
+        else:
+            self.kI_new = k_I.view(B, N, -1)[:, N - 1:N, :]
         self.summ_new = summ[:, NH - 1:NH, :]
         self.scores = torch.empty((T, N), dtype=torch.float32, device=dev)
         self.idx = torch.empty((T, k), dtype=torch.int32, device=dev)
@@ -53,10 +63,24 @@ class DecodeStep:
         b, c, ib, ic = i["blk"], i["carry"], i["iblk"], i["icarry"]
         compress(b["Ca"], b["Za"], b["Cb"], b["Zb"], c["C"], c["Z"], ratio=4, overlap=1, out=self.kv_new)
         compress(ib["Ca"], ib["Za"], ib["Cb"], ib["Zb"], ic["C"], ic["Z"], ratio=4, overlap=1, out=self.kI_new)
+        if self.mxfp4:  # rotate and encode the new key into the last entry of each sequence
+            kI, ks = i["k_I"], i["k_I_scale"]
+            N = kI.shape[1]
+            for b in range(kI.shape[0]):
+                quantize_mxfp4(self.kI_new[b].view(64, 128), hadamard=True, codes=kI[b, N - 1], scales=ks[b, N - 1])
+
+    def index_prep(self):
+        """MXFP4 keys: the query's index vectors rotated and encoded (nothing otherwise)."""
+        if self.mxfp4:
+            quantize_mxfp4(self.inp["q_I"], hadamard=True, codes=self.qc, scales=self.qs)
 
     def index(self):
         i = self.inp
-        index_scores(i["q_I"], i["w"], i["k_I"], i["q_seq"], i["q_pos"], scores=self.scores)
+        if self.mxfp4:
+            index_scores(self.qc, i["w"], i["k_I"], i["q_seq"], i["q_pos"], q_I_scale=self.qs,
+                         k_I_scale=i["k_I_scale"], mxfp4=True, scores=self.scores)
+        else:
+            index_scores(i["q_I"], i["w"], i["k_I"], i["q_seq"], i["q_pos"], scores=self.scores)
 
     def select(self):
         topk(self.scores, self.k, idx=self.idx, workspace=self.topk_ws)
@@ -80,6 +104,7 @@ class DecodeStep:
     def __call__(self, index_events=None):
         """The whole step; `index_events` = (start, end) events recorded around the scan."""
         self.compress()
+        self.index_prep()
         if index_events is not None:
             index_events[0].record()
         self.index()

@@ -76,15 +76,19 @@ def _gathered_rows(kv, seqs, idx):
     return kv_c, idx_c
 
 
-@pytest.mark.parametrize("name,shared", [("flash_decode_128k", False), ("pro_decode_1m", False),
-                                         ("pro_decode_1m", True)])
-def test_decode_step_full_size(csa, orc, name, shared):
-    """shared=True: the side line with one 128-dim index key per entry for all heads."""
+@pytest.mark.parametrize("name,keys", [("flash_decode_128k", "bf16"), ("pro_decode_1m", "bf16"),
+                                       ("pro_decode_1m", "shared"), ("pro_decode_1m", "mxfp4")])
+def test_decode_step_full_size(csa, orc, name, keys):
+    """keys="shared": the side line with one 128-dim index key per entry for all heads;
+    keys="mxfp4": MXFP4 index keys, with the step's q_I and new key Hadamard-rotated and
+    encoded on the GPU (checked bit-exact against the oracle's encoder, fed the same
+    values) and the scan checked on the decoded codes."""
     from long_context_compressed_amd import pipeline
 
     cfg = W.CONFIGS[name]
-    say("full-size decode step", name, "shared keys" if shared else "")
-    inp = W.decode_step_inputs(cfg, DEV, shared_keys=shared)
+    shared, fp4 = keys == "shared", keys == "mxfp4"
+    say("full-size decode step", name, keys)
+    inp = W.decode_step_inputs(cfg, DEV, shared_keys=shared, mxfp4=fp4)
     step = pipeline.DecodeStep(inp, cfg.k, cfg.window, cfg.rope_dim, cfg.scale)
     step()
     torch.cuda.synchronize()
@@ -100,7 +104,17 @@ def test_decode_step_full_size(csa, orc, name, shared):
 
     # index scores: 1,024 sampled entries (both ends included) of every sequence
     ids = np.unique(np.concatenate([[0, 1, N - 2, N - 1], W.distinct_sample(1020, N, cfg.seed, "fullsize_ids")]))
-    _check_index_sample(orc, step.scores, inp["q_I"], inp["w"], inp["k_I"], inp["q_seq"], inp["q_pos"], ids)
+    if fp4:
+        rc, rs = orc.mxfp4_encode(step.kI_new.view(B, 64, 128), hadamard=True)
+        np.testing.assert_array_equal(inp["k_I"][:, N - 1].cpu().numpy(), rc)
+        np.testing.assert_array_equal(inp["k_I_scale"][:, N - 1].cpu().numpy(), rs)
+        rc, rs = orc.mxfp4_encode(inp["q_I"], hadamard=True)
+        np.testing.assert_array_equal(step.qc.cpu().numpy(), rc)
+        np.testing.assert_array_equal(step.qs.cpu().numpy(), rs)
+        _check_index_sample(orc, step.scores, step.qc, inp["w"], inp["k_I"], inp["q_seq"], inp["q_pos"], ids,
+                            mxfp4_scales=(step.qs, inp["k_I_scale"]))
+    else:
+        _check_index_sample(orc, step.scores, inp["q_I"], inp["w"], inp["k_I"], inp["q_seq"], inp["q_pos"], ids)
 
     # top-k over the full 262,144 / 32,768 scores of every query
     _check_topk_fed(orc, step.scores, step.idx, cfg.k)

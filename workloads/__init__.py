@@ -115,6 +115,24 @@ def quantize_mxfp4(x: torch.Tensor):
     return codes, scales
 
 
+def normal_mxfp4(shape, cfg_seed: int, name: str, device="cpu", chunk_rows: int = 1 << 17):
+    """MXFP4 codes [..., D/2] and E8M0 scales [..., D/32] of an N(0,1) tensor of `shape`
+    [..., D], drawn and encoded (quantize_mxfp4) in chunks of rows, each chunk from its own
+    seed, so that no fp32 copy of the whole tensor is held.
+    """
+    D = shape[-1]
+    rows = int(np.prod(shape[:-1])) if len(shape) > 1 else 1
+    codes = torch.empty((rows, D // 2), dtype=torch.uint8, device=device)
+    scales = torch.empty((rows, D // 32), dtype=torch.uint8, device=device)
+    for r0 in range(0, rows, chunk_rows):
+        r1 = min(rows, r0 + chunk_rows)
+        g = _gen(derive_seed(cfg_seed, f"{name}#{r0 // chunk_rows}"), device)
+        c, sc = quantize_mxfp4(torch.randn((r1 - r0, D), generator=g, device=device, dtype=torch.float32))
+        codes[r0:r1] = c
+        scales[r0:r1] = sc
+    return codes.view(*shape[:-1], D // 2), scales.view(*shape[:-1], D // 32)
+
+
 def rope_table(positions: torch.Tensor, rope_dim: int, base: float = 10000.0) -> torch.Tensor:
     """(cos, sin) angle table [T][rope_dim/2][2] fp32 for absolute `positions` [T].
 
@@ -206,12 +224,15 @@ def tiny_inputs(device="cpu", cfg: Config = TINY) -> dict:
     return inp
 
 
-def decode_inputs(cfg: Config, device="cpu", with_index=True, shared_keys=False) -> dict:
+def decode_inputs(cfg: Config, device="cpu", with_index=True, shared_keys=False, mxfp4=False) -> dict:
     """Decode-step tensors for B independent sequences, one query each at t = n.
 
     Index keys, compressed KV, SWA rows, queries and sinks are N(0,1); the indexer
     head weights are N(0,1) for the Pro shape and 0.05 N(0,1) for the Flash shape
     (projection-derived). Tensors are bf16 except w, sink (fp32).
+    mxfp4: the stored index keys are MXFP4 (k_I codes [B][N][64][64] + k_I_scale
+    [B][N][64][4], encoded from N(0,1); a Hadamard rotation of iid N(0,1) vectors is again
+    iid N(0,1), so these stand for rotated keys); q_I stays bf16 (the step encodes it).
     """
     s, B, N, D, dt = cfg.seed, cfg.B, cfg.N, cfg.c, cfg.torch_dtype
     n = cfg.n
@@ -231,12 +252,14 @@ def decode_inputs(cfg: Config, device="cpu", with_index=True, shared_keys=False)
         inp["w"] = normal((cfg.T, cfg.H_I), s, "w", scale=wscale, device=device)
         if shared_keys:  # one 128-dim key per entry for every head
             inp["k_I"] = normal((B, N, 1, cfg.D_I), s, "k_I_shared", dtype=dt, device=device)
+        elif mxfp4:
+            inp["k_I"], inp["k_I_scale"] = normal_mxfp4((B, N, cfg.H_I, cfg.D_I), s, "k_I_fp4", device=device)
         else:
             inp["k_I"] = normal((B, N, cfg.H_I, cfg.D_I), s, "k_I", dtype=dt, device=device)
     return inp
 
 
-def decode_step_inputs(cfg: Config, device="cpu", shared_keys=False) -> dict:
+def decode_step_inputs(cfg: Config, device="cpu", shared_keys=False, mxfp4=False) -> dict:
     """Everything one decode step of a CSA layer plus an HCA layer reads, for B sequences.
 
     On top of decode_inputs: the block [n-4, n) that completes with the step (a- and
@@ -244,10 +267,11 @@ def decode_step_inputs(cfg: Config, device="cpu", shared_keys=False) -> dict:
     block [n-8, n-4)), the HCA summaries [B][n/128][D] with their own sinks, and the
     ratio-128 block that completes the last summary. All N(0,1) bf16 (sinks fp32).
     shared_keys: the index keys are one 128-dim key per entry for all heads.
+    mxfp4: the stored index keys are MXFP4 (see decode_inputs).
     """
     s, B, D, bf = cfg.seed, cfg.B, cfg.c, torch.bfloat16
     NH = cfg.n // 128
-    inp = decode_inputs(cfg, device, shared_keys=shared_keys)
+    inp = decode_inputs(cfg, device, shared_keys=shared_keys, mxfp4=mxfp4)
     inp["summ"] = normal((B, NH, D), HCA.seed, "summ", dtype=bf, device=device)
     inp["sink_h"] = normal((cfg.H,), HCA.seed, "sink", device=device)
     inp["blk"] = {nm: normal((B, 4, D), s, "new_" + nm, dtype=bf, device=device) for nm in ("Ca", "Cb", "Za", "Zb")}
