@@ -242,7 +242,8 @@ index_mxfp4_mfma_kernel(const uint8_t *__restrict__ qI, const uint8_t *__restric
 // applied inside the instruction); lane (l16, g4) holds C[4g4 + r][l16], so the diagonal
 // sits in the lanes with l16 / 4 == g4, component l16 % 4. The entry's 256 bytes of key
 // scales come in as one 4-byte load per lane (head `lane`'s four blocks) and reach the
-// lanes that need them by a permute. SP entries are in flight per wavefront.
+// lanes that need them by a permute. SP entries are in flight per wavefront; the code
+// loads are non-temporal (each byte is read once).
 constexpr int SE = 64;  // entries per wavefront
 constexpr int SP = 4;   // entries loaded ahead
 
@@ -291,14 +292,15 @@ index_mxfp4_scan_kernel(const uint8_t *__restrict__ qI, const uint8_t *__restric
             }
             const uint8_t *kb = kI + (int64_t)s * N * 4096 + l16 * 64 + 16 * g4;
             const uint32_t *ksb = reinterpret_cast<const uint32_t *>(kS + (int64_t)s * N * 256) + lane;
-            uint4 kc[SP][4];
+            i32x4v kc[SP][4];
             uint32_t kw[SP];
             // entries past the run re-read its last visible entry (cache hits), so every load
             // is unconditional and the waits stay exact
             auto load = [&](int u, int64_t e) __attribute__((always_inline)) {
                 e = e < ev ? e : ev - 1;
 #pragma unroll
-                for (int hb = 0; hb < 4; ++hb) kc[u][hb] = *reinterpret_cast<const uint4 *>(kb + e * 4096 + hb * 1024);
+                for (int hb = 0; hb < 4; ++hb)
+                    kc[u][hb] = __builtin_nontemporal_load(reinterpret_cast<const i32x4v *>(kb + e * 4096 + hb * 1024));
                 kw[u] = ksb[e * 64];
             };
 #pragma unroll
@@ -312,8 +314,7 @@ index_mxfp4_scan_kernel(const uint8_t *__restrict__ qI, const uint8_t *__restric
 #pragma unroll
                         for (int hb = 0; hb < 4; ++hb) {
                             const int sa = (__builtin_amdgcn_ds_bpermute(4 * (16 * hb + l16), (int)kw[u]) >> (8 * g4)) & 0xFF;
-                            const i32x8 A = i32x8{(int)kc[u][hb].x, (int)kc[u][hb].y, (int)kc[u][hb].z,
-                                                  (int)kc[u][hb].w, 0, 0, 0, 0};
+                            const i32x8 A = i32x8{kc[u][hb].x, kc[u][hb].y, kc[u][hb].z, kc[u][hb].w, 0, 0, 0, 0};
                             const f32x4 c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                                 A, qb[hb], f32x4{0.f, 0.f, 0.f, 0.f}, 4, 4, 0, sa, 0, sb[hb]);
                             const float x = r == 0 ? c[0] : (r == 1 ? c[1] : (r == 2 ? c[2] : c[3]));
