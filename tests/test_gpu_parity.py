@@ -249,6 +249,11 @@ def _attn_inputs(seed, T, H, D, B, N, k, swa_rows, dt, pos, with_rope=True, bad_
     dict(T=256, H=128, D=512, B=1, N=600, k=64, swa=400, dt=torch.bfloat16, pos=None),
     # 64 heads (Flash shape), split path
     dict(T=2, H=64, D=512, B=2, N=900, k=512, swa=128, dt=torch.bfloat16, pos=[131072, 131072]),
+    # SWA-only layers (k = 0, no compressed rows): Flash decode shape, a query near the start
+    dict(T=3, H=64, D=512, B=2, N=900, k=0, swa=128, dt=torch.bfloat16, pos=[131072, 131072, 50]),
+    # SWA-only, many queries (the 32-heads-per-wavefront kernel), and fp32
+    dict(T=256, H=128, D=512, B=1, N=600, k=0, swa=400, dt=torch.bfloat16, pos=None),
+    dict(T=40, H=8, D=128, B=1, N=256, k=0, swa=1024, dt=torch.float32, pos=None),
 ])
 def test_sparse_attn(csa, orc, case):
     c = dict(case)
