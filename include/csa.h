@@ -104,6 +104,20 @@ int csa_index_scores(const void *q_I, const uint8_t *q_I_scale, const float *w,
                      csa_dtype dt, float *scores, void *stream);
 
 /*
+ * csa_index_rescore - Lightning Indexer scores (the formula of csa_index_scores) of a
+ * per-query candidate list: the re-rank step after an FP4 scan has picked 2k candidates
+ * (the indexer builds its candidates at twice the top-k, "DeepSeek-V4 混合注意力" §9).
+ *
+ * cand:   [T][M] int32 entry indices; a negative, >= N or not visible entry scores -inf.
+ * q_I, w, k_I, q_seq, q_pos, ratio, dt: as csa_index_scores (per-head keys, F32 | BF16).
+ * scores: [T][M] fp32 out, slot by slot.
+ * Supported: H_I == 64, D_I == 128. T, M may be 0.
+ */
+int csa_index_rescore(const void *q_I, const float *w, const void *k_I, const int32_t *cand, int M,
+                      const int32_t *q_seq, const int64_t *q_pos, int T, int B, int64_t N,
+                      int H_I, int D_I, int ratio, csa_dtype dt, float *scores, void *stream);
+
+/*
  * csa_quantize_mxfp4 - MXFP4 encoding of indexer operands, with the optional Hadamard
  * rotation that the DeepSeek-V4-Pro-MXFP4 page puts in front of the FP4 index dot
  * products (its Indexer section: the query goes through RoPE and a Hadamard rotation
@@ -143,6 +157,19 @@ size_t csa_topk_workspace_bytes(int T, int64_t N, int k);
 int csa_topk(const float *scores, int T, int64_t N, int k,
              int32_t *topk_idxs, float *topk_vals,
              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * csa_topk_ids - csa_topk over per-query candidate lists: row t of scores [T][M] scores
+ * the entries ids [T][M]; topk_idxs [T][k] receives the entries of the k largest scores
+ * in list order (ascending entry order for ascending lists, such as csa_topk's output),
+ * ties to the earlier list position, -1 padded; topk_vals as csa_topk. An entry whose
+ * score is -INFINITY (e.g. a -1 slot after csa_index_rescore) is never taken.
+ * workspace: at least csa_topk_workspace_bytes(T, M, k) bytes. Supported: 1 <= k <= 4096.
+ */
+int csa_topk_ids(const float *scores, const int32_t *ids, int T, int64_t M, int k,
+                 int32_t *topk_idxs, float *topk_vals, void *workspace,
+                 size_t workspace_bytes, void *stream);
+
 
 /*
  * csa_sparse_attn - shared-KV multi-query attention with an attention sink

@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(_HERE, "libcsa.so")
 
 F32, BF16, MXFP4 = 0, 1, 2
 STATUS = {0: "CSA_OK", 1: "CSA_EINVAL", 2: "CSA_EUNSUPPORTED", 3: "CSA_EWORKSPACE", 4: "CSA_EHIP"}
-EXPORTS = ("csa_compress", "csa_index_scores", "csa_quantize_mxfp4", "csa_topk_workspace_bytes", "csa_topk",
+EXPORTS = ("csa_compress", "csa_index_scores", "csa_index_rescore", "csa_quantize_mxfp4", "csa_topk_workspace_bytes",
+           "csa_topk", "csa_topk_ids",
            "csa_attn_workspace_bytes", "csa_sparse_attn", "hca_attn", "csa_status_str",
            "csa_last_error")
 
@@ -43,6 +44,8 @@ def lib() -> C.CDLL:
         L.csa_compress.argtypes = [P, P, P, P, P, P, P, i32, i64, i32, i32, i32, i32, P, i64, P]
         L.csa_index_scores.argtypes = [P, P, P, P, P, P, P, i32, i32, i64, i32, i32, i32, i32, i32, P, P]
         L.csa_quantize_mxfp4.argtypes = [P, i64, i32, i32, i32, P, P, P]
+        L.csa_index_rescore.argtypes = [P, P, P, P, i32, P, P, i32, i32, i64, i32, i32, i32, i32, P, P]
+        L.csa_topk_ids.argtypes = [P, P, i32, i64, i32, P, P, P, sz, P]
         L.csa_topk_workspace_bytes.argtypes = [i32, i64, i32]
         L.csa_topk_workspace_bytes.restype = sz
         L.csa_topk.argtypes = [P, i32, i64, i32, P, P, P, sz, P]
@@ -52,8 +55,8 @@ def lib() -> C.CDLL:
                                       i32, i32, i64, i32, i32, i32, P, P, P, sz, P]
         L.hca_attn.argtypes = [P, P, P, i32, f32, P, P, i32, i32, P, P, P, i32,
                                i32, i32, i64, i32, i32, i32, P, P, P, sz, P]
-        for f in ("csa_compress", "csa_index_scores", "csa_quantize_mxfp4", "csa_topk", "csa_sparse_attn",
-                  "hca_attn"):
+        for f in ("csa_compress", "csa_index_scores", "csa_index_rescore", "csa_quantize_mxfp4", "csa_topk",
+                  "csa_topk_ids", "csa_sparse_attn", "hca_attn"):
             getattr(L, f).restype = C.c_int
         L.csa_status_str.argtypes = [C.c_int]
         L.csa_status_str.restype = C.c_char_p
@@ -126,6 +129,19 @@ def index_scores(q_I, w, k_I, q_seq, q_pos, ratio=4, q_I_scale=None, k_I_scale=N
     return scores
 
 
+def index_rescore(q_I, w, k_I, cand, q_seq, q_pos, ratio=4, scores=None, stream=None):
+    """csa_index_rescore -> scores [T][M] fp32 of the candidate entries cand [T][M] (per-head
+    keys k_I [B][N][64][128], fp32 or bf16)."""
+    T, M = cand.shape
+    B, N = k_I.shape[0], k_I.shape[1]
+    if scores is None:
+        scores = torch.empty((T, M), dtype=torch.float32, device=q_I.device)
+    rc = lib().csa_index_rescore(_ptr(q_I), _ptr(w), _ptr(k_I), _ptr(cand), M, _ptr(q_seq), _ptr(q_pos), T, B, N,
+                                 q_I.shape[1], q_I.shape[2], ratio, _dt(q_I), _ptr(scores), _stream(stream))
+    _check("csa_index_rescore", rc)
+    return scores
+
+
 def quantize_mxfp4(x, hadamard=False, codes=None, scales=None, stream=None):
     """csa_quantize_mxfp4 -> (codes [..., D/2] uint8, scales [..., D/32] uint8) of x [..., D]
     (fp32 or bf16), after the Hadamard rotation when `hadamard`."""
@@ -159,6 +175,24 @@ def topk(scores, k, idx=None, vals=None, workspace=None, with_vals=False, stream
     rc = lib().csa_topk(_ptr(scores), T, N, k, _ptr(idx), _ptr(vals), _ptr(workspace), wsb,
                         _stream(stream))
     _check("csa_topk", rc)
+    return idx, vals
+
+
+def topk_ids(scores, ids, k, idx=None, vals=None, workspace=None, with_vals=False, stream=None):
+    """csa_topk_ids -> (entry ids [T][k] int32 of the k best candidates, list order, -1 padded;
+    vals or None)."""
+    T, M = scores.shape
+    if idx is None:
+        idx = torch.empty((T, k), dtype=torch.int32, device=scores.device)
+    if vals is None and with_vals:
+        vals = torch.empty((T, k), dtype=torch.float32, device=scores.device)
+    need = topk_workspace_bytes(T, M, k)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib().csa_topk_ids(_ptr(scores), _ptr(ids), T, M, k, _ptr(idx), _ptr(vals), _ptr(workspace), wsb,
+                            _stream(stream))
+    _check("csa_topk_ids", rc)
     return idx, vals
 
 

@@ -104,6 +104,19 @@ int csa_index_scores(const void *q_I, const uint8_t *q_I_scale, const float *w, 
                                scores, (hipStream_t)stream);
 }
 
+int csa_index_rescore(const void *q_I, const float *w, const void *k_I, const int32_t *cand, int M,
+                      const int32_t *q_seq, const int64_t *q_pos, int T, int B, int64_t N, int H_I, int D_I,
+                      int ratio, csa_dtype dt, float *scores, void *stream) {
+    clear_error();
+    REQUIRE(T >= 0 && M >= 0 && B > 0 && N >= 0 && ratio > 0, CSA_EINVAL,
+            "csa_index_rescore: need T >= 0, M >= 0, B > 0, N >= 0, ratio > 0");
+    REQUIRE(dt == CSA_F32 || dt == CSA_BF16, CSA_EINVAL, "csa_index_rescore: dt must be CSA_F32 or CSA_BF16");
+    REQUIRE(H_I == 64 && D_I == 128, CSA_EUNSUPPORTED, "csa_index_rescore: only H_I = 64, D_I = 128 is built");
+    if (T == 0 || M == 0) return CSA_OK;
+    REQUIRE(q_I && w && k_I && cand && q_seq && q_pos && scores, CSA_EINVAL, "csa_index_rescore: NULL tensor");
+    return launch_index_rescore(q_I, w, k_I, cand, M, q_seq, q_pos, T, B, N, ratio, dt, scores, (hipStream_t)stream);
+}
+
 int csa_quantize_mxfp4(const void *x, int64_t rows, int D, csa_dtype dt, int hadamard, uint8_t *codes,
                        uint8_t *scales, void *stream) {
     clear_error();
@@ -130,7 +143,19 @@ int csa_topk(const float *scores, int T, int64_t N, int k, int32_t *topk_idxs, f
     REQUIRE(N < ((int64_t)1 << 31), CSA_EUNSUPPORTED, "csa_topk: N must fit int32 indices");
     if (T == 0) return CSA_OK;
     REQUIRE(topk_idxs && (scores || N == 0), CSA_EINVAL, "csa_topk: NULL tensor");
-    return launch_topk(scores, T, N, k, topk_idxs, topk_vals, workspace, workspace_bytes, (hipStream_t)stream);
+    return launch_topk(scores, nullptr, T, N, k, topk_idxs, topk_vals, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+int csa_topk_ids(const float *scores, const int32_t *ids, int T, int64_t M, int k, int32_t *topk_idxs,
+                 float *topk_vals, void *workspace, size_t workspace_bytes, void *stream) {
+    clear_error();
+    REQUIRE(T >= 0 && M >= 0, CSA_EINVAL, "csa_topk_ids: need T >= 0 and M >= 0");
+    REQUIRE(k > 0, CSA_EINVAL, "csa_topk_ids: k must be positive");
+    REQUIRE(k <= 4096, CSA_EUNSUPPORTED, "csa_topk_ids: k > 4096 is not built");
+    REQUIRE(M < ((int64_t)1 << 31), CSA_EUNSUPPORTED, "csa_topk_ids: M must fit int32 positions");
+    if (T == 0) return CSA_OK;
+    REQUIRE(topk_idxs && (M == 0 || (scores && ids)), CSA_EINVAL, "csa_topk_ids: NULL tensor");
+    return launch_topk(scores, ids, T, M, k, topk_idxs, topk_vals, workspace, workspace_bytes, (hipStream_t)stream);
 }
 
 size_t csa_attn_workspace_bytes(int T, int H, int D, int64_t max_rows) {

@@ -118,11 +118,15 @@ __device__ __forceinline__ float entry_score(const u32x4 (&buf)[ScanTraits<KT>::
     return wave_sum(fmaxf(v[0], 0.f) * wl);
 }
 
-template <typename KT, int EPW>
+// kCand: the wave's slots are positions of a per-query candidate list (cand [T][L], entry
+// index or -1) instead of consecutive entries, and scores are written per slot
+// ([T][L]); a slot whose entry is negative, past N or not visible scores -inf (its loads
+// read entry 0, so every load stays unconditional).
+template <typename KT, int EPW, bool kCand>
 __global__ void __launch_bounds__(256)
 index_scan_kernel(const KT *__restrict__ qI, const float *__restrict__ w, const KT *__restrict__ kI,
                   const int32_t *__restrict__ q_seq, const int64_t *__restrict__ q_pos, int B,
-                  int64_t N, int ratio, float *__restrict__ scores)
+                  int64_t N, int ratio, const int32_t *__restrict__ cand, int64_t L, float *__restrict__ scores)
 {
     using TR = ScanTraits<KT>;
     constexpr int EU = 8192 / TR::VEC;  // 16-byte units per entry
@@ -130,14 +134,18 @@ index_scan_kernel(const KT *__restrict__ qI, const float *__restrict__ w, const 
     const int wv = threadIdx.x >> 6;
     const int t = blockIdx.y;
     const int64_t e0 = ((int64_t)blockIdx.x * 4 + wv) * EPW;
-    if (e0 >= N) return;
-    const int64_t e1 = (e0 + EPW < N) ? e0 + EPW : N;
+    if (e0 >= L) return;
+    const int64_t e1 = (e0 + EPW < L) ? e0 + EPW : L;
 
     const int s = q_seq[t];
     int64_t nvis = q_pos[t] / ratio;
     if (nvis > N) nvis = N;
     if (nvis < 0 || s < 0 || s >= B) nvis = 0;
-    const int64_t ev = (e1 < nvis) ? e1 : nvis;  // [e0, ev) are read, [ev, e1) masked
+    // consecutive entries: [e0, ev) are read, [ev, e1) masked; candidate slots: all read
+    const int64_t ev = kCand ? (nvis > 0 ? e1 : e0) : ((e1 < nvis) ? e1 : nvis);
+    int32_t my_id = -1;  // candidate slots: lane j holds the entry of slot e0 + j
+    if (kCand && lane < (int)(e1 - e0)) my_id = cand[(int64_t)t * L + e0 + lane];
+    const bool my_ok = !kCand || (my_id >= 0 && (int64_t)my_id < nvis);
 
     float my_score = -INFINITY;
     if (e0 < ev) {
@@ -148,21 +156,27 @@ index_scan_kernel(const KT *__restrict__ qI, const float *__restrict__ w, const 
         const float wl = w[(int64_t)t * 64 + (lane % TR::G) * TR::HPL + lane / TR::G];
 
         const u32x4 *kb = reinterpret_cast<const u32x4 *>(kI + ((int64_t)s * N) * 8192);
+        // entry of slot e (wave-uniform)
+        auto ent = [&](int64_t e) __attribute__((always_inline)) -> int64_t {
+            if (!kCand) return e;
+            const int id = __builtin_amdgcn_readlane(my_ok ? my_id : 0, (int)(e - e0));
+            return (int64_t)id;
+        };
         u32x4 bufA[TR::J], bufB[TR::J];
-        load_entry<KT>(bufA, kb + e0 * EU, lane);
+        load_entry<KT>(bufA, kb + ent(e0) * EU, lane);
         int64_t e = e0;
         // steady state: both loads of an iteration are unconditional, so the wait before
         // scoring A leaves B's loads in flight
         for (; e + 2 < ev; e += 2) {
-            load_entry<KT>(bufB, kb + (e + 1) * EU, lane);
+            load_entry<KT>(bufB, kb + ent(e + 1) * EU, lane);
             float sc = entry_score<KT>(bufA, qf, wl, lane);
             if (lane == (int)(e - e0)) my_score = sc;
-            load_entry<KT>(bufA, kb + (e + 2) * EU, lane);
+            load_entry<KT>(bufA, kb + ent(e + 2) * EU, lane);
             sc = entry_score<KT>(bufB, qf, wl, lane);
             if (lane == (int)(e + 1 - e0)) my_score = sc;
         }
         if (e + 1 < ev) {
-            load_entry<KT>(bufB, kb + (e + 1) * EU, lane);
+            load_entry<KT>(bufB, kb + ent(e + 1) * EU, lane);
             float sc = entry_score<KT>(bufA, qf, wl, lane);
             if (lane == (int)(e - e0)) my_score = sc;
             sc = entry_score<KT>(bufB, qf, wl, lane);
@@ -171,8 +185,9 @@ index_scan_kernel(const KT *__restrict__ qI, const float *__restrict__ w, const 
             const float sc = entry_score<KT>(bufA, qf, wl, lane);
             if (lane == (int)(e - e0)) my_score = sc;
         }
+        if (!my_ok) my_score = -INFINITY;
     }
-    if (lane < (int)(e1 - e0)) scores[(int64_t)t * N + e0 + lane] = my_score;
+    if (lane < (int)(e1 - e0)) scores[(int64_t)t * L + e0 + lane] = my_score;
 }
 
 // ---- shared keys: one 128-dim key per entry for all 64 heads ----------------------------
@@ -280,11 +295,28 @@ int launch_index_scores(const void *qI, const uint8_t *qs, const float *w, const
     constexpr int EPW = 64;
     dim3 grid((unsigned)((N + 4 * EPW - 1) / (4 * EPW)), (unsigned)T);
     if (dt == CSA_BF16) {
-        hipLaunchKernelGGL((index_scan_kernel<bf16_t, EPW>), grid, dim3(256), 0, st,
-                           (const bf16_t *)qI, w, (const bf16_t *)kI, q_seq, q_pos, B, N, ratio, scores);
+        hipLaunchKernelGGL((index_scan_kernel<bf16_t, EPW, false>), grid, dim3(256), 0, st, (const bf16_t *)qI, w,
+                           (const bf16_t *)kI, q_seq, q_pos, B, N, ratio, nullptr, N, scores);
     } else {
-        hipLaunchKernelGGL((index_scan_kernel<float, EPW>), grid, dim3(256), 0, st,
-                           (const float *)qI, w, (const float *)kI, q_seq, q_pos, B, N, ratio, scores);
+        hipLaunchKernelGGL((index_scan_kernel<float, EPW, false>), grid, dim3(256), 0, st, (const float *)qI, w,
+                           (const float *)kI, q_seq, q_pos, B, N, ratio, nullptr, N, scores);
+    }
+    return check_launch("index_scan_kernel");
+}
+
+int launch_index_rescore(const void *qI, const float *w, const void *kI, const int32_t *cand, int M,
+                         const int32_t *q_seq, const int64_t *q_pos, int T, int B, int64_t N, int ratio,
+                         csa_dtype dt, float *scores, hipStream_t st)
+{
+    if (T == 0 || M == 0) return CSA_OK;
+    constexpr int EPW = 64;
+    dim3 grid((unsigned)((M + 4 * EPW - 1) / (4 * EPW)), (unsigned)T);
+    if (dt == CSA_BF16) {
+        hipLaunchKernelGGL((index_scan_kernel<bf16_t, EPW, true>), grid, dim3(256), 0, st, (const bf16_t *)qI, w,
+                           (const bf16_t *)kI, q_seq, q_pos, B, N, ratio, cand, (int64_t)M, scores);
+    } else {
+        hipLaunchKernelGGL((index_scan_kernel<float, EPW, true>), grid, dim3(256), 0, st, (const float *)qI, w,
+                           (const float *)kI, q_seq, q_pos, B, N, ratio, cand, (int64_t)M, scores);
     }
     return check_launch("index_scan_kernel");
 }

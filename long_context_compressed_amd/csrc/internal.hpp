@@ -23,7 +23,12 @@ int launch_quantize_mxfp4(const void *x, int64_t rows, int D, csa_dtype dt, bool
                           uint8_t *scales, hipStream_t st);
 
 size_t topk_workspace_bytes(int T, int64_t N, int k);
-int launch_topk(const float *scores, int T, int64_t N, int k, int32_t *idx, float *vals,
+int launch_index_rescore(const void *qI, const float *w, const void *kI, const int32_t *cand, int M,
+                         const int32_t *q_seq, const int64_t *q_pos, int T, int B, int64_t N, int ratio,
+                         csa_dtype dt, float *scores, hipStream_t st);
+
+// ids: NULL (position p of a row is entry p) or [T][N] entry ids of the row's positions
+int launch_topk(const float *scores, const int32_t *ids, int T, int64_t N, int k, int32_t *idx, float *vals,
                 void *ws, size_t ws_bytes, hipStream_t st);
 
 // Rows of one query: the first `k` slots come from topk_idxs (sparse mode) or from

@@ -485,8 +485,8 @@ size_t topk_workspace_bytes(int T, int64_t N, int k) {
     return (size_t)2 * (size_t)T * (size_t)(nch * slots) * 8u;
 }
 
-int launch_topk(const float *scores, int T, int64_t N, int k, int32_t *idx, float *vals, void *ws,
-                size_t ws_bytes, hipStream_t st) {
+int launch_topk(const float *scores, const int32_t *ids, int T, int64_t N, int k, int32_t *idx, float *vals,
+                void *ws, size_t ws_bytes, hipStream_t st) {
     if (T == 0) return CSA_OK;
     const int cap = topk_cap();
     const size_t need = topk_workspace_bytes(T, N, k);
@@ -494,7 +494,7 @@ int launch_topk(const float *scores, int T, int64_t N, int k, int32_t *idx, floa
         return fail(CSA_EWORKSPACE, "csa_topk: workspace smaller than csa_topk_workspace_bytes()");
     const int64_t half = (int64_t)(need / 2);
     const float *vin = scores;
-    const int32_t *iin = nullptr;
+    const int32_t *iin = ids;
     int64_t L = N;
     int flip = 0;
     bool first = true;

@@ -141,6 +141,57 @@ def test_decode_step_full_size(csa, orc, name, keys):
     _free()
 
 
+def test_pro_decode_fp4_candidates_rerank(csa, orc):
+    """Pro 1M decode shape: the bf16 index keys and queries are Hadamard-rotated and MXFP4-
+    encoded on the GPU (sampled rows bit-exact with the oracle's encoder); the FP4 scan picks
+    2k = 2,048 candidates per query, csa_index_rescore scores them exactly (bf16 keys) and
+    csa_topk_ids keeps the best k = 1,024, which must be the oracle's top-k of the candidates
+    by those scores. Prints the recall of the exact bf16 top-k by the 2k candidates (the
+    quantity the pages report as 99.7% for the trained indexer; here on N(0,1) data)."""
+    cfg = W.PRO
+    B, T, N, k = cfg.B, cfg.T, cfg.N, cfg.k
+    say("FP4 candidates + exact re-rank, Pro 1M decode")
+    inp = W.decode_inputs(cfg, DEV)
+    q_I, w, k_I, q_seq, q_pos = inp["q_I"], inp["w"], inp["k_I"], inp["q_seq"], inp["q_pos"]
+    kc, ks = csa.quantize_mxfp4(k_I, hadamard=True)
+    qc, qs = csa.quantize_mxfp4(q_I, hadamard=True)
+    torch.cuda.synchronize()
+    rows = torch.from_numpy(W.distinct_sample(256, N, cfg.seed, "fp4_rows")).to(DEV)
+    rc, rs = orc.mxfp4_encode(k_I[1].index_select(0, rows), hadamard=True)
+    np.testing.assert_array_equal(kc[1].index_select(0, rows).cpu().numpy(), rc)
+    np.testing.assert_array_equal(ks[1].index_select(0, rows).cpu().numpy(), rs)
+    rc, rs = orc.mxfp4_encode(q_I, hadamard=True)
+    np.testing.assert_array_equal(qc.cpu().numpy(), rc)
+    np.testing.assert_array_equal(qs.cpu().numpy(), rs)
+
+    s4 = csa.index_scores(qc, w, kc, q_seq, q_pos, q_I_scale=qs, k_I_scale=ks, mxfp4=True)
+    cand, _ = csa.topk(s4, 2 * k)
+    exact = csa.index_rescore(q_I, w, k_I, cand, q_seq, q_pos)
+    final, _ = csa.topk_ids(exact, cand, k)
+    full = csa.index_scores(q_I, w, k_I, q_seq, q_pos)
+    ref_top, _ = csa.topk(full, k)
+    torch.cuda.synchronize()
+    del kc, ks, s4
+    _free()
+
+    # re-rank: the kept entries are the oracle's top-k of the candidates by the exact scores
+    ex = exact.cpu().double().numpy()
+    c_np, f_np = cand.cpu().numpy(), final.cpu().numpy()
+    for t in range(T):
+        sub = orc.index_scores(q_I[t:t + 1], w[t:t + 1], k_I[int(q_seq[t])].index_select(
+            0, torch.from_numpy(c_np[t].astype(np.int64)).to(DEV))[None], np.zeros(1, dtype=np.int32),
+            q_pos[t:t + 1].cpu().numpy(), entry_ids=c_np[t].astype(np.int64))
+        assert_rel(ex[t], sub[0], TOL_F32, "exact scores of the candidates")
+        pos, _ = orc.topk(ex[t:t + 1], k)
+        assert sorted(f_np[t].tolist()) == sorted(c_np[t][pos[0]].tolist()), f"re-ranked set of query {t}"
+    recall_c = np.mean([len(set(c_np[t]) & set(ref_top[t].cpu().numpy())) / k for t in range(T)])
+    recall_f = np.mean([len(set(f_np[t]) & set(ref_top[t].cpu().numpy())) / k for t in range(T)])
+    say(f"recall of the exact top-{k} by the FP4 2k candidates: {recall_c:.4f}; after the re-rank: {recall_f:.4f}")
+    assert recall_f >= recall_c - 1e-12
+    del inp, cand, exact, final, full, ref_top
+    _free()
+
+
 def test_pro_prefill_chunk_full_size(csa, orc):
     from long_context_compressed_amd import pipeline
 

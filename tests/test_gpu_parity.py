@@ -150,6 +150,73 @@ def test_index_mxfp4(csa, orc, T, N, B, p_lo, p_hi):
     assert_rel(sc, ref, TOL_F32, "index mxfp4")
 
 
+def _oracle_rescore(orc, q_I, w, k_I, cand, q_seq, q_pos, ratio=4):
+    """Oracle scores [T][M] of per-query candidate lists (-inf for -1 / out-of-range slots)."""
+    T, M = cand.shape
+    N = k_I.shape[1]
+    c = cand.cpu().numpy()
+    out = np.full((T, M), -np.inf)
+    for t in range(T):
+        ok = (c[t] >= 0) & (c[t] < N)
+        ids = c[t][ok].astype(np.int64)
+        if len(ids) == 0:
+            continue
+        s_t = int(q_seq[t])
+        kg = k_I[s_t].index_select(0, torch.from_numpy(ids).to(k_I.device))[None]
+        ref = orc.index_scores(q_I[t:t + 1], w[t:t + 1], kg, np.zeros(1, dtype=np.int32),
+                               q_pos[t:t + 1].cpu().numpy(), ratio=ratio, entry_ids=ids)
+        out[t, ok] = ref[0]
+    return out
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_index_rescore(csa, orc, dt):
+    """Scores of per-query candidate lists: valid, -1, past-N and not-yet-visible slots;
+    a ragged list length (M = 150, three wavefronts' runs)."""
+    say("index_rescore", dt)
+    T, B, N, M = 5, 2, 3000, 150
+    s = 515
+    q = W.normal((T, 64, 128), s, "q", dtype=dt, device=DEV)
+    k = W.normal((B, N, 64, 128), s, "k", dtype=dt, device=DEV)
+    w = W.normal((T, 64), s, "w", device=DEV)
+    q_seq = (torch.arange(T, dtype=torch.int32, device=DEV) % B)
+    q_pos = torch.tensor([4 * N, 4 * N, 2000, 4 * N, 40], dtype=torch.int64, device=DEV)
+    cand = torch.stack([torch.from_numpy(np.sort(W.distinct_sample(M, N, s, f"c{t}"))) for t in range(T)])
+    cand = cand.to(torch.int32)
+    cand[0, 7] = -1
+    cand[1, 9] = N + 5
+    cand = cand.to(DEV)
+    sc = csa.index_rescore(q, w, k, cand, q_seq, q_pos)
+    torch.cuda.synchronize()
+    ref = _oracle_rescore(orc, q, w, k, cand, q_seq, q_pos)
+    gpu = sc.cpu().double().numpy()
+    fin = np.isfinite(ref)
+    assert np.array_equal(fin, np.isfinite(gpu))
+    assert np.all(gpu[~fin] == -np.inf)
+    assert_rel(gpu[fin], ref[fin], TOL_F32, "rescore")
+
+
+def test_topk_ids(csa, orc):
+    """Top-k over candidate lists: the chosen entries are the ids of the oracle's top-k
+    positions (ties to the earlier position), in list order, -1 padded."""
+    say("topk_ids")
+    T, M, k = 6, 3000, 256
+    sc = torch.round(W.normal((T, M), 61, "s", device=DEV) * 16) / 16  # ties
+    sc[2, 100:] = -float("inf")                                          # fewer than k finite
+    ids = torch.stack([torch.from_numpy(np.sort(W.distinct_sample(M, 200000, 61, f"i{t}"))) for t in range(T)])
+    ids = ids.to(torch.int32).to(DEV)
+    idx, vals = csa.topk_ids(sc, ids, k, with_vals=True)
+    torch.cuda.synchronize()
+    rpos, _ = orc.topk(sc.cpu(), k)
+    gi, ii = idx.cpu().numpy(), ids.cpu().numpy()
+    for t in range(T):
+        rp = rpos[t][rpos[t] >= 0]
+        expect = sorted(ii[t][rp].tolist())
+        got = gi[t][gi[t] >= 0]
+        assert got.tolist() == expect, f"row {t}"
+        assert np.all(gi[t, len(got):] == -1)
+
+
 @pytest.mark.parametrize("D,dt,had", [(128, torch.float32, False), (128, torch.float32, True),
                                       (128, torch.bfloat16, True), (256, torch.float32, True),
                                       (512, torch.bfloat16, False), (512, torch.float32, True)])
