@@ -110,3 +110,29 @@ def test_attn_validation(L):
     g = lambda **kw: L.hca_attn(1, 1, 1, kw.get("ratio", 128), C.c_float(0.1), 1, 1, 8, 128, 1, 1, None, 0,
                                 2, 1, 8, 8, 128, 0, 1, None, None, 0, None)
     assert g(ratio=0) == 1
+
+
+def test_quantize_mxfp4_validation(L):
+    f = lambda **kw: L.csa_quantize_mxfp4(kw.get("x", 1), kw.get("rows", 4), kw.get("D", 128), kw.get("dt", 0),
+                                          kw.get("had", 1), kw.get("codes", 1), kw.get("scales", 1), None)
+    assert f(D=100) == 1                        # not a multiple of 32
+    assert f(D=96) == 2                         # valid, not built
+    assert f(dt=2) == 1                         # MXFP4 is the output, not an input dtype
+    assert f(x=None) == 1 and f(codes=None) == 1
+    assert f(rows=-1) == 1
+    assert f(rows=0) == 0
+
+
+def test_index_rescore_and_topk_ids_validation(L):
+    r = lambda **kw: L.csa_index_rescore(*[kw.get(k, v) for k, v in (
+        ("q", 1), ("w", 1), ("k", 1), ("cand", 1), ("M", 16), ("qseq", 1), ("qpos", 1), ("T", 2), ("B", 1),
+        ("N", 8), ("H", 64), ("D", 128), ("ratio", 4), ("dt", 1), ("scores", 1), ("st", None))])
+    assert r(dt=2) == 1                         # candidate lists re-score exact (bf16 / fp32) keys
+    assert r(H=32) == 2
+    assert r(cand=None) == 1
+    assert r(M=-1) == 1
+    assert r(T=0) == 0 and r(M=0) == 0
+    assert L.csa_topk_ids(1, 1, 4, 100, 0, 1, None, None, 0, None) == 1
+    assert L.csa_topk_ids(1, 1, 4, 100, 5000, 1, None, None, 0, None) == 2
+    assert L.csa_topk_ids(1, None, 4, 100, 10, 1, None, None, 0, None) == 1
+    assert L.csa_topk_ids(1, 1, 0, 100, 10, None, None, None, 0, None) == 0
