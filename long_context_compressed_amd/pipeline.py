@@ -103,6 +103,8 @@ class DecodeStep:
 
     def __call__(self, index_events=None):
         """The whole step; `index_events` = (start, end) events recorded around the scan."""
+        if self.graphs is not None:
+            return self.replay(index_events)
         self.compress()
         self.index_prep()
         if index_events is not None:
@@ -114,6 +116,39 @@ class DecodeStep:
         self.attend()
         self.hca_compress()
         self.hca()
+
+    graphs = None
+
+    def capture(self):
+        """Record the small calls around the index scan as two HIP graphs (before it: the
+        compressors and the query encoding; after it: top-k, sparse attention, the HCA
+        compressor and attention), so a step is two graph launches and one scan launch
+        instead of a dozen library calls from the host. The scan itself is launched directly
+        between the events that time it (a graph launch adds latency a single long kernel
+        does not need). Every buffer the step touches is allocated in __init__, so the
+        graphs stay valid for the object's life; the library records no memset, only
+        kernels."""
+        parts = ((self.compress, self.index_prep), (self.select, self.attend, self.hca_compress, self.hca))
+        graphs = []
+        torch.cuda.synchronize()
+        for fns in parts:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for f in fns:
+                    f()
+            graphs.append(g)
+        torch.cuda.synchronize()
+        self.graphs = graphs
+
+    def replay(self, index_events=None):
+        pre, post = self.graphs
+        pre.replay()
+        if index_events is not None:
+            index_events[0].record()
+        self.index()
+        if index_events is not None:
+            index_events[1].record()
+        post.replay()
 
 
 class ProPrefillChunk:
