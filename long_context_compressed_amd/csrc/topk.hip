@@ -1,24 +1,28 @@
 // Per-query top-k over index scores on gfx950 ("DeepSeek-V4 混合注意力" §4.2: each
 // query keeps the k = 512 / 1,024 highest-scoring compressed entries).
 //
-// A workgroup (256 lanes, four wavefronts) owns one chunk of at most 256 * J scores of
-// one row and keeps it in registers as order-preserving 32-bit keys (-inf / NaN map to 0
-// and are never taken): lane `tid` holds the keys of positions j * 256 + tid, j < J, read
-// with coalesced 4-byte loads. The LDS footprint is small (a 2,048-bin histogram and a
-// few counters), so several workgroups share a compute unit and the barriers of one hide
-// behind the arithmetic of the others.
-//   1. three radix passes (digits of 11, 11 and 10 bits from the top) over the register
-//      keys find the exact key tau of the k-th largest element and how many elements
-//      equal to tau are to be taken (ties go to the lower index); histogram increments of
-//      the lanes of a wavefront that share the first active lane's digit are merged into
-//      one LDS atomic;
-//   2. per (slot j, wavefront) counts of keys above and equal to tau, scanned in position
-//      order, give every selected key its output slot, so the (value, index) pairs are
-//      written in ascending index order. The value is recovered from the key.
+// A workgroup (256 or 1,024 lanes) owns one chunk of at most RT * J scores of one row and
+// keeps it in registers as order-preserving 32-bit keys (-inf / NaN map to 0 and are
+// never taken): lane `tid` holds the keys of positions j * RT + tid, j < J, read with
+// coalesced buffer loads bounded to the chunk. LDS holds only a histogram, a list and a
+// few counters (about 27 KB), so 256-lane workgroups share a compute unit four at a time
+// and the barriers of one hide behind the arithmetic of the others; grids too small for
+// that use 1,024-lane workgroups (sixteen wavefronts on one chunk).
+//   1. Radix select with digits of 11, 11 and 10 bits from the top finds the exact key
+//      tau of the k-th largest element and how many elements equal to tau are taken
+//      (ties go to the lower position). The first pass histograms every register key;
+//      the keys of the chosen leading bin are then compacted into an LDS list (each lane
+//      writes its own scanned range) and the two later passes read only that list (the
+//      register keys again when the bin is larger than the list).
+//   2. Output: per (slot j, wavefront) counts of the taken keys, scanned in position
+//      order, give every taken key its output slot, so the (value, index) pairs come out
+//      in ascending position order; the value is recovered from the key. The pairs are
+//      staged in the LDS list and written with coalesced stores.
 // Rows longer than the chunk cap are cut into chunks; the exact top-k of the row is a
-// subset of the union of the chunks' top-k sets, so the chunk winners (kept in index
+// subset of the union of the chunks' top-k sets, so the chunk winners (kept in position
 // order, padded with (-inf, -1)) form a shorter row that the same kernel reduces again
-// until one chunk remains.
+// until one chunk remains. A row may come with an id per position (a candidate list):
+// the ids are what is written out.
 #include "common.hpp"
 #include "internal.hpp"
 
