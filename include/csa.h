@@ -132,6 +132,10 @@ int csa_index_rescore(const void *q_I, const float *w, const void *k_I, const in
  *         D/2, then one multiply by the fp32 value of 1/sqrt(D). hadamard == 0: y = x.
  * codes:  [rows][D/2] out, E2M1 nibbles, even element in the low nibble.
  * scales: [rows][D/32] out, E8M0 (value = code * 2^(scale - 127)).
+ * out_group_rows, out_group_stride: 0, 0 for the layout above; otherwise input row r is
+ *         written to output row (r / out_group_rows) * out_group_stride + r % out_group_rows
+ *         of codes and scales (e.g. one entry of 64 head rows per sequence straight into a
+ *         [B][N][64] key cache: out_group_rows = 64, out_group_stride = 64 N).
  * Encoding (OCP Microscaling v1.0): per block of 32, scale exponent
  *   E = floor(log2(max |y|)) - 2 clamped to [-127, 127] (-127 for an all-zero block);
  *   each y / 2^E rounds to the nearest of {0, .5, 1, 1.5, 2, 3, 4, 6} (ties to the even
@@ -139,7 +143,8 @@ int csa_index_rescore(const void *q_I, const float *w, const void *k_I, const in
  * Supported: D in {128, 256, 512}. rows may be 0 (nothing is launched).
  */
 int csa_quantize_mxfp4(const void *x, int64_t rows, int D, csa_dtype dt, int hadamard,
-                       uint8_t *codes, uint8_t *scales, void *stream);
+                       uint8_t *codes, uint8_t *scales, int64_t out_group_rows,
+                       int64_t out_group_stride, void *stream);
 
 /*
  * csa_topk - per-query top-k selection over index scores (§4.2).

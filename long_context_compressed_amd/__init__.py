@@ -43,7 +43,7 @@ def lib() -> C.CDLL:
         P, i32, i64, f32, sz = C.c_void_p, C.c_int, C.c_int64, C.c_float, C.c_size_t
         L.csa_compress.argtypes = [P, P, P, P, P, P, P, i32, i64, i32, i32, i32, i32, P, i64, P]
         L.csa_index_scores.argtypes = [P, P, P, P, P, P, P, i32, i32, i64, i32, i32, i32, i32, i32, P, P]
-        L.csa_quantize_mxfp4.argtypes = [P, i64, i32, i32, i32, P, P, P]
+        L.csa_quantize_mxfp4.argtypes = [P, i64, i32, i32, i32, P, P, i64, i64, P]
         L.csa_index_rescore.argtypes = [P, P, P, P, i32, P, P, i32, i32, i64, i32, i32, i32, i32, P, P]
         L.csa_topk_ids.argtypes = [P, P, i32, i64, i32, P, P, P, sz, P]
         L.csa_topk_workspace_bytes.argtypes = [i32, i64, i32]
@@ -142,9 +142,11 @@ def index_rescore(q_I, w, k_I, cand, q_seq, q_pos, ratio=4, scores=None, stream=
     return scores
 
 
-def quantize_mxfp4(x, hadamard=False, codes=None, scales=None, stream=None):
+def quantize_mxfp4(x, hadamard=False, codes=None, scales=None, group_rows=0, group_stride=0, stream=None):
     """csa_quantize_mxfp4 -> (codes [..., D/2] uint8, scales [..., D/32] uint8) of x [..., D]
-    (fp32 or bf16), after the Hadamard rotation when `hadamard`."""
+    (fp32 or bf16), after the Hadamard rotation when `hadamard`. With group_rows > 0, input
+    row r goes to output row (r // group_rows) * group_stride + r % group_rows of the given
+    codes / scales tensors (their data pointers are the base)."""
     D = x.shape[-1]
     rows = x.numel() // D if D else 0
     if codes is None:
@@ -152,7 +154,7 @@ def quantize_mxfp4(x, hadamard=False, codes=None, scales=None, stream=None):
     if scales is None:
         scales = torch.empty(x.shape[:-1] + (D // 32,), dtype=torch.uint8, device=x.device)
     rc = lib().csa_quantize_mxfp4(_ptr(x), rows, D, _dt(x), int(bool(hadamard)), _ptr(codes), _ptr(scales),
-                                  _stream(stream))
+                                  group_rows, group_stride, _stream(stream))
     _check("csa_quantize_mxfp4", rc)
     return codes, scales
 

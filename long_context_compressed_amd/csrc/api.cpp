@@ -118,15 +118,18 @@ int csa_index_rescore(const void *q_I, const float *w, const void *k_I, const in
 }
 
 int csa_quantize_mxfp4(const void *x, int64_t rows, int D, csa_dtype dt, int hadamard, uint8_t *codes,
-                       uint8_t *scales, void *stream) {
+                       uint8_t *scales, int64_t out_group_rows, int64_t out_group_stride, void *stream) {
     clear_error();
     REQUIRE(rows >= 0 && D > 0, CSA_EINVAL, "csa_quantize_mxfp4: need rows >= 0 and D > 0");
     REQUIRE(D % 32 == 0, CSA_EINVAL, "csa_quantize_mxfp4: D must be a multiple of 32");
     REQUIRE(dt == CSA_F32 || dt == CSA_BF16, CSA_EINVAL, "csa_quantize_mxfp4: dt must be CSA_F32 or CSA_BF16");
     REQUIRE(D == 128 || D == 256 || D == 512, CSA_EUNSUPPORTED, "csa_quantize_mxfp4: D must be 128, 256 or 512");
+    REQUIRE(out_group_rows >= 0 && (out_group_rows == 0 || out_group_stride >= out_group_rows), CSA_EINVAL,
+            "csa_quantize_mxfp4: need out_group_rows >= 0 and out_group_stride >= out_group_rows");
     if (rows == 0) return CSA_OK;
     REQUIRE(x && codes && scales, CSA_EINVAL, "csa_quantize_mxfp4: NULL tensor");
-    return launch_quantize_mxfp4(x, rows, D, dt, hadamard != 0, codes, scales, (hipStream_t)stream);
+    return launch_quantize_mxfp4(x, rows, D, dt, hadamard != 0, codes, scales, out_group_rows, out_group_stride,
+                                 (hipStream_t)stream);
 }
 
 size_t csa_topk_workspace_bytes(int T, int64_t N, int k) {

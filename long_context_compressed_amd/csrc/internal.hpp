@@ -20,7 +20,7 @@ int launch_index_mxfp4(const uint8_t *qI, const uint8_t *qs, const float *w, con
                        int ratio, float *scores, hipStream_t st);
 
 int launch_quantize_mxfp4(const void *x, int64_t rows, int D, csa_dtype dt, bool hadamard, uint8_t *codes,
-                          uint8_t *scales, hipStream_t st);
+                          uint8_t *scales, int64_t group_rows, int64_t group_stride, hipStream_t st);
 
 size_t topk_workspace_bytes(int T, int64_t N, int k);
 int launch_index_rescore(const void *qI, const float *w, const void *kI, const int32_t *cand, int M,

@@ -20,7 +20,8 @@ namespace {
 template <int E>
 __global__ void __launch_bounds__(256)
 quantize_mxfp4_kernel(const void *__restrict__ x, int64_t rows, csa_dtype dt, int hadamard, float inv_sqrt_d,
-                      uint8_t *__restrict__ codes, uint8_t *__restrict__ scales)
+                      uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, int64_t group_rows,
+                      int64_t group_stride)
 {
     constexpr int D = 64 * E;
     constexpr int LPB = 32 / E;  // lanes per 32-element block
@@ -77,18 +78,19 @@ quantize_mxfp4_kernel(const void *__restrict__ x, int64_t rows, csa_dtype dt, in
         uint32_t packed = 0u;
 #pragma unroll
         for (int j = 0; j < E; ++j) packed |= nib[j] << (4 * j);
-        uint8_t *dst = codes + row * (D / 2) + (E / 2) * lane;
+        const int64_t orow = group_rows > 0 ? (row / group_rows) * group_stride + row % group_rows : row;
+        uint8_t *dst = codes + orow * (D / 2) + (E / 2) * lane;
         if (E == 2) *dst = (uint8_t)packed;
         else if (E == 4) *reinterpret_cast<uint16_t *>(dst) = (uint16_t)packed;
         else *reinterpret_cast<uint32_t *>(dst) = packed;
-        if (lane % LPB == 0) scales[row * (D / 32) + lane / LPB] = (uint8_t)(es + 127);
+        if (lane % LPB == 0) scales[orow * (D / 32) + lane / LPB] = (uint8_t)(es + 127);
     }
 }
 
 }  // namespace
 
 int launch_quantize_mxfp4(const void *x, int64_t rows, int D, csa_dtype dt, bool hadamard, uint8_t *codes,
-                          uint8_t *scales, hipStream_t st) {
+                          uint8_t *scales, int64_t group_rows, int64_t group_stride, hipStream_t st) {
     const float inv_sqrt_d = (float)(1.0 / std::sqrt((double)D));
     int64_t blocks = (rows + 3) / 4;
     if (blocks > 65536) blocks = 65536;
@@ -96,15 +98,15 @@ int launch_quantize_mxfp4(const void *x, int64_t rows, int D, csa_dtype dt, bool
     switch (D) {
         case 128:
             hipLaunchKernelGGL(quantize_mxfp4_kernel<2>, grid, dim3(256), 0, st, x, rows, dt, (int)hadamard,
-                               inv_sqrt_d, codes, scales);
+                               inv_sqrt_d, codes, scales, group_rows, group_stride);
             break;
         case 256:
             hipLaunchKernelGGL(quantize_mxfp4_kernel<4>, grid, dim3(256), 0, st, x, rows, dt, (int)hadamard,
-                               inv_sqrt_d, codes, scales);
+                               inv_sqrt_d, codes, scales, group_rows, group_stride);
             break;
         default:
             hipLaunchKernelGGL(quantize_mxfp4_kernel<8>, grid, dim3(256), 0, st, x, rows, dt, (int)hadamard,
-                               inv_sqrt_d, codes, scales);
+                               inv_sqrt_d, codes, scales, group_rows, group_stride);
             break;
     }
     return check_launch("quantize_mxfp4_kernel");

@@ -63,11 +63,11 @@ class DecodeStep:
         b, c, ib, ic = i["blk"], i["carry"], i["iblk"], i["icarry"]
         compress(b["Ca"], b["Za"], b["Cb"], b["Zb"], c["C"], c["Z"], ratio=4, overlap=1, out=self.kv_new)
         compress(ib["Ca"], ib["Za"], ib["Cb"], ib["Zb"], ic["C"], ic["Z"], ratio=4, overlap=1, out=self.kI_new)
-        if self.mxfp4:  # rotate and encode the new key into the last entry of each sequence
+        if self.mxfp4:  # rotate and encode the new key into the last entry of every sequence
             kI, ks = i["k_I"], i["k_I_scale"]
             N = kI.shape[1]
-            for b in range(kI.shape[0]):
-                quantize_mxfp4(self.kI_new[b].view(64, 128), hadamard=True, codes=kI[b, N - 1], scales=ks[b, N - 1])
+            quantize_mxfp4(self.kI_new.view(-1, 64, 128), hadamard=True, codes=kI[0, N - 1], scales=ks[0, N - 1],
+                           group_rows=64, group_stride=64 * N)
 
     def index_prep(self):
         """MXFP4 keys: the query's index vectors rotated and encoded (nothing otherwise)."""

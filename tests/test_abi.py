@@ -114,12 +114,15 @@ def test_attn_validation(L):
 
 def test_quantize_mxfp4_validation(L):
     f = lambda **kw: L.csa_quantize_mxfp4(kw.get("x", 1), kw.get("rows", 4), kw.get("D", 128), kw.get("dt", 0),
-                                          kw.get("had", 1), kw.get("codes", 1), kw.get("scales", 1), None)
+                                          kw.get("had", 1), kw.get("codes", 1), kw.get("scales", 1),
+                                          kw.get("gr", 0), kw.get("gs", 0), None)
     assert f(D=100) == 1                        # not a multiple of 32
     assert f(D=96) == 2                         # valid, not built
     assert f(dt=2) == 1                         # MXFP4 is the output, not an input dtype
     assert f(x=None) == 1 and f(codes=None) == 1
     assert f(rows=-1) == 1
+    assert f(gr=64, gs=10) == 1                 # groups would overlap
+    assert f(gr=-1) == 1
     assert f(rows=0) == 0
 
 
