@@ -196,14 +196,15 @@ def test_index_rescore(csa, orc, dt):
     assert_rel(gpu[fin], ref[fin], TOL_F32, "rescore")
 
 
-def test_topk_ids(csa, orc):
+@pytest.mark.parametrize("T,M,k", [(6, 3000, 256), (3, 40000, 1024)])
+def test_topk_ids(csa, orc, T, M, k):
     """Top-k over candidate lists: the chosen entries are the ids of the oracle's top-k
-    positions (ties to the earlier position), in list order, -1 padded."""
-    say("topk_ids")
-    T, M, k = 6, 3000, 256
-    sc = torch.round(W.normal((T, M), 61, "s", device=DEV) * 16) / 16  # ties
+    positions (ties to the earlier position), in list order, -1 padded; M = 40,000 takes
+    two reduction levels, the first reading the ids."""
+    say("topk_ids", T, M, k)
+    sc = torch.round(W.normal((T, M), 61 + M, "s", device=DEV) * 16) / 16  # ties
     sc[2, 100:] = -float("inf")                                          # fewer than k finite
-    ids = torch.stack([torch.from_numpy(np.sort(W.distinct_sample(M, 200000, 61, f"i{t}"))) for t in range(T)])
+    ids = torch.stack([torch.from_numpy(np.sort(W.distinct_sample(M, 200000, 61 + M, f"i{t}"))) for t in range(T)])
     ids = ids.to(torch.int32).to(DEV)
     idx, vals = csa.topk_ids(sc, ids, k, with_vals=True)
     torch.cuda.synchronize()
