@@ -14,9 +14,14 @@
 // buffered: head h+2 is loaded into registers while head h is computed, and head h+1 is
 // written to the other buffer. The E8M0 scales are staged 8 heads at a time (32 bytes of
 // each row per load, not 4), since the scattered 4-byte loads of one head's scales cost
-// more address-unit cycles than its codes. The epilogue of every MFMA (ReLU, times w[t][h], accumulate) is VALU work and
-// bounds the kernel. The 16-byte chunks of each 64-byte code row are XOR-swizzled in LDS so
-// the per-lane 16-byte operand reads of 8 consecutive rows hit distinct banks.
+// more address-unit cycles than its codes. The epilogue of every MFMA (ReLU, times
+// w[t][h], accumulate) is VALU work and bounds the kernel. The 16-byte chunks of each
+// 64-byte code row are XOR-swizzled in LDS so the per-lane 16-byte operand reads of 8
+// consecutive rows hit distinct banks.
+//
+// Decode (a few queries per key store): there is no reuse of keys across queries, so each
+// query streams its keys from HBM (index_mxfp4_scan_kernel below) and the same matrix op
+// computes 16 heads' dots of one entry on its diagonal.
 #include "common.hpp"
 #include "internal.hpp"
 
