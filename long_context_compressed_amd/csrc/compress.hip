@@ -110,7 +110,8 @@ int launch_compress(const void *Ca, const void *Cb, const void *Za, const void *
 {
     const int64_t E = n / ratio;
     if (B == 0 || E == 0) return CSA_OK;
-    const int SG = ratio * (1 + overlap) >= 64 ? 4 : 1;
+    // long pools: 16 slot groups of 8 slots (one batch of loads each) over 16 channels
+    const int SG = ratio * (1 + overlap) >= 64 ? 16 : 1;
     const int CX = 256 / SG;
     const int ctiles = (c + CX - 1) / CX;
     const int64_t blocks = (int64_t)ctiles * E * B;
