@@ -45,12 +45,13 @@ def lib():
         L.oracle_mxfp4_encode.argtypes = [P, i64, i32, i32, P, P]
         L.oracle_hadamard.argtypes = [P, i64, i32, P]
         L.oracle_topk.argtypes = [P, i32, i64, i32, P, P]
+        L.oracle_rmsnorm_rope.argtypes = [P, i64, i32, P, f64, P, i32, i64, P]
         L.oracle_sparse_attn.argtypes = [P, P, P, P, i32, f64, P, P, i32, i32, P, P, P, i32,
                                          i32, i32, i64, i32, i32, P, P]
         L.oracle_hca_attn.argtypes = [P, P, P, i32, f64, P, P, i32, i32, P, P, P, i32,
                                       i32, i32, i64, i32, i32, P, P]
         for f in ("oracle_compress", "oracle_index_scores", "oracle_mxfp4_decode", "oracle_mxfp4_encode",
-                  "oracle_hadamard", "oracle_topk",
+                  "oracle_hadamard", "oracle_topk", "oracle_rmsnorm_rope",
                   "oracle_sparse_attn", "oracle_hca_attn"):
             getattr(L, f).restype = C.c_int
         _lib = L
@@ -144,6 +145,21 @@ def hadamard(x):
     out = np.empty_like(xf)
     D = xf.shape[-1]
     _check(lib().oracle_hadamard(_p(xf), xf.size // D, D, _p(out)), "hadamard")
+    return out
+
+
+def rmsnorm_rope(x, g, eps, rope_cs=None, rope_dim=0, group=1):
+    """RMSNorm of each row of x [..., D] with gains g [D], then the last rope_dim dims
+    rotated by rope_cs [rows // group][rope_dim/2][2] (row r takes table row r // group);
+    fp64 out of x's shape."""
+    xx, gg = _f64(x), _f64(g)
+    D = xx.shape[-1]
+    rows = xx.size // D
+    cs = _f64(rope_cs)
+    R = rope_dim if cs is not None else 0
+    out = np.empty(xx.shape, dtype=np.float64)
+    _check(lib().oracle_rmsnorm_rope(_p(xx), rows, D, _p(gg), float(eps), _p(cs), R, int(group), _p(out)),
+           "rmsnorm_rope")
     return out
 
 

@@ -16,6 +16,7 @@
  *   SWA, partial RoPE     §6 (window 128, RoPE on the last 64 dims, inverse RoPE on o)
  *   MXFP4 operands        the MXFP4 model-card page (one E8M0 scale per 32 E2M1 values)
  *   Hadamard rotation     the same page's Indexer section (q rotated before FP4 scoring)
+ *   RMSNorm               §6, equation for RMSNorm(x) (Q and the compressed entries)
  *
  * Every sum, dot product and softmax is accumulated in double precision and each
  * logit vector is materialised before it is normalised.
@@ -29,7 +30,8 @@
  *  - the SWA rows of a query at t are positions max(0, t-window+1) .. t;
  *  - a RoPE pair is the interleaved pair (D-R+2p, D-R+2p+1), rotated by (cos, sin)
  *    of the caller's table; the output is rotated back with (cos, -sin);
- *  - top-k ties are broken by the lower entry index; -INF scores are never taken.
+ *  - top-k ties are broken by the lower entry index; -INF scores are never taken;
+ *  - RMSNorm of an all-zero row with eps = 0 (0/0) is read as a zero row.
  */
 #include <math.h>
 #include <stdint.h>
@@ -240,6 +242,35 @@ int oracle_mxfp4_encode(const float *x, int64_t rows, int D, int hadamard, uint8
         }
     }
     free(y);
+    return OR_OK;
+}
+
+/* ---------------------------------------------------------------------------------
+ * RMSNorm of a row, then RoPE on its last R dims ("DeepSeek-V4 混合注意力" §6: RMSNorm
+ * on Q and on the compressed representation, x / sqrt(mean(x^2) + eps) scaled per dim
+ * by g; RoPE on the last 64 dims of each head):
+ *   y_d = x_d / sqrt(eps + (1/D) sum_e x_e^2) * g_d
+ *   (y_{D-R+2p}, y_{D-R+2p+1}) <- (y0 c - y1 s, y0 s + y1 c),  (c, s) = cs[r / group][p]
+ * x, out: [rows][D]; g: [D]; cs: [rows / group][R/2][2] or NULL (R = 0).
+ * ------------------------------------------------------------------------------- */
+int oracle_rmsnorm_rope(const double *x, int64_t rows, int D, const double *g, double eps,
+                        const double *cs, int R, int64_t group, double *out)
+{
+    if (D <= 0 || !(eps >= 0.0) || R < 0 || R % 2 || R > D || (R > 0 && !cs) || group < 1) return OR_EINVAL;
+    for (int64_t r = 0; r < rows; ++r) {
+        const double *xr = x + r * D;
+        double *y = out + r * D;
+        double ss = 0.0;
+        for (int d = 0; d < D; ++d) ss += xr[d] * xr[d];
+        const double den = sqrt(ss / D + eps);
+        for (int d = 0; d < D; ++d) y[d] = (den > 0.0) ? xr[d] / den * g[d] : 0.0;
+        const double *c = (R > 0) ? cs + (r / group) * R : NULL;
+        for (int p = 0; p < R / 2; ++p) {
+            const double y0 = y[D - R + 2 * p], y1 = y[D - R + 2 * p + 1];
+            y[D - R + 2 * p] = y0 * c[2 * p] - y1 * c[2 * p + 1];
+            y[D - R + 2 * p + 1] = y0 * c[2 * p + 1] + y1 * c[2 * p];
+        }
+    }
     return OR_OK;
 }
 

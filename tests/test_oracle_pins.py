@@ -544,3 +544,68 @@ def test_swa_window_rows(orc):
     _, lse = orc.sparse_attn(q[:1], _rand(1, 4, D), sink, np.full((1, 1), -1, np.int32), 1.0, swa[:, :50],
                              np.array([3970]), 128, np.zeros(1), np.array([4000]))
     np.testing.assert_allclose(np.exp(lse) - 1.0, 31, rtol=1e-12)  # positions 3970..4000
+
+
+# ---- RMSNorm + RoPE of a row ("DeepSeek-V4 混合注意力" §6) ------------------------------
+
+def test_rmsnorm_worked_rows(orc):
+    """Closed forms: a constant row 3 with eps = 16 has rms 5, so y = 0.6 g; the row (3, 4)
+    with eps = 0 has mean square 12.5, so y = (3, 4) * sqrt(2) / 5 * g."""
+    g = np.array([1.0, -2.0, 0.5, 4.0])
+    y = orc.rmsnorm_rope(np.full((1, 4), 3.0), g, 16.0)
+    np.testing.assert_allclose(y[0], 0.6 * g, rtol=1e-15)
+    y2 = orc.rmsnorm_rope(np.array([[3.0, 4.0]]), np.array([1.0, 2.0]), 0.0)
+    np.testing.assert_allclose(y2[0], [3 * math.sqrt(2) / 5, 2 * 4 * math.sqrt(2) / 5], rtol=1e-15)
+
+
+def test_rmsnorm_unit_mean_square_and_scale_invariance(orc):
+    """With g = 1 and eps = 0 every output row has mean square 1 (before and after RoPE,
+    a rotation), and positive scaling of a row does not change its output."""
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((7, 128)) * rng.uniform(0.1, 10, size=(7, 1))
+    ang = rng.uniform(-3, 3, size=(7, 32))
+    cs = np.stack([np.cos(ang), np.sin(ang)], -1)
+    for c, R in ((None, 0), (cs, 64)):
+        y = orc.rmsnorm_rope(x, np.ones(128), 0.0, rope_cs=c, rope_dim=R)
+        np.testing.assert_allclose((y ** 2).mean(-1), 1.0, rtol=1e-13)
+        np.testing.assert_allclose(orc.rmsnorm_rope(x * 37.5, np.ones(128), 0.0, rope_cs=c, rope_dim=R), y,
+                                   rtol=1e-13, atol=1e-15)
+
+
+def test_rmsnorm_matches_torch_rms_norm(orc):
+    """Without RoPE it is torch's rms_norm over the last dim with the same weight and eps."""
+    rng = np.random.default_rng(22)
+    x = rng.standard_normal((33, 512))
+    g = rng.uniform(0.5, 1.5, size=512)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (512,), weight=torch.from_numpy(g), eps=1e-6)
+    np.testing.assert_allclose(orc.rmsnorm_rope(x, g, 1e-6), ref.numpy(), rtol=1e-13, atol=1e-15)
+
+
+def test_rmsnorm_rope_special_angles_and_groups(orc):
+    """Only the last R dims rotate, pair (D-R+2p, D-R+2p+1) by its own table entry: angle
+    pi/2 maps (a, b) to (-b, a), angle pi to (-a, -b), angle 0 is the identity; row r takes
+    table row r // group."""
+    rng = np.random.default_rng(23)
+    D, R, rows, group = 16, 8, 6, 2
+    x = rng.standard_normal((rows, D))
+    g = rng.uniform(0.5, 1.5, size=D)
+    plain = orc.rmsnorm_rope(x, g, 1e-3)
+    angles = np.array([np.pi / 2, np.pi, 0.0])  # table row j: every pair turns by angles[j]
+    cs = np.zeros((rows // group, R // 2, 2))
+    cs[..., 0] = np.round(np.cos(angles))[:, None]
+    cs[..., 1] = np.round(np.sin(angles))[:, None]
+    y = orc.rmsnorm_rope(x, g, 1e-3, rope_cs=cs, rope_dim=R, group=group)
+    np.testing.assert_array_equal(y[:, :D - R], plain[:, :D - R])
+    a, b = plain[:, D - R::2], plain[:, D - R + 1::2]
+    for r in range(rows):
+        j = r // group
+        exp_a, exp_b = [(-b[r], a[r]), (-a[r], -b[r]), (a[r], b[r])][j]
+        np.testing.assert_array_equal(y[r, D - R::2], exp_a)
+        np.testing.assert_array_equal(y[r, D - R + 1::2], exp_b)
+
+
+def test_rmsnorm_zero_row(orc):
+    """A zero row stays zero, with eps > 0 (0 / sqrt(eps)) and with eps = 0 (the reading
+    of 0 / 0)."""
+    for eps in (0.0, 1e-6):
+        np.testing.assert_array_equal(orc.rmsnorm_rope(np.zeros((2, 64)), np.ones(64), eps), 0.0)
