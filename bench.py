@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--workload", default="pro_decode_1m",
                     choices=["pro_decode_1m", "flash_decode_128k", "pro_decode_1m_shared_keys", "pro_decode_1m_mxfp4",
                              "pro_prefill_chunk",
-                             "hca_prefill_4k"],
+                             "hca_prefill_4k", "pro_prefill_q_norm_rope"],
                     help="pro_decode_1m is the benchmark line; the others print the same record for "
                          "the other configurations' shapes (profiling aid)")
     ap.add_argument("--profile-copy", action="store_true",
@@ -87,6 +87,8 @@ def main():
     csa.lib()
     if a.workload in ("pro_prefill_chunk", "hca_prefill_4k"):
         return prefill_main(a)
+    if a.workload == "pro_prefill_q_norm_rope":
+        return rownorm_main(a)
     cfg = W.FLASH if a.workload == "flash_decode_128k" else W.PRO
     shared = a.workload == "pro_decode_1m_shared_keys"
     fp4 = a.workload == "pro_decode_1m_mxfp4"
@@ -277,6 +279,64 @@ def prefill_main(a):
                      "median_launch_ms": round(float(np.median(dom_ms)), 4),
                      "min_launch_ms": round(float(np.min(dom_ms)), 4)},
         "stages_ms": stage_ms,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def rownorm_main(a):
+    """RMSNorm + partial RoPE of the Pro prefill chunk's queries (profiling aid):
+    csa_rmsnorm_rope over 8,192 tokens x 128 heads rows of 512 bf16 dims, gains U(0.5, 1.5),
+    eps 1e-6, the last 64 dims rotated at each token's position (one angle row per 128 head
+    rows), into a separate bf16 output. An HBM stream: 2 x 1,024 bytes per row plus the
+    256-byte angle row of each token."""
+    import numpy as np
+    import torch
+
+    import long_context_compressed_amd as csa
+    import workloads as W
+
+    cfg = W.PRO_PREFILL
+    T, H, D, R, s = cfg.T, cfg.H, cfg.c, cfg.rope_dim, cfg.seed
+    q = W.normal((T, H, D), s, "q", dtype=torch.bfloat16, device="cuda")
+    g = W.uniform((D,), s, "q_norm_gain", lo=0.5, hi=1.5, device="cuda")
+    cs = W.rope_table(torch.arange(cfg.n, cfg.n + T, dtype=torch.int64), R).to("cuda")
+    out = torch.empty_like(q)
+    st = torch.cuda.current_stream()
+    alg = T * H * D * 2 * 2 + T * R * 4 + D * 4
+    for _ in range(a.warmup):
+        csa.rmsnorm_rope(q, g, 1e-6, rope_cs=cs, rope_group=H, out=out, stream=st)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in ev:
+        e0.record(st)
+        csa.rmsnorm_rope(q, g, 1e-6, rope_cs=cs, rope_group=H, out=out, stream=st)
+        e1.record(st)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    avg = float(np.mean(ms)) / 1e3
+    gbs = alg / avg / 1e9
+    # context: torch's device copy of the same rows (the same read + write bytes)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out.copy_(q)
+    c0.record(st)
+    for _ in range(20):
+        out.copy_(q)
+    c1.record(st)
+    torch.cuda.synchronize()
+    copy_ms = c0.elapsed_time(c1) / 20
+    res = {
+        "metric": "query rows/s, RMSNorm + RoPE of the Pro prefill chunk's q (profiling line, not the benchmark)",
+        "value": round(T * H * a.steps / elapsed, 1), "unit": "rows/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(elapsed / a.steps * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": a.workload, "rows": T * H, "dim": D, "rope_dim": R},
+        "roofline": {"kernel": "rmsnorm_rope_kernel", "bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0,
+                     "unit": "GB/s", "frac": round(gbs / 8000.0, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": alg, "avg_launch_ms": round(avg * 1e3, 4),
+                     "median_launch_ms": round(float(np.median(ms)), 4), "min_launch_ms": round(float(np.min(ms)), 4),
+                     "torch_copy_same_rows_ms": round(copy_ms, 4)},
     }
     print(json.dumps(res), flush=True)
 

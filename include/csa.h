@@ -147,6 +147,32 @@ int csa_quantize_mxfp4(const void *x, int64_t rows, int D, csa_dtype dt, int had
                        int64_t out_group_stride, void *stream);
 
 /*
+ * csa_rmsnorm_rope - RMSNorm of each row, then RoPE on its last R dims: the normalisation
+ * that "DeepSeek-V4 混合注意力" §6 applies to the queries and to the compressed
+ * representation (RMSNorm(x) = x / sqrt(mean(x^2) + eps) times a per-dim gain g), and the
+ * partial RoPE of the same section (only the last 64 dims of a head rotate).
+ *
+ * x:      [rows][D] in dt_in (CSA_F32 | CSA_BF16).
+ * g:      [D] fp32 gains.  eps: >= 0 (finite).
+ * rope_cs: [ceil(rows / rope_group)][R] fp32, (cos, sin) of pair p at [2p], [2p + 1]; row r uses
+ *         table row r / rope_group (rope_group = H for query rows [T][H][D] that share their
+ *         token's angles, 1 for one entry per row). NULL when R == 0.
+ * out:    [rows][D] in dt_out (CSA_F32 | CSA_BF16); may be x itself when dt_out == dt_in.
+ *         x, out, g and rope_cs are 16-byte aligned (rows move as vector accesses).
+ * Per row (fp32 arithmetic): y_d = x_d * g_d / sqrt(sum_e x_e^2 / D + eps), 0 when the
+ *   denominator is 0; then for p < R/2 the pair (a, b) = (y[D-R+2p], y[D-R+2p+1]) becomes
+ *   (a cos - b sin, a sin + b cos); bf16 output rounds to nearest even.
+ * Supported: D in {128, 256, 512}; R even, 0 <= R <= D, and a multiple of D / 64 (R = 64
+ *   for the pages' heads). rows may be 0 (nothing is launched).
+ * Errors: CSA_EINVAL for a bad size, dtype, eps, R or rope_group, a NULL or misaligned
+ *   tensor, or out == x with different dtypes; CSA_EUNSUPPORTED for another D or an R
+ *   that is not a multiple of D / 64.
+ */
+int csa_rmsnorm_rope(const void *x, csa_dtype dt_in, int64_t rows, int D, const float *g, float eps,
+                     const float *rope_cs, int R, int64_t rope_group, void *out, csa_dtype dt_out,
+                     void *stream);
+
+/*
  * csa_topk - per-query top-k selection over index scores (§4.2).
  *
  * scores: [T][N] fp32; -INFINITY (and NaN) entries are never selected.

@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(_HERE, "libcsa.so")
 
 F32, BF16, MXFP4 = 0, 1, 2
 STATUS = {0: "CSA_OK", 1: "CSA_EINVAL", 2: "CSA_EUNSUPPORTED", 3: "CSA_EWORKSPACE", 4: "CSA_EHIP"}
-EXPORTS = ("csa_compress", "csa_index_scores", "csa_index_rescore", "csa_quantize_mxfp4", "csa_topk_workspace_bytes",
+EXPORTS = ("csa_compress", "csa_index_scores", "csa_index_rescore", "csa_quantize_mxfp4", "csa_rmsnorm_rope",
+           "csa_topk_workspace_bytes",
            "csa_topk", "csa_topk_ids",
            "csa_attn_workspace_bytes", "csa_sparse_attn", "hca_attn", "csa_status_str",
            "csa_last_error")
@@ -44,6 +45,7 @@ def lib() -> C.CDLL:
         L.csa_compress.argtypes = [P, P, P, P, P, P, P, i32, i64, i32, i32, i32, i32, P, i64, P]
         L.csa_index_scores.argtypes = [P, P, P, P, P, P, P, i32, i32, i64, i32, i32, i32, i32, i32, P, P]
         L.csa_quantize_mxfp4.argtypes = [P, i64, i32, i32, i32, P, P, i64, i64, P]
+        L.csa_rmsnorm_rope.argtypes = [P, i32, i64, i32, P, f32, P, i32, i64, P, i32, P]
         L.csa_index_rescore.argtypes = [P, P, P, P, i32, P, P, i32, i32, i64, i32, i32, i32, i32, P, P]
         L.csa_topk_ids.argtypes = [P, P, i32, i64, i32, P, P, P, sz, P]
         L.csa_topk_workspace_bytes.argtypes = [i32, i64, i32]
@@ -55,7 +57,8 @@ def lib() -> C.CDLL:
                                       i32, i32, i64, i32, i32, i32, P, P, P, sz, P]
         L.hca_attn.argtypes = [P, P, P, i32, f32, P, P, i32, i32, P, P, P, i32,
                                i32, i32, i64, i32, i32, i32, P, P, P, sz, P]
-        for f in ("csa_compress", "csa_index_scores", "csa_index_rescore", "csa_quantize_mxfp4", "csa_topk",
+        for f in ("csa_compress", "csa_index_scores", "csa_index_rescore", "csa_quantize_mxfp4", "csa_rmsnorm_rope",
+                  "csa_topk",
                   "csa_topk_ids", "csa_sparse_attn", "hca_attn"):
             getattr(L, f).restype = C.c_int
         L.csa_status_str.argtypes = [C.c_int]
@@ -157,6 +160,21 @@ def quantize_mxfp4(x, hadamard=False, codes=None, scales=None, group_rows=0, gro
                                   group_rows, group_stride, _stream(stream))
     _check("csa_quantize_mxfp4", rc)
     return codes, scales
+
+
+def rmsnorm_rope(x, g, eps, rope_cs=None, rope_group=1, out=None, out_dtype=None, stream=None):
+    """csa_rmsnorm_rope -> out [..., D]: RMSNorm of each row of x (fp32 or bf16) with fp32
+    gains g [D], then the last R dims rotated by rope_cs [ceil(rows / rope_group)][R/2][2]
+    (or [..][R]) fp32 (cos, sin) pairs. out may be x (same dtype) for the in-place form."""
+    D = x.shape[-1]
+    rows = x.numel() // D if D else 0
+    if out is None:
+        out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
+    R = 0 if rope_cs is None else int(rope_cs.numel() // rope_cs.shape[0])
+    rc = lib().csa_rmsnorm_rope(_ptr(x), _dt(x), rows, D, _ptr(g), float(eps), _ptr(rope_cs), R, int(rope_group),
+                                _ptr(out), _dt(out), _stream(stream))
+    _check("csa_rmsnorm_rope", rc)
+    return out
 
 
 def topk_workspace_bytes(T, N, k) -> int:

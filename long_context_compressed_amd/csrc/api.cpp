@@ -132,6 +132,26 @@ int csa_quantize_mxfp4(const void *x, int64_t rows, int D, csa_dtype dt, int had
                                  (hipStream_t)stream);
 }
 
+int csa_rmsnorm_rope(const void *x, csa_dtype dt_in, int64_t rows, int D, const float *g, float eps,
+                     const float *rope_cs, int R, int64_t rope_group, void *out, csa_dtype dt_out, void *stream) {
+    clear_error();
+    REQUIRE(rows >= 0 && D > 0, CSA_EINVAL, "csa_rmsnorm_rope: need rows >= 0 and D > 0");
+    REQUIRE((dt_in == CSA_F32 || dt_in == CSA_BF16) && (dt_out == CSA_F32 || dt_out == CSA_BF16), CSA_EINVAL,
+            "csa_rmsnorm_rope: dt_in and dt_out must be CSA_F32 or CSA_BF16");
+    REQUIRE(std::isfinite(eps) && eps >= 0.f, CSA_EINVAL, "csa_rmsnorm_rope: eps must be finite and >= 0");
+    REQUIRE(R >= 0 && R % 2 == 0 && R <= D, CSA_EINVAL, "csa_rmsnorm_rope: R must be even and in [0, D]");
+    REQUIRE(rope_group >= 1, CSA_EINVAL, "csa_rmsnorm_rope: rope_group must be >= 1");
+    REQUIRE(D == 128 || D == 256 || D == 512, CSA_EUNSUPPORTED, "csa_rmsnorm_rope: D must be 128, 256 or 512");
+    REQUIRE(R % (D / 64) == 0, CSA_EUNSUPPORTED, "csa_rmsnorm_rope: R must be a multiple of D / 64");
+    if (rows == 0) return CSA_OK;
+    REQUIRE(x && g && out && (R == 0 || rope_cs), CSA_EINVAL, "csa_rmsnorm_rope: NULL tensor");
+    REQUIRE(x != out || dt_in == dt_out, CSA_EINVAL, "csa_rmsnorm_rope: in place needs dt_out == dt_in");
+    REQUIRE((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(g) |
+             reinterpret_cast<uintptr_t>(R > 0 ? rope_cs : g)) % 16 == 0,
+            CSA_EINVAL, "csa_rmsnorm_rope: x, out, g and rope_cs must be 16-byte aligned");
+    return launch_rmsnorm_rope(x, dt_in, rows, D, g, eps, rope_cs, R, rope_group, out, dt_out, (hipStream_t)stream);
+}
+
 size_t csa_topk_workspace_bytes(int T, int64_t N, int k) {
     if (T <= 0 || N <= 0 || k <= 0) return 0;
     return topk_workspace_bytes(T, N, k);

@@ -126,6 +126,24 @@ def test_quantize_mxfp4_validation(L):
     assert f(rows=0) == 0
 
 
+def test_rmsnorm_rope_validation(L):
+    f = lambda **kw: L.csa_rmsnorm_rope(kw.get("x", 16), kw.get("dti", 1), kw.get("rows", 4), kw.get("D", 512),
+                                        kw.get("g", 48), kw.get("eps", 1e-6), kw.get("cs", 64), kw.get("R", 64),
+                                        kw.get("grp", 1), kw.get("out", 32), kw.get("dto", 1), None)
+    assert f(D=48) == 1                         # R = 64 > D
+    assert f(D=100) == 2 and f(D=100, R=0) == 2  # valid, not built
+    assert f(D=0) == 1 and f(rows=-1) == 1
+    assert f(dti=2) == 1 and f(dto=2) == 1      # MXFP4 is neither an input nor an output here
+    assert f(eps=-1.0) == 1 and f(eps=float("inf")) == 1 and f(eps=float("nan")) == 1
+    assert f(R=3) == 1 and f(R=-2) == 1 and f(R=514) == 1
+    assert f(grp=0) == 1
+    assert f(R=2) == 2 and f(D=256, R=6) == 2  # R not a multiple of D / 64: not built
+    assert f(x=None) == 1 and f(g=None) == 1 and f(out=None) == 1 and f(cs=None) == 1
+    assert f(out=16, dto=0) == 1                # in place with a dtype change
+    assert f(x=18) == 1 and f(out=40) == 1 and f(g=52) == 1 and f(cs=72) == 1  # not 16-byte aligned
+    assert f(rows=0) == 0
+
+
 def test_index_rescore_and_topk_ids_validation(L):
     r = lambda **kw: L.csa_index_rescore(*[kw.get(k, v) for k, v in (
         ("q", 1), ("w", 1), ("k", 1), ("cand", 1), ("M", 16), ("qseq", 1), ("qpos", 1), ("T", 2), ("B", 1),

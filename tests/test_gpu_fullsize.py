@@ -253,3 +253,29 @@ def test_hca_prefill_chunk_full_size(csa, orc):
     assert_rel(ch.lse.index_select(0, st), rlse, 2e-3, "HCA prefill attention lse")
     del inp, ch
     _free()
+
+
+def test_pro_prefill_q_norm_rope_full_size(csa, orc):
+    """RMSNorm + RoPE of the Pro prefill chunk's queries as bench.py times it (8,192 x 128
+    rows of 512 bf16, one angle row per token): 2,000 sampled rows against the oracle; and
+    at every row, with unit gains, eps = 0 and fp32 output, a mean square of 1 (the
+    normalisation's invariant, which the rotation keeps)."""
+    cfg = W.PRO_PREFILL
+    T, H, D, R, s = cfg.T, cfg.H, cfg.c, cfg.rope_dim, cfg.seed
+    say("q_norm_rope full size", T, H, D)
+    q = W.normal((T, H, D), s, "q", dtype=torch.bfloat16, device=DEV)
+    g = W.uniform((D,), s, "q_norm_gain", lo=0.5, hi=1.5, device=DEV)
+    cs = W.rope_table(torch.arange(cfg.n, cfg.n + T, dtype=torch.int64), R).to(DEV)
+    out = csa.rmsnorm_rope(q, g, 1e-6, rope_cs=cs, rope_group=H)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(7).choice(T * H, 2000, replace=False))
+    rt = torch.from_numpy(rows).to(DEV)
+    ref = orc.rmsnorm_rope(q.view(T * H, D)[rt], g, 1e-6, rope_cs=cs[torch.from_numpy(rows // H).to(DEV)],
+                           rope_dim=R)
+    assert_rel(out.view(T * H, D)[rt], ref, TOL_BF16, "q_norm_rope sample")
+    del out
+    y = csa.rmsnorm_rope(q, torch.ones(D, device=DEV), 0.0, rope_cs=cs, rope_group=H, out_dtype=torch.float32)
+    ms = (y.view(T * H, D).double() ** 2).mean(-1)
+    assert float((ms - 1.0).abs().max()) < 1e-5
+    del y, ms
+    _free()

@@ -242,6 +242,43 @@ def test_quantize_mxfp4(csa, orc, D, dt, had):
     np.testing.assert_array_equal(codes.cpu().numpy(), rc)
 
 
+@pytest.mark.parametrize("rows,D,dti,dto,R,group,inplace",
+                         [(1, 512, torch.bfloat16, torch.bfloat16, 64, 1, False),
+                          (1001, 512, torch.bfloat16, torch.bfloat16, 64, 128, False),
+                          (333, 128, torch.float32, torch.float32, 0, 1, False),
+                          (4097, 256, torch.float32, torch.bfloat16, 64, 1, False),
+                          (2048, 512, torch.bfloat16, torch.bfloat16, 64, 1, True),
+                          (777, 512, torch.float32, torch.float32, 512, 3, True),
+                          (300000, 128, torch.bfloat16, torch.float32, 128, 7, False)])
+def test_rmsnorm_rope(csa, orc, rows, D, dti, dto, R, group, inplace):
+    """RMSNorm (gain, eps) + RoPE of the last R dims against the oracle, element by element:
+    rows at scales 2^-20 .. 2^20, a zero row, a constant row, per-table-row angles shared by
+    `group` consecutive rows, in place and out of place; the 300,000-row case runs past the
+    grid cap (a grid-stride loop)."""
+    say("rmsnorm_rope", rows, D, dti, dto, R, group, inplace)
+    x = W.normal((rows, D), 4242 + D, "x", device=DEV)
+    x = x * torch.pow(2.0, torch.linspace(-20, 20, rows, device=DEV)).unsqueeze(1)
+    x[0] = 0.0 if rows > 1 else x[0]
+    if rows > 2:
+        x[1] = 3.0
+    x = x.to(dti)
+    g = W.uniform((D,), 4242 + D, "g", lo=-1.5, hi=1.5, device=DEV)
+    nt = (rows + group - 1) // group
+    cs = None
+    if R > 0:
+        cs = W.rope_table(torch.arange(nt, dtype=torch.int64) * 977 + 5, R).to(DEV)
+    ref = orc.rmsnorm_rope(x, g, 1e-6, rope_cs=cs, rope_dim=R, group=group)
+    xin = x.clone()
+    out = csa.rmsnorm_rope(xin, g, 1e-6, rope_cs=cs, rope_group=group, out=xin if inplace else None,
+                           out_dtype=dto)
+    torch.cuda.synchronize()
+    assert out.dtype == dto
+    tol = TOL_F32 if dto == torch.float32 else TOL_BF16
+    assert_rel(out, ref, tol, "rmsnorm_rope")
+    if rows > 1:
+        assert torch.all(out[0] == 0)
+
+
 # ------------------------------------------------------------------------------------
 # top-k
 # ------------------------------------------------------------------------------------
