@@ -17,7 +17,9 @@
 // more address-unit cycles than its codes. The epilogue of every MFMA (ReLU, times
 // w[t][h], accumulate) is VALU work and bounds the kernel. The 16-byte chunks of each
 // 64-byte code row are XOR-swizzled in LDS so the per-lane 16-byte operand reads of 8
-// consecutive rows hit distinct banks.
+// consecutive rows hit distinct banks. The head weights of the tile's queries sit in LDS
+// head-major, so the 4 weights a lane needs per MFMA tile (4 consecutive queries) are one
+// 16-byte read.
 //
 // Decode (a few queries per key store): there is no reuse of keys across queries, so each
 // query streams its keys from HBM (index_mxfp4_scan_kernel below) and the same matrix op
@@ -31,7 +33,6 @@ namespace {
 
 constexpr int TQ = 256;       // queries per workgroup
 constexpr int TE = 128;       // entries per workgroup
-constexpr int WPITCH = 65;    // fp32 pitch of a query's 64 head weights in LDS
 
 typedef int i32x4v __attribute__((ext_vector_type(4)));
 
@@ -49,7 +50,7 @@ index_mxfp4_mfma_kernel(const uint8_t *__restrict__ qI, const uint8_t *__restric
     // scale words of 8 heads at a time, head-major ([head % 8][row]), double buffered
     __shared__ __attribute__((aligned(16))) uint32_t QSs[2][8][TQ];
     __shared__ __attribute__((aligned(16))) uint32_t KSs[2][8][TE];
-    __shared__ float Ws[TQ * WPITCH];
+    __shared__ __attribute__((aligned(16))) float Ws[64 * TQ];  // head-major: [head][query]
     __shared__ int64_t nvis_s[TQ];
     __shared__ int red[2];
 
@@ -92,9 +93,9 @@ index_mxfp4_mfma_kernel(const uint8_t *__restrict__ qI, const uint8_t *__restric
         // head weights of the tile's queries
 #pragma unroll 4
         for (int x = tid; x < TQ * 64; x += 512) {
-            const int qq = x >> 6, h = x & 63;
+            const int qq = x % TQ, h = x / TQ;
             const int t = t0 + qq;
-            Ws[qq * WPITCH + h] = (t < T) ? w[(int64_t)t * 64 + h] : 0.f;
+            Ws[h * TQ + qq] = (t < T) ? w[(int64_t)t * 64 + h] : 0.f;
         }
         // per-wave share of one head's codes: 32 q rows and 16 k rows (16 bytes per lane per
         // 16-row group), loaded into registers while the previous head is computed, then
@@ -172,9 +173,8 @@ index_mxfp4_mfma_kernel(const uint8_t *__restrict__ qI, const uint8_t *__restric
             const i32x4v av = *reinterpret_cast<const i32x4v *>(&Qs[BUF][row * 64 + ((g4 ^ swz(row)) * 16)]); \
             const i32x8 A = i32x8{av[0], av[1], av[2], av[3], 0, 0, 0, 0};              \
             const int sa = (int)((QSs[sbuf][HS][row] >> (8 * g4)) & 0xFFu);             \
-            float wr[4];                                                                \
-            _Pragma("unroll") for (int r = 0; r < 4; ++r)                               \
-                wr[r] = Ws[(qg * 64 + 16 * m + 4 * g4 + r) * WPITCH + (HH)];            \
+            const float4 w4 = *reinterpret_cast<const float4 *>(&Ws[(HH) * TQ + qg * 64 + 16 * m + 4 * g4]); \
+            const float wr[4] = {w4.x, w4.y, w4.z, w4.w};                               \
             _Pragma("unroll") for (int n = 0; n < 4; ++n) {                             \
                 const i32x8 Bn = i32x8{Bv[n][0], Bv[n][1], Bv[n][2], Bv[n][3], 0, 0, 0, 0}; \
                 const f32x4 c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(       \
