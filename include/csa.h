@@ -16,7 +16,8 @@
  *  - Every tensor pointer is a DEVICE pointer (hipMalloc'd or a torch tensor's
  *    data_ptr()). Tensors are row-major with the innermost dimension contiguous.
  *  - The caller owns every buffer, including outputs and workspaces. The library
- *    allocates no device memory and keeps no pointer after a call returns.
+ *    allocates no device memory and keeps no pointer after a call returns (the one
+ *    exception is the fixed device array behind csa_topk_noalloc, below).
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the null
  *    stream). Results are ready when that stream is synchronised.
  *  - Positions are 0-based absolute token positions. Compressed entry i of a
@@ -188,6 +189,25 @@ size_t csa_topk_workspace_bytes(int T, int64_t N, int k);
 int csa_topk(const float *scores, int T, int64_t N, int k,
              int32_t *topk_idxs, float *topk_vals,
              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * csa_topk_noalloc - csa_topk without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). It takes the same arguments as csa_topk minus the workspace and
+ * returns the same result (same kernels, bit-identical output).
+ *
+ * The chunk winners of the multi-level selection (rows longer than 32,768 scores) live in
+ * a device array inside the library, 16 MiB per GPU, allocated when the library's code is
+ * loaded on that GPU and held until the process ends; nothing is allocated per call. The
+ * call needs csa_topk_workspace_bytes(T, N, k) <= 16 MiB (e.g. T <= 64 rows of 262,144
+ * scores at k = 1,024); larger requests return CSA_EWORKSPACE and launch nothing.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on one GPU
+ * (different streams, or threads without ordering) race and must not be issued; calls
+ * ordered on one stream are safe. The array needs no clearing (each call writes what it
+ * reads).
+ */
+int csa_topk_noalloc(const float *scores, int T, int64_t N, int k,
+                     int32_t *topk_idxs, float *topk_vals, void *stream);
 
 /*
  * csa_topk_ids - csa_topk over per-query candidate lists: row t of scores [T][M] scores

@@ -20,7 +20,7 @@ F32, BF16, MXFP4 = 0, 1, 2
 STATUS = {0: "CSA_OK", 1: "CSA_EINVAL", 2: "CSA_EUNSUPPORTED", 3: "CSA_EWORKSPACE", 4: "CSA_EHIP"}
 EXPORTS = ("csa_compress", "csa_index_scores", "csa_index_rescore", "csa_quantize_mxfp4", "csa_rmsnorm_rope",
            "csa_topk_workspace_bytes",
-           "csa_topk", "csa_topk_ids",
+           "csa_topk", "csa_topk_noalloc", "csa_topk_ids",
            "csa_attn_workspace_bytes", "csa_sparse_attn", "hca_attn", "csa_status_str",
            "csa_last_error")
 
@@ -51,6 +51,7 @@ def lib() -> C.CDLL:
         L.csa_topk_workspace_bytes.argtypes = [i32, i64, i32]
         L.csa_topk_workspace_bytes.restype = sz
         L.csa_topk.argtypes = [P, i32, i64, i32, P, P, P, sz, P]
+        L.csa_topk_noalloc.argtypes = [P, i32, i64, i32, P, P, P]
         L.csa_attn_workspace_bytes.argtypes = [i32, i32, i32, i64]
         L.csa_attn_workspace_bytes.restype = sz
         L.csa_sparse_attn.argtypes = [P, P, P, P, i32, f32, P, P, i32, i32, P, P, P, i32,
@@ -58,7 +59,7 @@ def lib() -> C.CDLL:
         L.hca_attn.argtypes = [P, P, P, i32, f32, P, P, i32, i32, P, P, P, i32,
                                i32, i32, i64, i32, i32, i32, P, P, P, sz, P]
         for f in ("csa_compress", "csa_index_scores", "csa_index_rescore", "csa_quantize_mxfp4", "csa_rmsnorm_rope",
-                  "csa_topk",
+                  "csa_topk", "csa_topk_noalloc",
                   "csa_topk_ids", "csa_sparse_attn", "hca_attn"):
             getattr(L, f).restype = C.c_int
         L.csa_status_str.argtypes = [C.c_int]
@@ -195,6 +196,20 @@ def topk(scores, k, idx=None, vals=None, workspace=None, with_vals=False, stream
     rc = lib().csa_topk(_ptr(scores), T, N, k, _ptr(idx), _ptr(vals), _ptr(workspace), wsb,
                         _stream(stream))
     _check("csa_topk", rc)
+    return idx, vals
+
+
+def topk_noalloc(scores, k, idx=None, vals=None, with_vals=False, stream=None):
+    """csa_topk_noalloc -> (idx [T][k] int32 ascending, -1 padded; vals or None), using the
+    library's own device scratch instead of a workspace (the output tensors, when not given,
+    are still allocated here by torch)."""
+    T, N = scores.shape
+    if idx is None:
+        idx = torch.empty((T, k), dtype=torch.int32, device=scores.device)
+    if vals is None and with_vals:
+        vals = torch.empty((T, k), dtype=torch.float32, device=scores.device)
+    rc = lib().csa_topk_noalloc(_ptr(scores), T, N, k, _ptr(idx), _ptr(vals), _stream(stream))
+    _check("csa_topk_noalloc", rc)
     return idx, vals
 
 

@@ -169,6 +169,27 @@ int csa_topk(const float *scores, int T, int64_t N, int k, int32_t *topk_idxs, f
     return launch_topk(scores, nullptr, T, N, k, topk_idxs, topk_vals, workspace, workspace_bytes, (hipStream_t)stream);
 }
 
+int csa_topk_noalloc(const float *scores, int T, int64_t N, int k, int32_t *topk_idxs, float *topk_vals,
+                     void *stream) {
+    clear_error();
+    REQUIRE(T >= 0 && N >= 0, CSA_EINVAL, "csa_topk_noalloc: need T >= 0 and N >= 0");
+    REQUIRE(k > 0, CSA_EINVAL, "csa_topk_noalloc: k must be positive");
+    REQUIRE(k <= 4096, CSA_EUNSUPPORTED, "csa_topk_noalloc: k > 4096 is not built");
+    REQUIRE(N < ((int64_t)1 << 31), CSA_EUNSUPPORTED, "csa_topk_noalloc: N must fit int32 indices");
+    if (T == 0) return CSA_OK;
+    REQUIRE(topk_idxs && (scores || N == 0), CSA_EINVAL, "csa_topk_noalloc: NULL tensor");
+    const size_t need = topk_workspace_bytes(T, N, k);
+    REQUIRE(need <= topk_scratch_bytes(), CSA_EWORKSPACE,
+            "csa_topk_noalloc: T, N, k need " + std::to_string(need) + " bytes of scratch, more than the " +
+                std::to_string(topk_scratch_bytes()) + " the library holds; use csa_topk with a workspace");
+    void *ws = nullptr;
+    if (need > 0) {
+        const int rc = topk_scratch_ptr(&ws);
+        if (rc != CSA_OK) return rc;
+    }
+    return launch_topk(scores, nullptr, T, N, k, topk_idxs, topk_vals, ws, need, (hipStream_t)stream);
+}
+
 int csa_topk_ids(const float *scores, const int32_t *ids, int T, int64_t M, int k, int32_t *topk_idxs,
                  float *topk_vals, void *workspace, size_t workspace_bytes, void *stream) {
     clear_error();

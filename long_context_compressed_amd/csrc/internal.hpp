@@ -33,6 +33,10 @@ int launch_index_rescore(const void *qI, const float *w, const void *kI, const i
 // ids: NULL (position p of a row is entry p) or [T][N] entry ids of the row's positions
 int launch_topk(const float *scores, const int32_t *ids, int T, int64_t N, int k, int32_t *idx, float *vals,
                 void *ws, size_t ws_bytes, hipStream_t st);
+// the allocation-free top-k's file-scope device scratch: its size, and its device address
+// on the current device (looked up once per device)
+size_t topk_scratch_bytes();
+int topk_scratch_ptr(void **ptr);
 
 // Rows of one query: the first `k` slots come from topk_idxs (sparse mode) or from
 // the visible summaries 0..nvis-1 (dense mode, k < 0 selects it with ratio = -k),

@@ -23,6 +23,9 @@
 // order, padded with (-inf, -1)) form a shorter row that the same kernel reduces again
 // until one chunk remains. A row may come with an id per position (a candidate list):
 // the ids are what is written out.
+#include <mutex>
+#include <string>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -518,6 +521,41 @@ int launch_topk(const float *scores, const int32_t *ids, int T, int64_t N, int k
         flip ^= 1;
         first = false;
     }
+}
+
+}  // namespace csa
+
+// ======================================================================================
+// Allocation-free variant: the chunk winners of multi-level selection live in a
+// file-scope device array instead of a caller workspace. Every device the library runs on
+// holds its own copy of the array for the life of the process; its device address is
+// looked up once per device (with that device current) and kept here.
+// ======================================================================================
+namespace csa {
+
+constexpr size_t kTopkScratchBytes = size_t{16} << 20;
+static __device__ __align__(256) uint8_t scratch[kTopkScratchBytes];
+
+size_t topk_scratch_bytes() { return kTopkScratchBytes; }
+
+int topk_scratch_ptr(void **ptr) {
+    constexpr int kMaxDev = 64;
+    static std::mutex mu;
+    static void *cached[kMaxDev] = {};
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev)
+        return fail(CSA_EHIP, "csa_topk_noalloc: no current HIP device (or device id >= 64)");
+    std::lock_guard<std::mutex> lock(mu);
+    if (cached[dev] == nullptr) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr)
+            return fail(CSA_EHIP, std::string("csa_topk_noalloc: hipGetSymbolAddress(scratch): ") +
+                                      hipGetErrorString(e));
+        cached[dev] = p;
+    }
+    *ptr = cached[dev];
+    return CSA_OK;
 }
 
 }  // namespace csa

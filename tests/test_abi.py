@@ -87,6 +87,16 @@ def test_topk_validation(L):
     assert L.csa_topk(1, 0, 100, 10, None, None, None, 0, None) == 0
 
 
+def test_topk_noalloc_validation(L):
+    assert L.csa_topk_noalloc(1, 4, 100, 0, 1, None, None) == 1
+    assert L.csa_topk_noalloc(1, 4, 100, 5000, 1, None, None) == 2
+    assert L.csa_topk_noalloc(1, 4, 100, 10, None, None, None) == 1
+    assert L.csa_topk_noalloc(1, 0, 100, 10, None, None, None) == 0
+    # more chunk winners than the library's fixed 16 MiB scratch holds: refused up front
+    assert L.csa_topk_noalloc(1, 512, 262144, 1024, 1, None, None) == 3
+    assert b"scratch" in L.csa_last_error()
+
+
 def test_attn_validation(L):
     def f(**kw):
         a = dict(q=1, kv=1, sink=1, idx=1, k=4, scale=0.1, swa=1, p0=1, rows=8, win=128, qseq=1, qpos=1,
