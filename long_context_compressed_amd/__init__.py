@@ -97,6 +97,17 @@ def _check(fn, rc):
         raise CsaError(fn, rc, lib().csa_last_error().decode())
 
 
+def _require(cond, fn, msg):
+    """Host-side shape checks the C ABI cannot make (it sees pointers, not extents):
+    raised before anything is enqueued."""
+    if not cond:
+        raise ValueError(f"{fn}: {msg}")
+
+
+def _rope_rows(rope_cs):
+    return 0 if rope_cs is None else int(rope_cs.shape[0])
+
+
 # ---- the five calls ------------------------------------------------------------------
 
 def compress(C_a, Z_a, C_b=None, Z_b=None, carry_C_b=None, carry_Z_b=None, logit_bias=None,
@@ -169,8 +180,17 @@ def rmsnorm_rope(x, g, eps, rope_cs=None, rope_group=1, out=None, out_dtype=None
     (or [..][R]) fp32 (cos, sin) pairs. out may be x (same dtype) for the in-place form."""
     D = x.shape[-1]
     rows = x.numel() // D if D else 0
+    fn = "rmsnorm_rope"
+    _require(x.is_contiguous() and g.is_contiguous(), fn, "x and g must be contiguous")
+    _require(g.numel() == D, fn, f"g has {g.numel()} gains for rows of {D}")
+    if rope_cs is not None:
+        _require(rope_cs.is_contiguous() and rope_cs.dtype == torch.float32, fn, "rope_cs must be contiguous fp32")
+        _require(int(rope_group) >= 1 and _rope_rows(rope_cs) * int(rope_group) >= rows, fn,
+                 f"rope_cs has {_rope_rows(rope_cs)} angle rows; {rows} rows at rope_group={rope_group} need "
+                 f"{-(-rows // max(1, int(rope_group)))}")
     if out is None:
         out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
+    _require(out.is_contiguous() and out.numel() == x.numel(), fn, "out must be contiguous and as large as x")
     R = 0 if rope_cs is None else int(rope_cs.numel() // rope_cs.shape[0])
     rc = lib().csa_rmsnorm_rope(_ptr(x), _dt(x), rows, D, _ptr(g), float(eps), _ptr(rope_cs), R, int(rope_group),
                                 _ptr(out), _dt(out), _stream(stream))
@@ -235,6 +255,20 @@ def attn_workspace_bytes(T, H, D, max_rows) -> int:
     return int(lib().csa_attn_workspace_bytes(T, H, D, max_rows))
 
 
+def _check_attn_args(fn, q, kv, swa_kv, q_seq, q_pos, rope_cs, rope_dim):
+    T, H, D = q.shape
+    _require(q.is_contiguous() and kv.is_contiguous(), fn, "q and the key/value rows must be contiguous")
+    _require(kv.dim() == 3 and kv.shape[2] == D and kv.dtype == q.dtype, fn, "kv must be [B][N][D] in q's dtype")
+    _require(swa_kv is None or (swa_kv.is_contiguous() and swa_kv.shape[0] == kv.shape[0]
+                                and swa_kv.shape[2] == D), fn, "swa_kv must be a contiguous [B][rows][D] tensor")
+    _require(q_seq.numel() >= T and q_pos.numel() >= T, fn, "q_seq and q_pos need T entries")
+    if rope_cs is not None:
+        _require(rope_cs.is_contiguous() and rope_cs.dtype == torch.float32, fn, "rope_cs must be contiguous fp32")
+        _require(_rope_rows(rope_cs) >= T, fn, f"rope_cs has {_rope_rows(rope_cs)} rows for {T} queries")
+        _require(rope_cs.numel() // max(1, _rope_rows(rope_cs)) >= rope_dim, fn,
+                 f"rope_cs rows hold fewer than rope_dim = {rope_dim} values")
+
+
 def sparse_attn(q, kv, attn_sink, topk_idxs, softmax_scale, swa_kv, swa_pos0, window, q_seq, q_pos,
                 rope_cs=None, rope_dim=0, out=None, lse=None, workspace=None, with_lse=True, stream=None):
     """csa_sparse_attn -> (out [T][H][D], lse [T][H] or None)."""
@@ -242,6 +276,10 @@ def sparse_attn(q, kv, attn_sink, topk_idxs, softmax_scale, swa_kv, swa_pos0, wi
     B, N = kv.shape[0], kv.shape[1]
     k = topk_idxs.shape[1] if topk_idxs is not None else 0
     swa_rows = swa_kv.shape[1] if swa_kv is not None else 0
+    _check_attn_args("sparse_attn", q, kv, swa_kv, q_seq, q_pos, rope_cs, rope_dim)
+    _require(topk_idxs is None or (topk_idxs.is_contiguous() and topk_idxs.shape[0] == T
+                                   and topk_idxs.dtype == torch.int32), "sparse_attn",
+             "topk_idxs must be a contiguous int32 [T][k] tensor")
     if out is None:
         out = torch.empty_like(q)
     if lse is None and with_lse:
@@ -264,6 +302,7 @@ def hca_attn(q, summ, attn_sink, ratio, softmax_scale, swa_kv, swa_pos0, window,
     T, H, D = q.shape
     B, N = summ.shape[0], summ.shape[1]
     swa_rows = swa_kv.shape[1] if swa_kv is not None else 0
+    _check_attn_args("hca_attn", q, summ, swa_kv, q_seq, q_pos, rope_cs, rope_dim)
     if out is None:
         out = torch.empty_like(q)
     if lse is None and with_lse:

@@ -237,6 +237,8 @@ int csa_sparse_attn(const void *q, const void *kv, const float *attn_sink, const
     REQUIRE(k >= 0, CSA_EINVAL, "csa_sparse_attn: k must be >= 0");
     REQUIRE(k <= 4096, CSA_EUNSUPPORTED, "csa_sparse_attn: k > 4096 is not built");
     REQUIRE(std::isfinite(softmax_scale), CSA_EINVAL, "csa_sparse_attn: softmax_scale must be finite");
+    // the matrix-core kernels take the largest raw score as the largest logit
+    REQUIRE(softmax_scale > 0.f, CSA_EUNSUPPORTED, "csa_sparse_attn: softmax_scale must be positive");
     if (T == 0) return CSA_OK;
     REQUIRE(k == 0 || topk_idxs, CSA_EINVAL, "csa_sparse_attn: NULL topk_idxs");
     AttnArgs a{q, kv, attn_sink, topk_idxs, k, 0, softmax_scale, swa_kv, swa_pos0, swa_rows, window, q_seq, q_pos,
@@ -254,6 +256,7 @@ int hca_attn(const void *q, const void *summ, const float *attn_sink, int ratio,
     if (rc != CSA_OK) return rc;
     REQUIRE(ratio > 0, CSA_EINVAL, "hca_attn: ratio must be positive");
     REQUIRE(std::isfinite(softmax_scale), CSA_EINVAL, "hca_attn: softmax_scale must be finite");
+    REQUIRE(softmax_scale > 0.f, CSA_EUNSUPPORTED, "hca_attn: softmax_scale must be positive");
     if (T == 0) return CSA_OK;
     AttnArgs a{q, summ, attn_sink, nullptr, 0, ratio, softmax_scale, swa_kv, swa_pos0, swa_rows, window, q_seq,
                q_pos, rope_cs, rope_cs ? rope_dim : 0, T, B, N, H, D, dt, out, lse, workspace, workspace_bytes};

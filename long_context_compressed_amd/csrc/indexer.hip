@@ -278,30 +278,41 @@ index_shared_kernel(const bf16_t *__restrict__ qI, const float *__restrict__ w, 
 
 }  // namespace
 
+// Launches put queries on grid.y, which holds at most 65,535 rows: larger T goes out in
+// slices of queries (pointer offsets into the per-query tensors).
+constexpr int kMaxGridY = 65535;
+
 int launch_index_scores(const void *qI, const uint8_t *qs, const float *w, const void *kI,
                         const uint8_t *ks, const int32_t *q_seq, const int64_t *q_pos, int T,
                         int B, int64_t N, int k_heads, int ratio, csa_dtype dt, float *scores, hipStream_t st)
 {
     if (T == 0 || N == 0) return CSA_OK;
-    if (k_heads == 1) {  // shared keys (bf16; checked by the caller)
-        dim3 grid((unsigned)((N + 4 * 16 * SH_TPW - 1) / (4 * 16 * SH_TPW)), (unsigned)T);
-        hipLaunchKernelGGL(index_shared_kernel, grid, dim3(256), 0, st, (const bf16_t *)qI, w, (const bf16_t *)kI,
-                           q_seq, q_pos, B, N, ratio, scores);
-        return check_launch("index_shared_kernel");
-    }
     if (dt == CSA_MXFP4)
         return launch_index_mxfp4((const uint8_t *)qI, qs, w, (const uint8_t *)kI, ks, q_seq, q_pos, T, B, N,
                                   ratio, scores, st);
-    constexpr int EPW = 64;
-    dim3 grid((unsigned)((N + 4 * EPW - 1) / (4 * EPW)), (unsigned)T);
-    if (dt == CSA_BF16) {
-        hipLaunchKernelGGL((index_scan_kernel<bf16_t, EPW, false>), grid, dim3(256), 0, st, (const bf16_t *)qI, w,
-                           (const bf16_t *)kI, q_seq, q_pos, B, N, ratio, nullptr, N, scores);
-    } else {
-        hipLaunchKernelGGL((index_scan_kernel<float, EPW, false>), grid, dim3(256), 0, st, (const float *)qI, w,
-                           (const float *)kI, q_seq, q_pos, B, N, ratio, nullptr, N, scores);
+    const size_t qbytes = (dt == CSA_F32 ? 4 : 2) * (size_t)64 * 128;  // one query's q_I
+    for (int t0 = 0; t0 < T; t0 += kMaxGridY) {
+        const int tn = (T - t0 < kMaxGridY) ? T - t0 : kMaxGridY;
+        const void *q_t = (const char *)qI + (size_t)t0 * qbytes;
+        const float *w_t = w + (int64_t)t0 * 64;
+        float *s_t = scores + (int64_t)t0 * N;
+        if (k_heads == 1) {  // shared keys (bf16; checked by the caller)
+            dim3 grid((unsigned)((N + 4 * 16 * SH_TPW - 1) / (4 * 16 * SH_TPW)), (unsigned)tn);
+            hipLaunchKernelGGL(index_shared_kernel, grid, dim3(256), 0, st, (const bf16_t *)q_t, w_t,
+                               (const bf16_t *)kI, q_seq + t0, q_pos + t0, B, N, ratio, s_t);
+            continue;
+        }
+        constexpr int EPW = 64;
+        dim3 grid((unsigned)((N + 4 * EPW - 1) / (4 * EPW)), (unsigned)tn);
+        if (dt == CSA_BF16) {
+            hipLaunchKernelGGL((index_scan_kernel<bf16_t, EPW, false>), grid, dim3(256), 0, st, (const bf16_t *)q_t,
+                               w_t, (const bf16_t *)kI, q_seq + t0, q_pos + t0, B, N, ratio, nullptr, N, s_t);
+        } else {
+            hipLaunchKernelGGL((index_scan_kernel<float, EPW, false>), grid, dim3(256), 0, st, (const float *)q_t,
+                               w_t, (const float *)kI, q_seq + t0, q_pos + t0, B, N, ratio, nullptr, N, s_t);
+        }
     }
-    return check_launch("index_scan_kernel");
+    return check_launch(k_heads == 1 ? "index_shared_kernel" : "index_scan_kernel");
 }
 
 int launch_index_rescore(const void *qI, const float *w, const void *kI, const int32_t *cand, int M,
@@ -310,13 +321,21 @@ int launch_index_rescore(const void *qI, const float *w, const void *kI, const i
 {
     if (T == 0 || M == 0) return CSA_OK;
     constexpr int EPW = 64;
-    dim3 grid((unsigned)((M + 4 * EPW - 1) / (4 * EPW)), (unsigned)T);
-    if (dt == CSA_BF16) {
-        hipLaunchKernelGGL((index_scan_kernel<bf16_t, EPW, true>), grid, dim3(256), 0, st, (const bf16_t *)qI, w,
-                           (const bf16_t *)kI, q_seq, q_pos, B, N, ratio, cand, (int64_t)M, scores);
-    } else {
-        hipLaunchKernelGGL((index_scan_kernel<float, EPW, true>), grid, dim3(256), 0, st, (const float *)qI, w,
-                           (const float *)kI, q_seq, q_pos, B, N, ratio, cand, (int64_t)M, scores);
+    const size_t qbytes = (dt == CSA_F32 ? 4 : 2) * (size_t)64 * 128;
+    for (int t0 = 0; t0 < T; t0 += kMaxGridY) {
+        const int tn = (T - t0 < kMaxGridY) ? T - t0 : kMaxGridY;
+        const void *q_t = (const char *)qI + (size_t)t0 * qbytes;
+        const float *w_t = w + (int64_t)t0 * 64;
+        const int32_t *c_t = cand + (int64_t)t0 * M;
+        float *s_t = scores + (int64_t)t0 * M;
+        dim3 grid((unsigned)((M + 4 * EPW - 1) / (4 * EPW)), (unsigned)tn);
+        if (dt == CSA_BF16) {
+            hipLaunchKernelGGL((index_scan_kernel<bf16_t, EPW, true>), grid, dim3(256), 0, st, (const bf16_t *)q_t,
+                               w_t, (const bf16_t *)kI, q_seq + t0, q_pos + t0, B, N, ratio, c_t, (int64_t)M, s_t);
+        } else {
+            hipLaunchKernelGGL((index_scan_kernel<float, EPW, true>), grid, dim3(256), 0, st, (const float *)q_t,
+                               w_t, (const float *)kI, q_seq + t0, q_pos + t0, B, N, ratio, c_t, (int64_t)M, s_t);
+        }
     }
     return check_launch("index_scan_kernel");
 }

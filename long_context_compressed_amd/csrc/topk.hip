@@ -453,11 +453,17 @@ int first_chunk(int64_t N, int k, int cap) {
 int launch_select(const float *vin, const int32_t *iin, int64_t L, int k, int chunk, int64_t nch, int T, float *vo,
                   int32_t *io, int64_t out_ld, int out_slots, hipStream_t st) {
     const int64_t longest = L < chunk ? L : chunk;
-    const dim3 grid((unsigned)nch, (unsigned)T);
+    // rows go on grid.y (at most 65,535): more rows go out in slices, offset by whole rows
+    constexpr int kMaxGridY = 65535;
 #define CSA_TOPK_LAUNCH(RR, JJ)                                                                               \
     if (longest <= (RR) * (JJ)) {                                                                            \
-        hipLaunchKernelGGL((topk_select_kernel<RR, JJ>), grid, dim3(RR), 0, st, vin, iin, L, k, chunk, vo, io,  \
-                           out_ld, out_slots);                                                               \
+        for (int t0 = 0; t0 < T; t0 += kMaxGridY) {                                                          \
+            const int tn = (T - t0 < kMaxGridY) ? T - t0 : kMaxGridY;                                        \
+            hipLaunchKernelGGL((topk_select_kernel<RR, JJ>), dim3((unsigned)nch, (unsigned)tn), dim3(RR), 0, st, \
+                               vin + (int64_t)t0 * L, iin ? iin + (int64_t)t0 * L : nullptr, L, k, chunk,   \
+                               vo ? vo + (int64_t)t0 * out_ld : nullptr, io + (int64_t)t0 * out_ld, out_ld,  \
+                               out_slots);                                                                   \
+        }                                                                                                    \
         return check_launch("topk_select_kernel");                                                           \
     }
     if (nch * T >= 4 * (int64_t)device_cu_count()) {

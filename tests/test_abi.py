@@ -114,12 +114,15 @@ def test_attn_validation(L):
     assert f(idx=None) == 1
     assert f(p0=None) == 1
     assert f(scale=float("nan")) == 1
+    assert f(scale=0.0) == 2          # the matrix-core kernels assume a positive scale
+    assert f(scale=-0.1) == 2
     assert f(k=-1) == 1
     assert f(dt=2) == 1
     assert f(T=0) == 0
-    g = lambda **kw: L.hca_attn(1, 1, 1, kw.get("ratio", 128), C.c_float(0.1), 1, 1, 8, 128, 1, 1, None, 0,
-                                2, 1, 8, 8, 128, 0, 1, None, None, 0, None)
+    g = lambda **kw: L.hca_attn(1, 1, 1, kw.get("ratio", 128), C.c_float(kw.get("scale", 0.1)), 1, 1, 8, 128, 1,
+                                1, None, 0, 2, 1, 8, 8, 128, 0, 1, None, None, 0, None)
     assert g(ratio=0) == 1
+    assert g(scale=-1.0) == 2
 
 
 def test_quantize_mxfp4_validation(L):
@@ -167,3 +170,28 @@ def test_index_rescore_and_topk_ids_validation(L):
     assert L.csa_topk_ids(1, 1, 4, 100, 5000, 1, None, None, 0, None) == 2
     assert L.csa_topk_ids(1, None, 4, 100, 10, 1, None, None, 0, None) == 1
     assert L.csa_topk_ids(1, 1, 0, 100, 10, None, None, None, 0, None) == 0
+
+
+def test_binding_rejects_short_rope_tables_before_launch():
+    """The Python binding checks what the ABI cannot (table extents) and raises before any
+    call is made: CPU tensors here, so reaching a launch would fail differently."""
+    import torch
+    import long_context_compressed_amd as csa
+    x = torch.zeros((8, 4, 128), dtype=torch.bfloat16)
+    g = torch.ones(128)
+    with pytest.raises(ValueError, match="rope_group"):
+        csa.rmsnorm_rope(x, g, 1e-6, rope_cs=torch.zeros((2, 64)), rope_group=4)  # needs 8 angle rows
+    with pytest.raises(ValueError, match="gains"):
+        csa.rmsnorm_rope(x, torch.ones(64), 1e-6)
+    q = torch.zeros((3, 8, 128), dtype=torch.bfloat16)
+    kv = torch.zeros((1, 16, 128), dtype=torch.bfloat16)
+    idx = torch.zeros((3, 4), dtype=torch.int32)
+    seq = torch.zeros(3, dtype=torch.int32)
+    pos = torch.full((3,), 64, dtype=torch.int64)
+    sink = torch.zeros(8)
+    with pytest.raises(ValueError, match="rows for 3 queries"):
+        csa.sparse_attn(q, kv, sink, idx, 0.1, None, None, 0, seq, pos, torch.zeros((2, 64)), 64)
+    with pytest.raises(ValueError, match="rows for 3 queries"):
+        csa.hca_attn(q, kv, sink, 4, 0.1, None, None, 0, seq, pos, torch.zeros((2, 64)), 64)
+    with pytest.raises(ValueError, match="topk_idxs"):
+        csa.sparse_attn(q, kv, sink, idx[:2], 0.1, None, None, 0, seq, pos)

@@ -359,6 +359,11 @@ def _attn_inputs(seed, T, H, D, B, N, k, swa_rows, dt, pos, with_rope=True, bad_
     # SWA-only, many queries (the 32-heads-per-wavefront kernel), and fp32
     dict(T=256, H=128, D=512, B=1, N=600, k=0, swa=400, dt=torch.bfloat16, pos=None),
     dict(T=40, H=8, D=128, B=1, N=256, k=0, swa=1024, dt=torch.float32, pos=None),
+    # few queries, row-split form: 10 + 128 rows = 5 tiles over 3 splits of two row halves,
+    # so the last split's second half starts past the end of its rows
+    dict(T=2, H=128, D=512, B=2, N=900, k=10, swa=128, dt=torch.bfloat16, pos=[131072, 4000]),
+    # one query of 64 heads: 64 split units of 2 tiles each
+    dict(T=1, H=64, D=512, B=1, N=5000, k=4000, swa=128, dt=torch.bfloat16, pos=[40000]),
 ])
 def test_sparse_attn(csa, orc, case):
     c = dict(case)
@@ -527,3 +532,28 @@ def test_tiny_chain(csa, orc):
     same = np.array([set(idx[t].cpu().tolist()) == set(ridx[t].tolist()) for t in range(1024)])
     assert same.sum() >= 1024 - n_near_ties
     assert_rel(out, rout, TOL_F32, "chain attention", mask=same)
+
+
+def test_many_query_launches_past_grid_y(csa, orc):
+    """More queries than grid.y holds (70,000 > 65,535): the bf16 scan, the shared-key scan
+    and top-k go out in slices of queries. Rows on both sides of the slice boundary, and
+    the last rows, are checked against the oracle."""
+    T, N, k = 70000, 40, 8
+    s = 6565
+    qI = W.normal((T, 64, 128), s, "q", dtype=torch.bfloat16, device=DEV)
+    w = W.normal((T, 64), s, "w", device=DEV)
+    kI = W.normal((1, N, 64, 128), s, "k", dtype=torch.bfloat16, device=DEV)
+    kS = W.normal((1, N, 1, 128), s, "ks", dtype=torch.bfloat16, device=DEV)
+    q_seq = torch.zeros(T, dtype=torch.int32, device=DEV)
+    q_pos = (torch.arange(T, dtype=torch.int64, device=DEV) % (4 * N + 8))
+    sc = csa.index_scores(qI, w, kI, q_seq, q_pos)
+    scs = csa.index_scores(qI, w, kS, q_seq, q_pos)
+    idx, _ = csa.topk(sc, k)
+    torch.cuda.synchronize()
+    rows = torch.tensor(list(range(0, 8)) + list(range(65530, 65545)) + list(range(T - 8, T)), device=DEV)
+    sub = lambda x: x.index_select(0, rows)
+    ref = orc.index_scores(sub(qI), sub(w), kI, sub(q_seq), sub(q_pos))
+    assert_rel(sub(sc), ref, TOL_F32, "index bf16, sliced launch")
+    ref_s = orc.index_scores(sub(qI), sub(w), kS, sub(q_seq), sub(q_pos))
+    assert_rel(sub(scs), ref_s, TOL_F32, "index shared keys, sliced launch")
+    check_topk_sets(sub(idx), to_np(sub(sc)), k)
