@@ -40,6 +40,9 @@ def lib():
         P = C.c_void_p
         i32, i64, f64 = C.c_int, C.c_int64, C.c_double
         L.oracle_compress.argtypes = [P, P, P, P, P, P, P, i32, i64, i32, i32, i32, P]
+        L.oracle_matmul_nt.argtypes = [P, P, i64, i64, i64, P]
+        L.oracle_compress_hidden.argtypes = [P, P, P, P, i32, i64, i64, i32, i32, i32, P]
+        L.oracle_out_proj.argtypes = [P, i32, i32, i32, i32, P, i32, P, i32, P]
         L.oracle_index_scores.argtypes = [P, P, P, P, P, P, i32, i32, i64, i32, i32, i32, i32, P]
         L.oracle_mxfp4_decode.argtypes = [P, P, i64, P]
         L.oracle_mxfp4_encode.argtypes = [P, i64, i32, i32, P, P]
@@ -50,7 +53,7 @@ def lib():
                                          i32, i32, i64, i32, i32, P, P]
         L.oracle_hca_attn.argtypes = [P, P, P, i32, f64, P, P, i32, i32, P, P, P, i32,
                                       i32, i32, i64, i32, i32, P, P]
-        for f in ("oracle_compress", "oracle_index_scores", "oracle_mxfp4_decode", "oracle_mxfp4_encode",
+        for f in ("oracle_compress", "oracle_matmul_nt", "oracle_compress_hidden", "oracle_out_proj", "oracle_index_scores", "oracle_mxfp4_decode", "oracle_mxfp4_encode",
                   "oracle_hadamard", "oracle_topk", "oracle_rmsnorm_rope",
                   "oracle_sparse_attn", "oracle_hca_attn"):
             getattr(L, f).restype = C.c_int
@@ -107,6 +110,43 @@ def compress(C_a, Z_a, C_b=None, Z_b=None, carry_C_b=None, carry_Z_b=None, bias=
     rc = lib().oracle_compress(_p(Ca), _p(Cb), _p(Za), _p(Zb), _p(cCb), _p(cZb), _p(bi),
                                B, n, c, ratio, overlap, _p(out))
     _check(rc, "compress")
+    return out
+
+
+def matmul_nt(X, W):
+    """Y = X W^T (fp64): X [M][K], W [N][K]."""
+    Xa, Wa = _f64(X), _f64(W)
+    M, K = Xa.shape
+    N = Wa.shape[0]
+    Y = np.empty((M, N), dtype=np.float64)
+    _check(lib().oracle_matmul_nt(_p(Xa), _p(Wa), M, N, K, _p(Y)), "matmul_nt")
+    return Y
+
+
+def compress_hidden(H, W, carry_H=None, bias=None, ratio=4, overlap=1):
+    """Compressed entries [B][n//ratio][c] (fp64) of hidden rows H [B][n][d] through the
+    projections W [(1+overlap)*2][c][d] (W_Ca, W_Za, W_Cb, W_Zb)."""
+    Ha, Wa = _f64(H), _f64(W)
+    B, n, d = Ha.shape
+    c = Wa.shape[1]
+    cH, bi = _f64(carry_H), _f64(bias)
+    out = np.empty((B, n // ratio, c), dtype=np.float64)
+    rc = lib().oracle_compress_hidden(_p(Ha), _p(cH), _p(Wa), _p(bi), B, n, d, c, ratio, overlap, _p(out))
+    _check(rc, "compress_hidden")
+    return out
+
+
+def out_proj(o, W_a, W_b=None):
+    """Grouped output projection (fp64): o [T][H][D], W_a [G][d_g][(H/G)*D], W_b
+    [d_model][G*d_g] or None -> [T][d_model] (or [T][G*d_g])."""
+    oa, wa = _f64(o), _f64(W_a)
+    T, H, D = oa.shape
+    G, d_g, _ = wa.shape
+    wb = _f64(W_b)
+    width = wb.shape[0] if wb is not None else G * d_g
+    out = np.empty((T, width), dtype=np.float64)
+    rc = lib().oracle_out_proj(_p(oa), T, H, D, G, _p(wa), d_g, _p(wb), width if wb is not None else 0, _p(out))
+    _check(rc, "out_proj")
     return out
 
 

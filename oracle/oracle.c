@@ -17,6 +17,9 @@
  *   MXFP4 operands        the MXFP4 model-card page (one E8M0 scale per 32 E2M1 values)
  *   Hadamard rotation     the same page's Indexer section (q rotated before FP4 scoring)
  *   RMSNorm               §6, equation for RMSNorm(x) (Q and the compressed entries)
+ *   projections           §4.1 (C^a, C^b, Z^a, Z^b formed from the hidden state H), §7
+ *                         (Compressor.forward: project_a / project_b), §4.2 and §7
+ *                         (outputs aggregated per group and projected to the model width)
  *
  * Every sum, dot product and softmax is accumulated in double precision and each
  * logit vector is materialised before it is normalised.
@@ -31,7 +34,11 @@
  *  - a RoPE pair is the interleaved pair (D-R+2p, D-R+2p+1), rotated by (cos, sin)
  *    of the caller's table; the output is rotated back with (cos, -sin);
  *  - top-k ties are broken by the lower entry index; -INF scores are never taken;
- *  - RMSNorm of an all-zero row with eps = 0 (0/0) is read as a zero row.
+ *  - RMSNorm of an all-zero row with eps = 0 (0/0) is read as a zero row;
+ *  - a projection is a plain linear map y = W x with W stored [out][in];
+ *  - the grouped output projection: the H heads form G groups of H/G consecutive heads;
+ *    group g's concatenated head outputs are mapped by its own W_a[g] to d_g values, and
+ *    the G results side by side are mapped by W_b to the model width.
  */
 #include <math.h>
 #include <stdint.h>
@@ -107,6 +114,84 @@ int oracle_compress(const double *Ca, const double *Cb, const double *Za, const 
             free(val);
             free(has);
         }
+    }
+    return OR_OK;
+}
+
+/* ---------------------------------------------------------------------------------
+ * Projection Y = X W^T: Y[m][o] = sum_k X[m][k] W[o][k].  X: [M][K], W: [N][K], Y: [M][N].
+ * ------------------------------------------------------------------------------- */
+int oracle_matmul_nt(const double *X, const double *W, int64_t M, int64_t N, int64_t K, double *Y)
+{
+    if (M < 0 || N < 0 || K < 0) return OR_EINVAL;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t o = 0; o < N; ++o) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k) acc += X[m * K + k] * W[o * K + k];
+            Y[m * N + o] = acc;
+        }
+    return OR_OK;
+}
+
+/* ---------------------------------------------------------------------------------
+ * The compressor fed from hidden rows.  §4.1: C^a, C^b, Z^a, Z^b are formed from H;
+ * §7: Compressor.forward projects the hidden rows (project_a, and project_b for the
+ * overlapped ratio-4 compressor) and then pools.
+ *
+ * H: [B][n][d]; carry_H: [B][4][d] hidden rows before the chunk (ratio 4), or NULL;
+ * W: [(1+overlap)*2][c][d] in the order W_Ca, W_Za (, W_Cb, W_Zb); bias as oracle_compress.
+ * out: [B][n/ratio][c].
+ * ------------------------------------------------------------------------------- */
+int oracle_compress_hidden(const double *H, const double *carry_H, const double *W, const double *bias,
+                           int B, int64_t n, int64_t d, int c, int ratio, int overlap, double *out)
+{
+    if (B < 0 || n < 0 || d <= 0 || c <= 0 || ratio <= 0 || (overlap != 0 && overlap != 1)) return OR_EINVAL;
+    if (!overlap && carry_H) return OR_EINVAL;
+    const int np = 2 * (1 + overlap);
+    const int64_t plane = (int64_t)B * n * c;
+    double *P = (double *)malloc(sizeof(double) * (size_t)(plane > 0 ? plane : 1) * np);
+    double *cP = carry_H ? (double *)malloc(sizeof(double) * (size_t)B * ratio * c * 2) : NULL;
+    for (int p = 0; p < np; ++p)           /* every hidden row through every projection */
+        oracle_matmul_nt(H, W + (int64_t)p * c * d, (int64_t)B * n, c, d, P + (int64_t)p * plane);
+    if (carry_H)                           /* the b-branch of the carry rows */
+        for (int p = 0; p < 2; ++p)
+            oracle_matmul_nt(carry_H, W + (int64_t)(2 + p) * c * d, (int64_t)B * ratio, c, d,
+                             cP + (int64_t)p * B * ratio * c);
+    int rc = oracle_compress(P, overlap ? P + 2 * plane : NULL, P + plane, overlap ? P + 3 * plane : NULL,
+                             cP, cP ? cP + (int64_t)B * ratio * c : NULL, bias, B, n, c, ratio, overlap, out);
+    free(P);
+    free(cP);
+    return rc;
+}
+
+/* ---------------------------------------------------------------------------------
+ * Grouped output projection.  §4.2: the attention outputs are aggregated per group and
+ * projected back to the model width; §7: grouped_output_projection(inverse_rope(o)).
+ *
+ * o: [T][H][D] (already rotated back); Wa: [G][d_g][(H/G)*D]; Wb: [d_model][G*d_g] or NULL.
+ * out: [T][d_model], or [T][G*d_g] (the group results) when Wb is NULL.
+ * ------------------------------------------------------------------------------- */
+int oracle_out_proj(const double *o, int T, int H, int D, int G, const double *Wa, int d_g,
+                    const double *Wb, int d_model, double *out)
+{
+    if (T < 0 || H <= 0 || D <= 0 || G <= 0 || d_g <= 0 || H % G != 0 || (Wb && d_model <= 0)) return OR_EINVAL;
+    const int64_t K1 = (int64_t)(H / G) * D, GY = (int64_t)G * d_g;
+    double *y = Wb ? (double *)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1) * GY) : out;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int t = 0; t < T; ++t)
+        for (int g = 0; g < G; ++g) {
+            const double *x = o + (int64_t)t * H * D + (int64_t)g * K1;   /* group g's heads, side by side */
+            for (int e = 0; e < d_g; ++e) {
+                const double *wr = Wa + ((int64_t)g * d_g + e) * K1;
+                double acc = 0.0;
+                for (int64_t k = 0; k < K1; ++k) acc += wr[k] * x[k];
+                y[(int64_t)t * GY + (int64_t)g * d_g + e] = acc;
+            }
+        }
+    if (Wb) {
+        oracle_matmul_nt(y, Wb, T, d_model, GY, out);
+        free(y);
     }
     return OR_OK;
 }

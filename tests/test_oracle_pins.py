@@ -609,3 +609,71 @@ def test_rmsnorm_zero_row(orc):
     of 0 / 0)."""
     for eps in (0.0, 1e-6):
         np.testing.assert_array_equal(orc.rmsnorm_rope(np.zeros((2, 64)), np.ones(64), eps), 0.0)
+
+
+# ------------------------------------------------------------------------------------
+# Projections: §4.1 / §7 (the compressor's inputs formed from hidden rows) and §4.2 / §7
+# (grouped output projection back to the model width)
+# ------------------------------------------------------------------------------------
+
+def test_matmul_nt_is_numpy_matmul(orc):
+    X, Wm = _rand(7, 13), _rand(5, 13)
+    np.testing.assert_allclose(orc.matmul_nt(X, Wm), X @ Wm.T, rtol=1e-13, atol=1e-13)
+    # a zero-width contraction gives zeros
+    assert np.all(orc.matmul_nt(np.zeros((3, 0)), np.zeros((4, 0))) == 0)
+
+
+def test_compress_hidden_wiring(orc):
+    """The four projections (numpy matmul) feed the compressor in the order W_Ca, W_Za,
+    W_Cb, W_Zb, and the carry rows' b-projections become entry 0's previous block."""
+    B, n, d, c = 2, 14, 6, 3
+    H, W, cH = _rand(B, n, d), _rand(4, c, d, scale=0.5), _rand(B, 4, d)
+    P = [H @ W[p].T for p in range(4)]
+    ref = orc.compress(P[0], P[1], P[2], P[3], cH @ W[2].T, cH @ W[3].T, ratio=4, overlap=1)
+    np.testing.assert_allclose(orc.compress_hidden(H, W, cH), ref, rtol=1e-12, atol=1e-12)
+    ref0 = orc.compress(P[0], P[1], P[2], P[3], ratio=4, overlap=1)
+    np.testing.assert_allclose(orc.compress_hidden(H, W), ref0, rtol=1e-12, atol=1e-12)
+    assert orc.compress_hidden(H, W).shape == (B, n // 4, c)
+
+
+@pytest.mark.parametrize("ratio,overlap,carry", [(4, 1, True), (4, 1, False), (128, 0, False)])
+def test_compress_hidden_uniform_logits_is_mean_pooling(orc, ratio, overlap, carry):
+    """Closed form: W_C = identity on the first c hidden dims and W_Z = 0 make every logit
+    0, so each entry is the plain mean of its receptive field's hidden values: 8 rows (the
+    previous block's and its own) for ratio 4, 4 for entry 0 without a carry, 128 for HCA."""
+    B, c = 1, 5
+    n = 3 * ratio + 1
+    d = 8
+    H = _rand(B, n, d)
+    cH = _rand(B, 4, d) if carry else None
+    npj = 2 * (1 + overlap)
+    W = np.zeros((npj, c, d))
+    for p in range(0, npj, 2):
+        W[p, :, :c] = np.eye(c)
+    got = orc.compress_hidden(H, W, cH, ratio=ratio, overlap=overlap)
+    for i in range(n // ratio):
+        rows = H[0, i * ratio:(i + 1) * ratio, :c]
+        if overlap:
+            prev = H[0, (i - 1) * ratio:i * ratio, :c] if i >= 1 else (cH[0, :, :c] if carry else None)
+            if prev is not None:
+                rows = np.concatenate([prev, rows])
+        np.testing.assert_allclose(got[0, i], rows.mean(axis=0), rtol=1e-12, atol=1e-12)
+
+
+def test_out_proj_groups(orc):
+    """Each group's heads, side by side, through its own matrix (numpy per group); W_b maps
+    the G results to the model width; G = 1 is a plain two-layer projection; a change to
+    the heads of group g moves only group g's results."""
+    T, H, D, G, d_g, dm = 3, 6, 4, 3, 5, 7
+    o, Wa, Wb = _rand(T, H, D), _rand(G, d_g, (H // G) * D), _rand(dm, G * d_g)
+    y_ref = np.concatenate([o[:, g * (H // G):(g + 1) * (H // G)].reshape(T, -1) @ Wa[g].T for g in range(G)], axis=1)
+    y = orc.out_proj(o, Wa)
+    np.testing.assert_allclose(y, y_ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(orc.out_proj(o, Wa, Wb), y_ref @ Wb.T, rtol=1e-12, atol=1e-12)
+    Wa1 = _rand(1, d_g, H * D)
+    np.testing.assert_allclose(orc.out_proj(o, Wa1, Wb[:, :d_g]), (o.reshape(T, -1) @ Wa1[0].T) @ Wb[:, :d_g].T,
+                               rtol=1e-12, atol=1e-12)
+    o2 = o.copy()
+    o2[:, H // G:2 * (H // G)] += 1.0  # the heads of group 1
+    d = orc.out_proj(o2, Wa) - y
+    assert np.all(d[:, :d_g] == 0) and np.all(d[:, 2 * d_g:] == 0) and np.abs(d[:, d_g:2 * d_g]).max() > 0
