@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--workload", default="pro_decode_1m",
                     choices=["pro_decode_1m", "flash_decode_128k", "pro_decode_1m_shared_keys", "pro_decode_1m_mxfp4",
                              "pro_prefill_chunk",
-                             "hca_prefill_4k", "pro_prefill_q_norm_rope"],
+                             "hca_prefill_4k", "pro_prefill_q_norm_rope", "pro_prefill_projections"],
                     help="pro_decode_1m is the benchmark line; the others print the same record for "
                          "the other configurations' shapes (profiling aid)")
     ap.add_argument("--profile-copy", action="store_true",
@@ -89,6 +89,8 @@ def main():
         return prefill_main(a)
     if a.workload == "pro_prefill_q_norm_rope":
         return rownorm_main(a)
+    if a.workload == "pro_prefill_projections":
+        return projections_main(a)
     cfg = W.FLASH if a.workload == "flash_decode_128k" else W.PRO
     shared = a.workload == "pro_decode_1m_shared_keys"
     fp4 = a.workload == "pro_decode_1m_mxfp4"
@@ -337,6 +339,75 @@ def rownorm_main(a):
                      "algorithmic_bytes_per_launch": alg, "avg_launch_ms": round(avg * 1e3, 4),
                      "median_launch_ms": round(float(np.median(ms)), 4), "min_launch_ms": round(float(np.min(ms)), 4),
                      "torch_copy_same_rows_ms": round(copy_ms, 4)},
+    }
+    print(json.dumps(res), flush=True)
+
+
+def projections_main(a):
+    """The projections around the Pro prefill chunk's attention (profiling aid), both bf16
+    matrix-core GEMMs with fp32 sums:
+      compress_hidden: the KV compressor fed from the chunk's hidden rows, 8,192 tokens x
+        7,168 (the Pro hidden width) through four 7,168 -> 512 projections, pooled 4:1 in
+        the epilogue: 2 x 8,192 x 7,168 x 2,048 = 240.5 GFLOP;
+      out_proj: 8,192 tokens x 128 heads x 512 -> 16 groups of 1,024 -> 7,168 (group count
+        and width are synthetic choices; the pages give neither): 2 x 8,192 x 65,536 x
+        1,024 + 2 x 8,192 x 16,384 x 7,168 = 3.024 TFLOP.
+    Weights 0.05 N(0, 1), activations N(0, 1), bf16."""
+    import numpy as np
+    import torch
+
+    import long_context_compressed_amd as csa
+    import workloads as W
+
+    dev = "cuda"
+    n, d, c = 8192, 7168, 512
+    T, H, D, G, dg, dm = 8192, 128, 512, 16, 1024, 7168
+    s = 1004
+    hid = W.normal((1, n, d), s, "proj_hidden", dtype=torch.bfloat16, device=dev)
+    Wc = W.normal((4, c, d), s, "proj_Wc", scale=0.05, dtype=torch.bfloat16, device=dev)
+    cH = W.normal((1, 4, d), s, "proj_carry", dtype=torch.bfloat16, device=dev)
+    kvo = torch.empty((1, n // 4, c), dtype=torch.bfloat16, device=dev)
+    o = W.normal((T, H, D), s, "proj_o", dtype=torch.bfloat16, device=dev)
+    Wa = W.normal((G, dg, (H // G) * D), s, "proj_Wa", scale=0.05, dtype=torch.bfloat16, device=dev)
+    Wb = W.normal((dm, G * dg), s, "proj_Wb", scale=0.05, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(csa.out_proj_workspace_bytes(T, G, dg), dtype=torch.uint8, device=dev)
+    y = torch.empty((T, dm), dtype=torch.bfloat16, device=dev)
+    st = torch.cuda.current_stream()
+    stages = {"compress_hidden": (lambda: csa.compress_hidden(hid, Wc, cH, out=kvo, stream=st), 2.0 * n * d * 4 * c),
+              "out_proj": (lambda: csa.out_proj(o, Wa, Wb, out=y, workspace=ws, stream=st),
+                           2.0 * T * H * D * dg + 2.0 * T * G * dg * dm)}
+    for _ in range(a.warmup):
+        for f, _fl in stages.values():
+            f()
+    torch.cuda.synchronize()
+    ms = {k: [] for k in stages}
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        for k, (f, _fl) in stages.items():
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            f()
+            e1.record(st)
+            ms[k].append((e0, e1))
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    avg = {k: float(np.mean([e0.elapsed_time(e1) for e0, e1 in v])) for k, v in ms.items()}
+    lines = {k: {"avg_launch_ms": round(avg[k], 4), "tflops": round(fl / avg[k] / 1e9, 1),
+                 "frac_of_bf16_peak": round(fl / avg[k] / 1e9 / 2500.0, 4), "algorithmic_flops": fl}
+             for k, (_f, fl) in stages.items()}
+    fl_tot = sum(fl for _f, fl in stages.values())
+    ach = fl_tot / (sum(avg.values()) / 1e3) / 1e12
+    res = {
+        "metric": "prefill projection TFLOP/s, pro_prefill_projections (profiling line, not the benchmark)",
+        "value": round(T * a.steps / elapsed, 1), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(elapsed / a.steps * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": a.workload, "tokens": T, "hidden": d, "kv_dim": c, "heads": H, "head_dim": D,
+                   "groups": G, "group_width": dg},
+        "roofline": {"kernel": "gemm_bf16_kernel / compress_hidden_kernel", "bound": "mfma",
+                     "achieved": round(ach, 1), "peak": 2500.0, "unit": "TFLOP/s", "frac": round(ach / 2500.0, 4),
+                     "traffic": None, "algorithmic_flops_per_step": fl_tot},
+        "stages": lines,
     }
     print(json.dumps(res), flush=True)
 

@@ -79,6 +79,53 @@ int csa_compress(const void *C_a, const void *C_b, const void *Z_a, const void *
                  void *out, int64_t out_bstride, void *stream);
 
 /*
+ * csa_compress_hidden - the compressor fed from hidden states (§4.1: the compressor forms
+ * C^a, C^b, Z^a, Z^b from H; §7: Compressor.forward opens with project_a / project_b of
+ * the hidden rows): the projections and the pooling of csa_compress in one kernel.
+ *
+ *   C^a = H Wa_C^T, Z^a = H Wa_Z^T (and C^b = H Wb_C^T, Z^b = H Wb_Z^T for ratio 4),
+ *   then out = csa_compress(C^a, C^b, Z^a, Z^b, ...) on those values, computed in fp32:
+ *   the projected values are not rounded before the pooling, the output is rounded once.
+ *
+ * hidden:       [B][n][d] bf16 hidden rows of the chunk.
+ * carry_hidden: [B][4][d] bf16, the last 4 hidden rows before the chunk (their b-branch
+ *               feeds entry 0), or NULL (entry 0 then pools its own block's a-branch
+ *               alone). ratio 4 only.
+ * W:            bf16 [(1+overlap)*2][c][d]: the projections as [out][in] matrices, in the
+ *               order Wa_C, Wa_Z, Wb_C, Wb_Z (ratio 4) or Wa_C, Wa_Z (ratio 128).
+ * logit_bias:   as csa_compress, or NULL.
+ * out:          [B][n/ratio][c] in out_dt (F32 | BF16), batch stride out_bstride elements
+ *               (0: (n/ratio)*c); a trailing partial block is not compressed.
+ * Supported: (ratio, overlap) = (4, 1) or (128, 0); d % 32 == 0; n*d*2 and the weights
+ * each under 4 GiB. Errors as csa_compress.
+ */
+int csa_compress_hidden(const void *hidden, const void *carry_hidden, const void *W, const float *logit_bias,
+                        int B, int64_t n, int64_t d, int c, int ratio, int overlap, csa_dtype out_dt,
+                        void *out, int64_t out_bstride, void *stream);
+
+/*
+ * csa_out_proj - grouped output projection after the attention (§4.2: the outputs are
+ * aggregated per group and projected back to the model width; §7:
+ * grouped_output_projection(inverse_rope(output))). The H heads form G groups of H/G
+ * consecutive heads; group g's concatenated outputs are projected by its own matrix:
+ *   y[t][g] = W_a[g] . concat_h o[t][g*H/G + h]            ([d_g], fp32 sums, bf16 y)
+ * and, when W_b is given, the G results side by side are projected to the model width:
+ *   out[t] = W_b . y[t]                                    ([d_model])
+ * The inverse RoPE of §6/§7 comes first: csa_sparse_attn / hca_attn with rope_cs apply
+ * it to their output, so o is passed as those calls return it.
+ *
+ * o:     [T][H][D] bf16.           W_a: [G][d_g][(H/G)*D] bf16 ([out][in] per group).
+ * W_b:   [d_model][G*d_g] bf16, or NULL (then out = y, [T][G*d_g]).
+ * out:   [T][d_model] (or [T][G*d_g]) in out_dt (F32 | BF16).
+ * workspace: csa_out_proj_workspace_bytes(T, G, d_g) bytes for y (unused without W_b).
+ * Supported: (H/G)*D and G*d_g multiples of 32. T may be 0.
+ */
+size_t csa_out_proj_workspace_bytes(int T, int G, int d_g);
+int csa_out_proj(const void *o, int T, int H, int D, int G, const void *W_a, int d_g, const void *W_b,
+                 int d_model, csa_dtype out_dt, void *out, void *workspace, size_t workspace_bytes,
+                 void *stream);
+
+/*
  * csa_index_scores - Lightning Indexer (§4.2):
  *   scores[t][i] = sum_h w[t][h] * ReLU(<q_I[t][h], k_I[q_seq[t]][i][h]>)
  * for every stored entry i with (i+1)*ratio <= q_pos[t]; -INFINITY otherwise.

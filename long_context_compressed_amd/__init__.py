@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(_HERE, "libcsa.so")
 
 F32, BF16, MXFP4 = 0, 1, 2
 STATUS = {0: "CSA_OK", 1: "CSA_EINVAL", 2: "CSA_EUNSUPPORTED", 3: "CSA_EWORKSPACE", 4: "CSA_EHIP"}
-EXPORTS = ("csa_compress", "csa_index_scores", "csa_index_rescore", "csa_quantize_mxfp4", "csa_rmsnorm_rope",
+EXPORTS = ("csa_compress", "csa_compress_hidden", "csa_out_proj_workspace_bytes", "csa_out_proj",
+           "csa_index_scores", "csa_index_rescore", "csa_quantize_mxfp4", "csa_rmsnorm_rope",
            "csa_topk_workspace_bytes",
            "csa_topk", "csa_topk_noalloc", "csa_topk_ids",
            "csa_attn_workspace_bytes", "csa_sparse_attn", "hca_attn", "csa_status_str",
@@ -43,6 +44,10 @@ def lib() -> C.CDLL:
         L = C.CDLL(LIB_PATH)
         P, i32, i64, f32, sz = C.c_void_p, C.c_int, C.c_int64, C.c_float, C.c_size_t
         L.csa_compress.argtypes = [P, P, P, P, P, P, P, i32, i64, i32, i32, i32, i32, P, i64, P]
+        L.csa_compress_hidden.argtypes = [P, P, P, P, i32, i64, i64, i32, i32, i32, i32, P, i64, P]
+        L.csa_out_proj_workspace_bytes.argtypes = [i32, i32, i32]
+        L.csa_out_proj_workspace_bytes.restype = sz
+        L.csa_out_proj.argtypes = [P, i32, i32, i32, i32, P, i32, P, i32, i32, P, P, sz, P]
         L.csa_index_scores.argtypes = [P, P, P, P, P, P, P, i32, i32, i64, i32, i32, i32, i32, i32, P, P]
         L.csa_quantize_mxfp4.argtypes = [P, i64, i32, i32, i32, P, P, i64, i64, P]
         L.csa_rmsnorm_rope.argtypes = [P, i32, i64, i32, P, f32, P, i32, i64, P, i32, P]
@@ -58,7 +63,7 @@ def lib() -> C.CDLL:
                                       i32, i32, i64, i32, i32, i32, P, P, P, sz, P]
         L.hca_attn.argtypes = [P, P, P, i32, f32, P, P, i32, i32, P, P, P, i32,
                                i32, i32, i64, i32, i32, i32, P, P, P, sz, P]
-        for f in ("csa_compress", "csa_index_scores", "csa_index_rescore", "csa_quantize_mxfp4", "csa_rmsnorm_rope",
+        for f in ("csa_compress", "csa_compress_hidden", "csa_out_proj", "csa_index_scores", "csa_index_rescore", "csa_quantize_mxfp4", "csa_rmsnorm_rope",
                   "csa_topk", "csa_topk_noalloc",
                   "csa_topk_ids", "csa_sparse_attn", "hca_attn"):
             getattr(L, f).restype = C.c_int
@@ -122,6 +127,60 @@ def compress(C_a, Z_a, C_b=None, Z_b=None, carry_C_b=None, carry_Z_b=None, logit
                             _ptr(carry_Z_b), _ptr(logit_bias), B, n, c, ratio, overlap,
                             _dt(C_a), _ptr(out), bstride, _stream(stream))
     _check("csa_compress", rc)
+    return out
+
+
+def compress_hidden(hidden, W, carry_hidden=None, logit_bias=None, ratio=4, overlap=1, out=None,
+                    out_dtype=None, stream=None):
+    """csa_compress_hidden. hidden [B][n][d] bf16, W [(1+overlap)*2][c][d] bf16 (Wa_C, Wa_Z,
+    Wb_C, Wb_Z) -> out [B][n//ratio][c] (or a view with a larger batch stride)."""
+    B, n, d = hidden.shape
+    npj, c, d2 = W.shape
+    fn = "compress_hidden"
+    _require(hidden.dtype == torch.bfloat16 and W.dtype == torch.bfloat16, fn, "hidden and W must be bf16")
+    _require(hidden.is_contiguous() and W.is_contiguous(), fn, "hidden and W must be contiguous")
+    _require(d2 == d and npj == 2 * (1 + overlap), fn, f"W must be [{2 * (1 + overlap)}][c][{d}]")
+    _require(carry_hidden is None or (carry_hidden.is_contiguous() and tuple(carry_hidden.shape) == (B, 4, d)),
+             fn, "carry_hidden must be a contiguous [B][4][d] tensor")
+    if out is None:
+        out = torch.empty((B, n // ratio, c), dtype=out_dtype or torch.bfloat16, device=hidden.device)
+    _require(out.stride(-1) == 1 and out.shape[-1] == c, fn, "out rows must be contiguous [..][c]")
+    bstride = out.stride(0) if out.dim() == 3 else 0
+    rc = lib().csa_compress_hidden(_ptr(hidden), _ptr(carry_hidden), _ptr(W), _ptr(logit_bias), B, n, d, c, ratio,
+                                   overlap, _dt(out), _ptr(out), bstride, _stream(stream))
+    _check("csa_compress_hidden", rc)
+    return out
+
+
+def out_proj_workspace_bytes(T, G, d_g) -> int:
+    return int(lib().csa_out_proj_workspace_bytes(T, G, d_g))
+
+
+def out_proj(o, W_a, W_b=None, out=None, out_dtype=None, workspace=None, stream=None):
+    """csa_out_proj. o [T][H][D] bf16, W_a [G][d_g][(H/G)*D] bf16, W_b [d_model][G*d_g] bf16 or
+    None -> out [T][d_model] (or [T][G*d_g] without W_b)."""
+    T, H, D = o.shape
+    G, d_g, K1 = W_a.shape
+    fn = "out_proj"
+    _require(o.dtype == torch.bfloat16 and W_a.dtype == torch.bfloat16, fn, "o and W_a must be bf16")
+    _require(o.is_contiguous() and W_a.is_contiguous(), fn, "o and W_a must be contiguous")
+    _require(H % G == 0 and K1 == (H // G) * D, fn, f"W_a must be [G][d_g][{(H // max(G, 1)) * D}]")
+    d_model = 0
+    if W_b is not None:
+        _require(W_b.dtype == torch.bfloat16 and W_b.is_contiguous() and W_b.shape[1] == G * d_g, fn,
+                 f"W_b must be a contiguous bf16 [d_model][{G * d_g}] tensor")
+        d_model = W_b.shape[0]
+    width = d_model if W_b is not None else G * d_g
+    if out is None:
+        out = torch.empty((T, width), dtype=out_dtype or torch.bfloat16, device=o.device)
+    _require(out.is_contiguous() and tuple(out.shape) == (T, width), fn, f"out must be a contiguous [T][{width}]")
+    need = out_proj_workspace_bytes(T, G, d_g) if W_b is not None else 0
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=o.device)
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib().csa_out_proj(_ptr(o), T, H, D, G, _ptr(W_a), d_g, _ptr(W_b), d_model, _dt(out), _ptr(out),
+                            _ptr(workspace), wsb, _stream(stream))
+    _check("csa_out_proj", rc)
     return out
 
 

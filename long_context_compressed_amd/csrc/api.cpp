@@ -84,6 +84,62 @@ int csa_compress(const void *C_a, const void *C_b, const void *Z_a, const void *
                            logit_bias, B, n, c, ratio, overlap, dt, out, out_bstride, (hipStream_t)stream);
 }
 
+int csa_compress_hidden(const void *hidden, const void *carry_hidden, const void *W, const float *logit_bias, int B,
+                        int64_t n, int64_t d, int c, int ratio, int overlap, csa_dtype out_dt, void *out,
+                        int64_t out_bstride, void *stream) {
+    clear_error();
+    REQUIRE(B >= 0 && n >= 0 && d > 0 && c > 0, CSA_EINVAL, "csa_compress_hidden: need B >= 0, n >= 0, d > 0, c > 0");
+    REQUIRE(ratio > 0 && (overlap == 0 || overlap == 1), CSA_EINVAL,
+            "csa_compress_hidden: ratio > 0, overlap in {0,1}");
+    REQUIRE(out_dt == CSA_F32 || out_dt == CSA_BF16, CSA_EINVAL, "csa_compress_hidden: out_dt must be CSA_F32 or CSA_BF16");
+    REQUIRE((ratio == 4 && overlap == 1) || (ratio == 128 && overlap == 0), CSA_EUNSUPPORTED,
+            "csa_compress_hidden: supported (ratio, overlap) pairs are (4, 1) and (128, 0)");
+    REQUIRE(d % 32 == 0, CSA_EUNSUPPORTED, "csa_compress_hidden: d must be a multiple of 32");
+    REQUIRE(n * d * 2 < ((int64_t)1 << 32) - 64 && (int64_t)(2 + 2 * overlap) * c * d * 2 < ((int64_t)1 << 32) - 64,
+            CSA_EUNSUPPORTED, "csa_compress_hidden: one sequence's hidden rows and the weights must each stay under 4 GiB");
+    REQUIRE(overlap || carry_hidden == nullptr, CSA_EINVAL, "csa_compress_hidden: a carry needs overlap == 1");
+    const int64_t E = n / ratio;
+    REQUIRE(out_bstride == 0 || out_bstride >= E * c, CSA_EINVAL, "csa_compress_hidden: out_bstride < (n/ratio)*c");
+    if (B == 0 || E == 0) return CSA_OK;
+    REQUIRE(hidden && W && out, CSA_EINVAL, "csa_compress_hidden: hidden, W and out are required");
+    return launch_compress_hidden((const bf16_t *)hidden, (const bf16_t *)carry_hidden, (const bf16_t *)W, logit_bias,
+                                  B, n, d, c, ratio, out, out_dt == CSA_F32, out_bstride, (hipStream_t)stream);
+}
+
+size_t csa_out_proj_workspace_bytes(int T, int G, int d_g) {
+    if (T <= 0 || G <= 0 || d_g <= 0) return 0;
+    return (size_t)T * (size_t)G * (size_t)d_g * sizeof(uint16_t);
+}
+
+int csa_out_proj(const void *o, int T, int H, int D, int G, const void *W_a, int d_g, const void *W_b, int d_model,
+                 csa_dtype out_dt, void *out, void *workspace, size_t workspace_bytes, void *stream) {
+    clear_error();
+    REQUIRE(T >= 0 && H > 0 && D > 0 && G > 0 && d_g > 0, CSA_EINVAL, "csa_out_proj: need T >= 0 and H, D, G, d_g > 0");
+    REQUIRE(H % G == 0, CSA_EINVAL, "csa_out_proj: H must be a multiple of G");
+    REQUIRE(W_b == nullptr || d_model > 0, CSA_EINVAL, "csa_out_proj: d_model must be positive with W_b");
+    REQUIRE(out_dt == CSA_F32 || out_dt == CSA_BF16, CSA_EINVAL, "csa_out_proj: out_dt must be CSA_F32 or CSA_BF16");
+    const int64_t K1 = (int64_t)(H / G) * D, K2 = (int64_t)G * d_g;
+    REQUIRE(K1 % 32 == 0 && (W_b == nullptr || K2 % 32 == 0), CSA_EUNSUPPORTED,
+            "csa_out_proj: (H/G)*D and G*d_g must be multiples of 32");
+    REQUIRE(128 * (int64_t)H * D * 2 < ((int64_t)1 << 32) && (int64_t)d_g * K1 * 2 < ((int64_t)1 << 32) &&
+                (W_b == nullptr || (int64_t)d_model * K2 * 2 < ((int64_t)1 << 32)),
+            CSA_EUNSUPPORTED, "csa_out_proj: operand tiles must stay under 4 GiB");
+    if (T == 0) return CSA_OK;
+    REQUIRE(o && W_a && out, CSA_EINVAL, "csa_out_proj: o, W_a and out are required");
+    hipStream_t st = (hipStream_t)stream;
+    if (W_b == nullptr)  // the grouped stage alone: out [T][G * d_g]
+        return launch_gemm_bf16((const bf16_t *)o, (int64_t)H * D, K1, (const bf16_t *)W_a, K1, (int64_t)d_g * K1, out,
+                                K2, d_g, out_dt == CSA_F32, T, d_g, K1, G, st);
+    const size_t need = csa_out_proj_workspace_bytes(T, G, d_g);
+    REQUIRE(workspace && workspace_bytes >= need, CSA_EWORKSPACE,
+            "csa_out_proj: workspace smaller than csa_out_proj_workspace_bytes()");
+    int rc = launch_gemm_bf16((const bf16_t *)o, (int64_t)H * D, K1, (const bf16_t *)W_a, K1, (int64_t)d_g * K1,
+                              workspace, K2, d_g, false, T, d_g, K1, G, st);
+    if (rc != CSA_OK) return rc;
+    return launch_gemm_bf16((const bf16_t *)workspace, K2, 0, (const bf16_t *)W_b, K2, 0, out, d_model, 0,
+                            out_dt == CSA_F32, T, d_model, K2, 1, st);
+}
+
 int csa_index_scores(const void *q_I, const uint8_t *q_I_scale, const float *w, const void *k_I,
                      const uint8_t *k_I_scale, const int32_t *q_seq, const int64_t *q_pos, int T, int B,
                      int64_t N, int H_I, int D_I, int k_heads, int ratio, csa_dtype dt, float *scores,

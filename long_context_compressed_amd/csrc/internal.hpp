@@ -67,6 +67,15 @@ struct AttnArgs {
     size_t ws_bytes;
 };
 
+// bf16 matrix-core GEMMs (gemm.hip): C[z][m][n] = sum_k A[z][m][k] B[z][n][k], K % 32 == 0
+int launch_gemm_bf16(const bf16_t *A, int64_t lda, int64_t sA, const bf16_t *B, int64_t ldb, int64_t sB, void *C,
+                     int64_t ldc, int64_t sC, bool c_f32, int64_t M, int64_t N, int64_t K, int batch,
+                     hipStream_t st);
+// projection of hidden rows + compressor pooling in one kernel (ratio 4 overlapped, 128)
+int launch_compress_hidden(const bf16_t *Hs, const bf16_t *carry, const bf16_t *W, const float *bias, int B,
+                           int64_t n, int64_t d, int c, int ratio, void *out, bool out_f32, int64_t out_bstride,
+                           hipStream_t st);
+
 size_t attn_workspace_bytes(int T, int H, int D, int64_t max_rows);
 int launch_attn(const AttnArgs &a, hipStream_t st);
 bool wide_attn_ok(csa_dtype dt, int H, int D);
