@@ -41,6 +41,10 @@ def lib():
         i32, i64, f64 = C.c_int, C.c_int64, C.c_double
         L.oracle_compress.argtypes = [P, P, P, P, P, P, P, i32, i64, i32, i32, i32, P]
         L.oracle_matmul_nt.argtypes = [P, P, i64, i64, i64, P]
+        L.oracle_kv8_row_bytes.argtypes = [i32, i32]
+        L.oracle_kv8_encode.argtypes = [P, i64, i32, i32, P]
+        L.oracle_kv8_decode.argtypes = [P, i64, i32, i32, P]
+        L.oracle_e4m3_table.argtypes = [P]
         L.oracle_compress_hidden.argtypes = [P, P, P, P, i32, i64, i64, i32, i32, i32, P]
         L.oracle_out_proj.argtypes = [P, i32, i32, i32, i32, P, i32, P, i32, P]
         L.oracle_index_scores.argtypes = [P, P, P, P, P, P, i32, i32, i64, i32, i32, i32, i32, P]
@@ -53,7 +57,8 @@ def lib():
                                          i32, i32, i64, i32, i32, P, P]
         L.oracle_hca_attn.argtypes = [P, P, P, i32, f64, P, P, i32, i32, P, P, P, i32,
                                       i32, i32, i64, i32, i32, P, P]
-        for f in ("oracle_compress", "oracle_matmul_nt", "oracle_compress_hidden", "oracle_out_proj", "oracle_index_scores", "oracle_mxfp4_decode", "oracle_mxfp4_encode",
+        for f in ("oracle_kv8_row_bytes", "oracle_kv8_encode", "oracle_kv8_decode", "oracle_e4m3_table",
+                  "oracle_compress", "oracle_matmul_nt", "oracle_compress_hidden", "oracle_out_proj", "oracle_index_scores", "oracle_mxfp4_decode", "oracle_mxfp4_encode",
                   "oracle_hadamard", "oracle_topk", "oracle_rmsnorm_rope",
                   "oracle_sparse_attn", "oracle_hca_attn"):
             getattr(L, f).restype = C.c_int
@@ -110,6 +115,39 @@ def compress(C_a, Z_a, C_b=None, Z_b=None, carry_C_b=None, carry_Z_b=None, bias=
     rc = lib().oracle_compress(_p(Ca), _p(Cb), _p(Za), _p(Zb), _p(cCb), _p(cZb), _p(bi),
                                B, n, c, ratio, overlap, _p(out))
     _check(rc, "compress")
+    return out
+
+
+def kv8_row_bytes(D=512, R=64):
+    n = lib().oracle_kv8_row_bytes(D, R)
+    if n < 0:
+        raise ValueError("kv8: D - R must be a non-negative multiple of 32")
+    return n
+
+
+def kv8_encode(x, R=64):
+    """Rows x [..., D] (taken as fp32) -> uint8 [..., kv8_row_bytes(D, R)]: MXFP8 (E4M3 +
+    E8M0 per 32) for dims 0..D-R-1, bf16 for the last R dims."""
+    xa = _arr(x, np.float32)
+    D = xa.shape[-1]
+    rows = xa.size // D if D else 0
+    out = np.zeros(xa.shape[:-1] + (kv8_row_bytes(D, R),), dtype=np.uint8)
+    _check(lib().oracle_kv8_encode(_p(xa), rows, D, R, _p(out)), "kv8_encode")
+    return out
+
+
+def kv8_decode(rows, D=512, R=64):
+    """uint8 rows [..., kv8_row_bytes(D, R)] -> fp64 [..., D]."""
+    ra = _arr(rows, np.uint8)
+    n = ra.size // kv8_row_bytes(D, R)
+    out = np.empty(ra.shape[:-1] + (D,), dtype=np.float64)
+    _check(lib().oracle_kv8_decode(_p(ra), n, D, R, _p(out)), "kv8_decode")
+    return out
+
+
+def e4m3_table():
+    out = np.empty(256, dtype=np.float64)
+    _check(lib().oracle_e4m3_table(_p(out)), "e4m3_table")
     return out
 
 

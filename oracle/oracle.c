@@ -17,6 +17,7 @@
  *   MXFP4 operands        the MXFP4 model-card page (one E8M0 scale per 32 E2M1 values)
  *   Hadamard rotation     the same page's Indexer section (q rotated before FP4 scoring)
  *   RMSNorm               §6, equation for RMSNorm(x) (Q and the compressed entries)
+ *   FP8 KV storage        §4.2 last paragraph (RoPE dims BF16, the rest FP8)
  *   projections           §4.1 (C^a, C^b, Z^a, Z^b formed from the hidden state H), §7
  *                         (Compressor.forward: project_a / project_b), §4.2 and §7
  *                         (outputs aggregated per group and projected to the model width)
@@ -230,6 +231,115 @@ int oracle_index_scores(const double *qI, const double *w, const double *kI,
             scores[(int64_t)t * N + i] = sc;
         }
     }
+    return OR_OK;
+}
+
+/* ---------------------------------------------------------------------------------
+ * Compressed-KV storage format.  §4.2 (last paragraph): the RoPE-related dims of the
+ * compressed representation are kept in BF16 and the rest is stored in FP8. Read here as
+ * the OCP Microscaling v1.0 MXFP8 form for the non-RoPE dims: E4M3 elements (bias 7,
+ * largest finite 448, S.1111.111 is NaN) sharing one E8M0 scale per 32 elements; the last
+ * R dims as bf16 (round to nearest even).
+ *
+ * Row of D dims with R RoPE dims (D - R a multiple of 32), in bytes:
+ *   [0, D-R)              E4M3 codes of dims 0 .. D-R-1
+ *   [D-R, D+R)            bf16 of dims D-R .. D-1 (little endian)
+ *   [D+R, D+R+(D-R)/32)   E8M0 scales (value 2^(s-127)), one per 32 codes
+ *   padding to a multiple of 16 bytes (zeros)
+ * D = 512, R = 64: 448 + 128 + 14 (+2) = 592 bytes, against 1,024 in bf16.
+ *
+ * Encoding of a block of 32 (x as fp32): e = floor(log2(amax)) - 8 (8 = the largest E4M3
+ * exponent), clamped to [-127, 127], -127 for an all-zero block; each element becomes the
+ * finite E4M3 value nearest to |x| / 2^e (ties to the even code; beyond 448 saturates to
+ * 448) with the sign of x unless the code is 0.
+ * ------------------------------------------------------------------------------- */
+static double or_e4m3(int code)
+{
+    const int e = (code >> 3) & 15, m = code & 7;
+    if (e == 15 && m == 7) return NAN;
+    const double v = (e == 0) ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, e - 7);
+    return (code & 0x80) ? -v : v;
+}
+
+int oracle_kv8_row_bytes(int D, int R)
+{
+    if (D <= 0 || R < 0 || R > D || (D - R) % 32) return -1;
+    const int raw = (D - R) + 2 * R + (D - R) / 32;
+    return (raw + 15) / 16 * 16;
+}
+
+static uint16_t or_bf16_rne(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7f800000u) == 0x7f800000u) return (uint16_t)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+int oracle_kv8_encode(const float *x, int64_t rows, int D, int R, uint8_t *out)
+{
+    const int rb = oracle_kv8_row_bytes(D, R);
+    if (rb < 0) return OR_EINVAL;
+    const int nq = D - R;
+    for (int64_t r = 0; r < rows; ++r) {
+        const float *xr = x + r * D;
+        uint8_t *o = out + r * rb;
+        memset(o, 0, (size_t)rb);
+        for (int b = 0; b < nq / 32; ++b) {
+            double amax = 0.0;
+            for (int i = 32 * b; i < 32 * b + 32; ++i)
+                if (fabs((double)xr[i]) > amax) amax = fabs((double)xr[i]);
+            int e = (amax > 0.0) ? (int)floor(log2(amax)) - 8 : -127;
+            if (e < -127) e = -127;
+            if (e > 127) e = 127;
+            o[nq + 2 * R + b] = (uint8_t)(e + 127);
+            for (int i = 32 * b; i < 32 * b + 32; ++i) {
+                const double v = fabs((double)xr[i]) / ldexp(1.0, e);
+                int best = 0;
+                for (int c = 1; c < 127; ++c) {  /* the finite non-negative codes */
+                    const double dc = fabs(v - or_e4m3(c)), db = fabs(v - or_e4m3(best));
+                    if (dc < db || (dc == db && (c % 2 == 0) && (best % 2 != 0))) best = c;
+                }
+                o[i] = (uint8_t)((xr[i] < 0.0f && best != 0) ? (best | 0x80) : best);
+            }
+        }
+        for (int i = 0; i < R; ++i) {
+            const uint16_t h = or_bf16_rne(xr[nq + i]);
+            o[nq + 2 * i] = (uint8_t)(h & 0xff);
+            o[nq + 2 * i + 1] = (uint8_t)(h >> 8);
+        }
+    }
+    return OR_OK;
+}
+
+int oracle_kv8_decode(const uint8_t *rows, int64_t nrows, int D, int R, double *out)
+{
+    const int rb = oracle_kv8_row_bytes(D, R);
+    if (rb < 0) return OR_EINVAL;
+    const int nq = D - R;
+    for (int64_t r = 0; r < nrows; ++r) {
+        const uint8_t *o = rows + r * rb;
+        double *y = out + r * D;
+        for (int i = 0; i < nq; ++i) {
+            const uint8_t sc = o[nq + 2 * R + i / 32];
+            y[i] = (sc == 255) ? NAN : or_e4m3(o[i]) * ldexp(1.0, (int)sc - 127);
+        }
+        for (int i = 0; i < R; ++i) {
+            const uint32_t h = (uint32_t)o[nq + 2 * i] | ((uint32_t)o[nq + 2 * i + 1] << 8);
+            const uint32_t u = h << 16;
+            float f;
+            memcpy(&f, &u, 4);
+            y[nq + i] = f;
+        }
+    }
+    return OR_OK;
+}
+
+/* the E4M3 value of each code (closed form above), for the pins */
+int oracle_e4m3_table(double *out256)
+{
+    for (int c = 0; c < 256; ++c) out256[c] = or_e4m3(c);
     return OR_OK;
 }
 

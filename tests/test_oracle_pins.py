@@ -677,3 +677,65 @@ def test_out_proj_groups(orc):
     o2[:, H // G:2 * (H // G)] += 1.0  # the heads of group 1
     d = orc.out_proj(o2, Wa) - y
     assert np.all(d[:, :d_g] == 0) and np.all(d[:, 2 * d_g:] == 0) and np.abs(d[:, d_g:2 * d_g]).max() > 0
+
+
+# ------------------------------------------------------------------------------------
+# Compressed-KV storage, §4.2 last paragraph (RoPE dims BF16, the rest FP8), read as
+# OCP MX v1.0 MXFP8: E4M3 elements with one E8M0 scale per 32
+# ------------------------------------------------------------------------------------
+
+def test_e4m3_all_codes_against_torch_and_spec(orc):
+    """All 256 codes: torch's own float8_e4m3fn (an independent implementation of the OCP
+    format) gives the same values; the spec's extremes: 448 largest finite, 2^-6 smallest
+    normal, 2^-9 smallest subnormal, S.1111.111 NaN."""
+    t = orc.e4m3_table()
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(t), np.isnan(ref)) and np.isnan(t[0x7F]) and np.isnan(t[0xFF])
+    fin = ~np.isnan(ref)
+    assert np.array_equal(t[fin], ref[fin])
+    assert t[0x7E] == 448.0 and t[0x08] == 2.0 ** -6 and t[0x01] == 2.0 ** -9 and t[0x80] == 0.0
+
+
+def test_kv8_layout_and_roundtrip(orc):
+    assert orc.kv8_row_bytes(512, 64) == 592  # 448 codes + 128 bytes of bf16 + 14 scales + 2 pad
+    rng2 = np.random.default_rng(7)
+    # values on the grid: codes times a per-block power of two come back exactly when the
+    # block's largest code is 448 (code 126), so that the block exponent picked by the
+    # floor(log2 amax) - 8 rule is that power of two (with a smaller maximum, an amax whose
+    # mantissa exceeds 1.75 would saturate: the MX rule clips there)
+    codes = rng2.integers(0, 127, size=(3, 448))
+    codes[:, ::32] = 126
+    sign = rng2.choice([-1.0, 1.0], size=(3, 448))
+    exps = rng2.integers(-20, 10, size=(3, 14))
+    tab = orc.e4m3_table()
+    x = np.zeros((3, 512), np.float32)
+    x[:, :448] = (sign * tab[codes] * np.repeat(2.0 ** exps, 32, axis=1)).astype(np.float32)
+    x[:, 448:] = torch.randn(3, 64).to(torch.bfloat16).float().numpy()  # bf16-exact rope dims
+    y = orc.kv8_decode(orc.kv8_encode(x))
+    np.testing.assert_array_equal(y, x.astype(np.float64))
+
+
+def test_kv8_block_scale_rule_saturation_and_rne(orc):
+    """Scale exponent floor(log2 amax) - 8 per block of 32; values beyond 448 * scale
+    saturate; in-range elements round to nearest even exactly as torch's float8 cast; the
+    RoPE dims are the bf16 round-to-nearest-even of the input."""
+    x = np.zeros((1, 512), np.float32)
+    x[0, 0] = 500.0                      # block 0: amax 500 -> e = 8 - 8 = 0 -> saturates to 448
+    x[0, 1] = 0.75
+    x[0, 32] = 3.0e-3                    # block 1: amax 0.003 -> e = -9 - 8 = -17
+    x[0, 33] = -1.0e-3
+    blk = np.random.default_rng(8).standard_normal(32).astype(np.float32) * 7
+    x[0, 64:96] = blk                    # block 2: random values
+    x[0, 448:] = np.linspace(-3, 3, 64, dtype=np.float32) + np.float32(1e-3)
+    enc = orc.kv8_encode(x)
+    sc = enc[0, 576:590].astype(int) - 127
+    assert sc[0] == 0 and sc[1] == -17 and sc[2] == int(np.floor(np.log2(np.abs(blk).max()))) - 8
+    assert sc[3] == -127                 # an all-zero block
+    dec = orc.kv8_decode(enc)
+    assert dec[0, 0] == 448.0 and dec[0, 1] == 0.75
+    for b, lo in ((1, 32), (2, 64)):
+        xs = torch.from_numpy(x[0, lo:lo + 32].astype(np.float64) / 2.0 ** sc[b]).to(torch.float32)
+        ref = xs.to(torch.float8_e4m3fn).to(torch.float64).numpy() * 2.0 ** sc[b]
+        np.testing.assert_array_equal(dec[0, lo:lo + 32], ref)
+    ref_rope = torch.from_numpy(x[0, 448:]).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(dec[0, 448:], ref_rope)
