@@ -42,6 +42,7 @@ def parse():
                     help="index entries per query in the oracle's bounded sample")
     ap.add_argument("--workload", default="pro_decode_1m",
                     choices=["pro_decode_1m", "flash_decode_128k", "pro_decode_1m_shared_keys", "pro_decode_1m_mxfp4",
+                             "pro_decode_1m_kv8",
                              "pro_prefill_chunk",
                              "hca_prefill_4k", "pro_prefill_q_norm_rope", "pro_prefill_projections"],
                     help="pro_decode_1m is the benchmark line; the others print the same record for "
@@ -94,11 +95,12 @@ def main():
     cfg = W.FLASH if a.workload == "flash_decode_128k" else W.PRO
     shared = a.workload == "pro_decode_1m_shared_keys"
     fp4 = a.workload == "pro_decode_1m_mxfp4"
+    kv8 = a.workload == "pro_decode_1m_kv8"  # compressed KV and summaries in the FP8 storage format
     B, T, n, N, D, H, k = cfg.B, cfg.T, cfg.n, cfg.N, cfg.c, cfg.H, cfg.k
     NH = cfg.n // 128  # HCA summaries (8,192 at 2^20 tokens)
 
     # ---- inputs (HBM-resident) and the step's buffers -----------------------------------
-    inp = W.decode_step_inputs(cfg, dev, shared_keys=shared, mxfp4=fp4)
+    inp = W.decode_step_inputs(cfg, dev, shared_keys=shared, mxfp4=fp4, kv8=kv8)
     step = pipeline.DecodeStep(inp, k, cfg.window, cfg.rope_dim, cfg.scale)
     torch.cuda.synchronize()
 
@@ -175,7 +177,8 @@ def main():
                          f"t={n}; {N:,} entries x {'1 shared' if shared else '64 per-head'} x 128 "
                          f"{'MXFP4 (Hadamard-rotated)' if fp4 else 'bf16'} index keys "
                          f"per sequence, top-k {k:,}, "
-                         f"{H} heads x {D} shared KV, SWA {cfg.window}, {NH:,} HCA summaries"),
+                         f"{H} heads x {D} shared KV{' (FP8 rows, 592 B)' if kv8 else ''}, SWA {cfg.window}, "
+                         f"{NH:,} HCA summaries"),
             "batch": B, "context": n, "index_entries": N, "topk": k, "heads": H, "head_dim": D,
         },
         "roofline": {

@@ -42,7 +42,9 @@
 extern "C" {
 #endif
 
-typedef enum { CSA_F32 = 0, CSA_BF16 = 1, CSA_MXFP4 = 2 } csa_dtype;
+/* CSA_KV8: compressed KV rows in the FP8 storage format of csa_quantize_kv8 (the other
+ * tensors of the call are bf16); accepted by csa_sparse_attn and hca_attn for kv / summ. */
+typedef enum { CSA_F32 = 0, CSA_BF16 = 1, CSA_MXFP4 = 2, CSA_KV8 = 3 } csa_dtype;
 
 typedef enum {
     CSA_OK = 0,
@@ -195,6 +197,29 @@ int csa_quantize_mxfp4(const void *x, int64_t rows, int D, csa_dtype dt, int had
                        int64_t out_group_stride, void *stream);
 
 /*
+ * csa_quantize_kv8 - FP8 storage of compressed KV rows ("DeepSeek-V4 混合注意力" §4.2, last
+ * paragraph: the RoPE-related dims of the compressed representation are kept in BF16 and
+ * the rest is stored in FP8). Read as the OCP Microscaling v1.0 MXFP8 form for the non-RoPE
+ * dims. A row of 512 dims (the last 64 the RoPE dims) becomes 592 bytes:
+ *   bytes [0, 448)    E4M3 codes of dims 0..447 (OCP E4M3: bias 7, largest finite 448)
+ *   bytes [448, 576)  dims 448..511 as bf16 (round to nearest even), little endian
+ *   bytes [576, 590)  E8M0 scales, one per 32 codes (value 2^(s - 127))
+ *   bytes [590, 592)  zero
+ * Per block of 32: e = floor(log2(max |x|)) - 8, clamped to [-127, 127] (-127 for an
+ * all-zero block); each code is the finite E4M3 value nearest to |x| / 2^e (ties to the
+ * even code, everything above 448 becomes 448) with the sign of x unless it is 0. A row
+ * decodes to code * 2^(e) for dims 0..447 and the bf16 values for 448..511.
+ *
+ * x:      [rows][512] in dt (CSA_F32 | CSA_BF16).
+ * out:    [rows][592] bytes; with out_group_rows > 0, input row r goes to output row
+ *         (r / out_group_rows) * out_group_stride + r % out_group_rows (e.g. one new entry
+ *         per sequence into a [B][N][592] cache: out_group_rows = 1, out_group_stride = N).
+ * Supported: rows >= 0 (0 launches nothing). x and out 16-byte aligned.
+ */
+int csa_quantize_kv8(const void *x, int64_t rows, csa_dtype dt, uint8_t *out, int64_t out_group_rows,
+                     int64_t out_group_stride, void *stream);
+
+/*
  * csa_rmsnorm_rope - RMSNorm of each row, then RoPE on its last R dims: the normalisation
  * that "DeepSeek-V4 混合注意力" §6 applies to the queries and to the compressed
  * representation (RMSNorm(x) = x / sqrt(mean(x^2) + eps) times a per-dim gain g), and the
@@ -288,7 +313,9 @@ int csa_topk_ids(const float *scores, const int32_t *ids, int T, int64_t M, int 
  * swa_kv: [B][swa_rows][D] dt or NULL (then window is ignored); swa_pos0: [B] int64;
  * rope_cs: [T][rope_dim/2][2] fp32 or NULL (rope_dim ignored); out: [T][H][D] dt;
  * lse: [T][H] fp32 or NULL; workspace: csa_attn_workspace_bytes(...) bytes.
- * Supported: dt F32 | BF16, D <= 1024, D % 64 == 0, rope_dim even and <= D, 0 <= k <= 4096.
+ * Supported: dt F32 | BF16, D <= 1024, D % 64 == 0, rope_dim even and <= D, 0 <= k <= 4096;
+ * dt = CSA_KV8: kv rows [B][N][592] bytes in the format of csa_quantize_kv8 (q, swa_kv and
+ * out bf16), D = 512 and H a multiple of 64.
  */
 size_t csa_attn_workspace_bytes(int T, int H, int D, int64_t max_rows);
 int csa_sparse_attn(const void *q, const void *kv, const float *attn_sink,

@@ -16,9 +16,10 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcsa.so")
 
-F32, BF16, MXFP4 = 0, 1, 2
+F32, BF16, MXFP4, KV8 = 0, 1, 2, 3
+KV8_ROW_BYTES = 592  # one 512-dim compressed row in the FP8 storage format
 STATUS = {0: "CSA_OK", 1: "CSA_EINVAL", 2: "CSA_EUNSUPPORTED", 3: "CSA_EWORKSPACE", 4: "CSA_EHIP"}
-EXPORTS = ("csa_compress", "csa_compress_hidden", "csa_out_proj_workspace_bytes", "csa_out_proj",
+EXPORTS = ("csa_compress", "csa_compress_hidden", "csa_quantize_kv8", "csa_out_proj_workspace_bytes", "csa_out_proj",
            "csa_index_scores", "csa_index_rescore", "csa_quantize_mxfp4", "csa_rmsnorm_rope",
            "csa_topk_workspace_bytes",
            "csa_topk", "csa_topk_noalloc", "csa_topk_ids",
@@ -44,6 +45,7 @@ def lib() -> C.CDLL:
         L = C.CDLL(LIB_PATH)
         P, i32, i64, f32, sz = C.c_void_p, C.c_int, C.c_int64, C.c_float, C.c_size_t
         L.csa_compress.argtypes = [P, P, P, P, P, P, P, i32, i64, i32, i32, i32, i32, P, i64, P]
+        L.csa_quantize_kv8.argtypes = [P, i64, i32, P, i64, i64, P]
         L.csa_compress_hidden.argtypes = [P, P, P, P, i32, i64, i64, i32, i32, i32, i32, P, i64, P]
         L.csa_out_proj_workspace_bytes.argtypes = [i32, i32, i32]
         L.csa_out_proj_workspace_bytes.restype = sz
@@ -63,7 +65,7 @@ def lib() -> C.CDLL:
                                       i32, i32, i64, i32, i32, i32, P, P, P, sz, P]
         L.hca_attn.argtypes = [P, P, P, i32, f32, P, P, i32, i32, P, P, P, i32,
                                i32, i32, i64, i32, i32, i32, P, P, P, sz, P]
-        for f in ("csa_compress", "csa_compress_hidden", "csa_out_proj", "csa_index_scores", "csa_index_rescore", "csa_quantize_mxfp4", "csa_rmsnorm_rope",
+        for f in ("csa_compress", "csa_compress_hidden", "csa_quantize_kv8", "csa_out_proj", "csa_index_scores", "csa_index_rescore", "csa_quantize_mxfp4", "csa_rmsnorm_rope",
                   "csa_topk", "csa_topk_noalloc",
                   "csa_topk_ids", "csa_sparse_attn", "hca_attn"):
             getattr(L, f).restype = C.c_int
@@ -128,6 +130,29 @@ def compress(C_a, Z_a, C_b=None, Z_b=None, carry_C_b=None, carry_Z_b=None, logit
                             _dt(C_a), _ptr(out), bstride, _stream(stream))
     _check("csa_compress", rc)
     return out
+
+
+def quantize_kv8(x, out=None, group_rows=0, group_stride=0, stream=None):
+    """csa_quantize_kv8: rows x [..., 512] (fp32 or bf16) -> uint8 [..., 592] in the FP8 KV
+    storage format. With group_rows > 0, input row r goes to output row
+    (r // group_rows) * group_stride + r % group_rows of `out` (its data pointer is the base)."""
+    D = x.shape[-1]
+    fn = "quantize_kv8"
+    _require(D == 512 and x.is_contiguous(), fn, "x must be a contiguous [..][512] tensor")
+    rows = x.numel() // D
+    if out is None:
+        out = torch.empty(x.shape[:-1] + (KV8_ROW_BYTES,), dtype=torch.uint8, device=x.device)
+    _require(out.dtype == torch.uint8, fn, "out must be uint8")
+    if group_rows == 0:
+        _require(out.is_contiguous() and out.numel() >= rows * KV8_ROW_BYTES, fn, "out must hold rows x 592 bytes")
+    rc = lib().csa_quantize_kv8(_ptr(x), rows, _dt(x), _ptr(out), group_rows, group_stride, _stream(stream))
+    _check("csa_quantize_kv8", rc)
+    return out
+
+
+def _attn_dt(q, kv):
+    """The call's dtype: q's, or CSA_KV8 when the compressed rows are uint8 FP8-format rows."""
+    return KV8 if kv.dtype == torch.uint8 else _dt(q)
 
 
 def compress_hidden(hidden, W, carry_hidden=None, logit_bias=None, ratio=4, overlap=1, out=None,
@@ -317,7 +342,10 @@ def attn_workspace_bytes(T, H, D, max_rows) -> int:
 def _check_attn_args(fn, q, kv, swa_kv, q_seq, q_pos, rope_cs, rope_dim):
     T, H, D = q.shape
     _require(q.is_contiguous() and kv.is_contiguous(), fn, "q and the key/value rows must be contiguous")
-    _require(kv.dim() == 3 and kv.shape[2] == D and kv.dtype == q.dtype, fn, "kv must be [B][N][D] in q's dtype")
+    _require(kv.dim() == 3 and ((kv.dtype == q.dtype and kv.shape[2] == D) or
+                                (kv.dtype == torch.uint8 and kv.shape[2] == KV8_ROW_BYTES and D == 512
+                                 and q.dtype == torch.bfloat16)),
+             fn, "kv must be [B][N][D] in q's dtype, or uint8 [B][N][592] FP8-format rows with bf16 q")
     _require(swa_kv is None or (swa_kv.is_contiguous() and swa_kv.shape[0] == kv.shape[0]
                                 and swa_kv.shape[2] == D), fn, "swa_kv must be a contiguous [B][rows][D] tensor")
     _require(q_seq.numel() >= T and q_pos.numel() >= T, fn, "q_seq and q_pos need T entries")
@@ -350,7 +378,7 @@ def sparse_attn(q, kv, attn_sink, topk_idxs, softmax_scale, swa_kv, swa_pos0, wi
     rc = lib().csa_sparse_attn(_ptr(q), _ptr(kv), _ptr(attn_sink), _ptr(topk_idxs), k, float(softmax_scale),
                                _ptr(swa_kv), _ptr(swa_pos0), swa_rows, window, _ptr(q_seq), _ptr(q_pos),
                                _ptr(rope_cs), rope_dim if rope_cs is not None else 0, T, B, N, H, D,
-                               _dt(q), _ptr(out), _ptr(lse), _ptr(workspace), wsb, _stream(stream))
+                               _attn_dt(q, kv), _ptr(out), _ptr(lse), _ptr(workspace), wsb, _stream(stream))
     _check("csa_sparse_attn", rc)
     return out, lse
 
@@ -373,6 +401,6 @@ def hca_attn(q, summ, attn_sink, ratio, softmax_scale, swa_kv, swa_pos0, window,
     rc = lib().hca_attn(_ptr(q), _ptr(summ), _ptr(attn_sink), ratio, float(softmax_scale),
                         _ptr(swa_kv), _ptr(swa_pos0), swa_rows, window, _ptr(q_seq), _ptr(q_pos),
                         _ptr(rope_cs), rope_dim if rope_cs is not None else 0, T, B, N, H, D,
-                        _dt(q), _ptr(out), _ptr(lse), _ptr(workspace), wsb, _stream(stream))
+                        _attn_dt(q, summ), _ptr(out), _ptr(lse), _ptr(workspace), wsb, _stream(stream))
     _check("hca_attn", rc)
     return out, lse

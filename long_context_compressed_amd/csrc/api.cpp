@@ -188,6 +188,20 @@ int csa_quantize_mxfp4(const void *x, int64_t rows, int D, csa_dtype dt, int had
                                  (hipStream_t)stream);
 }
 
+int csa_quantize_kv8(const void *x, int64_t rows, csa_dtype dt, uint8_t *out, int64_t out_group_rows,
+                     int64_t out_group_stride, void *stream) {
+    clear_error();
+    REQUIRE(rows >= 0, CSA_EINVAL, "csa_quantize_kv8: need rows >= 0");
+    REQUIRE(dt == CSA_F32 || dt == CSA_BF16, CSA_EINVAL, "csa_quantize_kv8: dt must be CSA_F32 or CSA_BF16");
+    REQUIRE(out_group_rows >= 0 && (out_group_rows == 0 || out_group_stride >= out_group_rows), CSA_EINVAL,
+            "csa_quantize_kv8: need out_group_rows >= 0 and out_group_stride >= out_group_rows");
+    if (rows == 0) return CSA_OK;
+    REQUIRE(x && out, CSA_EINVAL, "csa_quantize_kv8: NULL tensor");
+    REQUIRE((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(out)) % 16 == 0, CSA_EINVAL,
+            "csa_quantize_kv8: x and out must be 16-byte aligned");
+    return launch_quantize_kv8(x, rows, dt, out, out_group_rows, out_group_stride, (hipStream_t)stream);
+}
+
 int csa_rmsnorm_rope(const void *x, csa_dtype dt_in, int64_t rows, int D, const float *g, float eps,
                      const float *rope_cs, int R, int64_t rope_group, void *out, csa_dtype dt_out, void *stream) {
     clear_error();
@@ -270,7 +284,10 @@ static int check_attn_common(const void *q, const void *kv, const float *sink, c
     const std::string w(who);
     REQUIRE(T >= 0 && B > 0 && N >= 0 && H > 0 && D > 0, CSA_EINVAL, w + ": need T >= 0, B > 0, N >= 0, H > 0, D > 0");
     REQUIRE(window >= 0 && swa_rows >= 0, CSA_EINVAL, w + ": window and swa_rows must be >= 0");
-    REQUIRE(dt == CSA_F32 || dt == CSA_BF16, CSA_EINVAL, w + ": dt must be CSA_F32 or CSA_BF16");
+    REQUIRE(dt == CSA_F32 || dt == CSA_BF16 || dt == CSA_KV8, CSA_EINVAL,
+            w + ": dt must be CSA_F32, CSA_BF16 or CSA_KV8");
+    REQUIRE(dt != CSA_KV8 || (D == 512 && H % 64 == 0), CSA_EUNSUPPORTED,
+            w + ": FP8 KV rows (CSA_KV8) need D = 512 and H a multiple of 64");
     REQUIRE(!rope_cs || (rope_dim > 0 && rope_dim % 2 == 0 && rope_dim <= D), CSA_EINVAL,
             w + ": rope_dim must be even, positive and <= D");
     REQUIRE(D % 64 == 0 && D <= 1024, CSA_EUNSUPPORTED, w + ": D must be a multiple of 64 and <= 1024");

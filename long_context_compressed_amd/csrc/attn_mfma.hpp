@@ -61,15 +61,17 @@ __device__ __forceinline__ v4i16 ld_tr(const bf16_t *p) {
 
 // Row of slot j of a query (a top-k row, a summary or an SWA row), or `standin` when the
 // slot holds no row. Slots [j0, j0 + kIdxCache) of the top-k list are read from `sidx`.
+// kv_row: bf16 elements between consecutive compressed rows (WD, or half the byte size of
+// an FP8-format row).
 __device__ __forceinline__ const bf16_t *slot_row(const RowCtx &c, int64_t j, int64_t j0, int64_t j1, int ratio,
                                                   const int32_t *sidx, const int32_t *idx_t, int64_t N,
                                                   const bf16_t *kv, const bf16_t *swa, int swa_rows,
-                                                  const bf16_t *standin) {
+                                                  const bf16_t *standin, int64_t kv_row = WD) {
     const bf16_t *p = standin;
     if (j < j1) {
         if (j < c.nmain) {
             const int64_t id = (ratio > 0) ? j : (j - j0 < kIdxCache ? (int64_t)sidx[j - j0] : (int64_t)idx_t[j]);
-            if (id >= 0 && id < N) p = kv + ((int64_t)c.s * N + id) * WD;
+            if (id >= 0 && id < N) p = kv + ((int64_t)c.s * N + id) * kv_row;
         } else {
             const int64_t r = c.lo + (j - c.nmain) - c.swa0;
             if (r >= 0 && r < swa_rows) p = swa + ((int64_t)c.s * swa_rows + r) * WD;

@@ -40,7 +40,10 @@ constexpr int PVA = 2;  // V fragments
 
 // NWV wavefronts per workgroup: 4 (64 heads; two workgroups share a CU) or 8 (128 heads,
 // one workgroup per CU: every gathered row is loaded once for all 128 heads).
-template <int NWV>
+// KV8: the compressed rows are in the FP8 storage format (592 bytes: E4M3 codes with one
+// E8M0 scale per 32, then the bf16 RoPE dims); each wavefront expands the rows it loaded to
+// bf16 in place in LDS once they have landed, so the tile loop itself is unchanged.
+template <int NWV, bool KV8>
 __global__ void __launch_bounds__(64 * NWV, 8 / NWV)
 attn_wide_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, const float *__restrict__ sink,
                  const int32_t *__restrict__ idx, int k, int ratio, float scale_log2,
@@ -115,9 +118,14 @@ attn_wide_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, co
     // Row addresses of the tile at slot jt: lane r < 32 resolves slot jt + r to a byte
     // address (the stand-in when the slot has no row) and the tile's 32-bit validity mask
     // comes from a ballot.
-    auto tile_rows = [&](int64_t jt, uint64_t &addr) -> uint32_t {
-        const bf16_t *p = slot_row(c, jt + (lane & 31), j0, j1, ratio, sidx, idx_t, N, kv, swa, swa_rows, standin);
+    constexpr int64_t kKvRow = KV8 ? kKv8RowBytes / 2 : WD;  // bf16 elements per compressed row
+    // (KV8) kvm: the tile's rows that are compressed rows (the rest are SWA rows, already
+    // bf16, or stand-ins)
+    auto tile_rows = [&](int64_t jt, uint64_t &addr, uint32_t &kvm) -> uint32_t {
+        const int64_t j = jt + (lane & 31);
+        const bf16_t *p = slot_row(c, j, j0, j1, ratio, sidx, idx_t, N, kv, swa, swa_rows, standin, kKvRow);
         addr = (uint64_t)(uintptr_t)p;
+        kvm = KV8 ? (uint32_t)(__ballot(p != standin && j < c.nmain) & 0xffffffffull) : 0u;
         return (uint32_t)(__ballot(p != standin) & 0xffffffffull);
     };
     // Rows go from memory straight into LDS: wavefront w loads rows RPW*w .. RPW*w + RPW-1
@@ -128,27 +136,65 @@ attn_wide_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, co
     // instructions, so the compiler can tell that loads into one buffer never alias reads
     // of the other and keeps the loads in flight across a whole tile.
     const int wu = __builtin_amdgcn_readfirstlane(w);
-    auto dma_row = [&](bf16_t *buf, int i, uint64_t addr) {
+    // (the resource of an FP8-format row ends with the row: the rest of the 1 KiB load
+    // reads zeros instead of the next row)
+    auto dma_row = [&](bf16_t *buf, int i, uint64_t addr, uint32_t kvm) {
         const int row = RPW * wu + i;
         const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)addr, row);
         const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(addr >> 32), row);
+        const int bytes = (KV8 && ((kvm >> row) & 1u)) ? kKv8RowBytes : WD * 2;
         const __amdgpu_buffer_rsrc_t rs =
-            __builtin_amdgcn_make_buffer_rsrc((void *)(((uint64_t)hi << 32) | lo), 0, WD * 2, kBufDword3);
+            __builtin_amdgcn_make_buffer_rsrc((void *)(((uint64_t)hi << 32) | lo), 0, bytes, kBufDword3);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(buf + row * WP), 16,
                                                  lane * 16, 0, 0, 0);
     };
+    // (KV8) the wave's compressed rows of a landed tile, expanded to bf16 in place: lanes
+    // 0..27 turn 16 codes each into 32 bytes of bf16 (one scale per lane pair), lanes 28..35
+    // move the 128 bytes of bf16 RoPE dims to dims 448..511. Each row's reads are issued
+    // before its writes (one wavefront: LDS in order), so a row converts where it lies.
+    auto kv8_expand = [&](bf16_t *buf, uint32_t kvm) {
+        if constexpr (KV8) {
+#pragma unroll
+            for (int i = 0; i < RPW; ++i) {
+                const int row = RPW * wu + i;
+                if (!((kvm >> row) & 1u)) continue;
+                uint8_t *rb = reinterpret_cast<uint8_t *>(buf + row * WP);
+                uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+                uint32_t sb = 127u;
+                if (lane < 36) raw = *reinterpret_cast<const uint4 *>(rb + 16 * lane);
+                if (lane < 28) sb = rb[448 + 128 + (lane >> 1)];
+                if (lane < 28) {
+                    const int e = (int)sb - 127;
+                    const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+                    uint32_t o[8];
+#pragma unroll
+                    for (int qd = 0; qd < 4; ++qd) {
+                        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(wd[qd], false);
+                        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(wd[qd], true);
+                        o[2 * qd] = pack_bf16x2(__builtin_ldexpf(lo[0], e), __builtin_ldexpf(lo[1], e));
+                        o[2 * qd + 1] = pack_bf16x2(__builtin_ldexpf(hi[0], e), __builtin_ldexpf(hi[1], e));
+                    }
+                    *reinterpret_cast<uint4 *>(rb + 32 * lane) = make_uint4(o[0], o[1], o[2], o[3]);
+                    *reinterpret_cast<uint4 *>(rb + 32 * lane + 16) = make_uint4(o[4], o[5], o[6], o[7]);
+                } else if (lane < 36) {
+                    *reinterpret_cast<uint4 *>(rb + 896 + 16 * (lane - 28)) = raw;
+                }
+            }
+        }
+    };
 
-    uint32_t valid = 0u, valid_next = 0u;
+    uint32_t valid = 0u, valid_next = 0u, kvm = 0u, kvm_next = 0u;
     uint64_t ra;  // row addresses of the next tile, resolved one tile ahead
     if (j0 < j1) {
-        valid = tile_rows(j0, ra);
+        valid = tile_rows(j0, ra, kvm);
 #pragma unroll
-        for (int i = 0; i < RPW; ++i) dma_row(KV0, i, ra);
+        for (int i = 0; i < RPW; ++i) dma_row(KV0, i, ra, kvm);
     }
-    valid_next = tile_rows(j0 + WR, ra);
+    valid_next = tile_rows(j0 + WR, ra, kvm_next);
     // Every prologue load (Q fragments, first tile) has landed: without this the
     // loop's wait counters start pessimistic and stall the first matrix ops.
     __builtin_amdgcn_s_waitcnt(0);
+    kv8_expand(KV0, kvm);
     __syncthreads();
 
     // One 32-row tile: compute from `tile`, load the next tile's rows into `nxt`. Past the
@@ -156,10 +202,11 @@ attn_wide_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, co
     // branch.
     auto tile_step = [&](const bf16_t *tile, bf16_t *nxt, int64_t jt, bool first) {
         uint64_t ra2;
-        uint32_t valid_next2;
+        uint32_t valid_next2, kvm_next2;
+        const uint32_t kvm_nxt = kvm_next;  // compressed rows of the tile loaded into nxt
 
 #pragma unroll
-        for (int i = 0; i < RPW; ++i) dma_row(nxt, i, ra);
+        for (int i = 0; i < RPW; ++i) dma_row(nxt, i, ra, kvm_nxt);
 
         // ---- S^T = K Q^T (a ring keeps SDA chunks of K fragments in flight)
         f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
@@ -186,7 +233,7 @@ attn_wide_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, co
         }
         // rows of the tile after next: the index read and the address arithmetic overlap
         // the matrix ops still in flight
-        valid_next2 = tile_rows(jt + 2 * WR, ra2);
+        valid_next2 = tile_rows(jt + 2 * WR, ra2, kvm_next2);
 
         // ---- online softmax with the lazy reference maximum
         // rows without data (only in a split's last tile or for padded / missing slots) are
@@ -271,10 +318,13 @@ attn_wide_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, co
 
         valid = valid_next;
         valid_next = valid_next2;
+        kvm = kvm_next;
+        kvm_next = kvm_next2;
         ra = ra2;
         // the next tile's rows have landed in `nxt` (this wave's own loads), and after the
-        // barrier everyone's have and nobody reads `tile` any more
+        // barrier everyone's have (expanded, for FP8 rows) and nobody reads `tile` any more
         __builtin_amdgcn_s_waitcnt(0);
+        kv8_expand(nxt, kvm_nxt);
         __syncthreads();
     };
 
@@ -333,7 +383,7 @@ attn_wide_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, co
 
 }  // namespace
 
-bool wide_attn_ok(csa_dtype dt, int H, int D) { return dt == CSA_BF16 && D == WD && H % 64 == 0; }
+bool wide_attn_ok(csa_dtype dt, int H, int D) { return (dt == CSA_BF16 || dt == CSA_KV8) && D == WD && H % 64 == 0; }
 
 int launch_attn_wide(const AttnArgs &a, float sl2, int nsplit, int64_t split_slots, hipStream_t st) {
     // many queries, one split each: 32 heads per wavefront, so every LDS fragment read
@@ -349,15 +399,24 @@ int launch_attn_wide(const AttnArgs &a, float sl2, int nsplit, int64_t split_slo
     const int WH = wide8 ? 128 : 64;
     const int64_t U = (int64_t)a.T * nsplit * (a.H / WH);
     const int64_t blocks = ((U + 7) / 8) * 8;
-#define CSA_WIDE_LAUNCH(NWV_)                                                                                  \
-    hipLaunchKernelGGL(attn_wide_kernel<NWV_>, dim3((unsigned)blocks), dim3(64 * NWV_), 0, st, (const bf16_t *)a.q, \
+#define CSA_WIDE_LAUNCH(NWV_, KV8_)                                                                            \
+    hipLaunchKernelGGL((attn_wide_kernel<NWV_, KV8_>), dim3((unsigned)blocks), dim3(64 * NWV_), 0, st, (const bf16_t *)a.q, \
                        (const bf16_t *)a.kv, a.sink, a.idx, a.k, a.ratio, sl2, (const bf16_t *)a.swa, a.swa_pos0, \
                        a.swa_rows, a.window, a.q_seq, a.q_pos, a.rope_cs, a.rope_dim, a.T, a.B, a.N, a.H,        \
                        (bf16_t *)a.out, a.lse, (float *)a.ws, nsplit, split_slots);
+    const bool kv8 = a.dt == CSA_KV8;
     if (wide8) {
-        CSA_WIDE_LAUNCH(8)
+        if (kv8) {
+            CSA_WIDE_LAUNCH(8, true)
+        } else {
+            CSA_WIDE_LAUNCH(8, false)
+        }
     } else {
-        CSA_WIDE_LAUNCH(4)
+        if (kv8) {
+            CSA_WIDE_LAUNCH(4, true)
+        } else {
+            CSA_WIDE_LAUNCH(4, false)
+        }
     }
 #undef CSA_WIDE_LAUNCH
     return check_launch("attn_wide_kernel");

@@ -50,6 +50,10 @@ template <> struct elem<bf16_t> {
     __device__ __forceinline__ static void store(bf16_t *p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
 };
 
+// bytes of one compressed KV row in the FP8 storage format (512 dims: 448 E4M3 codes, 64
+// bf16 RoPE dims, 14 E8M0 scales, 2 zero bytes)
+constexpr int kKv8RowBytes = 592;
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

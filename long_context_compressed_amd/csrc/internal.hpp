@@ -22,6 +22,9 @@ int launch_index_mxfp4(const uint8_t *qI, const uint8_t *qs, const float *w, con
 int launch_quantize_mxfp4(const void *x, int64_t rows, int D, csa_dtype dt, bool hadamard, uint8_t *codes,
                           uint8_t *scales, int64_t group_rows, int64_t group_stride, hipStream_t st);
 
+int launch_quantize_kv8(const void *x, int64_t rows, csa_dtype dt, uint8_t *out, int64_t group_rows,
+                        int64_t group_stride, hipStream_t st);
+
 int launch_rmsnorm_rope(const void *x, csa_dtype dt_in, int64_t rows, int D, const float *g, float eps,
                         const float *rope_cs, int R, int64_t group, void *out, csa_dtype dt_out, hipStream_t st);
 

@@ -9,8 +9,8 @@ from __future__ import annotations
 
 import torch
 
-from . import (attn_workspace_bytes, compress, hca_attn, index_scores, quantize_mxfp4, sparse_attn, topk,
-               topk_workspace_bytes)
+from . import (attn_workspace_bytes, compress, hca_attn, index_scores, quantize_kv8, quantize_mxfp4, sparse_attn,
+               topk, topk_workspace_bytes)
 
 
 def _ws(nbytes, dev):
@@ -29,6 +29,9 @@ class DecodeStep:
     With MXFP4 index keys (k_I codes [B][N][64][64] and k_I_scale [B][N][64][4] in `inp`)
     the new index key is compressed to bf16, rotated by the Hadamard transform and encoded
     into the last entry, and each step's q_I is rotated and encoded before the scan.
+    With FP8-format caches (kv [B][N][592] and summ [B][n/128][592] uint8) the new KV entry
+    and summary are compressed to bf16 and encoded (csa_quantize_kv8) into the last rows,
+    and both attention calls read the FP8 rows.
     """
 
     def __init__(self, inp: dict, k: int, window: int, rope_dim: int, scale: float):
@@ -38,7 +41,14 @@ class DecodeStep:
         B, N = kv.shape[0], kv.shape[1]
         NH = summ.shape[1]
         dev = q.device
-        self.kv_new = kv[:, N - 1:N, :]
+        # FP8-format caches (uint8 rows): the step compresses into bf16 staging rows and
+        # encodes them into the last row of each sequence's cache
+        self.kv8 = kv.dtype == torch.uint8
+        if self.kv8:
+            self.kv_new = torch.empty((B, 1, D), dtype=torch.bfloat16, device=dev)
+            self.summ_new_bf = torch.empty((B, 1, D), dtype=torch.bfloat16, device=dev)
+        else:
+            self.kv_new = kv[:, N - 1:N, :]
         self.mxfp4 = inp.get("k_I_scale") is not None
         if self.mxfp4:
             qI = inp["q_I"]
@@ -47,7 +57,7 @@ class DecodeStep:
             self.qs = torch.empty(qI.shape[:-1] + (qI.shape[-1] // 32,), dtype=torch.uint8, device=dev)
         else:
             self.kI_new = k_I.view(B, N, -1)[:, N - 1:N, :]
-        self.summ_new = summ[:, NH - 1:NH, :]
+        self.summ_new = self.summ_new_bf if self.kv8 else summ[:, NH - 1:NH, :]
         self.scores = torch.empty((T, N), dtype=torch.float32, device=dev)
         self.idx = torch.empty((T, k), dtype=torch.int32, device=dev)
         self.topk_ws = _ws(topk_workspace_bytes(T, N, k), dev)
@@ -62,6 +72,9 @@ class DecodeStep:
         i = self.inp
         b, c, ib, ic = i["blk"], i["carry"], i["iblk"], i["icarry"]
         compress(b["Ca"], b["Za"], b["Cb"], b["Zb"], c["C"], c["Z"], ratio=4, overlap=1, out=self.kv_new)
+        if self.kv8:  # the new entry of every sequence into row N-1 of its FP8 cache
+            N = i["kv"].shape[1]
+            quantize_kv8(self.kv_new, out=i["kv"][0, N - 1], group_rows=1, group_stride=N)
         compress(ib["Ca"], ib["Za"], ib["Cb"], ib["Zb"], ic["C"], ic["Z"], ratio=4, overlap=1, out=self.kI_new)
         if self.mxfp4:  # rotate and encode the new key into the last entry of every sequence
             kI, ks = i["k_I"], i["k_I_scale"]
@@ -94,6 +107,9 @@ class DecodeStep:
     def hca_compress(self):
         h = self.inp["hblk"]
         compress(h["C"], h["Z"], ratio=128, overlap=0, out=self.summ_new)
+        if self.kv8:
+            NH = self.inp["summ"].shape[1]
+            quantize_kv8(self.summ_new, out=self.inp["summ"][0, NH - 1], group_rows=1, group_stride=NH)
 
     def hca(self):
         i = self.inp

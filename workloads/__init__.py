@@ -133,6 +133,31 @@ def normal_mxfp4(shape, cfg_seed: int, name: str, device="cpu", chunk_rows: int 
     return codes.view(*shape[:-1], D // 2), scales.view(*shape[:-1], D // 32)
 
 
+KV8_ROW_BYTES = 592  # 448 E4M3 codes + 64 bf16 + 14 E8M0 scales + 2 zero bytes
+
+
+def random_kv8(rows_shape, cfg_seed: int, name: str, device="cpu", chunk_rows: int = 1 << 18):
+    """Synthetic compressed KV rows already in the FP8 storage format [..., 592] bytes: each
+    of the 448 codes a uniformly drawn finite E4M3 code (the two NaN codes 0x7F, 0xFF
+    excluded), each of the 14 E8M0 block scales drawn from 2^-9 .. 2^-7 (so the decoded
+    values lie within about +-3.5, like N(0,1) rows), the 64 RoPE dims N(0,1) rounded to
+    bf16, two zero bytes. Drawn in chunks of rows, each from its own seed."""
+    rows = int(np.prod(rows_shape)) if len(rows_shape) else 1
+    out = torch.zeros((rows, KV8_ROW_BYTES), dtype=torch.uint8, device=device)
+    for r0 in range(0, rows, chunk_rows):
+        r1 = min(rows, r0 + chunk_rows)
+        g = _gen(derive_seed(cfg_seed, f"{name}#{r0 // chunk_rows}"), device)
+        m = r1 - r0
+        code = torch.randint(0, 254, (m, 448), generator=g, device=device, dtype=torch.int32)
+        code = code + (code >= 0x7F).to(torch.int32)  # skip 0x7F: values 0..253 -> 0..0x7E, 0x80..0xFE
+        out[r0:r1, :448] = code.to(torch.uint8)
+        rope = torch.randn((m, 64), generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+        out[r0:r1, 448:576] = rope.view(torch.uint8).view(m, 128)
+        out[r0:r1, 576:590] = torch.randint(118, 121, (m, 14), generator=g, device=device, dtype=torch.int32).to(
+            torch.uint8)
+    return out.view(*rows_shape, KV8_ROW_BYTES)
+
+
 def rope_table(positions: torch.Tensor, rope_dim: int, base: float = 10000.0) -> torch.Tensor:
     """(cos, sin) angle table [T][rope_dim/2][2] fp32 for absolute `positions` [T].
 
@@ -259,7 +284,7 @@ def decode_inputs(cfg: Config, device="cpu", with_index=True, shared_keys=False,
     return inp
 
 
-def decode_step_inputs(cfg: Config, device="cpu", shared_keys=False, mxfp4=False) -> dict:
+def decode_step_inputs(cfg: Config, device="cpu", shared_keys=False, mxfp4=False, kv8=False) -> dict:
     """Everything one decode step of a CSA layer plus an HCA layer reads, for B sequences.
 
     On top of decode_inputs: the block [n-4, n) that completes with the step (a- and
@@ -268,11 +293,18 @@ def decode_step_inputs(cfg: Config, device="cpu", shared_keys=False, mxfp4=False
     ratio-128 block that completes the last summary. All N(0,1) bf16 (sinks fp32).
     shared_keys: the index keys are one 128-dim key per entry for all heads.
     mxfp4: the stored index keys are MXFP4 (see decode_inputs).
+    kv8: the compressed KV rows and the HCA summaries are stored in the FP8 format
+    (random_kv8: [B][N][592] and [B][n/128][592] bytes).
     """
     s, B, D, bf = cfg.seed, cfg.B, cfg.c, torch.bfloat16
     NH = cfg.n // 128
     inp = decode_inputs(cfg, device, shared_keys=shared_keys, mxfp4=mxfp4)
-    inp["summ"] = normal((B, NH, D), HCA.seed, "summ", dtype=bf, device=device)
+    if kv8:
+        del inp["kv"]
+        inp["kv"] = random_kv8((B, cfg.N), s, "kv8", device=device)
+        inp["summ"] = random_kv8((B, NH), HCA.seed, "summ8", device=device)
+    else:
+        inp["summ"] = normal((B, NH, D), HCA.seed, "summ", dtype=bf, device=device)
     inp["sink_h"] = normal((cfg.H,), HCA.seed, "sink", device=device)
     inp["blk"] = {nm: normal((B, 4, D), s, "new_" + nm, dtype=bf, device=device) for nm in ("Ca", "Cb", "Za", "Zb")}
     inp["carry"] = {nm: normal((B, 4, D), s, "carry_" + nm, dtype=bf, device=device) for nm in ("C", "Z")}
