@@ -114,8 +114,10 @@ constexpr int MHG = 64;      // heads per workgroup
 constexpr int MTR = 32;      // rows per tile
 
 // log-sum-exp merge of split partials + sink + inverse RoPE; one block per (query, head).
-// The per-split weights 2^(m_s - M) are formed once in LDS; every thread then streams
-// its two output dims over all splits with independent loads.
+// Workspace layout: [T][nsplit][H][2] fp32 (m_s, l_s), then [T][nsplit][H][D] bf16 partial
+// sums (each split's unnormalised O, rounded once to bf16: half the bytes of fp32, and the
+// merged output is bf16 anyway). The per-split weights 2^(m_s - M) are formed once in LDS;
+// every thread then streams its two output dims over all splits with independent loads.
 template <typename ET>
 __global__ void __launch_bounds__(256)
 attn_merge_kernel(const float *__restrict__ part, const float *__restrict__ sink, int nsplit,
@@ -127,7 +129,7 @@ attn_merge_kernel(const float *__restrict__ part, const float *__restrict__ sink
     const int64_t unit = blockIdx.x;
     const int t = (int)(unit / H), g = (int)(unit % H);
     const float *pml = part;
-    const float *pacc = part + (int64_t)T * nsplit * H * 2;
+    const uint32_t *pacc = reinterpret_cast<const uint32_t *>(part + (int64_t)T * nsplit * H * 2);
     const float sk = sink[g] * kLog2e;
     if (threadIdx.x < 64) {
         // one wavefront forms the global max, the denominator and the split weights
@@ -157,12 +159,12 @@ attn_merge_kernel(const float *__restrict__ part, const float *__restrict__ sink
     const float inv = L > 0.f ? 1.f / L : 0.f;
     for (int d0 = 2 * threadIdx.x; d0 < D; d0 += 2 * blockDim.x) {
         float x0 = 0.f, x1 = 0.f;
-        const float *pp = pacc + (((int64_t)t * nsplit) * H + g) * D + d0;
+        const uint32_t *pp = pacc + ((((int64_t)t * nsplit) * H + g) * D + d0) / 2;
 #pragma unroll 8
         for (int s2 = 0; s2 < nsplit; ++s2) {
-            const float2 v = *reinterpret_cast<const float2 *>(pp + (int64_t)s2 * H * D);
-            x0 = fmaf(v.x, fs[s2], x0);
-            x1 = fmaf(v.y, fs[s2], x1);
+            const uint32_t v = pp[(int64_t)s2 * H * D / 2];
+            x0 = fmaf(lo_bf16(v), fs[s2], x0);
+            x1 = fmaf(hi_bf16(v), fs[s2], x1);
         }
         x0 *= inv;
         x1 *= inv;
@@ -223,7 +225,7 @@ size_t attn_workspace_bytes(int T, int H, int D, int64_t max_rows) {
     if (D != MD || H % MHG != 0) return 0;
     const int ns = mfma_splits(T, H, max_rows);
     if (ns <= 1) return 0;
-    return (size_t)T * ns * H * (size_t)(D + 2) * sizeof(float);
+    return (size_t)T * ns * H * (2 * sizeof(float) + (size_t)D * sizeof(bf16_t));
 }
 
 int launch_attn(const AttnArgs &a, hipStream_t st) {

@@ -167,9 +167,9 @@ __device__ __forceinline__ void unit_fallback(
                 part[pu * 2] = mx;
                 part[pu * 2 + 1] = l;
             }
-            float *prow = part + (int64_t)T * nsplit * H * 2 + pu * WD + d0;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) prow[e] = o[e];
+            bf16_t *prow = reinterpret_cast<bf16_t *>(part + (int64_t)T * nsplit * H * 2) + pu * WD + d0;
+            *reinterpret_cast<uint4 *>(prow) = make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
+                                                          pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7]));
         }
     }
 }
@@ -609,22 +609,22 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
                     *reinterpret_cast<const uint4 *>(ostage + hr * OSP + 8 * lane);
         } else {
             const int64_t pu = ((int64_t)t * nsplit + sp) * H + h;
-            float *pml = part;                                 // [T][nsplit][H][2]
-            float *pacc = part + (int64_t)T * nsplit * H * 2;  // [T][nsplit][H][D]
+            float *pml = part;                                                               // [T][nsplit][H][2]
+            bf16_t *pacc = reinterpret_cast<bf16_t *>(part + (int64_t)T * nsplit * H * 2);  // [T][nsplit][H][D] bf16
             if (g4 == 0) {
                 pml[pu * 2] = m_ref[b];
                 pml[pu * 2 + 1] = lacc[b][0];
             }
 #pragma unroll
             for (int ng = 0; ng < NDN; ng += 4) {
-                float4 v[4];
+                uint2 v[4];
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4)
-                    v[q4] = make_float4(agpr_read(acc[b][ng + q4][0]), agpr_read(acc[b][ng + q4][1]),
-                                        agpr_read(acc[b][ng + q4][2]), agpr_read(acc[b][ng + q4][3]));
+                    v[q4] = make_uint2(pack_bf16x2(agpr_read(acc[b][ng + q4][0]), agpr_read(acc[b][ng + q4][1])),
+                                       pack_bf16x2(agpr_read(acc[b][ng + q4][2]), agpr_read(acc[b][ng + q4][3])));
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4)
-                    *reinterpret_cast<float4 *>(pacc + pu * WD + 16 * (ng + q4) + 4 * g4) = v[q4];
+                    *reinterpret_cast<uint2 *>(pacc + pu * WD + 16 * (ng + q4) + 4 * g4) = v[q4];
                 __builtin_amdgcn_sched_barrier(0);
             }
         }

@@ -365,8 +365,8 @@ attn_wide_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, co
         }
     } else {
         const int64_t pu = ((int64_t)t * nsplit + sp) * H + head0;
-        float *pml = part;                                  // [T][nsplit][H][2]
-        float *pacc = part + (int64_t)T * nsplit * H * 2;   // [T][nsplit][H][D]
+        float *pml = part;                                                               // [T][nsplit][H][2]
+        bf16_t *pacc = reinterpret_cast<bf16_t *>(part + (int64_t)T * nsplit * H * 2);  // [T][nsplit][H][D]
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const float mr = __shfl(m_ref, 4 * g4 + r);
@@ -374,9 +374,27 @@ attn_wide_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, co
                 pml[(pu + 4 * g4 + r) * 2] = mr;
                 pml[(pu + 4 * g4 + r) * 2 + 1] = lacc[r];
             }
-            float *prow = pacc + (pu + 4 * g4 + r) * WD;
+        }
+        // bf16 pairs of adjacent dims: lanes l16 and l16 ^ 1 swap their values (DPP), then the
+        // even lane of a pair stores heads 4g4 and 4g4 + 1 at dims (d, d + 1) and the odd lane
+        // heads 4g4 + 2 and 4g4 + 3, so every lane issues two 4-byte stores per dim block
+        const bool odd = (l16 & 1) != 0;
+        const int ra = odd ? 2 : 0;
+        const int dl = l16 & ~1;
 #pragma unroll
-            for (int nd = 0; nd < NDN; ++nd) prow[16 * nd + l16] = acc[nd][r];
+        for (int nd = 0; nd < NDN; ++nd) {
+            float nb[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                nb[r] = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc[nd][r]), 0xB1, 0xF, 0xF, false));
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int r = ra + e;
+                const float mine = odd ? acc[nd][2 + e] : acc[nd][e];
+                const float other = odd ? nb[2 + e] : nb[e];
+                const uint32_t w = odd ? pack_bf16x2(other, mine) : pack_bf16x2(mine, other);
+                *reinterpret_cast<uint32_t *>(pacc + (pu + 4 * g4 + r) * WD + 16 * nd + dl) = w;
+            }
         }
     }
 }
