@@ -141,8 +141,8 @@ def main():
     stages = {
         "compress_csa_kv_and_index_key": timed(step.compress),
         **({"quantize_q_mxfp4": timed(step.index_prep)} if fp4 else {}),
-        "index_scores": timed(step.index, reps=10),
-        "topk": timed(step.select),
+        **({"index_topk_fused": timed(step.index, reps=10)} if step.fused else
+           {"index_scores": timed(step.index, reps=10), "topk": timed(step.select)}),
         "sparse_attn": timed(step.attend),
         "compress_hca": timed(step.hca_compress),
         "hca_attn": timed(step.hca),
@@ -152,8 +152,8 @@ def main():
     # algorithmic bytes of one index-scan launch: every visible key block once
     # (64 x 128 bf16 = 16 KiB per entry per sequence) + q_I + w + the fp32 scores
     # (MXFP4: 64 x 64 bytes of codes + 64 x 4 E8M0 scales = 4,352 B per entry, same for q_I)
-    if fp4:
-        alg_bytes = B * N * 4352 + T * 4352 + T * 64 * 4 + T * N * 4
+    if fp4:  # (fused with the top-k: no score array, the k winners of each 4,096-entry chunk)
+        alg_bytes = B * N * 4352 + T * 4352 + T * 64 * 4 + T * ((N + 4095) // 4096) * k * 8
     else:
         alg_bytes = B * N * (1 if shared else 64) * 128 * 2 + T * 64 * 128 * 2 + T * 64 * 4 + T * N * 4
     achieved = alg_bytes / scan_avg_s / 1e9
@@ -183,7 +183,8 @@ def main():
         },
         "roofline": {
             "kernel": ("index_shared_kernel (csa_index_scores, bf16 keys shared by the 64 heads)" if shared
-                       else "index_mxfp4_scan_kernel (csa_index_scores, MXFP4 per-head keys)" if fp4
+                       else "index_mxfp4_topk_kernel + the selection over its chunk winners (csa_index_topk: "
+                            "MXFP4 per-head keys, scan fused with the top-k; the time covers both)" if fp4
                        else "index_scan_kernel (csa_index_scores, bf16 per-head keys)"),
             "bound": "hbm",
             "achieved": round(achieved, 1),

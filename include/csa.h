@@ -154,6 +154,30 @@ int csa_index_scores(const void *q_I, const uint8_t *q_I_scale, const float *w,
                      csa_dtype dt, float *scores, void *stream);
 
 /*
+ * csa_index_topk - the MXFP4 decode scan fused with the top-k (§4.2: FP4 index scores of
+ * every stored entry, then each query's k highest), with no [T][N] score array: the scores
+ * of a 4,096-entry chunk stay in registers and only the chunk's k winners reach memory;
+ * the top-k selection of csa_topk then runs over the winners. topk_idxs / topk_vals equal what
+ * csa_topk returns for the scores csa_index_scores computes from the same arguments:
+ * ascending index order, ties to the lower index, (-1, -INFINITY) padding past the visible
+ * entries.
+ *
+ * q_I, q_I_scale, w, k_I, k_I_scale, q_seq, q_pos, T, B, N, ratio: as csa_index_scores with
+ *       dt = CSA_MXFP4 and per-head keys ([B][N][64][64] codes, [B][N][64][4] scales).
+ * topk_idxs: [T][k] int32 out.   topk_vals: [T][k] fp32 out, or NULL.
+ * workspace: csa_index_topk_workspace_bytes(T, N, k) bytes (0 when N <= 4,096) for the
+ *       chunk winners and the final selection.
+ * Supported: H_I == 64, D_I == 128, 1 <= k <= 4096, T <= 65,535, N < 2^31. T may be 0;
+ * with N == 0 (k_I and k_I_scale may then be NULL) every row is padding.
+ */
+size_t csa_index_topk_workspace_bytes(int T, int64_t N, int k);
+int csa_index_topk(const uint8_t *q_I, const uint8_t *q_I_scale, const float *w,
+                   const uint8_t *k_I, const uint8_t *k_I_scale,
+                   const int32_t *q_seq, const int64_t *q_pos, int T, int B, int64_t N,
+                   int H_I, int D_I, int ratio, int k, int32_t *topk_idxs, float *topk_vals,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * csa_index_rescore - Lightning Indexer scores (the formula of csa_index_scores) of a
  * per-query candidate list: the re-rank step after an FP4 scan has picked 2k candidates
  * (the indexer builds its candidates at twice the top-k, "DeepSeek-V4 混合注意力" §9).

@@ -20,7 +20,7 @@ F32, BF16, MXFP4, KV8 = 0, 1, 2, 3
 KV8_ROW_BYTES = 592  # one 512-dim compressed row in the FP8 storage format
 STATUS = {0: "CSA_OK", 1: "CSA_EINVAL", 2: "CSA_EUNSUPPORTED", 3: "CSA_EWORKSPACE", 4: "CSA_EHIP"}
 EXPORTS = ("csa_compress", "csa_compress_hidden", "csa_quantize_kv8", "csa_out_proj_workspace_bytes", "csa_out_proj",
-           "csa_index_scores", "csa_index_rescore", "csa_quantize_mxfp4", "csa_rmsnorm_rope",
+           "csa_index_scores", "csa_index_topk_workspace_bytes", "csa_index_topk", "csa_index_rescore", "csa_quantize_mxfp4", "csa_rmsnorm_rope",
            "csa_topk_workspace_bytes",
            "csa_topk", "csa_topk_noalloc", "csa_topk_ids",
            "csa_attn_workspace_bytes", "csa_sparse_attn", "hca_attn", "csa_status_str",
@@ -51,6 +51,9 @@ def lib() -> C.CDLL:
         L.csa_out_proj_workspace_bytes.restype = sz
         L.csa_out_proj.argtypes = [P, i32, i32, i32, i32, P, i32, P, i32, i32, P, P, sz, P]
         L.csa_index_scores.argtypes = [P, P, P, P, P, P, P, i32, i32, i64, i32, i32, i32, i32, i32, P, P]
+        L.csa_index_topk_workspace_bytes.argtypes = [i32, i64, i32]
+        L.csa_index_topk_workspace_bytes.restype = sz
+        L.csa_index_topk.argtypes = [P, P, P, P, P, P, P, i32, i32, i64, i32, i32, i32, i32, P, P, P, sz, P]
         L.csa_quantize_mxfp4.argtypes = [P, i64, i32, i32, i32, P, P, i64, i64, P]
         L.csa_rmsnorm_rope.argtypes = [P, i32, i64, i32, P, f32, P, i32, i64, P, i32, P]
         L.csa_index_rescore.argtypes = [P, P, P, P, i32, P, P, i32, i32, i64, i32, i32, i32, i32, P, P]
@@ -65,7 +68,7 @@ def lib() -> C.CDLL:
                                       i32, i32, i64, i32, i32, i32, P, P, P, sz, P]
         L.hca_attn.argtypes = [P, P, P, i32, f32, P, P, i32, i32, P, P, P, i32,
                                i32, i32, i64, i32, i32, i32, P, P, P, sz, P]
-        for f in ("csa_compress", "csa_compress_hidden", "csa_quantize_kv8", "csa_out_proj", "csa_index_scores", "csa_index_rescore", "csa_quantize_mxfp4", "csa_rmsnorm_rope",
+        for f in ("csa_compress", "csa_compress_hidden", "csa_quantize_kv8", "csa_out_proj", "csa_index_scores", "csa_index_topk", "csa_index_rescore", "csa_quantize_mxfp4", "csa_rmsnorm_rope",
                   "csa_topk", "csa_topk_noalloc",
                   "csa_topk_ids", "csa_sparse_attn", "hca_attn"):
             getattr(L, f).restype = C.c_int
@@ -226,6 +229,46 @@ def index_scores(q_I, w, k_I, q_seq, q_pos, ratio=4, q_I_scale=None, k_I_scale=N
                                 _ptr(scores), _stream(stream))
     _check("csa_index_scores", rc)
     return scores
+
+
+def index_topk_workspace_bytes(T, N, k) -> int:
+    return int(lib().csa_index_topk_workspace_bytes(T, N, k))
+
+
+def index_topk_workspace(T, N, k, device):
+    """A workspace for csa_index_topk (None when the call needs none)."""
+    need = index_topk_workspace_bytes(T, N, k)
+    return torch.empty(need, dtype=torch.uint8, device=device) if need > 0 else None
+
+
+def index_topk(q_I, w, k_I, q_seq, q_pos, k, q_I_scale, k_I_scale, ratio=4, idx=None, vals=None, workspace=None,
+               with_vals=False, stream=None):
+    """csa_index_topk -> (idx [T][k] int32 ascending, -1 padded; vals or None): the MXFP4
+    scan fused with the top-k (uint8 codes q_I [T][64][64], k_I [B][N][64][64] and their
+    E8M0 scales)."""
+    T = q_I.shape[0]
+    B, N = k_I.shape[0], k_I.shape[1]
+    fn = "csa_index_topk"
+    _require(q_I.dtype == torch.uint8 and k_I.dtype == torch.uint8, fn, "MXFP4 codes are uint8")
+    _require(tuple(q_I.shape[1:]) == (64, 64) and tuple(k_I.shape[2:]) == (64, 64), fn,
+             "codes must be [T][64][64] and [B][N][64][64]")
+    _require(q_I_scale is not None and k_I_scale is not None, fn, "both scale tensors are needed")
+    _require(tuple(q_I_scale.shape) == (T, 64, 4) and tuple(k_I_scale.shape) == (B, N, 64, 4), fn,
+             "scales must be [T][64][4] and [B][N][64][4]")
+    _require(tuple(w.shape) == (T, 64) and tuple(q_seq.shape) == (T,) and tuple(q_pos.shape) == (T,), fn,
+             "w must be [T][64], q_seq and q_pos [T]")
+    if idx is None:
+        idx = torch.empty((T, k), dtype=torch.int32, device=q_I.device)
+    if vals is None and with_vals:
+        vals = torch.empty((T, k), dtype=torch.float32, device=q_I.device)
+    if workspace is None:
+        workspace = index_topk_workspace(T, N, k, q_I.device)
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib().csa_index_topk(_ptr(q_I), _ptr(q_I_scale), _ptr(w), _ptr(k_I), _ptr(k_I_scale), _ptr(q_seq),
+                              _ptr(q_pos), T, B, N, 64, 128, ratio, k, _ptr(idx), _ptr(vals), _ptr(workspace), wsb,
+                              _stream(stream))
+    _check("csa_index_topk", rc)
+    return idx, vals
 
 
 def index_rescore(q_I, w, k_I, cand, q_seq, q_pos, ratio=4, scores=None, stream=None):

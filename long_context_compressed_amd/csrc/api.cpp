@@ -160,6 +160,29 @@ int csa_index_scores(const void *q_I, const uint8_t *q_I_scale, const float *w, 
                                scores, (hipStream_t)stream);
 }
 
+size_t csa_index_topk_workspace_bytes(int T, int64_t N, int k) {
+    if (T <= 0 || N < 0) return 0;
+    return index_topk_workspace_bytes(T, N, k);
+}
+
+int csa_index_topk(const uint8_t *q_I, const uint8_t *q_I_scale, const float *w, const uint8_t *k_I,
+                   const uint8_t *k_I_scale, const int32_t *q_seq, const int64_t *q_pos, int T, int B, int64_t N,
+                   int H_I, int D_I, int ratio, int k, int32_t *topk_idxs, float *topk_vals, void *workspace,
+                   size_t workspace_bytes, void *stream) {
+    clear_error();
+    REQUIRE(T >= 0 && B > 0 && N >= 0 && ratio > 0, CSA_EINVAL, "csa_index_topk: need T >= 0, B > 0, N >= 0, ratio > 0");
+    REQUIRE(k >= 1, CSA_EINVAL, "csa_index_topk: need k >= 1");
+    REQUIRE(H_I == 64 && D_I == 128, CSA_EUNSUPPORTED, "csa_index_topk: only H_I = 64, D_I = 128 is built");
+    REQUIRE(k <= 4096, CSA_EUNSUPPORTED, "csa_index_topk: k must be <= 4096");
+    REQUIRE(T <= 65535, CSA_EUNSUPPORTED, "csa_index_topk: at most 65,535 queries per call");
+    REQUIRE(N < (int64_t{1} << 31), CSA_EUNSUPPORTED, "csa_index_topk: N must be below 2^31 (32-bit entry indices)");
+    if (T == 0) return CSA_OK;
+    REQUIRE(q_I && q_I_scale && w && q_seq && q_pos && topk_idxs && (N == 0 || (k_I && k_I_scale)), CSA_EINVAL,
+            "csa_index_topk: NULL tensor");
+    return launch_index_topk_mxfp4(q_I, q_I_scale, w, k_I, k_I_scale, q_seq, q_pos, T, B, N, ratio, k, topk_idxs,
+                                   topk_vals, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
 int csa_index_rescore(const void *q_I, const float *w, const void *k_I, const int32_t *cand, int M,
                       const int32_t *q_seq, const int64_t *q_pos, int T, int B, int64_t N, int H_I, int D_I,
                       int ratio, csa_dtype dt, float *scores, void *stream) {

@@ -26,6 +26,7 @@
 // computes 16 heads' dots of one entry on its diagonal.
 #include "common.hpp"
 #include "internal.hpp"
+#include "topk_select.hpp"
 
 namespace csa {
 
@@ -264,6 +265,56 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
 }
 
+// The query side of one decode query (codes, scales and head weights of the 16 heads a
+// lane's matrix-op column serves) and the score of one entry from its codes and scales.
+struct Fp4Query {
+    i32x8 qb[4];
+    int sb[4];
+    float wd[4];
+};
+
+__device__ __forceinline__ Fp4Query load_fp4_query(const uint8_t *qI, const uint8_t *qS, const float *w, int t) {
+    const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
+    Fp4Query f;
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+        const int64_t qh = (int64_t)t * 64 + 16 * hb + l16;
+        const uint4 v = *reinterpret_cast<const uint4 *>(qI + qh * 64 + 16 * g4);
+        f.qb[hb] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+        f.sb[hb] = (int)qS[qh * 4 + g4];
+        f.wd[hb] = w[qh];
+    }
+    return f;
+}
+
+// s = sum_h w_h ReLU(<q_h, k_h>) of one entry (kc: its codes in the A-operand layout, kw:
+// head `lane`'s four block scales); the total is uniform over the wavefront
+__device__ __forceinline__ float fp4_entry_score(const Fp4Query &f, const i32x4v (&kc)[4], uint32_t kw) {
+    const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
+    const bool diag = (l16 >> 2) == g4;
+    const int r = lane & 3;
+    float acc = 0.f;
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+        const int sa = (__builtin_amdgcn_ds_bpermute(4 * (16 * hb + l16), (int)kw) >> (8 * g4)) & 0xFF;
+        const i32x8 A = i32x8{kc[hb].x, kc[hb].y, kc[hb].z, kc[hb].w, 0, 0, 0, 0};
+        const f32x4 c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, f.qb[hb], f32x4{0.f, 0.f, 0.f, 0.f}, 4, 4,
+                                                                         0, sa, 0, f.sb[hb]);
+        const float x = r == 0 ? c[0] : (r == 1 ? c[1] : (r == 2 ? c[2] : c[3]));
+        acc = fmaf(f.wd[hb], __int_as_float(max(__float_as_int(x), 0)), acc);
+    }
+    return wave_sum_dpp(diag ? acc : 0.f);
+}
+
+// visible entries of query t: the first q_pos / ratio of its sequence (none for a query of
+// no sequence)
+__device__ __forceinline__ int64_t fp4_visible(int t, const int32_t *q_seq, const int64_t *q_pos, int B, int64_t N,
+                                               int ratio, int &s) {
+    s = q_seq[t];
+    int64_t nv = (s >= 0 && s < B) ? q_pos[t] / ratio : 0;
+    return nv < 0 ? 0 : (nv > N ? N : nv);
+}
+
 __global__ void __launch_bounds__(256)
 index_mxfp4_scan_kernel(const uint8_t *__restrict__ qI, const uint8_t *__restrict__ qS,
                         const float *__restrict__ w, const uint8_t *__restrict__ kI,
@@ -275,26 +326,13 @@ index_mxfp4_scan_kernel(const uint8_t *__restrict__ qI, const uint8_t *__restric
     const int64_t e0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * SE;
     if (e0 >= N) return;
     const int64_t e1 = e0 + SE < N ? e0 + SE : N;
-    const bool diag = (l16 >> 2) == g4;
-    const int r = lane & 3;
     for (int t = blockIdx.y; t < T; t += gridDim.y) {
-        const int s = q_seq[t];
-        int64_t nv = (s >= 0 && s < B) ? q_pos[t] / ratio : 0;
-        nv = nv < 0 ? 0 : (nv > N ? N : nv);
+        int s;
+        const int64_t nv = fp4_visible(t, q_seq, q_pos, B, N, ratio, s);
         const int64_t ev = e1 < nv ? e1 : nv;  // visible entries of the run: [e0, ev)
         float out = -INFINITY;                 // lane j: the score of entry e0 + j
         if (ev > e0) {
-            i32x8 qb[4];
-            int sb[4];
-            float wd[4];
-#pragma unroll
-            for (int hb = 0; hb < 4; ++hb) {
-                const int64_t qh = (int64_t)t * 64 + 16 * hb + l16;
-                const uint4 v = *reinterpret_cast<const uint4 *>(qI + qh * 64 + 16 * g4);
-                qb[hb] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-                sb[hb] = (int)qS[qh * 4 + g4];
-                wd[hb] = w[qh];
-            }
+            const Fp4Query f = load_fp4_query(qI, qS, w, t);
             const uint8_t *kb = kI + (int64_t)s * N * 4096 + l16 * 64 + 16 * g4;
             const uint32_t *ksb = reinterpret_cast<const uint32_t *>(kS + (int64_t)s * N * 256) + lane;
             i32x4v kc[SP][4];
@@ -315,17 +353,7 @@ index_mxfp4_scan_kernel(const uint8_t *__restrict__ qI, const uint8_t *__restric
                 for (int u = 0; u < SP; ++u) {
                     const int64_t e = eb + u;
                     if (e < ev) {
-                        float acc = 0.f;
-#pragma unroll
-                        for (int hb = 0; hb < 4; ++hb) {
-                            const int sa = (__builtin_amdgcn_ds_bpermute(4 * (16 * hb + l16), (int)kw[u]) >> (8 * g4)) & 0xFF;
-                            const i32x8 A = i32x8{kc[u][hb].x, kc[u][hb].y, kc[u][hb].z, kc[u][hb].w, 0, 0, 0, 0};
-                            const f32x4 c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                                A, qb[hb], f32x4{0.f, 0.f, 0.f, 0.f}, 4, 4, 0, sa, 0, sb[hb]);
-                            const float x = r == 0 ? c[0] : (r == 1 ? c[1] : (r == 2 ? c[2] : c[3]));
-                            acc = fmaf(wd[hb], __int_as_float(max(__float_as_int(x), 0)), acc);
-                        }
-                        const float tot = wave_sum_dpp(diag ? acc : 0.f);
+                        const float tot = fp4_entry_score(f, kc[u], kw[u]);
                         out = (lane == (int)(e - e0)) ? tot : out;
                     }
                     load(u, eb + SP + u);
@@ -335,6 +363,88 @@ index_mxfp4_scan_kernel(const uint8_t *__restrict__ qI, const uint8_t *__restric
         if (e0 + lane < e1) scores[(int64_t)t * N + e0 + lane] = out;
     }
 }
+
+// ---- the decode scan fused with the top-k ("DeepSeek-V4 混合注意力" §4.2: the FP4 index
+// scores of every compressed entry, then the k best) -------------------------------------
+// Workgroup (chunk, query): 8 wavefronts stream the 4,096 entries of the chunk (wavefront
+// w, run j: entries c0 + 512 j + 64 w .. +63, the loads of the next run already in flight
+// at the end of a run); each lane keeps its scores in registers as selection keys, so the
+// chunk's exact top-k (select_chunk: ties to the lower position, ascending position
+// order) comes straight out of the registers and only the k (value, index) winners reach
+// memory. The exact top-k of a row is a subset of the union of its chunks' top-k sets, so
+// the csa_topk selection over the winners (kept in position order, with their indices)
+// finishes the job. At the Pro 1M decode shape (64 chunks x 1,024 winners per query) that
+// selection runs in two short launches (8,192-winner chunks, then 8,192 survivors), which
+// measured faster than one 1,024-lane workgroup over each query's 65,536 winners.
+constexpr int FT_RT = 512;            // lanes per workgroup
+constexpr int FT_J0 = 8;              // keys per lane
+constexpr int FT_CH = FT_RT * FT_J0;  // entries per chunk
+static_assert(64 % SP == 0, "a run of 64 entries is a whole number of load groups");
+
+__global__ void __launch_bounds__(FT_RT)
+index_mxfp4_topk_kernel(const uint8_t *__restrict__ qI, const uint8_t *__restrict__ qS,
+                        const float *__restrict__ w, const uint8_t *__restrict__ kI,
+                        const uint8_t *__restrict__ kS, const int32_t *__restrict__ q_seq,
+                        const int64_t *__restrict__ q_pos, int T, int B, int64_t N, int ratio, int k,
+                        float *__restrict__ win_v, int32_t *__restrict__ win_i, int64_t win_ld)
+{
+    __shared__ tksel::SelectLds<FT_RT, FT_J0> sm;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int t = blockIdx.y;
+    const int64_t chunk = blockIdx.x;
+    const int64_t c0 = chunk * FT_CH;
+    tksel::select_begin(sm);
+
+    int s;
+    const int64_t nv = fp4_visible(t, q_seq, q_pos, B, N, ratio, s);
+    uint32_t key[FT_J0];
+#pragma unroll
+    for (int j = 0; j < FT_J0; ++j) key[j] = 0u;
+    const int64_t wb = c0 + 64 * wv;  // first entry of the wavefront's run 0
+    if (wb < nv) {
+        const Fp4Query f = load_fp4_query(qI, qS, w, t);
+        const uint8_t *kb = kI + (int64_t)s * N * 4096 + l16 * 64 + 16 * g4;
+        const uint32_t *ksb = reinterpret_cast<const uint32_t *>(kS + (int64_t)s * N * 256) + lane;
+        i32x4v kc[SP][4];
+        uint32_t kw[SP];
+        // step i of the wavefront (0 .. 64 FT_J0 - 1) is entry wb + 512 (i / 64) + i % 64;
+        // steps past the visible entries re-read the last visible one (cache hits), so every
+        // load is unconditional and the waits stay exact
+        auto load = [&](int u, int i) __attribute__((always_inline)) {
+            int64_t e = wb + (int64_t)FT_RT * (i >> 6) + (i & 63);
+            e = e < nv ? e : nv - 1;
+#pragma unroll
+            for (int hb = 0; hb < 4; ++hb)
+                kc[u][hb] = __builtin_nontemporal_load(reinterpret_cast<const i32x4v *>(kb + e * 4096 + hb * 1024));
+            kw[u] = ksb[e * 64];
+        };
+#pragma unroll
+        for (int u = 0; u < SP; ++u) load(u, u);
+#pragma unroll
+        for (int j = 0; j < FT_J0; ++j) {
+            const int64_t rb = wb + (int64_t)FT_RT * j;
+            float out = -INFINITY;  // lane x: the score of entry rb + x
+            for (int i0 = 0; i0 < 64; i0 += SP) {
+#pragma unroll
+                for (int u = 0; u < SP; ++u) {
+                    if (rb + i0 + u < nv) {
+                        const float tot = fp4_entry_score(f, kc[u], kw[u]);
+                        out = (lane == i0 + u) ? tot : out;
+                    }
+                    load(u, 64 * j + i0 + u + SP);
+                }
+            }
+            key[j] = tksel::order_key(out);
+        }
+    }
+    const int n = (int)((N - c0 < FT_CH) ? (N > c0 ? N - c0 : 0) : FT_CH);
+    const int64_t o = (int64_t)t * win_ld + chunk * k;
+    tksel::select_chunk<FT_RT, FT_J0>(key, n, k, nullptr, c0, win_v ? win_v + o : nullptr, win_i + o, k, sm);
+}
+
+// chunks per query row of N entries (one empty chunk when N == 0, so the output is padded)
+int64_t fused_chunks(int64_t N) { return N > 0 ? (N + FT_CH - 1) / FT_CH : 1; }
 
 }  // namespace
 
@@ -356,6 +466,42 @@ int launch_index_mxfp4(const uint8_t *qI, const uint8_t *qs, const float *w, con
     hipLaunchKernelGGL(index_mxfp4_scan_kernel, grid, dim3(256), 0, st, qI, qs, w, kI, ks, q_seq, q_pos, T, B, N,
                        ratio, scores);
     return check_launch("index_mxfp4_scan_kernel");
+}
+
+size_t index_topk_workspace_bytes(int T, int64_t N, int k) {
+    if (T <= 0 || k < 1) return 0;
+    const int64_t nch = fused_chunks(N);
+    if (nch == 1) return 0;  // the chunk's winners are the output
+    const int64_t L = nch * k;
+    const size_t pairs = (size_t)T * (size_t)L * 8u;
+    return ((pairs + 255) / 256) * 256 + topk_workspace_bytes(T, L, k);
+}
+
+int launch_index_topk_mxfp4(const uint8_t *qI, const uint8_t *qs, const float *w, const uint8_t *kI,
+                            const uint8_t *ks, const int32_t *q_seq, const int64_t *q_pos, int T, int B, int64_t N,
+                            int ratio, int k, int32_t *idx, float *vals, void *ws, size_t ws_bytes, hipStream_t st)
+{
+    const int64_t nch = fused_chunks(N);
+    const size_t need = index_topk_workspace_bytes(T, N, k);
+    if (need > ws_bytes || (need > 0 && ws == nullptr))
+        return fail(CSA_EWORKSPACE, "csa_index_topk: workspace smaller than csa_index_topk_workspace_bytes()");
+    const dim3 grid((unsigned)nch, (unsigned)T);
+    if (nch == 1) {
+        // a single chunk: its winners are the answer (a NULL value output goes to a dropped,
+        // zero-length buffer inside the selection)
+        hipLaunchKernelGGL(index_mxfp4_topk_kernel, grid, dim3(FT_RT), 0, st, qI, qs, w, kI, ks, q_seq, q_pos, T, B, N,
+                           ratio, k, vals, idx, (int64_t)k);
+        return check_launch("index_mxfp4_topk_kernel");
+    }
+    const int64_t L = nch * k;
+    float *wv = static_cast<float *>(ws);
+    int32_t *wi = reinterpret_cast<int32_t *>(wv + (size_t)T * L);
+    const size_t pair_bytes = (((size_t)T * (size_t)L * 8u + 255) / 256) * 256;
+    hipLaunchKernelGGL(index_mxfp4_topk_kernel, grid, dim3(FT_RT), 0, st, qI, qs, w, kI, ks, q_seq, q_pos, T, B, N,
+                       ratio, k, wv, wi, L);
+    const int rc = check_launch("index_mxfp4_topk_kernel");
+    if (rc != CSA_OK) return rc;
+    return launch_topk(wv, wi, T, L, k, idx, vals, static_cast<char *>(ws) + pair_bytes, ws_bytes - pair_bytes, st);
 }
 
 }  // namespace csa

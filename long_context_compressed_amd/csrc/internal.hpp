@@ -18,6 +18,10 @@ int launch_index_scores(const void *qI, const uint8_t *qs, const float *w, const
 int launch_index_mxfp4(const uint8_t *qI, const uint8_t *qs, const float *w, const uint8_t *kI,
                        const uint8_t *ks, const int32_t *q_seq, const int64_t *q_pos, int T, int B, int64_t N,
                        int ratio, float *scores, hipStream_t st);
+size_t index_topk_workspace_bytes(int T, int64_t N, int k);
+int launch_index_topk_mxfp4(const uint8_t *qI, const uint8_t *qs, const float *w, const uint8_t *kI,
+                            const uint8_t *ks, const int32_t *q_seq, const int64_t *q_pos, int T, int B, int64_t N,
+                            int ratio, int k, int32_t *idx, float *vals, void *ws, size_t ws_bytes, hipStream_t st);
 
 int launch_quantize_mxfp4(const void *x, int64_t rows, int D, csa_dtype dt, bool hadamard, uint8_t *codes,
                           uint8_t *scales, int64_t group_rows, int64_t group_stride, hipStream_t st);

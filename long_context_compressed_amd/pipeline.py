@@ -9,8 +9,8 @@ from __future__ import annotations
 
 import torch
 
-from . import (attn_workspace_bytes, compress, hca_attn, index_scores, quantize_kv8, quantize_mxfp4, sparse_attn,
-               topk, topk_workspace_bytes)
+from . import (attn_workspace_bytes, compress, hca_attn, index_scores, index_topk, index_topk_workspace,
+               quantize_kv8, quantize_mxfp4, sparse_attn, topk, topk_workspace_bytes)
 
 
 def _ws(nbytes, dev):
@@ -28,13 +28,15 @@ class DecodeStep:
     and summary into the last row of kv, k_I and summ, then scores, selects and attends.
     With MXFP4 index keys (k_I codes [B][N][64][64] and k_I_scale [B][N][64][4] in `inp`)
     the new index key is compressed to bf16, rotated by the Hadamard transform and encoded
-    into the last entry, and each step's q_I is rotated and encoded before the scan.
+    into the last entry, and each step's q_I is rotated and encoded before the scan; the scan
+    and the top-k are then one csa_index_topk call (the scores stay on chip), unless
+    `fused_topk` is False.
     With FP8-format caches (kv [B][N][592] and summ [B][n/128][592] uint8) the new KV entry
     and summary are compressed to bf16 and encoded (csa_quantize_kv8) into the last rows,
     and both attention calls read the FP8 rows.
     """
 
-    def __init__(self, inp: dict, k: int, window: int, rope_dim: int, scale: float):
+    def __init__(self, inp: dict, k: int, window: int, rope_dim: int, scale: float, fused_topk: bool = True):
         self.inp, self.k, self.window, self.rope_dim, self.scale = inp, k, window, rope_dim, scale
         q, kv, k_I, summ = inp["q"], inp["kv"], inp["k_I"], inp["summ"]
         T, H, D = q.shape
@@ -58,9 +60,10 @@ class DecodeStep:
         else:
             self.kI_new = k_I.view(B, N, -1)[:, N - 1:N, :]
         self.summ_new = self.summ_new_bf if self.kv8 else summ[:, NH - 1:NH, :]
-        self.scores = torch.empty((T, N), dtype=torch.float32, device=dev)
+        self.fused = self.mxfp4 and fused_topk
+        self.scores = None if self.fused else torch.empty((T, N), dtype=torch.float32, device=dev)
         self.idx = torch.empty((T, k), dtype=torch.int32, device=dev)
-        self.topk_ws = _ws(topk_workspace_bytes(T, N, k), dev)
+        self.topk_ws = index_topk_workspace(T, N, k, dev) if self.fused else _ws(topk_workspace_bytes(T, N, k), dev)
         self.attn_ws = _ws(attn_workspace_bytes(T, H, D, k + window), dev)
         self.hca_ws = _ws(attn_workspace_bytes(T, H, D, NH + window), dev)
         self.out = torch.empty((T, H, D), dtype=q.dtype, device=dev)
@@ -88,15 +91,21 @@ class DecodeStep:
             quantize_mxfp4(self.inp["q_I"], hadamard=True, codes=self.qc, scales=self.qs)
 
     def index(self):
+        """The index scan (fused: the scan and the top-k)."""
         i = self.inp
-        if self.mxfp4:
+        if self.fused:
+            index_topk(self.qc, i["w"], i["k_I"], i["q_seq"], i["q_pos"], self.k, self.qs, i["k_I_scale"],
+                       idx=self.idx, workspace=self.topk_ws)
+        elif self.mxfp4:
             index_scores(self.qc, i["w"], i["k_I"], i["q_seq"], i["q_pos"], q_I_scale=self.qs,
                          k_I_scale=i["k_I_scale"], mxfp4=True, scores=self.scores)
         else:
             index_scores(i["q_I"], i["w"], i["k_I"], i["q_seq"], i["q_pos"], scores=self.scores)
 
     def select(self):
-        topk(self.scores, self.k, idx=self.idx, workspace=self.topk_ws)
+        """The top-k over the scores (done inside index() when fused)."""
+        if not self.fused:
+            topk(self.scores, self.k, idx=self.idx, workspace=self.topk_ws)
 
     def attend(self):
         i = self.inp

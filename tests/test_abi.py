@@ -97,6 +97,26 @@ def test_topk_noalloc_validation(L):
     assert b"scratch" in L.csa_last_error()
 
 
+def test_index_topk_validation(L):
+    def f(**kw):
+        a = dict(T=4, B=1, N=262144, H=64, D=128, ratio=4, k=1024, idx=1, ws=None, wsb=0)
+        a.update(kw)
+        return L.csa_index_topk(1, 1, 1, 1, 1, 1, 1, a["T"], a["B"], a["N"], a["H"], a["D"], a["ratio"], a["k"],
+                                a["idx"], None, a["ws"], a["wsb"], None)
+    assert f(k=0) == 1
+    assert f(k=5000) == 2
+    assert f(H=32) == 2
+    assert f(T=70000) == 2
+    assert f(ratio=0) == 1
+    assert f(idx=None) == 1
+    assert f(T=0) == 0
+    # the chunk winners need a workspace: refused before any launch
+    assert L.csa_index_topk_workspace_bytes(4, 262144, 1024) >= 4 * 64 * 1024 * 8
+    assert f(wsb=16) == 3
+    # one chunk: its winners are the output, no workspace at all
+    assert L.csa_index_topk_workspace_bytes(4, 4096, 1024) == 0
+
+
 def test_attn_validation(L):
     def f(**kw):
         a = dict(q=1, kv=1, sink=1, idx=1, k=4, scale=0.1, swa=1, p0=1, rows=8, win=128, qseq=1, qpos=1,

@@ -111,13 +111,21 @@ def test_decode_step_full_size(csa, orc, name, keys):
         rc, rs = orc.mxfp4_encode(inp["q_I"], hadamard=True)
         np.testing.assert_array_equal(step.qc.cpu().numpy(), rc)
         np.testing.assert_array_equal(step.qs.cpu().numpy(), rs)
-        _check_index_sample(orc, step.scores, step.qc, inp["w"], inp["k_I"], inp["q_seq"], inp["q_pos"], ids,
+        # the step's scan is fused with the top-k (no score array): the same scores from the
+        # plain scan must select exactly the step's indices
+        scores = csa.index_scores(step.qc, inp["w"], inp["k_I"], inp["q_seq"], inp["q_pos"], q_I_scale=step.qs,
+                                  k_I_scale=inp["k_I_scale"], mxfp4=True)
+        ridx, _ = csa.topk(scores, cfg.k)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(step.idx.cpu().numpy(), ridx.cpu().numpy())
+        _check_index_sample(orc, scores, step.qc, inp["w"], inp["k_I"], inp["q_seq"], inp["q_pos"], ids,
                             mxfp4_scales=(step.qs, inp["k_I_scale"]))
     else:
-        _check_index_sample(orc, step.scores, inp["q_I"], inp["w"], inp["k_I"], inp["q_seq"], inp["q_pos"], ids)
+        scores = step.scores
+        _check_index_sample(orc, scores, inp["q_I"], inp["w"], inp["k_I"], inp["q_seq"], inp["q_pos"], ids)
 
     # top-k over the full 262,144 / 32,768 scores of every query
-    _check_topk_fed(orc, step.scores, step.idx, cfg.k)
+    _check_topk_fed(orc, scores, step.idx, cfg.k)
 
     # sparse attention of every query over its selected rows + SWA
     kv_c, idx_c = _gathered_rows(inp["kv"], inp["q_seq"].cpu().numpy(), step.idx)
