@@ -203,6 +203,7 @@ def main():
         res["metric"] = f"decode queries/s + indexer GB/s, {a.workload} (profiling line, not the benchmark)"
     if not a.no_cpu and a.workload == "pro_decode_1m":
         res["cpu_baseline"] = cpu_baseline(a, inp, kv, k_I, summ, sink_h, scores, idx, cfg, NH)
+    res["host"] = host_info()
     print(json.dumps(res), flush=True)
 
 
@@ -286,6 +287,7 @@ def prefill_main(a):
                      "min_launch_ms": round(float(np.min(dom_ms)), 4)},
         "stages_ms": stage_ms,
     }
+    res["host"] = host_info()
     print(json.dumps(res), flush=True)
 
 
@@ -344,6 +346,7 @@ def rownorm_main(a):
                      "median_launch_ms": round(float(np.median(ms)), 4), "min_launch_ms": round(float(np.min(ms)), 4),
                      "torch_copy_same_rows_ms": round(copy_ms, 4)},
     }
+    res["host"] = host_info()
     print(json.dumps(res), flush=True)
 
 
@@ -413,6 +416,7 @@ def projections_main(a):
                      "traffic": None, "algorithmic_flops_per_step": fl_tot},
         "stages": lines,
     }
+    res["host"] = host_info()
     print(json.dumps(res), flush=True)
 
 
@@ -465,6 +469,29 @@ def cpu_baseline(a, inp, kv, k_I, summ, sink_h, scores, idx, cfg, NH):
                   f"{t_idx:.2f}, topk {t_topk:.2f}, attn {t_attn:.2f}, hca {t_hca:.2f}; 'cores' is the OpenMP "
                   f"thread count (attention steps use at most one thread per query)",
     }
+
+
+def host_info():
+    """CPU model, host threads, ROCm / torch versions and the GPU's name, for the record."""
+    import platform
+
+    import torch
+
+    cpu = platform.processor() or ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    rocm = None
+    try:
+        rocm = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        pass
+    return {"cpu_model": cpu, "host_threads": len(os.sched_getaffinity(0)), "rocm": rocm,
+            "torch": torch.__version__, "gpu": torch.cuda.get_device_name(0)}
 
 
 def _time_call(fn):

@@ -11,10 +11,12 @@
 // One GEMM core serves both: C[m][n] = sum_k A[m][k] B[n][k] (both operands K-contiguous,
 // as activations [rows][K] and weights [out][in] are stored), fp32 accumulation on
 // v_mfma_f32_32x32x16_bf16.
-//   - workgroup tile 128 (M) x 128 (N), 4 wavefronts of 64 x 64 (2 x 2 blocks of 32 x 32);
-//   - the K loop runs over 32-wide slices through a ring of kStages LDS stages; slices
-//     go from memory straight into LDS by buffer loads with the LDS destination (16 bytes
-//     per lane), kStages - 1 slices ahead of the one being multiplied;
+//   - workgroup tile 64 MI (M) x 128 (N), 2 x 2 wavefronts of 32 MI x 64 (MI x 2 blocks of
+//     32 x 32): MI = 4 for the plain GEMM, MI = 2 for the compressor (its epilogue tile
+//     has to fit LDS);
+//   - the K loop runs over 32-wide slices through a ring of LDS stages; slices go from
+//     memory straight into LDS by buffer loads with the LDS destination (16 bytes per
+//     lane), all but one stage ahead of the slice being multiplied;
 //   - a slice row is 64 bytes = four 16-byte chunks; chunk c of tile row r sits in LDS slot
 //     c ^ ((r / 4) % 4) (the lanes of a load fetch the permuted chunks, so the LDS side
 //     stays one contiguous 1 KiB write per instruction), which spreads the 32 rows of a
