@@ -14,7 +14,8 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# CSA_ORACLE_LIB names another build of oracle.c (the sanitizer test's instrumented one)
+LIB_PATH = os.environ.get("CSA_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 SRC_PATH = os.path.join(_HERE, "oracle.c")
 
 

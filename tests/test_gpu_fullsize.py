@@ -102,8 +102,8 @@ def test_decode_step_full_size(csa, orc, name, keys):
                "new index key")
     assert_rel(step.summ_new, orc.compress(hb["C"], hb["Z"], ratio=128, overlap=0), TOL_BF16, "new summary")
 
-    # index scores: 1,024 sampled entries (both ends included) of every sequence
-    ids = np.unique(np.concatenate([[0, 1, N - 2, N - 1], W.distinct_sample(1020, N, cfg.seed, "fullsize_ids")]))
+    # index scores: 4,096 sampled entries (both ends included) of every sequence
+    ids = np.unique(np.concatenate([[0, 1, N - 2, N - 1], W.distinct_sample(4092, N, cfg.seed, "fullsize_ids")]))
     if fp4:
         rc, rs = orc.mxfp4_encode(step.kI_new.view(B, 64, 128), hadamard=True)
         np.testing.assert_array_equal(inp["k_I"][:, N - 1].cpu().numpy(), rc)
@@ -216,8 +216,8 @@ def test_pro_prefill_chunk_full_size(csa, orc):
     assert_rel(ch.kv_new, orc.compress(C["Ca"], C["Za"], C["Cb"], C["Zb"], cr["C"], cr["Z"]), TOL_BF16,
                "chunk KV entries")
 
-    # 16 sampled queries (both ends of the chunk included)
-    sel = np.unique(np.concatenate([[0, 1, T // 2, T - 2, T - 1], W.distinct_sample(11, T, cfg.seed, "fs_q")]))
+    # every 64th query plus the first and last 16 (160 queries)
+    sel = np.unique(np.concatenate([np.arange(16), np.arange(T - 16, T), np.arange(0, T, 64)]))
     st = torch.from_numpy(sel).to(DEV)
     pos = inp["q_pos"].index_select(0, st)
     # index scores: 2,048 sampled entries, including each sampled query's causal boundary
@@ -252,7 +252,8 @@ def test_hca_prefill_chunk_full_size(csa, orc):
         f()
     torch.cuda.synchronize()
     assert_rel(ch.summ_new, orc.compress(inp["C"], inp["Z"], ratio=128, overlap=0), TOL_BF16, "chunk summaries")
-    sel = np.unique(np.concatenate([[0, 127, 128, T - 1], W.distinct_sample(4, T, cfg.seed, "fs_h")]))
+    # every 64th query plus the first and last 16 (96 queries; 127 / 128 straddle a summary edge)
+    sel = np.unique(np.concatenate([np.arange(16), np.arange(T - 16, T), np.arange(0, T, 64), [127, 128]]))
     st = torch.from_numpy(sel).to(DEV)
     ref, rlse = orc.hca_attn(inp["q"].index_select(0, st), inp["summ"], inp["sink"], 128, cfg.scale, inp["swa"],
                              inp["swa_pos0"], cfg.window, inp["q_seq"].index_select(0, st),
