@@ -139,12 +139,11 @@ def main():
         return e0.elapsed_time(e1) / reps
 
     stages = {
-        "compress_csa_kv_and_index_key": timed(step.compress),
+        "compress_kv_index_key_summary": timed(step.compress),
         **({"quantize_q_mxfp4": timed(step.index_prep)} if fp4 else {}),
         **({"index_topk_fused": timed(step.index, reps=10)} if step.fused else
            {"index_scores": timed(step.index, reps=10), "topk": timed(step.select)}),
         "sparse_attn": timed(step.attend),
-        "compress_hca": timed(step.hca_compress),
         "hca_attn": timed(step.hca),
     }
     kv, k_I, summ, sink_h, scores, idx = inp["kv"], inp["k_I"], inp["summ"], inp["sink_h"], step.scores, step.idx

@@ -81,6 +81,28 @@ int csa_compress(const void *C_a, const void *C_b, const void *Z_a, const void *
                  void *out, int64_t out_bstride, void *stream);
 
 /*
+ * csa_compress_batch - several csa_compress poolings in one launch (a decode step's new KV
+ * entry, index key and HCA summary: §4.1 and §5 applied to the block that completes with
+ * the step). Each job has exactly the arguments and meaning of csa_compress; all jobs share
+ * dt. Jobs whose rows allow 16-byte accesses (c a multiple of 8 for bf16 / 4 for fp32,
+ * 16-byte aligned tensors and batch stride) run in one kernel; otherwise the jobs run one
+ * launch each, in order. Jobs must not write what another job of the call reads.
+ * Supported: 0 <= njobs <= 8; each job as csa_compress. Errors: as csa_compress, checked
+ * for every job before anything is launched.
+ */
+typedef struct csa_compress_job {
+    const void *C_a, *C_b, *Z_a, *Z_b;     /* [B][n][c] (C_b, Z_b for overlap == 1) */
+    const void *carry_C_b, *carry_Z_b;     /* [B][ratio][c] or both NULL */
+    const float *logit_bias;               /* [(1+overlap)*ratio][c] or NULL */
+    int B;
+    int64_t n;
+    int c, ratio, overlap;
+    void *out;                             /* [B][n/ratio][c], batch stride out_bstride */
+    int64_t out_bstride;
+} csa_compress_job;
+int csa_compress_batch(const csa_compress_job *jobs, int njobs, csa_dtype dt, void *stream);
+
+/*
  * csa_compress_hidden - the compressor fed from hidden states (§4.1: the compressor forms
  * C^a, C^b, Z^a, Z^b from H; §7: Compressor.forward opens with project_a / project_b of
  * the hidden rows): the projections and the pooling of csa_compress in one kernel.

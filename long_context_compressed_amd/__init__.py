@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libcsa.so")
 F32, BF16, MXFP4, KV8 = 0, 1, 2, 3
 KV8_ROW_BYTES = 592  # one 512-dim compressed row in the FP8 storage format
 STATUS = {0: "CSA_OK", 1: "CSA_EINVAL", 2: "CSA_EUNSUPPORTED", 3: "CSA_EWORKSPACE", 4: "CSA_EHIP"}
-EXPORTS = ("csa_compress", "csa_compress_hidden", "csa_quantize_kv8", "csa_out_proj_workspace_bytes", "csa_out_proj",
+EXPORTS = ("csa_compress", "csa_compress_batch", "csa_compress_hidden", "csa_quantize_kv8", "csa_out_proj_workspace_bytes", "csa_out_proj",
            "csa_index_scores", "csa_index_topk_workspace_bytes", "csa_index_topk", "csa_index_rescore", "csa_quantize_mxfp4", "csa_rmsnorm_rope",
            "csa_topk_workspace_bytes",
            "csa_topk", "csa_topk_noalloc", "csa_topk_ids",
@@ -45,6 +45,7 @@ def lib() -> C.CDLL:
         L = C.CDLL(LIB_PATH)
         P, i32, i64, f32, sz = C.c_void_p, C.c_int, C.c_int64, C.c_float, C.c_size_t
         L.csa_compress.argtypes = [P, P, P, P, P, P, P, i32, i64, i32, i32, i32, i32, P, i64, P]
+        L.csa_compress_batch.argtypes = [P, i32, i32, P]
         L.csa_quantize_kv8.argtypes = [P, i64, i32, P, i64, i64, P]
         L.csa_compress_hidden.argtypes = [P, P, P, P, i32, i64, i64, i32, i32, i32, i32, P, i64, P]
         L.csa_out_proj_workspace_bytes.argtypes = [i32, i32, i32]
@@ -68,7 +69,7 @@ def lib() -> C.CDLL:
                                       i32, i32, i64, i32, i32, i32, P, P, P, sz, P]
         L.hca_attn.argtypes = [P, P, P, i32, f32, P, P, i32, i32, P, P, P, i32,
                                i32, i32, i64, i32, i32, i32, P, P, P, sz, P]
-        for f in ("csa_compress", "csa_compress_hidden", "csa_quantize_kv8", "csa_out_proj", "csa_index_scores", "csa_index_topk", "csa_index_rescore", "csa_quantize_mxfp4", "csa_rmsnorm_rope",
+        for f in ("csa_compress", "csa_compress_batch", "csa_compress_hidden", "csa_quantize_kv8", "csa_out_proj", "csa_index_scores", "csa_index_topk", "csa_index_rescore", "csa_quantize_mxfp4", "csa_rmsnorm_rope",
                   "csa_topk", "csa_topk_noalloc",
                   "csa_topk_ids", "csa_sparse_attn", "hca_attn"):
             getattr(L, f).restype = C.c_int
@@ -156,6 +157,37 @@ def quantize_kv8(x, out=None, group_rows=0, group_stride=0, stream=None):
 def _attn_dt(q, kv):
     """The call's dtype: q's, or CSA_KV8 when the compressed rows are uint8 FP8-format rows."""
     return KV8 if kv.dtype == torch.uint8 else _dt(q)
+
+
+class _CompressJob(C.Structure):
+    # the layout of csa_compress_job in include/csa.h
+    _fields_ = [("C_a", C.c_void_p), ("C_b", C.c_void_p), ("Z_a", C.c_void_p), ("Z_b", C.c_void_p),
+                ("carry_C_b", C.c_void_p), ("carry_Z_b", C.c_void_p), ("logit_bias", C.c_void_p),
+                ("B", C.c_int), ("n", C.c_int64), ("c", C.c_int), ("ratio", C.c_int), ("overlap", C.c_int),
+                ("out", C.c_void_p), ("out_bstride", C.c_int64)]
+
+
+def compress_batch(jobs, stream=None):
+    """csa_compress_batch: `jobs` is a list of dicts with the arguments of compress()
+    (C_a, Z_a, C_b, Z_b, carry_C_b, carry_Z_b, logit_bias, ratio, overlap, out); every
+    `out` must be given (a tensor or a strided view into a cache). One launch for all."""
+    arr = (_CompressJob * max(1, len(jobs)))()
+    dt = None
+    for i, j in enumerate(jobs):
+        Ca, out = j["C_a"], j["out"]
+        B, n, c = Ca.shape
+        ratio = j.get("ratio", 4)
+        _require(out is not None and out.dim() == 3 and out.shape[0] == B and out.shape[2] == c
+                 and out.shape[1] >= n // ratio and out.stride(2) == 1 and out.stride(1) == c,
+                 "csa_compress_batch", f"job {i}: out must be [B][>= n/ratio][c] with rows of c contiguous")
+        d = _dt(Ca)
+        _require(dt is None or d == dt, "csa_compress_batch", "all jobs must share one dtype")
+        dt = d
+        arr[i] = _CompressJob(_ptr(Ca), _ptr(j.get("C_b")), _ptr(j["Z_a"]), _ptr(j.get("Z_b")),
+                              _ptr(j.get("carry_C_b")), _ptr(j.get("carry_Z_b")), _ptr(j.get("logit_bias")), B, n, c,
+                              ratio, j.get("overlap", 1 if ratio == 4 else 0), _ptr(out), out.stride(0))
+    rc = lib().csa_compress_batch(C.cast(arr, C.c_void_p), len(jobs), BF16 if dt is None else dt, _stream(stream))
+    _check("csa_compress_batch", rc)
 
 
 def compress_hidden(hidden, W, carry_hidden=None, logit_bias=None, ratio=4, overlap=1, out=None,

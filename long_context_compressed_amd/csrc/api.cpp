@@ -84,6 +84,36 @@ int csa_compress(const void *C_a, const void *C_b, const void *Z_a, const void *
                            logit_bias, B, n, c, ratio, overlap, dt, out, out_bstride, (hipStream_t)stream);
 }
 
+int csa_compress_batch(const csa_compress_job *jobs, int njobs, csa_dtype dt, void *stream) {
+    clear_error();
+    REQUIRE(njobs >= 0 && (njobs == 0 || jobs != nullptr), CSA_EINVAL, "csa_compress_batch: need jobs for njobs > 0");
+    REQUIRE(njobs <= 8, CSA_EUNSUPPORTED, "csa_compress_batch: at most 8 jobs per call");
+    REQUIRE(dt == CSA_F32 || dt == CSA_BF16, CSA_EINVAL, "csa_compress_batch: dt must be CSA_F32 or CSA_BF16");
+    CompressJobArgs args[8];
+    for (int i = 0; i < njobs; ++i) {
+        const csa_compress_job &j = jobs[i];
+        REQUIRE(j.B >= 0 && j.n >= 0 && j.c > 0, CSA_EINVAL, "csa_compress_batch: a job needs B >= 0, n >= 0, c > 0");
+        REQUIRE(j.ratio > 0 && (j.overlap == 0 || j.overlap == 1), CSA_EINVAL,
+                "csa_compress_batch: a job needs ratio > 0, overlap in {0,1}");
+        REQUIRE((j.ratio == 4 && j.overlap == 1) || (j.ratio == 128 && j.overlap == 0), CSA_EUNSUPPORTED,
+                "csa_compress_batch: supported (ratio, overlap) pairs are (4, 1) and (128, 0)");
+        const int64_t E = j.n / j.ratio;
+        REQUIRE((j.carry_C_b == nullptr) == (j.carry_Z_b == nullptr), CSA_EINVAL,
+                "csa_compress_batch: carry_C_b and carry_Z_b must both be given or both be NULL");
+        REQUIRE(j.overlap || j.carry_C_b == nullptr, CSA_EINVAL, "csa_compress_batch: a carry needs overlap == 1");
+        REQUIRE(j.out_bstride == 0 || j.out_bstride >= E * j.c, CSA_EINVAL, "csa_compress_batch: out_bstride < (n/ratio)*c");
+        if (j.B > 0 && E > 0) {
+            REQUIRE(j.C_a && j.Z_a && j.out, CSA_EINVAL, "csa_compress_batch: C_a, Z_a and out are required");
+            REQUIRE(!j.overlap || (j.C_b && j.Z_b), CSA_EINVAL,
+                    "csa_compress_batch: C_b and Z_b are required when overlap == 1");
+        }
+        args[i] = CompressJobArgs{j.C_a, j.overlap ? j.C_b : nullptr, j.Z_a, j.overlap ? j.Z_b : nullptr,
+                                  j.carry_C_b, j.carry_Z_b, j.logit_bias, j.B, j.n, j.c, j.ratio, j.overlap,
+                                  j.out, j.out_bstride};
+    }
+    return launch_compress_batch(args, njobs, dt, (hipStream_t)stream);
+}
+
 int csa_compress_hidden(const void *hidden, const void *carry_hidden, const void *W, const float *logit_bias, int B,
                         int64_t n, int64_t d, int c, int ratio, int overlap, csa_dtype out_dt, void *out,
                         int64_t out_bstride, void *stream) {

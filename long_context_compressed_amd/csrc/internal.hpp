@@ -5,6 +5,17 @@
 
 namespace csa {
 
+// one pooling of a batch (the arguments of csa_compress)
+struct CompressJobArgs {
+    const void *Ca, *Cb, *Za, *Zb, *cCb, *cZb;
+    const float *bias;
+    int B;
+    int64_t n;
+    int c, ratio, overlap;
+    void *out;
+    int64_t out_bstride;
+};
+int launch_compress_batch(const CompressJobArgs *jobs, int njobs, csa_dtype dt, hipStream_t st);
 int launch_compress(const void *Ca, const void *Cb, const void *Za, const void *Zb,
                     const void *cCb, const void *cZb, const float *bias, int B, int64_t n, int c,
                     int ratio, int overlap, csa_dtype dt, void *out, int64_t out_bstride,

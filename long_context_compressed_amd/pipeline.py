@@ -9,8 +9,8 @@ from __future__ import annotations
 
 import torch
 
-from . import (attn_workspace_bytes, compress, hca_attn, index_scores, index_topk, index_topk_workspace,
-               quantize_kv8, quantize_mxfp4, sparse_attn, topk, topk_workspace_bytes)
+from . import (attn_workspace_bytes, compress, compress_batch, hca_attn, index_scores, index_topk,
+               index_topk_workspace, quantize_kv8, quantize_mxfp4, sparse_attn, topk, topk_workspace_bytes)
 
 
 def _ws(nbytes, dev):
@@ -72,13 +72,22 @@ class DecodeStep:
         self.lse_h = torch.empty((T, H), dtype=torch.float32, device=dev)
 
     def compress(self):
+        """The block completing with the step, pooled three ways in one launch: the new KV
+        entry and index key (ratio 4, with their carries) and the new HCA summary (ratio
+        128); then the encodings of the FP8 caches / the MXFP4 index key, if any."""
         i = self.inp
-        b, c, ib, ic = i["blk"], i["carry"], i["iblk"], i["icarry"]
-        compress(b["Ca"], b["Za"], b["Cb"], b["Zb"], c["C"], c["Z"], ratio=4, overlap=1, out=self.kv_new)
-        if self.kv8:  # the new entry of every sequence into row N-1 of its FP8 cache
-            N = i["kv"].shape[1]
+        b, c, ib, ic, h = i["blk"], i["carry"], i["iblk"], i["icarry"], i["hblk"]
+        compress_batch([
+            dict(C_a=b["Ca"], Z_a=b["Za"], C_b=b["Cb"], Z_b=b["Zb"], carry_C_b=c["C"], carry_Z_b=c["Z"], ratio=4,
+                 out=self.kv_new),
+            dict(C_a=ib["Ca"], Z_a=ib["Za"], C_b=ib["Cb"], Z_b=ib["Zb"], carry_C_b=ic["C"], carry_Z_b=ic["Z"],
+                 ratio=4, out=self.kI_new),
+            dict(C_a=h["C"], Z_a=h["Z"], ratio=128, out=self.summ_new),
+        ])
+        if self.kv8:  # the new entry and summary of every sequence into the last rows of the FP8 caches
+            N, NH = i["kv"].shape[1], i["summ"].shape[1]
             quantize_kv8(self.kv_new, out=i["kv"][0, N - 1], group_rows=1, group_stride=N)
-        compress(ib["Ca"], ib["Za"], ib["Cb"], ib["Zb"], ic["C"], ic["Z"], ratio=4, overlap=1, out=self.kI_new)
+            quantize_kv8(self.summ_new, out=i["summ"][0, NH - 1], group_rows=1, group_stride=NH)
         if self.mxfp4:  # rotate and encode the new key into the last entry of every sequence
             kI, ks = i["k_I"], i["k_I_scale"]
             N = kI.shape[1]
@@ -113,13 +122,6 @@ class DecodeStep:
                     i["q_seq"], i["q_pos"], i["rope_cs"], self.rope_dim, out=self.out, lse=self.lse,
                     workspace=self.attn_ws)
 
-    def hca_compress(self):
-        h = self.inp["hblk"]
-        compress(h["C"], h["Z"], ratio=128, overlap=0, out=self.summ_new)
-        if self.kv8:
-            NH = self.inp["summ"].shape[1]
-            quantize_kv8(self.summ_new, out=self.inp["summ"][0, NH - 1], group_rows=1, group_stride=NH)
-
     def hca(self):
         i = self.inp
         hca_attn(i["q"], i["summ"], i["sink_h"], 128, self.scale, i["swa"], i["swa_pos0"], self.window,
@@ -139,7 +141,6 @@ class DecodeStep:
             index_events[1].record()
         self.select()
         self.attend()
-        self.hca_compress()
         self.hca()
 
     graphs = None
@@ -153,7 +154,7 @@ class DecodeStep:
         does not need). Every buffer the step touches is allocated in __init__, so the
         graphs stay valid for the object's life; the library records no memset, only
         kernels."""
-        parts = ((self.compress, self.index_prep), (self.select, self.attend, self.hca_compress, self.hca))
+        parts = ((self.compress, self.index_prep), (self.select, self.attend, self.hca))
         graphs = []
         torch.cuda.synchronize()
         for fns in parts:

@@ -97,6 +97,27 @@ def test_topk_noalloc_validation(L):
     assert b"scratch" in L.csa_last_error()
 
 
+def test_compress_batch_validation(L):
+    import long_context_compressed_amd as csa
+    Job = csa._CompressJob
+
+    def jobs(**kw):
+        a = dict(C_a=1, C_b=1, Z_a=1, Z_b=1, carry_C_b=None, carry_Z_b=None, logit_bias=None, B=1, n=8, c=512,
+                 ratio=4, overlap=1, out=1, out_bstride=0)
+        a.update(kw)
+        arr = (Job * 1)(Job(**a))
+        return C.cast(arr, C.c_void_p)
+    assert L.csa_compress_batch(None, 0, 1, None) == 0
+    assert L.csa_compress_batch(None, 1, 1, None) == 1
+    assert L.csa_compress_batch(jobs(), 9, 1, None) == 2
+    assert L.csa_compress_batch(jobs(), 1, 2, None) == 1          # MXFP4 is not a compressor dtype
+    assert L.csa_compress_batch(jobs(ratio=8), 1, 1, None) == 2
+    assert L.csa_compress_batch(jobs(carry_C_b=1), 1, 1, None) == 1
+    assert L.csa_compress_batch(jobs(C_b=None), 1, 1, None) == 1
+    assert L.csa_compress_batch(jobs(out_bstride=5), 1, 1, None) == 1
+    assert L.csa_compress_batch(jobs(n=3), 1, 1, None) == 0       # no complete block: nothing to launch
+
+
 def test_index_topk_validation(L):
     def f(**kw):
         a = dict(T=4, B=1, N=262144, H=64, D=128, ratio=4, k=1024, idx=1, ws=None, wsb=0)

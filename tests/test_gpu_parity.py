@@ -63,6 +63,43 @@ def test_compress_bias_and_cache_stride(csa, orc):
     assert torch.count_nonzero(cache[:, :N - 1]) == 0
 
 
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_compress_batch(csa, orc, dt):
+    """csa_compress_batch: a decode step's three poolings (two ratio-4 jobs with carries, one
+    ratio-128 job into a strided cache view) in one launch equal the separate calls bit for
+    bit and the oracle; with a job whose channel count rules out 16-byte rows the batch runs
+    job by job and still matches."""
+    say("compress_batch", dt)
+    s = 4321
+    B = 3
+    jobs, refs = [], []
+    for name, n, c, ratio in (("kv", 4, 512, 4), ("key", 4, 1024, 4), ("summ", 128, 256, 128), ("odd", 8, 200, 4)):
+        t = {k: W.normal((B, n, c), s, name + k, dtype=dt, device=DEV) for k in ("Ca", "Za", "Cb", "Zb")}
+        ov = 1 if ratio == 4 else 0
+        carry = {k: W.normal((B, 4, c), s, name + "carry" + k, dtype=dt, device=DEV) for k in ("C", "Z")}
+        cache = torch.zeros((B, 7, c), dtype=dt, device=DEV)
+        out = cache[:, 5:5 + n // ratio, :]
+        j = dict(C_a=t["Ca"], Z_a=t["Za"], ratio=ratio, out=out)
+        if ov:
+            j.update(C_b=t["Cb"], Z_b=t["Zb"], carry_C_b=carry["C"], carry_Z_b=carry["Z"])
+        jobs.append(j)
+        sep = csa.compress(t["Ca"], t["Za"], j.get("C_b"), j.get("Z_b"), j.get("carry_C_b"), j.get("carry_Z_b"),
+                           ratio=ratio, overlap=ov)
+        ref = orc.compress(t["Ca"], t["Za"], j.get("C_b"), j.get("Z_b"), j.get("carry_C_b"), j.get("carry_Z_b"),
+                           ratio=ratio, overlap=ov)
+        refs.append((name, cache, out, sep, ref))
+    tol = TOL_F32 if dt == torch.float32 else TOL_BF16
+    for sub in (jobs[:3], jobs):  # all 16-byte rows: one kernel; with the odd job: one launch per job
+        for _, cache, *_ in refs:
+            cache.zero_()
+        csa.compress_batch(sub)
+        torch.cuda.synchronize()
+        for (name, cache, out, sep, ref) in refs[:len(sub)]:
+            assert torch.equal(out, sep), f"{name}: batch vs separate call"
+            assert_rel(out, ref, tol, f"compress_batch {name}")
+            assert torch.count_nonzero(cache[:, :5]) == 0, f"{name}: wrote outside its rows"
+
+
 @pytest.mark.parametrize("dt,B,n,c", [(torch.float32, 1, 128 * 5 + 17, 64), (torch.bfloat16, 2, 4096, 512)])
 def test_compress_hca128(csa, orc, dt, B, n, c):
     say("compress128", dt, B, n, c)
