@@ -32,14 +32,17 @@ namespace csa {
 
 namespace {
 
-constexpr int TQ = 256;       // queries per workgroup
+constexpr int TQ = 128;       // queries per workgroup
 constexpr int TE = 128;       // entries per workgroup
 
 typedef int i32x4v __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 3; }
 
-__global__ void __launch_bounds__(512, 1)
+// Two workgroups of 4 wavefronts share a compute unit (77 KB of LDS each): each keeps its
+// own barriers, so while one runs a head's matrix ops the other can run its ReLU.w
+// epilogue on the same SIMDs (within one wavefront the two do not overlap).
+__global__ void __launch_bounds__(256, 2)
 index_mxfp4_mfma_kernel(const uint8_t *__restrict__ qI, const uint8_t *__restrict__ qS,
                         const float *__restrict__ w, const uint8_t *__restrict__ kI,
                         const uint8_t *__restrict__ kS, const int32_t *__restrict__ q_seq,
@@ -48,11 +51,11 @@ index_mxfp4_mfma_kernel(const uint8_t *__restrict__ qI, const uint8_t *__restric
 {
     __shared__ __attribute__((aligned(16))) uint8_t Qs[2][TQ * 64];
     __shared__ __attribute__((aligned(16))) uint8_t Ks[2][TE * 64];
-    // scale words of 8 heads at a time, head-major ([head % 8][row]), double buffered
-    __shared__ __attribute__((aligned(16))) uint32_t QSs[2][8][TQ];
-    __shared__ __attribute__((aligned(16))) uint32_t KSs[2][8][TE];
+    // scale words of 4 heads at a time, head-major ([head % 4][row]), double buffered
+    __shared__ __attribute__((aligned(16))) uint32_t QSs[2][4][TQ];
+    __shared__ __attribute__((aligned(16))) uint32_t KSs[2][4][TE];
     __shared__ __attribute__((aligned(16))) float Ws[64 * TQ];  // head-major: [head][query]
-    __shared__ int64_t nvis_s[TQ];
+    __shared__ int32_t nvis_s[TQ];
     __shared__ int red[2];
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -66,7 +69,8 @@ index_mxfp4_mfma_kernel(const uint8_t *__restrict__ qI, const uint8_t *__restric
     const int t0 = qb * TQ;
     const int64_t i0 = (int64_t)eb * TE;
 
-    // visibility of each query of the tile (a query of another sequence sees nothing)
+    // visibility of each query of the tile (a query of another sequence sees nothing);
+    // N < 2^31 entries (checked by the caller), so counts fit 32 bits
     if (tid < TQ) {
         const int t = t0 + tid;
         int64_t nv = 0;
@@ -74,7 +78,7 @@ index_mxfp4_mfma_kernel(const uint8_t *__restrict__ qI, const uint8_t *__restric
             nv = q_pos[t] / ratio;
             nv = nv < 0 ? 0 : (nv > N ? N : nv);
         }
-        nvis_s[tid] = nv;
+        nvis_s[tid] = (int32_t)nv;
     }
     if (tid == 0) red[0] = 0;
     __syncthreads();
@@ -83,7 +87,7 @@ index_mxfp4_mfma_kernel(const uint8_t *__restrict__ qI, const uint8_t *__restric
     const bool any_visible = red[0] != 0;
 
     // wave (qg, eg) owns queries qg*64.. and entries eg*64.. of the tile
-    const int qg = wv & 3, eg = wv >> 2;
+    const int qg = wv & 1, eg = wv >> 1;
     f32x4 acc[4][4];
 #pragma unroll
     for (int m = 0; m < 4; ++m)
@@ -93,69 +97,67 @@ index_mxfp4_mfma_kernel(const uint8_t *__restrict__ qI, const uint8_t *__restric
     if (any_visible) {
         // head weights of the tile's queries
 #pragma unroll 4
-        for (int x = tid; x < TQ * 64; x += 512) {
+        for (int x = tid; x < TQ * 64; x += 256) {
             const int qq = x % TQ, h = x / TQ;
             const int t = t0 + qq;
             Ws[h * TQ + qq] = (t < T) ? w[(int64_t)t * 64 + h] : 0.f;
         }
-        // per-wave share of one head's codes: 32 q rows and 16 k rows (16 bytes per lane per
+        // per-wave share of one head's codes: 32 q rows and 32 k rows (16 bytes per lane per
         // 16-row group), loaded into registers while the previous head is computed, then
         // written to LDS
         const int qrow0 = wv * 32 + (lane >> 2), qrow1 = qrow0 + 16;
-        const int krow = wv * 16 + (lane >> 2);
+        const int krow0 = qrow0, krow1 = qrow1;
         const int qpos0 = ((lane & 3) ^ swz(qrow0)) * 16, qpos1 = ((lane & 3) ^ swz(qrow1)) * 16;
-        const int kpos = ((lane & 3) ^ swz(krow)) * 16;
+        const int kpos0 = qpos0, kpos1 = qpos1;
         int tq0 = t0 + qrow0, tq1 = t0 + qrow1;
         tq0 = tq0 < T ? tq0 : T - 1;
         tq1 = tq1 < T ? tq1 : T - 1;
-        int64_t ek = i0 + krow;
-        ek = ek < N ? ek : N - 1;
+        int64_t ek0 = i0 + krow0, ek1 = i0 + krow1;
+        ek0 = ek0 < N ? ek0 : N - 1;
+        ek1 = ek1 < N ? ek1 : N - 1;
         const uint8_t *qsrc0 = qI + (int64_t)tq0 * 4096 + (lane & 3) * 16;
         const uint8_t *qsrc1 = qI + (int64_t)tq1 * 4096 + (lane & 3) * 16;
-        const uint8_t *ksrc = kI + ek * 4096 + (lane & 3) * 16;
-        // scales, 8 heads (32 bytes of a row) at a time: thread i loads 16 bytes of q row
-        // i / 2 and, for i < 256, of k row i / 2 (half i % 2 of the row's 8 heads); a block's
-        // scales are loaded at its predecessor's first head and stored at its last
-        const int srow = tid >> 1, shalf = tid & 1;
+        const uint8_t *ksrc0 = kI + ek0 * 4096 + (lane & 3) * 16;
+        const uint8_t *ksrc1 = kI + ek1 * 4096 + (lane & 3) * 16;
+        // scales, 4 heads (16 bytes of a row) at a time: threads 0..127 load q row tid,
+        // threads 128..255 k row tid - 128; a block's scales are loaded at its predecessor's
+        // first head and stored at its last
+        const bool sq = tid < TQ;
+        const int srow = sq ? tid : tid - TQ;
         int tsq = t0 + srow;
         tsq = tsq < T ? tsq : T - 1;
-        int64_t esk = i0 + (srow & (TE - 1));
+        int64_t esk = i0 + srow;
         esk = esk < N ? esk : N - 1;
-        const uint8_t *sqsrc = qS + (int64_t)tsq * 256 + shalf * 16;
-        const uint8_t *sksrc = kS + esk * 256 + shalf * 16;
-        uint4 rsq, rsk = uint4{0u, 0u, 0u, 0u};
+        const uint8_t *ssrc = sq ? qS + (int64_t)tsq * 256 : kS + esk * 256;
+        uint4 rs;
 #define FP4_SLOAD(BLK)                                                                   \
     {                                                                                   \
-        rsq = *reinterpret_cast<const uint4 *>(sqsrc + (BLK) * 32);                     \
-        if (tid < 2 * TE) rsk = *reinterpret_cast<const uint4 *>(sksrc + (BLK) * 32);   \
+        rs = *reinterpret_cast<const uint4 *>(ssrc + (BLK) * 16);                        \
     }
 #define FP4_SSTORE(SB)                                                                   \
     {                                                                                   \
-        QSs[SB][shalf * 4 + 0][srow] = rsq.x;                                           \
-        QSs[SB][shalf * 4 + 1][srow] = rsq.y;                                           \
-        QSs[SB][shalf * 4 + 2][srow] = rsq.z;                                           \
-        QSs[SB][shalf * 4 + 3][srow] = rsq.w;                                           \
-        if (tid < 2 * TE) {                                                             \
-            KSs[SB][shalf * 4 + 0][srow] = rsk.x;                                       \
-            KSs[SB][shalf * 4 + 1][srow] = rsk.y;                                       \
-            KSs[SB][shalf * 4 + 2][srow] = rsk.z;                                       \
-            KSs[SB][shalf * 4 + 3][srow] = rsk.w;                                       \
-        }                                                                               \
+        uint32_t(*dst)[TQ] = sq ? QSs[SB] : KSs[SB];                                    \
+        dst[0][srow] = rs.x;                                                            \
+        dst[1][srow] = rs.y;                                                            \
+        dst[2][srow] = rs.z;                                                            \
+        dst[3][srow] = rs.w;                                                            \
     }
         // two register sets (A: even heads, B: odd heads): head h+2 is loaded while head h
         // is computed, and head h+1 (loaded one head earlier) is written to LDS after it
-        uint4 rq0A, rq1A, rkA, rq0B, rq1B, rkB;
+        uint4 rq0A, rq1A, rk0A, rk1A, rq0B, rq1B, rk0B, rk1B;
 #define FP4_LOAD(S, HH)                                                                  \
     {                                                                                   \
         rq0##S = *reinterpret_cast<const uint4 *>(qsrc0 + (HH) * 64);                   \
         rq1##S = *reinterpret_cast<const uint4 *>(qsrc1 + (HH) * 64);                   \
-        rk##S = *reinterpret_cast<const uint4 *>(ksrc + (HH) * 64);                     \
+        rk0##S = *reinterpret_cast<const uint4 *>(ksrc0 + (HH) * 64);                   \
+        rk1##S = *reinterpret_cast<const uint4 *>(ksrc1 + (HH) * 64);                   \
     }
 #define FP4_STORE(S, BUF)                                                                \
     {                                                                                   \
         *reinterpret_cast<uint4 *>(&Qs[BUF][qrow0 * 64 + qpos0]) = rq0##S;              \
         *reinterpret_cast<uint4 *>(&Qs[BUF][qrow1 * 64 + qpos1]) = rq1##S;              \
-        *reinterpret_cast<uint4 *>(&Ks[BUF][krow * 64 + kpos]) = rk##S;                 \
+        *reinterpret_cast<uint4 *>(&Ks[BUF][krow0 * 64 + kpos0]) = rk0##S;              \
+        *reinterpret_cast<uint4 *>(&Ks[BUF][krow1 * 64 + kpos1]) = rk1##S;              \
     }
 
         // one head's contraction over LDS buffer BUF: the k codes of the wave's 4 entry tiles
@@ -197,11 +199,11 @@ index_mxfp4_mfma_kernel(const uint8_t *__restrict__ qI, const uint8_t *__restric
         FP4_STORE(A, 0)
         __syncthreads();
 #pragma unroll 1
-        for (int hb = 0; hb < 64; hb += 8) {
-            const int sbuf = (hb >> 3) & 1;
-            FP4_SLOAD(hb + 8 < 64 ? (hb >> 3) + 1 : 7)
+        for (int hb = 0; hb < 64; hb += 4) {
+            const int sbuf = (hb >> 2) & 1;
+            FP4_SLOAD(hb + 4 < 64 ? (hb >> 2) + 1 : 15)
 #pragma unroll 1
-            for (int hs = 0; hs < 8; hs += 2) {
+            for (int hs = 0; hs < 4; hs += 2) {
                 const int h = hb + hs;
                 FP4_LOAD(A, h + 2 < 64 ? h + 2 : 63)
                 FP4_COMPUTE(h, 0, hs)
@@ -209,7 +211,7 @@ index_mxfp4_mfma_kernel(const uint8_t *__restrict__ qI, const uint8_t *__restric
                 __syncthreads();
                 FP4_LOAD(B, h + 3 < 64 ? h + 3 : 63)
                 FP4_COMPUTE(h + 1, 1, hs + 1)
-                if (hs == 6) FP4_SSTORE(sbuf ^ 1)
+                if (hs == 2) FP4_SSTORE(sbuf ^ 1)
                 FP4_STORE(A, 0)
                 __syncthreads();
             }
@@ -458,7 +460,7 @@ int launch_index_mxfp4(const uint8_t *qI, const uint8_t *qs, const float *w, con
         const int nqb = (T + TQ - 1) / TQ;
         const int neb = (int)((N + TE - 1) / TE);
         const int64_t blocks = (int64_t)((nqb + 7) / 8) * 8 * neb;
-        hipLaunchKernelGGL(index_mxfp4_mfma_kernel, dim3((unsigned)blocks), dim3(512), 0, st, qI, qs, w, kI, ks,
+        hipLaunchKernelGGL(index_mxfp4_mfma_kernel, dim3((unsigned)blocks), dim3(256), 0, st, qI, qs, w, kI, ks,
                            q_seq, q_pos, T, N, ratio, nqb, neb, scores);
         return check_launch("index_mxfp4_mfma_kernel");
     }
