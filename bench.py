@@ -138,6 +138,27 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
+    # the same small stages in the step's own conditions: right after an index scan, which
+    # has streamed gigabytes of keys past every cache (the events are enqueued while the scan
+    # runs, so no host gap is timed); the median of 5
+    def in_step(fn, reps=5):
+        ts = []
+        for _ in range(reps):
+            step.index()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    stages_in_step = {
+        "compress_kv_index_key_summary": in_step(step.compress),
+        **({} if step.fused else {"topk": in_step(step.select)}),
+        "sparse_attn": in_step(step.attend),
+        "hca_attn": in_step(step.hca),
+    }
     stages = {
         "compress_kv_index_key_summary": timed(step.compress),
         **({"quantize_q_mxfp4": timed(step.index_prep)} if fp4 else {}),
@@ -197,6 +218,7 @@ def main():
             "min_launch_ms": round(float(np.min(scan_ms)), 4),
         },
         "stages_ms": {kk: round(v, 4) for kk, v in stages.items()},
+        "stages_in_step_ms": {kk: round(v, 4) for kk, v in stages_in_step.items()},
     }
     if a.workload != "pro_decode_1m":
         res["metric"] = f"decode queries/s + indexer GB/s, {a.workload} (profiling line, not the benchmark)"
