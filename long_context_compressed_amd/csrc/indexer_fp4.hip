@@ -8,18 +8,16 @@
 // (one instruction = one head's full dot for a 16 x 16 tile; E2M1 products are exact and
 // the E8M0 block scales are applied inside the instruction).
 //
-// Workgroup: 8 wavefronts, a 256-query x 128-entry tile, wave (qg, eg) owns 64 queries x
-// 64 entries (4 x 4 MFMA tiles, 64 fp32 score accumulators per lane). The loop runs over
-// the 64 heads; per head the tile's q and k codes (16 + 8 KiB) are staged in LDS, double
-// buffered: head h+2 is loaded into registers while head h is computed, and head h+1 is
-// written to the other buffer. The E8M0 scales are staged 8 heads at a time (32 bytes of
-// each row per load, not 4), since the scattered 4-byte loads of one head's scales cost
-// more address-unit cycles than its codes. The epilogue of every MFMA (ReLU, times
-// w[t][h], accumulate) is VALU work and bounds the kernel. The 16-byte chunks of each
-// 64-byte code row are XOR-swizzled in LDS so the per-lane 16-byte operand reads of 8
-// consecutive rows hit distinct banks. The head weights of the tile's queries sit in LDS
-// head-major, so the 4 weights a lane needs per MFMA tile (4 consecutive queries) are one
-// 16-byte read.
+// Workgroup: 4 wavefronts, a 128-query x 128-entry tile; wave (qg, eg) owns 64 queries x
+// 64 entries (4 x 4 matrix-op tiles with the entries as the A operand and the queries as
+// B, so a lane's 4 results of a tile belong to one query and need one head weight). The
+// loop runs over the 64 heads: per head the tile's q and k codes (8 + 8 KiB) go from
+// global memory straight into one of two LDS stages (direct-to-LDS buffer loads issued
+// one head ahead), and per group of 4 heads the tile's E8M0 scale words and head weights
+// (16-byte row slices) into one of two word buffers. The ReLU.w epilogue of each matrix
+// op is VALU work (an integer max and an fma per product), which with the matrix ops and
+// the LDS operand reads sets the kernel's time. Three workgroups share a compute unit
+// (45 KB of LDS, under 128 registers each), so the SIMDs interleave their wavefronts.
 //
 // Decode (a few queries per key store): there is no reuse of keys across queries, so each
 // query streams its keys from HBM (index_mxfp4_scan_kernel below) and the same matrix op
@@ -32,39 +30,164 @@ namespace csa {
 
 namespace {
 
-constexpr int TQ = 128;       // queries per workgroup
-constexpr int TE = 128;       // entries per workgroup
+constexpr int TQ = 128;  // queries per workgroup
+constexpr int TE = 128;  // entries per workgroup
+constexpr int NBUF = 2;  // LDS stages of one head's codes
 
 typedef int i32x4v __attribute__((ext_vector_type(4)));
+typedef int i32x4s __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 3; }
+// XOR swizzle of a code row's four 16-byte chunks in LDS: chunk c of row r sits in slot
+// c ^ swz(r). A 16-byte read instruction serves 16 lanes (64 banks x 4 bytes) per cycle;
+// with this swizzle the 16 rows of a 16-row block cover all 64 banks exactly once.
+__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 
-// Two workgroups of 4 wavefronts share a compute unit (77 KB of LDS each): each keeps its
-// own barriers, so while one runs a head's matrix ops the other can run its ReLU.w
-// epilogue on the same SIMDs (within one wavefront the two do not overlap).
-__global__ void __launch_bounds__(256, 2)
+// raw buffer resource words over [p, p + bytes) (wave-uniform): loads past the end return
+// zeros
+__device__ __forceinline__ i32x4s tile_rsrc(const void *p, uint32_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)p;
+    const int lo = (int)__builtin_amdgcn_readfirstlane((uint32_t)a);
+    const int hi = (int)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xFFFFu);
+    const int n = (int)__builtin_amdgcn_readfirstlane(bytes);
+    return i32x4s{lo, hi, n, 0x00020000};
+}
+
+// LDS byte address of a pointer into __shared__ memory (wave-uniform)
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)(const char *)p);
+}
+
+// Direct-to-LDS load: lane i writes 16 bytes at LDS address dst + 16 i. Written as
+// assembly so that the compiler does not track it: it would otherwise wait for every such
+// load in flight before each LDS read it cannot prove disjoint from them, which drains the
+// prefetch. Completion is waited for explicitly (vmcnt) before the barrier that publishes
+// a stage. The instruction has no register result. It sets M0 (the LDS address register
+// of the direct-to-LDS load; one wait state before the load reads it); nothing else in
+// this file's kernels uses M0 (the compiler reserves it and warns about the clobber).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(i32x4s rs, uint32_t off, uint32_t dst) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(off), "s"(rs), "s"(dst)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// wait until every vector-memory operation and LDS access of this wavefront has completed
+__device__ __forceinline__ void wait_vm_lds() { __builtin_amdgcn_s_waitcnt((7 << 4) | (0 << 8) | 0); }
+
+// workgroup barrier without a memory fence (the fence would wait for every load in flight,
+// the direct-to-LDS ones included); the wait before it says what has completed, and the
+// empty asm keeps the compiler from moving memory accesses across it
+__device__ __forceinline__ void stage_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// LDS: two stages of one head's codes; two buffers of a head group's scale words and
+// weights (row-major, the 4 heads of a row in 16 bytes)
+constexpr int ST_Q = 0, ST_K = TQ * 64, STAGE = ST_K + TE * 64;
+constexpr int MT_QS = 0, MT_KS = TQ * 16, MT_W = MT_KS + TE * 16, META = MT_W + TQ * 16;
+
+// The direct-to-LDS loads of one wavefront. Codes (per head; add h * 64): wave wv moves q
+// rows and k rows wv*32 .. wv*32+31 of the tile, two 16-row groups each (1 KiB per
+// instruction); lane i of a group fills LDS slot (row i/4, 16-byte slot i%4), which holds
+// the row's chunk (i%4) ^ swz(row). Scale words and weights (per group of 4 heads; add
+// g * 16): 16 bytes of a row per lane, one 64-row block per instruction: waves 0-1 move
+// the q scale words and the weights of query rows 64wv.., waves 2-3 the k scale words of
+// entry rows 64(wv-2)...
+struct Fp4Loads {
+    i32x4s qrs, krs, srs, wrs;
+    uint32_t coff, moff, sdst, wdst;
+    bool two;  // waves 0-1: scale words and weights
+};
+
+__device__ __forceinline__ void fp4_load_codes(const Fp4Loads &L, int h, int wv, uint32_t d) {
+    const uint32_t o = L.coff + (uint32_t)(wv * 32) * 4096u + (uint32_t)h * 64u;
+    dma16(L.qrs, o, d + ST_Q + wv * 32 * 64);
+    dma16(L.qrs, o + 16u * 4096u, d + ST_Q + (wv * 32 + 16) * 64);
+    dma16(L.krs, o, d + ST_K + wv * 32 * 64);
+    dma16(L.krs, o + 16u * 4096u, d + ST_K + (wv * 32 + 16) * 64);
+}
+
+__device__ __forceinline__ void fp4_load_words(const Fp4Loads &L, int g, uint32_t d) {
+    dma16(L.srs, L.moff + (uint32_t)g * 16u, d + L.sdst);
+    if (L.two) dma16(L.wrs, L.moff + (uint32_t)g * 16u, d + L.wdst);
+}
+
+// Per-lane LDS byte offsets of one wavefront's reads. The swizzle of a row depends only
+// on its row within a 16-row block (l16), so the 4 row blocks of a lane are 1 KiB apart
+// in a code stage and 256 bytes apart in the word buffers (immediate offsets).
+struct Fp4Lane {
+    uint32_t kc, qc;  // codes: entry row eg*64 + l16 / query row qg*64 + l16, the lane's 16-byte chunk
+    uint32_t ks, qs;  // scale byte g4 (block) of entry / query row, head 0
+    uint32_t wq;      // weight of query row qg*64 + l16, head 0
+};
+
+// One head (hs of its group) for one wavefront: 16 matrix ops, each 16-query row block's
+// 4 results followed by their ReLU.w epilogue into the lane's accumulators (entries
+// 16n + 4g4 + r of query 16m + l16). `rs` / `ms`: LDS byte offsets of the head's code
+// stage and of its group's word buffer.
+__device__ __forceinline__ void fp4_head(const char *lds, uint32_t rs, uint32_t ms, int hs, const Fp4Lane &O,
+                                         f32x4 (&acc)[4][4]) {
+    const char *kc = lds + rs + O.kc, *qc = lds + rs + O.qc;
+    const uint8_t *ks = reinterpret_cast<const uint8_t *>(lds + ms + MT_KS + O.ks + 4 * hs);
+    const uint8_t *qs = reinterpret_cast<const uint8_t *>(lds + ms + MT_QS + O.qs + 4 * hs);
+    const float *wq = reinterpret_cast<const float *>(lds + ms + MT_W + O.wq + 4 * hs);
+    i32x8 Ae[4];
+    int sa[4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+        const i32x4v v = *reinterpret_cast<const i32x4v *>(kc + ST_K + 1024 * n);
+        Ae[n] = i32x8{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+        sa[n] = ks[256 * n];  // the E8M0 byte of block g4 of the lane's row
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const i32x4v v = *reinterpret_cast<const i32x4v *>(qc + ST_Q + 1024 * m);
+        const i32x8 Bq = i32x8{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+        const int sb = qs[256 * m];
+        const float w = wq[64 * m];
+        f32x4 c[4];
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+            c[n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Ae[n], Bq, f32x4{0.f, 0.f, 0.f, 0.f}, 4, 4, 0,
+                                                                   sa[n], 0, sb);
+        // ReLU is an integer max on the bits (negative floats are negative integers)
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                acc[m][n][r] = fmaf(w, __int_as_float(max(__float_as_int(c[n][r]), 0)), acc[m][n][r]);
+    }
+}
+
+// second argument: wavefronts per SIMD the register allocation must allow
+__global__ void __launch_bounds__(256, 3)
 index_mxfp4_mfma_kernel(const uint8_t *__restrict__ qI, const uint8_t *__restrict__ qS,
                         const float *__restrict__ w, const uint8_t *__restrict__ kI,
                         const uint8_t *__restrict__ kS, const int32_t *__restrict__ q_seq,
                         const int64_t *__restrict__ q_pos, int T, int64_t N, int ratio, int nqb, int neb,
                         float *__restrict__ scores)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t Qs[2][TQ * 64];
-    __shared__ __attribute__((aligned(16))) uint8_t Ks[2][TE * 64];
-    // scale words of 4 heads at a time, head-major ([head % 4][row]), double buffered
-    __shared__ __attribute__((aligned(16))) uint32_t QSs[2][4][TQ];
-    __shared__ __attribute__((aligned(16))) uint32_t KSs[2][4][TE];
-    __shared__ __attribute__((aligned(16))) float Ws[64 * TQ];  // head-major: [head][query]
+    __shared__ __attribute__((aligned(16))) char lds[NBUF * STAGE + 2 * META];
     __shared__ int32_t nvis_s[TQ];
-    __shared__ int red[2];
+    __shared__ int red[1];
 
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g4 = lane >> 4;
-    // XCD-aware order: workgroups b, b+8, ... share an XCD; one query block per XCD at a
-    // time (its q tile stays in that XCD's L2) while the entry blocks stream
+    // XCD-aware order: the workgroups of one XCD (b, b+8, ...) run the query blocks
+    // xcd, xcd+8, ... against a group of entry blocks at a time, so at any moment an XCD's
+    // L2 holds a few query and entry tiles, each read by several of its workgroups
     const int b = blockIdx.x;
     const int xcd = b & 7, r8 = b >> 3;
-    const int qb = (r8 / neb) * 8 + xcd, eb = r8 % neb;
+    const int QX = (nqb + 7) >> 3;                 // query blocks per XCD
+    const int EGN = QX >= 64 ? 1 : 64 / QX;        // entry blocks per group
+    const int grp = r8 / (QX * EGN), within = r8 - grp * (QX * EGN);
+    const int qb = (within % QX) * 8 + xcd, eb = grp * EGN + within / QX;
     if (qb >= nqb) return;
     const int t0 = qb * TQ;
     const int64_t i0 = (int64_t)eb * TE;
@@ -95,150 +218,76 @@ index_mxfp4_mfma_kernel(const uint8_t *__restrict__ qI, const uint8_t *__restric
         for (int n = 0; n < 4; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     if (any_visible) {
-        // head weights of the tile's queries
-#pragma unroll 4
-        for (int x = tid; x < TQ * 64; x += 256) {
-            const int qq = x % TQ, h = x / TQ;
-            const int t = t0 + qq;
-            Ws[h * TQ + qq] = (t < T) ? w[(int64_t)t * 64 + h] : 0.f;
+        // rows past T or N read zeros (their scores are not stored)
+        const int rq = T - t0 < TQ ? T - t0 : TQ;
+        const int re = N - i0 < TE ? (int)(N - i0) : TE;
+        Fp4Loads L;
+        L.qrs = tile_rsrc(qI + (int64_t)t0 * 4096, (uint32_t)rq * 4096u);
+        L.krs = tile_rsrc(kI + i0 * 4096, (uint32_t)re * 4096u);
+        L.two = wv < 2;
+        L.srs = L.two ? tile_rsrc(qS + (int64_t)t0 * 256, (uint32_t)rq * 256u)
+                      : tile_rsrc(kS + i0 * 256, (uint32_t)re * 256u);
+        L.wrs = tile_rsrc(w + (int64_t)t0 * 64, (uint32_t)rq * 256u);
+        const int crow = lane >> 2;  // row within a 16-row group (the swizzle depends only on it)
+        L.coff = (uint32_t)crow * 4096u + (uint32_t)(((lane & 3) ^ swz(crow)) * 16);
+        L.moff = (uint32_t)(64 * (wv & 1) + lane) * 256u;
+        L.sdst = (L.two ? MT_QS : MT_KS) + (uint32_t)(wv & 1) * 1024u;
+        L.wdst = MT_W + (uint32_t)(wv & 1) * 1024u;
+        const uint32_t lbase = lds_addr(lds);
+        Fp4Lane O;
+        O.kc = (uint32_t)((eg * 64 + l16) * 64 + ((g4 ^ swz(l16)) * 16));
+        O.qc = (uint32_t)((qg * 64 + l16) * 64 + ((g4 ^ swz(l16)) * 16));
+        O.ks = (uint32_t)((eg * 64 + l16) * 16 + g4);
+        O.qs = (uint32_t)((qg * 64 + l16) * 16 + g4);
+        O.wq = (uint32_t)((qg * 64 + l16) * 16);
+
+        // head group 0's words, then head 0's codes (a group's words always go out before
+        // the codes of its first head, so waiting for those codes covers the words: loads
+        // complete in issue order)
+        fp4_load_words(L, 0, lbase + NBUF * STAGE);
+        fp4_load_codes(L, 0, wv, lbase);
+#pragma unroll 1
+        for (int h = 0; h < 64; ++h) {
+            // head h's loads have landed and every wavefront has finished head h-1, whose
+            // stage (and at a group's start, the word buffer of the group before) the next
+            // loads reuse
+            wait_vm_lds();
+            stage_barrier();
+            const int g = h >> 2, hs = h & 3;
+            if (hs == 0 && g + 1 < 16) fp4_load_words(L, g + 1, lbase + NBUF * STAGE + ((g + 1) & 1) * META);
+            if (h + 1 < 64) fp4_load_codes(L, h + 1, wv, lbase + ((h + 1) & 1) * STAGE);
+            __builtin_amdgcn_sched_barrier(0);
+            fp4_head(lds, (uint32_t)(h & 1) * STAGE, NBUF * STAGE + (uint32_t)(g & 1) * META, hs, O, acc);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        // per-wave share of one head's codes: 32 q rows and 32 k rows (16 bytes per lane per
-        // 16-row group), loaded into registers while the previous head is computed, then
-        // written to LDS
-        const int qrow0 = wv * 32 + (lane >> 2), qrow1 = qrow0 + 16;
-        const int krow0 = qrow0, krow1 = qrow1;
-        const int qpos0 = ((lane & 3) ^ swz(qrow0)) * 16, qpos1 = ((lane & 3) ^ swz(qrow1)) * 16;
-        const int kpos0 = qpos0, kpos1 = qpos1;
-        int tq0 = t0 + qrow0, tq1 = t0 + qrow1;
-        tq0 = tq0 < T ? tq0 : T - 1;
-        tq1 = tq1 < T ? tq1 : T - 1;
-        int64_t ek0 = i0 + krow0, ek1 = i0 + krow1;
-        ek0 = ek0 < N ? ek0 : N - 1;
-        ek1 = ek1 < N ? ek1 : N - 1;
-        const uint8_t *qsrc0 = qI + (int64_t)tq0 * 4096 + (lane & 3) * 16;
-        const uint8_t *qsrc1 = qI + (int64_t)tq1 * 4096 + (lane & 3) * 16;
-        const uint8_t *ksrc0 = kI + ek0 * 4096 + (lane & 3) * 16;
-        const uint8_t *ksrc1 = kI + ek1 * 4096 + (lane & 3) * 16;
-        // scales, 4 heads (16 bytes of a row) at a time: threads 0..127 load q row tid,
-        // threads 128..255 k row tid - 128; a block's scales are loaded at its predecessor's
-        // first head and stored at its last
-        const bool sq = tid < TQ;
-        const int srow = sq ? tid : tid - TQ;
-        int tsq = t0 + srow;
-        tsq = tsq < T ? tsq : T - 1;
-        int64_t esk = i0 + srow;
-        esk = esk < N ? esk : N - 1;
-        const uint8_t *ssrc = sq ? qS + (int64_t)tsq * 256 : kS + esk * 256;
-        uint4 rs;
-#define FP4_SLOAD(BLK)                                                                   \
-    {                                                                                   \
-        rs = *reinterpret_cast<const uint4 *>(ssrc + (BLK) * 16);                        \
-    }
-#define FP4_SSTORE(SB)                                                                   \
-    {                                                                                   \
-        uint32_t(*dst)[TQ] = sq ? QSs[SB] : KSs[SB];                                    \
-        dst[0][srow] = rs.x;                                                            \
-        dst[1][srow] = rs.y;                                                            \
-        dst[2][srow] = rs.z;                                                            \
-        dst[3][srow] = rs.w;                                                            \
-    }
-        // two register sets (A: even heads, B: odd heads): head h+2 is loaded while head h
-        // is computed, and head h+1 (loaded one head earlier) is written to LDS after it
-        uint4 rq0A, rq1A, rk0A, rk1A, rq0B, rq1B, rk0B, rk1B;
-#define FP4_LOAD(S, HH)                                                                  \
-    {                                                                                   \
-        rq0##S = *reinterpret_cast<const uint4 *>(qsrc0 + (HH) * 64);                   \
-        rq1##S = *reinterpret_cast<const uint4 *>(qsrc1 + (HH) * 64);                   \
-        rk0##S = *reinterpret_cast<const uint4 *>(ksrc0 + (HH) * 64);                   \
-        rk1##S = *reinterpret_cast<const uint4 *>(ksrc1 + (HH) * 64);                   \
-    }
-#define FP4_STORE(S, BUF)                                                                \
-    {                                                                                   \
-        *reinterpret_cast<uint4 *>(&Qs[BUF][qrow0 * 64 + qpos0]) = rq0##S;              \
-        *reinterpret_cast<uint4 *>(&Qs[BUF][qrow1 * 64 + qpos1]) = rq1##S;              \
-        *reinterpret_cast<uint4 *>(&Ks[BUF][krow0 * 64 + kpos0]) = rk0##S;              \
-        *reinterpret_cast<uint4 *>(&Ks[BUF][krow1 * 64 + kpos1]) = rk1##S;              \
     }
 
-        // one head's contraction over LDS buffer BUF: the k codes of the wave's 4 entry tiles
-        // stay in registers, the q codes are read per query tile
-#define FP4_COMPUTE(HH, BUF, HS)                                                         \
-    {                                                                                   \
-        i32x4v Bv[4];                                                                   \
-        int sb[4];                                                                      \
-        _Pragma("unroll") for (int n = 0; n < 4; ++n) {                                 \
-            const int row = eg * 64 + 16 * n + l16;                                     \
-            Bv[n] = *reinterpret_cast<const i32x4v *>(&Ks[BUF][row * 64 + ((g4 ^ swz(row)) * 16)]); \
-            sb[n] = (int)((KSs[sbuf][HS][row] >> (8 * g4)) & 0xFFu);                    \
-        }                                                                               \
-        _Pragma("unroll") for (int m = 0; m < 4; ++m) {                                 \
-            const int row = qg * 64 + 16 * m + l16;                                     \
-            const i32x4v av = *reinterpret_cast<const i32x4v *>(&Qs[BUF][row * 64 + ((g4 ^ swz(row)) * 16)]); \
-            const i32x8 A = i32x8{av[0], av[1], av[2], av[3], 0, 0, 0, 0};              \
-            const int sa = (int)((QSs[sbuf][HS][row] >> (8 * g4)) & 0xFFu);             \
-            const float4 w4 = *reinterpret_cast<const float4 *>(&Ws[(HH) * TQ + qg * 64 + 16 * m + 4 * g4]); \
-            const float wr[4] = {w4.x, w4.y, w4.z, w4.w};                               \
-            _Pragma("unroll") for (int n = 0; n < 4; ++n) {                             \
-                const i32x8 Bn = i32x8{Bv[n][0], Bv[n][1], Bv[n][2], Bv[n][3], 0, 0, 0, 0}; \
-                const f32x4 c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(       \
-                    A, Bn, f32x4{0.f, 0.f, 0.f, 0.f}, 4, 4, 0, sa, 0, sb[n]);           \
-                _Pragma("unroll") for (int r = 0; r < 4; ++r)                           \
-                    acc[m][n][r] = fmaf(wr[r], __int_as_float(max(__float_as_int(c[r]), 0)), acc[m][n][r]); \
-            }                                                                           \
-        }                                                                               \
-    }
-
-        // ReLU is an integer max on the bits (negative floats are negative integers): one
-        // instruction, where fmaxf also quiets NaNs. Loads past the last head or block re-read
-        // the last one and their stores go to a buffer nobody reads again, so every load and
-        // store is unconditional and the waits stay exact.
-        FP4_SLOAD(0)
-        FP4_LOAD(A, 0)
-        FP4_LOAD(B, 1)
-        FP4_SSTORE(0)
-        FP4_STORE(A, 0)
-        __syncthreads();
-#pragma unroll 1
-        for (int hb = 0; hb < 64; hb += 4) {
-            const int sbuf = (hb >> 2) & 1;
-            FP4_SLOAD(hb + 4 < 64 ? (hb >> 2) + 1 : 15)
-#pragma unroll 1
-            for (int hs = 0; hs < 4; hs += 2) {
-                const int h = hb + hs;
-                FP4_LOAD(A, h + 2 < 64 ? h + 2 : 63)
-                FP4_COMPUTE(h, 0, hs)
-                FP4_STORE(B, 1)
-                __syncthreads();
-                FP4_LOAD(B, h + 3 < 64 ? h + 3 : 63)
-                FP4_COMPUTE(h + 1, 1, hs + 1)
-                if (hs == 2) FP4_SSTORE(sbuf ^ 1)
-                FP4_STORE(A, 0)
-                __syncthreads();
+    // scores: lane holds entries 16n + 4g4 + r (r = 0..3, 16 contiguous bytes) of query
+    // 16m + l16 of the wave tile; the stores bypass the caches' retention (the score matrix
+    // is read once, by the top-k)
+    const bool vec = (N & 3) == 0;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int qq = qg * 64 + 16 * m + l16;
+        const int t = t0 + qq;
+        if (t >= T) continue;
+        const int64_t nv = nvis_s[qq];
+        float *srow = scores + (int64_t)t * N;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+            const int64_t i = i0 + eg * 64 + 16 * n + 4 * g4;
+            float v[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = (i + r < nv) ? acc[m][n][r] : -INFINITY;
+            if (vec && i + 3 < N) {
+                __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4 *>(srow + i));
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (i + r < N) __builtin_nontemporal_store(v[r], srow + i + r);
             }
         }
-#undef FP4_LOAD
-#undef FP4_STORE
-#undef FP4_SLOAD
-#undef FP4_SSTORE
-#undef FP4_COMPUTE
     }
-
-    // scores: lane holds (query 16m + 4g4 + r, entry 16n + l16) of the wave tile
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int qq = qg * 64 + 16 * m + 4 * g4 + r;
-            const int t = t0 + qq;
-            if (t >= T) continue;
-            const int64_t nv = nvis_s[qq];
-            float *srow = scores + (int64_t)t * N;
-#pragma unroll
-            for (int n = 0; n < 4; ++n) {
-                const int64_t i = i0 + eg * 64 + 16 * n + l16;
-                if (i < N) srow[i] = (i < nv) ? acc[m][n][r] : -INFINITY;
-            }
-        }
 }
 
 // ---- few queries per key store (decode): an HBM stream of each query's keys --------

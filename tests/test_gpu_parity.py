@@ -164,6 +164,7 @@ def test_index_bf16_shared_keys(csa, orc, T, B, N):
 @pytest.mark.parametrize("T,N,B,p_lo,p_hi", [
     (70, 300, 1, 600, 669),      # one workgroup tile, ragged in both directions (matrix cores)
     (520, 650, 1, 1000, 3000),   # 3 x 6 tiles, causal: partly and fully masked tiles
+    (1100, 1200, 1, 3000, 4800), # 9 x 10 tiles: two query tiles per XCD, a ragged entry group
     (10, 90, 2, 100, 400),       # two key stores: the per-query key stream
     (4, 1000, 4, 4001, 4001),    # decode shape: one query per store, every entry visible
     (6, 333, 1, 500, 1400),      # few queries on one store: the key stream, causal, ragged run
