@@ -38,9 +38,9 @@ typedef int i32x4v __attribute__((ext_vector_type(4)));
 typedef int i32x4s __attribute__((ext_vector_type(4)));
 
 // XOR swizzle of a code row's four 16-byte chunks in LDS: chunk c of row r sits in slot
-// c ^ swz(r). A 16-byte read instruction serves 16 lanes (64 banks x 4 bytes) per cycle;
-// with this swizzle the 16 rows of a 16-row block cover all 64 banks exactly once.
-__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
+// c ^ swz(r), so the 16-byte operand reads of 8 consecutive rows (the lanes a 16-byte read
+// serves together) fall in distinct banks.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 3; }
 
 // raw buffer resource words over [p, p + bytes) (wave-uniform): loads past the end return
 // zeros
