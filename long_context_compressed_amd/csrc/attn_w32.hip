@@ -1,28 +1,31 @@
-// Shared-KV MQA with an attention sink, 128 heads per workgroup, 32 heads per wavefront,
-// on gfx950 matrix cores.
+// Shared-KV MQA with an attention sink, 128 heads per workgroup, on gfx950 matrix cores.
 //
 // "DeepSeek-V4 混合注意力" §4.2 (one compressed vector is both K and V for every query head),
 // §5 (HCA: every visible summary), §6 (SWA rows, sink softmax, partial RoPE / inverse RoPE).
 //
-// The tile loop of shared-KV attention streams every row of a tile out of LDS twice per
-// wavefront (as K fragments for S^T and as transposed V fragments for P V), 1 KiB of LDS
-// per 16x16x32 matrix op. With 16 heads per wavefront that is twice what LDS delivers
-// while the matrix cores run. Here a wavefront owns 32 heads, so every fragment read feeds
-// two matrix ops: one workgroup of 4 wavefronts (one per SIMD) covers 128 heads of one
-// query, and each wavefront holds its 32 x 512 fp32 output in the 256 accumulation
-// registers (AGPRs) while q^T (32 heads x 512 dims, bf16) and the tile work sit in the
-// 256 ordinary ones. Per 32-row tile:
-//   - the rows go from memory straight into LDS by buffer loads with the LDS destination,
-//     into the other of two tile buffers while this tile is computed (8 rows per wave);
-//   - S^T = K Q^T (rows x heads, MFMA 16x16x32 bf16) for the two 16-head blocks;
-//   - the C layout of S^T is the A-operand layout of P, so P never leaves registers;
-//   - V fragments from ds_read_b64_tr_b16 transposing reads, each used for both head
-//     blocks; the softmax denominators ride one more matrix op per head block against a
-//     ones operand;
-//   - online softmax against a reference maximum fixed by the first tile; O is never
-//     rescaled. If a later tile's maximum exceeds it by more than 2^24 (rare), the pass is
-//     abandoned, a pass of S^T alone finds every head's exact maximum, and O is
-//     accumulated once more against that.
+// One workgroup of 4 wavefronts (one per SIMD) covers 128 heads of one query. The two
+// products of a 32-row tile are split differently over the wavefronts:
+//   - S^T = K Q^T (rows x heads, MFMA 16x16x32 bf16): wavefront w owns heads 32w .. 32w+31
+//     and all 512 dims, so q^T (32 heads x 512 dims, bf16) stays in 128 registers and every
+//     K fragment read from LDS feeds two matrix ops. The C layout of S^T is the B-operand
+//     layout of P; each wavefront turns its S^T into P (online softmax against a reference
+//     maximum fixed by the first tile, so O is never rescaled) and puts its two 16-head
+//     blocks of P into LDS (1 KiB each, lane-linear).
+//   - O^T += V^T P^T: wavefront w owns dims 128w .. 128w+127 of all 128 heads (its 128 x 128
+//     fp32 output block fills the 256 accumulation registers), reads P of every head from
+//     LDS and only its quarter of the V fragments (transposing reads), so each V fragment
+//     feeds eight matrix ops and each P fragment four.
+// Tiles are pipelined over four LDS tile buffers. While tile i's S^T runs, the rows of tile
+// i+2 go from memory straight into LDS (buffer loads with the LDS destination), one row per
+// two of its matrix-op steps; then the products of tile i-1 run with the softmax of tile i
+// (VALU work) issued a micro-step at a time between them. A single wavefront per SIMD issues
+// one instruction at a time, so the loop is written to keep the non-matrix instructions
+// few: the main slots and the SWA slots start on tile boundaries (every tile's rows come
+// from one region, one buffer resource per tile), and each row's offset is formed in a lane
+// beforehand. The softmax denominators ride one more matrix op per head block against a
+// ones operand. If a later tile's maximum exceeds the reference by more than 2^24 (rare),
+// the results are abandoned and a plain two-pass routine computes the wavefront's 32 heads
+// again.
 #include <type_traits>
 
 #include "attn_mfma.hpp"
@@ -35,34 +38,53 @@ namespace {
 using namespace amfma;
 
 constexpr int NWV = 4;            // wavefronts per workgroup
-constexpr int HB = 2;             // 16-head blocks per wavefront
+constexpr int HB = 2;             // 16-head blocks of a wavefront's S^T
 constexpr int WH = 16 * HB * NWV; // heads per workgroup
+constexpr int OB = WH / 16;       // 16-head blocks of the workgroup (every one in P V)
+constexpr int DPW = NDN / NWV;    // 16-dim output blocks of a wavefront
 constexpr int RPW = WR / NWV;     // tile rows loaded per wavefront
-static_assert(kIdxCache % (64 * NWV) == 0, "the index cache splits evenly over the threads");
-constexpr int SDA = 1;            // K fragment chunks read ahead
-constexpr int PVA = 2;            // V fragment chunks read ahead
+constexpr int TB = WR * WP;       // bf16 elements of one tile buffer
+constexpr int NTB = 4;            // tile buffers
+constexpr int kW32Idx = 1024;     // top-k entries of a query kept in LDS (the whole list)
+static_assert(kW32Idx % (64 * NWV) == 0, "the index copy splits evenly over the threads");
+static_assert(kW32Idx <= kIdxCache, "the two-pass routine reads the LDS copy below kIdxCache");
+// s_waitcnt: every LDS access done, all but the last RPW vector-memory operations (the row
+// loads of the tile two ahead) done
+constexpr int kWaitTileAhead = RPW | (7 << 4) | (0 << 8);
+static_assert(NDN % NWV == 0, "the output dims split evenly over the wavefronts");
+constexpr int SDA = 2;            // K fragment chunks read ahead
+constexpr int PVA = 2;            // P fragments read ahead
 constexpr float kHeadroom = 24.f; // log2 growth of a head's maximum the tile loop absorbs
 
-// The output accumulators and denominators live in AGPRs: the matrix ops that update them
-// are written out with an "a" constraint (the compiler's own MFMA selection would keep
-// every result in one register class and shuffle the 256 accumulators between the two).
-// The compiler does not see these as matrix ops, so the hazards it would otherwise cover
-// are covered here: a VALU result read by a matrix op gets >= 5 wait states (the s_nop at
-// the head of the first product that reads it), and the results are read back only after
+typedef int i32x4s __attribute__((ext_vector_type(4)));
+
+// max of two scores (finite or -inf) without the operand canonicalisation fmaxf brings:
+// the median of a, b and +inf
+__device__ __forceinline__ float fmax2(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, INFINITY); }
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
+// The output accumulators live in AGPRs: the matrix ops that update them are written out
+// with an "a" constraint (the compiler's own MFMA selection would keep every result in one
+// register class and shuffle the 256 accumulators between the two). The compiler does not
+// see these as matrix ops, so the hazards it would otherwise cover are covered here: a
+// source register possibly written by a VALU move gets >= 5 wait states (the s_nop at the
+// head of the first product of each V fragment), and the results are read back only after
 // two s_nop 15 (pv_fence).
 __device__ __forceinline__ void pv_mfma(f32x4 &acc, const bf16x8 a, const bf16x8 b) {
     asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
-// the first products of a tile, both head blocks in one statement behind the wait states
-// for P's VALU writes
-__device__ __forceinline__ void pv_mfma2_after_valu(f32x4 &acc0, f32x4 &acc1, const bf16x8 a, const bf16x8 b0,
-                                                    const bf16x8 b1) {
-    asm volatile("s_nop 4\n\tv_mfma_f32_16x16x32_bf16 %0, %2, %3, %0\n\tv_mfma_f32_16x16x32_bf16 %1, %2, %4, %1"
-                 : "+a"(acc0), "+a"(acc1)
-                 : "v"(a), "v"(b0), "v"(b1));
+__device__ __forceinline__ void pv_mfma_after_valu(f32x4 &acc, const bf16x8 a, const bf16x8 b) {
+    asm volatile("s_nop 4\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 // one accumulator read out of its AGPR where it is used (left to itself the compiler copies
-// every accumulator to VGPRs at the loop exit, more than there are)
+// every accumulator to VGPRs at once, more than there are)
 __device__ __forceinline__ float agpr_read(float a) {
     float v;
     asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
@@ -70,6 +92,40 @@ __device__ __forceinline__ float agpr_read(float a) {
 }
 __device__ __forceinline__ void pv_fence() { asm volatile("s_nop 15\n\ts_nop 15" ::: "memory"); }
 
+// raw buffer resource words over [p, p + bytes) (wave-uniform; loads past the end return
+// zeros)
+__device__ __forceinline__ i32x4s rows_rsrc(const void *p, uint32_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)p;
+    const int lo = (int)__builtin_amdgcn_readfirstlane((uint32_t)a);
+    const int hi = (int)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xFFFFu);
+    return i32x4s{lo, hi, (int)__builtin_amdgcn_readfirstlane(bytes), kBufDword3};
+}
+
+// One 1 KiB row from memory straight into LDS: lane i moves bytes 16i .. 16i+15 of the row
+// at `soff` within the resource to LDS byte address dst + 16i. Written as assembly so that
+// the compiler does not track it (it would otherwise wait for these loads before every LDS
+// read it cannot prove disjoint from them, which drains the prefetch); completion is waited
+// for explicitly before the barrier that ends a tile. It sets M0 (the LDS address of the
+// direct-to-LDS load; one wait state before the load reads it); nothing else in this
+// file's kernel uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void row_dma(i32x4s rs, uint32_t voff, uint32_t soff, uint32_t dst) {
+    asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :
+                 : "v"(voff), "s"(rs), "s"(soff), "s"(dst)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// workgroup barrier without a memory fence (the fence would wait for every load in flight,
+// the row loads of the tile two ahead included); the wait before it says what has
+// completed, and the empty asm keeps the compiler from moving memory accesses across it
+__device__ __forceinline__ void stage_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 // The 32 heads of one wavefront for one query (or one split of its rows), computed from
 // scratch with plain VALU arithmetic and two passes over the rows (exact maximum, then the
@@ -180,41 +236,40 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
                 const bf16_t *__restrict__ swa, const int64_t *__restrict__ swa_pos0, int swa_rows, int window,
                 const int32_t *__restrict__ q_seq, const int64_t *__restrict__ q_pos,
                 const float *__restrict__ rope_cs, int R, int T, int B, int64_t N, int H,
-                bf16_t *__restrict__ out, float *__restrict__ lse, float *__restrict__ part, int nsplit,
-                int64_t split_slots)
+                bf16_t *__restrict__ out, float *__restrict__ lse, int64_t max_slots)
 {
-    __shared__ __attribute__((aligned(16))) bf16_t KV0[WR * WP];  // tile buffers (separate arrays,
-    __shared__ __attribute__((aligned(16))) bf16_t KV1[WR * WP];  // see the row loads below)
-    __shared__ int32_t sidx[kIdxCache];
+    __shared__ __attribute__((aligned(16))) bf16_t KVB[NTB * TB];  // tile buffers
+    __shared__ __attribute__((aligned(16))) u32x4w PB[2][OB * 64];  // P of two tiles, fragment order
+    __shared__ int32_t sidx[kW32Idx];
+    __shared__ float invs[WH];
     __shared__ int redo;
 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int l16 = lane & 15, g4 = lane >> 4;
-    // XCD-aware placement: units (query, split, head group) are dealt to the 8 XCDs in
-    // contiguous runs, so neighbouring queries (which share SWA rows and summaries) meet
-    // in one L2
+    // XCD-aware placement: units (query, head group) are dealt to the 8 XCDs in contiguous
+    // runs, so neighbouring queries (which share SWA rows and summaries) meet in one L2
     const int HGN = H / WH;
-    const int64_t U = (int64_t)T * nsplit * HGN;
+    const int64_t U = (int64_t)T * HGN;
     const int64_t per_xcd = (U + 7) / 8;
     const int64_t bid = blockIdx.x;
     const int64_t u = (bid & 7) * per_xcd + (bid >> 3);
     if ((bid >> 3) >= per_xcd || u >= U) return;
     const int hg = (int)(u % HGN);
-    const int64_t tu = u / HGN;
-    const int t = (int)(tu / nsplit), sp = (int)(tu % nsplit);
-    const int head0 = hg * WH + 16 * HB * w;  // first head of this wave; block b = head0 + 16b ..
+    const int t = (int)(u / HGN);
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    const int hw0 = hg * WH;                 // first head of the workgroup
+    const int head0 = hw0 + 16 * HB * wu;    // first S^T head of this wave; block b = head0 + 16b ..
 
-    // The loads that depend only on the unit (q, its RoPE pairs, the sinks, the split's
-    // top-k indices) are all issued before anything waits on the row context.
-    const int64_t j0 = (int64_t)sp * split_slots;
-    constexpr int IPT = kIdxCache / (64 * NWV);  // top-k indices per thread
+    // The loads that depend only on the query (q, its RoPE pairs, the sinks, the top-k
+    // indices) are all issued before anything waits on the row context.
+    constexpr int IPT = kW32Idx / (64 * NWV);  // top-k indices per thread
     int32_t ir[IPT];
     {
-        const int64_t nc0 = (ratio <= 0) ? (k - j0 < kIdxCache ? k - j0 : kIdxCache) : 0;
+        const int64_t nc0 = (ratio <= 0) ? (k < kW32Idx ? k : kW32Idx) : 0;
 #pragma unroll
         for (int m = 0; m < IPT; ++m) {
             const int x = threadIdx.x + 64 * NWV * m;
-            ir[m] = (x < nc0) ? idx[(int64_t)t * k + j0 + x] : 0;
+            ir[m] = (x < nc0) ? idx[(int64_t)t * k + x] : 0;
         }
     }
     float sk[HB];
@@ -256,37 +311,32 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
     }
 
     const RowCtx c = row_ctx(t, q_seq, q_pos, B, N, k, ratio, swa, swa_pos0, window);
-    int64_t j1 = j0 + split_slots;
-    if (j1 > c.nslots) j1 = c.nslots;
+    const int64_t j1 = (max_slots < c.nslots) ? max_slots : c.nslots;  // slots [0, j1)
 
-    // softmax state per head block: m_ref of head 16b + l16 (replicated over the 4 lane
-    // groups); the denominators live in the output layout (head 16b + 4g4 + r in component
-    // r of lacc[b]) and are accumulated by a matrix op against a ones operand, so they sum
+    // softmax state of the wavefront's S^T heads: m_ref of head 16b + l16 (replicated over
+    // the 4 lane groups); the denominators in the output layout (head 16b + 4g4 + r in
+    // component r of lacc[b]), accumulated by a matrix op against a ones operand so they sum
     // the same bf16 weights that enter O. The sink's 2^(sink - m_ref) is added at the end.
-    const bool single = (nsplit == 1);
     const bf16x8 zero8 = __builtin_bit_cast(bf16x8, u32x4w{0u, 0u, 0u, 0u});
     float m_ref[HB];
     f32x4 lacc[HB];
-    f32x4 acc[HB][NDN];
-    auto reset_sums = [&]() __attribute__((always_inline)) {
-#pragma unroll
-        for (int b = 0; b < HB; ++b) {
-            lacc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-            // zeroed by a matrix op into AGPRs, so the accumulators never pass through VGPRs
-#pragma unroll
-            for (int nd = 0; nd < NDN; ++nd)
-                asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %1, 0" : "=a"(acc[b][nd]) : "v"(zero8));
-        }
-    };
+    f32x4 acc[OB][DPW];  // O^T: dims 16(DPW w + d) + 4g4 + r of head 16B + l16 of the workgroup
 #pragma unroll
     for (int b = 0; b < HB; ++b) {
-        m_ref[b] = single ? sk[b] * kLog2e : -INFINITY;
+        lacc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m_ref[b] = sk[b] * kLog2e;
     }
-    reset_sums();
+    // zeroed by matrix ops into AGPRs, so the accumulators never pass through VGPRs; the
+    // zero operand may have just been written by a VALU move, hence the wait states
+#pragma unroll
+    for (int ob = 0; ob < OB; ++ob)
+#pragma unroll
+        for (int d = 0; d < DPW; ++d)
+            asm volatile("s_nop 4\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %1, 0" : "=a"(acc[ob][d]) : "v"(zero8));
 
-    // The split's top-k indices (up to kIdxCache of them) are read once into LDS.
-    const int64_t jm = (j1 < c.nmain) ? j1 : c.nmain;  // main slots of this split: [j0, jm)
-    const int64_t ncache = (jm - j0 < kIdxCache) ? jm - j0 : kIdxCache;
+    // The top-k indices are read once into LDS.
+    const int64_t jm = (j1 < c.nmain) ? j1 : c.nmain;  // main slots: [0, jm)
+    const int64_t ncache = (jm < kW32Idx) ? jm : kW32Idx;
     if (ratio <= 0) {
 #pragma unroll
         for (int m = 0; m < IPT; ++m) {
@@ -296,6 +346,7 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
     }
     if (threadIdx.x == 0) redo = 0;
     __syncthreads();
+
     // Every row of the query lives in one of two regions: its sequence's compressed rows
     // (kv) or its SWA rows. Each gets one buffer resource for the whole unit, and a row is
     // named by a 32-bit code (region bit | row), so a row load only needs that code in a
@@ -303,82 +354,143 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
     // without data are masked out of the softmax and load row 0 (a buffer load past the
     // region's end returns zeros, so nothing outside it is ever touched).
     const int32_t *idx_t = (ratio > 0) ? nullptr : idx + (int64_t)t * k;
-    const int wu = __builtin_amdgcn_readfirstlane(w);
     const int s_u = __builtin_amdgcn_readfirstlane(c.s);
-    const __amdgpu_buffer_rsrc_t kv_rs = uniform_rsrc(kv + (int64_t)s_u * N * WD, (uint32_t)(N * WD * 2));
-    const __amdgpu_buffer_rsrc_t swa_rs =
-        uniform_rsrc(swa != nullptr ? swa + (int64_t)s_u * swa_rows * WD : kv, swa != nullptr ? (uint32_t)swa_rows * WD * 2 : 0u);
-    constexpr int32_t kSwaBit = 0x40000000;
-    // Row codes of the tile at slot jt: lane r < 32 codes slot jt + r (-1: no row); the
-    // tile's 32-bit validity mask comes from a ballot.
-    auto tile_rows = [&](int64_t jt, int32_t &code) __attribute__((always_inline)) -> uint32_t {
-        const int64_t j = jt + (lane & 31);
-        int32_t cd = -1;
-        if (j < j1) {
-            if (j < c.nmain) {
-                const int64_t id = (ratio > 0) ? j : (j - j0 < kIdxCache ? (int64_t)sidx[j - j0] : (int64_t)idx_t[j]);
-                if (id >= 0 && id < N) cd = (int32_t)id;
-            } else {
-                const int64_t r = c.lo + (j - c.nmain) - c.swa0;
-                if (r >= 0 && r < swa_rows) cd = kSwaBit | (int32_t)r;
-            }
-        }
-        code = cd;
-        return (uint32_t)(__ballot(cd >= 0) & 0xffffffffull);
+    const i32x4s kv_rs = rows_rsrc(kv + (int64_t)s_u * N * WD, (uint32_t)(N * WD * 2));
+    const i32x4s swa_rs = rows_rsrc(swa != nullptr ? swa + (int64_t)s_u * swa_rows * WD : kv,
+                                    swa != nullptr ? (uint32_t)swa_rows * WD * 2 : 0u);
+    const uint32_t kvb = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)(const char *)KVB);
+    const uint32_t voff = (uint32_t)lane * 16u;
+    // Tiles 0 .. ntm-1 hold the main slots (top-k entries or summaries, 32 per tile, the
+    // last one padded), tiles ntm .. nt-1 the SWA slots, so the rows of a tile all come from
+    // one region. Lane r < 32 describes row r of a tile: its byte offset in the region (row
+    // 0 when the row has no data), and a ballot gives the tile's validity mask. A sparse
+    // slot's top-k entry is read from the LDS copy of the list (this kernel runs only when
+    // it holds the whole list) well before the offset is formed. 32-bit arithmetic: slots
+    // and rows stay below 2^31.
+    const int nmain32 = (int)jm, nwin32 = (int)(j1 - jm);
+    const int ntm = __builtin_amdgcn_readfirstlane((nmain32 + WR - 1) / WR);  // (wave-uniform)
+    const int lo_rel = (int)(c.lo - c.swa0), n32 = (int)N;
+    auto code_read = [&](int i) __attribute__((always_inline)) -> int {
+        const int j = i * WR + (lane & 31);
+        if (ratio > 0) return j;
+        return sidx[j < kW32Idx ? j : kW32Idx - 1];
     };
-    // Wavefront w loads rows RPW*w .. RPW*w + RPW-1 of a tile, one 1 KiB row per
-    // buffer-load instruction (16 bytes per lane, LDS destination).
-    auto dma_row = [&](bf16_t *buf, int i, int32_t cd) __attribute__((always_inline)) {
-        const int row = RPW * wu + i;
-        const uint32_t off = cd < 0 ? 0u : (uint32_t)(cd & (kSwaBit - 1)) * (WD * 2);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds((cd >= 0 && (cd & kSwaBit)) ? swa_rs : kv_rs,
-                                                 (__attribute__((address_space(3))) void *)(buf + row * WP), 16,
-                                                 lane * 16, off, 0, 0);
-    };
-    // Dense attention walks the summaries in order, so a tile whose 32 slots are all
-    // summaries is 32 consecutive rows: one buffer resource covers it and no address leaves
-    // a lane (the per-row read-out above costs the wave more than the load itself).
-    const int64_t jc = (j1 < c.nmain) ? j1 : c.nmain;  // slots before jc are summaries
-    auto contig = [&](int64_t jn) __attribute__((always_inline)) { return ratio > 0 && jn + WR <= jc; };
-    // buffer resource over the 32 rows from slot jn (the address is read out of lane 0 so
-    // the compiler knows it is uniform)
-    auto contig_rsrc = [&](int64_t jn) __attribute__((always_inline)) {
-        const uint64_t a = (uint64_t)(uintptr_t)(kv + ((int64_t)c.s * N + jn) * WD);
-        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-        return __builtin_amdgcn_make_buffer_rsrc((void *)(((uint64_t)hi << 32) | lo), 0, WR * WD * 2, kBufDword3);
-    };
-    auto dma_row_contig = [&](bf16_t *buf, int i, __amdgpu_buffer_rsrc_t rs) __attribute__((always_inline)) {
-        const int row = RPW * wu + i;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(buf + row * WP), 16,
-                                                 lane * 16, row * WD * 2, 0, 0);
-    };
-
-    uint32_t valid = 0u, valid_next = 0u;
-    int32_t ra;  // row codes of the next tile, resolved one tile ahead
-
-    // One 32-row tile: compute from `tile`, load the next tile's rows into `nxt`. Past the
-    // last tile every slot of the next tile resolves to the stand-in, so the loads need no
-    // branch. O accumulates against the reference maximum set by the first tile and is
-    // never rescaled (so it is only ever touched by the products into it); a later tile
-    // whose maximum exceeds the reference by more than 2^kHeadroom raises `redo`.
-    auto tile_step = [&](const bf16_t *tile, bf16_t *nxt, int64_t jt, bool first) __attribute__((always_inline)) {
-        int32_t ra2 = -1;
-        uint32_t valid_next2;
-        int32_t dma_rows_code[RPW];
-        const bool cn = contig(jt + WR);  // the tile loaded during this one
-        const __amdgpu_buffer_rsrc_t crs = contig_rsrc(cn ? jt + WR : j0);
-        if (cn) {
-#pragma unroll
-            for (int i = 0; i < RPW; ++i) dma_row_contig(nxt, i, crs);
+    auto code_finish = [&](int i, int id, uint32_t &off) __attribute__((always_inline)) -> uint32_t {
+        const int r = lane & 31;
+        bool ok;
+        int row;
+        if (i < ntm) {
+            row = id;
+            ok = i * WR + r < nmain32 && id >= 0 && id < n32;
         } else {
-#pragma unroll
-            for (int i = 0; i < RPW; ++i) dma_rows_code[i] = __builtin_amdgcn_readlane(ra, RPW * wu + i);
-            // all codes are in scalar registers before the first load goes out
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int i = 0; i < RPW; ++i) dma_row(nxt, i, dma_rows_code[i]);
+            const int w = (i - ntm) * WR + r;
+            row = lo_rel + w;
+            ok = w < nwin32 && row >= 0 && row < swa_rows;
         }
+        off = ok ? (uint32_t)row * (WD * 2) : 0u;
+        return (uint32_t)(__ballot(ok) & 0xffffffffull);
+    };
+    // byte offsets of this wave's RPW rows of a tile, in scalar registers
+    auto row_offs = [&](uint32_t offs, uint32_t (&so)[RPW]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) so[r] = __builtin_amdgcn_readlane(offs, RPW * wu + r);
+    };
+    // row r of this wave's share of a tile into the tile buffer at bf16 offset nb
+    auto issue_row = [&](const i32x4s rs, int nb, int r, uint32_t soff) __attribute__((always_inline)) {
+        row_dma(rs, voff, soff, kvb + (uint32_t)(nb + (RPW * wu + r) * WP) * 2u);
+    };
+
+    // O^T += V^T P^T for the tile in the buffer at bf16 offset vb, with P from PB[pr]. The
+    // wave's 8 dim blocks go in two halves: the V fragments of a half (two transposing
+    // reads per 16-dim block, in the row order of the S^T C layout) stay in registers while
+    // the P fragments of the eight head blocks stream past, each feeding four products.
+    // The first half's V fragments and the first P fragments are read ahead (pv_pre).
+    // `step(p)` is called after product p (0 .. 63) and, with p = 100 + h, before the first
+    // product of half h: the softmax of the next tile goes there, a few instructions at a
+    // time.
+    struct PvPre {
+        bf16x4v va[DPW / 2], vb[DPW / 2];
+        bf16x8 pr[PVA];
+    };
+    auto pv_pre = [&](int vb, int pr, PvPre &P) __attribute__((always_inline)) {
+        const int s4 = l16 >> 2, sc = l16 & 3;
+        const bf16_t *v0 = KVB + vb + (4 * g4 + s4) * WP + 4 * sc + 16 * DPW * wu;
+        const bf16_t *v1 = v0 + 16 * WP;
+#pragma unroll
+        for (int dd = 0; dd < DPW / 2; ++dd) {
+            P.va[dd] = __builtin_bit_cast(bf16x4v, ld_tr(v0 + 16 * dd));
+            P.vb[dd] = __builtin_bit_cast(bf16x4v, ld_tr(v1 + 16 * dd));
+        }
+        const u32x4w *pp = &PB[pr][lane];
+#pragma unroll
+        for (int cc = 0; cc < PVA; ++cc) P.pr[cc] = __builtin_bit_cast(bf16x8, pp[cc * 64]);
+    };
+    auto pv_phase = [&](int vb, int pr, const PvPre &P, auto &&step) __attribute__((always_inline)) {
+        const int s4 = l16 >> 2, sc = l16 & 3;
+        const bf16_t *v0 = KVB + vb + (4 * g4 + s4) * WP + 4 * sc + 16 * DPW * wu;
+        const bf16_t *v1 = v0 + 16 * WP;
+        const u32x4w *pp = &PB[pr][lane];
+        static_for<0, 2>([&](auto DH) __attribute__((always_inline)) {
+            constexpr int dh = decltype(DH)::value;
+            constexpr int DQ = DPW / 2;
+            bf16x4v va[DQ], vb2[DQ];
+            bf16x8 pr_[PVA + 1];
+            if constexpr (dh == 0) {
+#pragma unroll
+                for (int dd = 0; dd < DQ; ++dd) {
+                    va[dd] = P.va[dd];
+                    vb2[dd] = P.vb[dd];
+                }
+#pragma unroll
+                for (int cc = 0; cc < PVA; ++cc) pr_[cc] = P.pr[cc];
+            } else {
+#pragma unroll
+                for (int dd = 0; dd < DQ; ++dd) {
+                    va[dd] = __builtin_bit_cast(bf16x4v, ld_tr(v0 + 16 * (DQ * dh + dd)));
+                    vb2[dd] = __builtin_bit_cast(bf16x4v, ld_tr(v1 + 16 * (DQ * dh + dd)));
+                }
+#pragma unroll
+                for (int cc = 0; cc < PVA; ++cc) pr_[cc] = __builtin_bit_cast(bf16x8, pp[cc * 64]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            step(std::integral_constant<int, 100 + dh>{});
+            __builtin_amdgcn_sched_barrier(0);
+            static_for<0, OB>([&](auto OBI) __attribute__((always_inline)) {
+                constexpr int ob = decltype(OBI)::value;
+                if constexpr (ob + PVA < OB) pr_[(ob + PVA) % (PVA + 1)] = __builtin_bit_cast(bf16x8, pp[(ob + PVA) * 64]);
+                __builtin_amdgcn_sched_barrier(0);
+                static_for<0, DQ>([&](auto DD) __attribute__((always_inline)) {
+                    constexpr int dd = decltype(DD)::value;
+                    const bf16x8 vf = __builtin_shufflevector(va[dd], vb2[dd], 0, 1, 2, 3, 4, 5, 6, 7);
+                    if constexpr (ob == 0)
+                        pv_mfma_after_valu(acc[ob][DQ * dh + dd], vf, pr_[ob % (PVA + 1)]);
+                    else
+                        pv_mfma(acc[ob][DQ * dh + dd], vf, pr_[ob % (PVA + 1)]);
+                    step(std::integral_constant<int, 32 * dh + DQ * ob + dd>{});
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+            });
+        });
+    };
+
+    const int nt = ntm + (nwin32 + WR - 1) / WR;  // tiles
+
+    // Tile i (in buffer i % 4): S^T, with the rows of tile i+2 requested a row at a time
+    // between its matrix ops, then its softmax interleaved with the products of tile i-1
+    // (none for the first tile), and P of tile i into PB[i & 1].
+    uint32_t v0 = 0u, v1 = 0u, v2 = 0u;  // validity of tiles i, i+1, i+2
+    uint32_t oa = 0u;                     // row offsets of tile i+2
+    float growth = -INFINITY;  // largest tile maximum above the reference, log2 units
+    float nmu[HB] = {0.f, 0.f};  // -m_ref (0 for an empty reference), fixed after the first tile
+    auto tile_iter = [&](int i, auto FIRST) __attribute__((always_inline)) {
+        constexpr bool kFirst = decltype(FIRST)::value;
+        const int cb = (i & 3) * TB, pb = ((i + 3) & 3) * TB, db = ((i + 2) & 3) * TB;
+        uint32_t so[RPW];
+        row_offs(oa, so);
+        const i32x4s drs = (i + 2 >= ntm) ? swa_rs : kv_rs;
+        const int id3 = code_read(i + 3);
+        PvPre pre;
 
         // ---- S^T = K Q^T: each K fragment feeds both head blocks
         f32x4 sacc[2][HB];
@@ -388,7 +500,7 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
             for (int b = 0; b < HB; ++b) sacc[m][b] = f32x4{0.f, 0.f, 0.f, 0.f};
         {
             bf16x8 ring[SDA + 1][2];
-            const bf16_t *kb = tile + l16 * WP + g4 * 8;
+            const bf16_t *kb = KVB + cb + l16 * WP + g4 * 8;
 #pragma unroll
             for (int cc = 0; cc < SDA; ++cc) {
                 ring[cc][0] = ld_bf16x8(kb + 32 * cc);
@@ -400,6 +512,8 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
                     ring[(kk + SDA) % (SDA + 1)][0] = ld_bf16x8(kb + 32 * (kk + SDA));
                     ring[(kk + SDA) % (SDA + 1)][1] = ld_bf16x8(kb + 16 * WP + 32 * (kk + SDA));
                 }
+                if (!kFirst && kk == KKN - 3) pv_pre(pb, (i - 1) & 1, pre);
+                if (kk & 1) issue_row(drs, db, kk >> 1, so[kk >> 1]);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int m = 0; m < 2; ++m)
@@ -410,250 +524,238 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        // rows of the tile after next: the index read and the address arithmetic overlap
-        // the matrix ops still in flight
-        valid_next2 = contig(jt + 2 * WR) ? 0xffffffffu : tile_rows(jt + 2 * WR, ra2);
-
+        static_assert(KKN == 2 * RPW, "one row load per two k-chunks");
+        // row offsets of tile i+3
+        uint32_t oa3;
+        const uint32_t v3 = code_finish(i + 3, id3, oa3);
         // rows without data are masked to -inf; full tiles skip the mask
-        if (valid != 0xffffffffu) {
+        if (v0 != 0xffffffffu) {
+            const uint32_t vb = v0 >> (4 * g4);  // bit 16m + r: row 16m + 4g4 + r
 #pragma unroll
             for (int m = 0; m < 2; ++m)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    if (!((valid >> (16 * m + 4 * g4 + r)) & 1u)) {
+                    if (!((vb >> (16 * m + r)) & 1u)) {
 #pragma unroll
                         for (int b = 0; b < HB; ++b) sacc[m][b][r] = -INFINITY;
                     }
         }
-        bf16x8 pf[HB];
+        // ---- softmax of this tile in 27 micro-steps of one instruction per head block (each
+        // depends on an earlier one), spread between the matrix ops of the previous tile so
+        // that every dependency has a matrix op to hide behind:
+        // p = 2^(s * scale - m_ref) packed to bf16 in the B-operand layout of P.
+        // v_exp_f32 flushes results below 2^-126 to zero, which only drops weights that no
+        // bf16 sum could hold.
+        float tq[HB][4];
+        float ev[HB][8];
+        uint32_t pk[HB][4];
+        auto sm_micro = [&](auto UI) __attribute__((always_inline)) {
+            constexpr int u = decltype(UI)::value;
 #pragma unroll
-        for (int b = 0; b < HB; ++b) {
-            // the next tile's row loads ride the softmax (VALU work, LDS idle): issued among
-            // it they queue in the address unit while the wave computes, where one burst at
-            // the start of the tile stalls every wavefront behind the others' loads
-
-            // the scale is positive, so the max of the raw scores gives the max logit
-            float smax = fmaxf(fmaxf(fmaxf(sacc[0][b][0], sacc[0][b][1]), fmaxf(sacc[0][b][2], sacc[0][b][3])),
-                               fmaxf(fmaxf(sacc[1][b][0], sacc[1][b][1]), fmaxf(sacc[1][b][2], sacc[1][b][3])));
-            {
-                const auto x32 =
-                    __builtin_amdgcn_permlane32_swap(__float_as_uint(smax), __float_as_uint(smax), false, false);
-                smax = fmaxf(__uint_as_float(x32[0]), __uint_as_float(x32[1]));
-                const auto x16 =
-                    __builtin_amdgcn_permlane16_swap(__float_as_uint(smax), __float_as_uint(smax), false, false);
-                smax = fmaxf(__uint_as_float(x16[0]), __uint_as_float(x16[1]));
-            }
-            const float tmax = smax * scale_log2;
-            if (first) {
-                m_ref[b] = fmaxf(m_ref[b], tmax);  // O and the sums are still zero
-            } else if (__ballot(tmax > m_ref[b] + kHeadroom) != 0ull) {
-                if (lane == 0) redo = 1;  // the loop is abandoned after this tile
-            }
-            // p = 2^(s * scale - m_ref), packed to bf16 in the A-operand layout of P.
-            // v_exp_f32 flushes results below 2^-126 to zero, which only drops weights that
-            // no bf16 sum could hold.
-
-            const float nmu = (m_ref[b] == -INFINITY) ? 0.f : -m_ref[b];
-            uint32_t pk[4];
-#pragma unroll
-            for (int m = 0; m < 2; ++m)
-#pragma unroll
-                for (int r = 0; r < 4; r += 2) {
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[m][b][r], scale_log2, nmu));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[m][b][r + 1], scale_log2, nmu));
-                    pk[2 * m + r / 2] = pack_bf16x2(p0, p1);
+            for (int b = 0; b < HB; ++b) {
+                if constexpr (u < 4) {
+                    constexpr int m = u >> 1, r = (u & 1) * 2;
+                    tq[b][u] = fmax2(sacc[m][b][r], sacc[m][b][r + 1]);
+                } else if constexpr (u == 4) {
+                    tq[b][0] = fmax2(tq[b][0], tq[b][1]);
+                } else if constexpr (u == 5) {
+                    tq[b][2] = fmax2(tq[b][2], tq[b][3]);
+                } else if constexpr (u == 6) {
+                    tq[b][0] = fmax2(tq[b][0], tq[b][2]);
+                } else if constexpr (u == 7) {
+                    const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(tq[b][0]), __float_as_uint(tq[b][0]),
+                                                                    false, false);
+                    tq[b][1] = __uint_as_float(x[0]);
+                    tq[b][2] = __uint_as_float(x[1]);
+                } else if constexpr (u == 8) {
+                    tq[b][0] = fmax2(tq[b][1], tq[b][2]);
+                } else if constexpr (u == 9) {
+                    const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(tq[b][0]), __float_as_uint(tq[b][0]),
+                                                                    false, false);
+                    tq[b][1] = __uint_as_float(x[0]);
+                    tq[b][2] = __uint_as_float(x[1]);
+                } else if constexpr (u == 10) {
+                    tq[b][0] = fmax2(tq[b][1], tq[b][2]);
+                } else if constexpr (u == 11) {
+                    // the scale is positive, so the max of the raw scores gives the max logit
+                    const float tmax = tq[b][0] * scale_log2;
+                    if constexpr (kFirst) {
+                        m_ref[b] = fmaxf(m_ref[b], tmax);  // O and the sums are still zero
+                        nmu[b] = (m_ref[b] == -INFINITY) ? 0.f : -m_ref[b];
+                    } else {
+                        growth = fmaxf(growth, tmax - m_ref[b]);
+                    }
+                } else if constexpr (u >= 12 && u <= 20) {
+                    constexpr int q = u - 12;  // exponent of value q-1, argument of value q
+                    if constexpr (q >= 1) ev[b][q - 1] = __builtin_amdgcn_exp2f(ev[b][q - 1]);
+                    if constexpr (q < 8) ev[b][q] = fmaf(sacc[q >> 2][b][q & 3], scale_log2, nmu[b]);
+                } else if constexpr (u >= 21 && u <= 24) {
+                    constexpr int j = u - 21;
+                    pk[b][j] = pack_bf16x2(ev[b][2 * j], ev[b][2 * j + 1]);
+                } else if constexpr (u == 25) {
+                    const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(pk[b][0], pk[b][1], pk[b][2], pk[b][3]));
+                    lacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_bf16x8(), pf, lacc[b], 0, 0, 0);
+                } else if constexpr (u == 26) {
+                    PB[i & 1][(HB * wu + b) * 64 + lane] = u32x4w{pk[b][0], pk[b][1], pk[b][2], pk[b][3]};
                 }
-            pf[b] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-            lacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_bf16x8(), pf[b], lacc[b], 0, 0, 0);
+            }
+        };
+        constexpr int kMicro = 27;
+        if constexpr (kFirst) {
+            static_for<0, kMicro>([&](auto UI) __attribute__((always_inline)) { sm_micro(UI); });
+        } else {
+            // micro-step 0 before the first product, 15-18 while the second half's V
+            // fragments are read, the others after every second product
+            pv_phase(pb, (i - 1) & 1, pre, [&](auto PI) __attribute__((always_inline)) {
+                constexpr int p = decltype(PI)::value;
+                if constexpr (p == 100) {
+                    sm_micro(std::integral_constant<int, 0>{});
+                } else if constexpr (p == 101) {
+                    static_for<15, 19>([&](auto UI) __attribute__((always_inline)) { sm_micro(UI); });
+                } else if constexpr (p < 28 && (p & 1)) {
+                    sm_micro(std::integral_constant<int, (p + 1) / 2>{});
+                } else if constexpr (p >= 33 && p < 100 && (p & 1) && (p - 33) / 2 + 19 < kMicro) {
+                    sm_micro(std::integral_constant<int, (p - 33) / 2 + 19>{});
+                }
+            });
         }
 
-        {
-            // ---- O += P V: V fragments (8 rows of one dim per lane, in the row order of the
-            // C layout above) from transposing LDS reads, each feeding both head blocks. The
-            // first product after P's VALU writes carries the wait states they need.
-            const int s4 = l16 >> 2, sc = l16 & 3;
-            const bf16_t *v0 = tile + (4 * g4 + s4) * WP + 4 * sc;
-            const bf16_t *v1 = v0 + 16 * WP;
-            bf16x4v vr[PVA + 1][2];
-#pragma unroll
-            for (int cc = 0; cc < PVA; ++cc) {
-                vr[cc][0] = __builtin_bit_cast(bf16x4v, ld_tr(v0 + 16 * cc));
-                vr[cc][1] = __builtin_bit_cast(bf16x4v, ld_tr(v1 + 16 * cc));
-            }
-#pragma unroll
-            for (int nd = 0; nd < NDN; ++nd) {
-                if (nd + PVA < NDN) {
-                    vr[(nd + PVA) % (PVA + 1)][0] = __builtin_bit_cast(bf16x4v, ld_tr(v0 + 16 * (nd + PVA)));
-                    vr[(nd + PVA) % (PVA + 1)][1] = __builtin_bit_cast(bf16x4v, ld_tr(v1 + 16 * (nd + PVA)));
-                }
-                __builtin_amdgcn_sched_barrier(0);
-                const bf16x8 vf = __builtin_shufflevector(vr[nd % (PVA + 1)][0], vr[nd % (PVA + 1)][1], 0, 1, 2, 3,
-                                                          4, 5, 6, 7);
-                if (nd == 0) {
-                    pv_mfma2_after_valu(acc[0][0], acc[1][0], vf, pf[0], pf[1]);
-                } else {
-#pragma unroll
-                    for (int b = 0; b < HB; ++b) pv_mfma(acc[b][nd], vf, pf[b]);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-
-        valid = valid_next;
-        valid_next = valid_next2;
-        ra = ra2;
-        // the next tile's rows have landed in `nxt` (this wave's own loads), and after the
-        // barrier everyone's have and nobody reads `tile` any more
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        v0 = v1;
+        v1 = v2;
+        v2 = v3;
+        oa = oa3;
+        // tile i+1's rows have landed (this wave's loads of it are older than the 8 of tile
+        // i+2), P of this tile is in LDS; after the barrier everyone's have, and nobody
+        // reads tile i-1 or P of tile i-1 any more
+        __builtin_amdgcn_s_waitcnt(kWaitTileAhead);
+        stage_barrier();
     };
 
-    if (j0 < j1) {
-        if (contig(j0)) {
-            valid = 0xffffffffu;
+    if (nt > 0) {
+        uint32_t o0, o1, so[RPW];
+        v0 = code_finish(0, code_read(0), o0);
+        v1 = code_finish(1, code_read(1), o1);
+        v2 = code_finish(2, code_read(2), oa);
+        row_offs(o0, so);
 #pragma unroll
-            for (int i = 0; i < RPW; ++i) dma_row_contig(KV0, i, contig_rsrc(j0));
-        } else {
-            valid = tile_rows(j0, ra);
+        for (int r = 0; r < RPW; ++r) issue_row(ntm > 0 ? kv_rs : swa_rs, 0, r, so[r]);
+        row_offs(o1, so);
 #pragma unroll
-            for (int i = 0; i < RPW; ++i) dma_row(KV0, i, __builtin_amdgcn_readlane(ra, RPW * wu + i));
-        }
+        for (int r = 0; r < RPW; ++r) issue_row(ntm > 1 ? kv_rs : swa_rs, TB, r, so[r]);
+        __builtin_amdgcn_s_waitcnt(kWaitTileAhead);
+        stage_barrier();
+        tile_iter(0, std::true_type{});
+        for (int i = 1; i < nt; ++i) tile_iter(i, std::false_type{});
+        // the loads of the two tiles past the end (stand-ins) land before anything else
+        // touches LDS
+        __builtin_amdgcn_s_waitcnt(0);
     }
-    valid_next = contig(j0 + WR) ? 0xffffffffu : tile_rows(j0 + WR, ra);
-    // every prologue load has landed before the loop (the loop's wait counters then start
-    // from a clean state)
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    // Tiles go in pairs (one per buffer) and the loop has a single exit: an odd count ends
-    // with a tile past j1, whose slots are all masked (no weight). An abandoned loop still
-    // runs to the end; its results are replaced below.
-    for (int64_t jt = j0; jt < j1; jt += 2 * WR) {
-        tile_step(KV0, KV1, jt, jt == j0);
-        tile_step(KV1, KV0, jt + WR, false);
-    }
-    const bool abandoned = redo != 0;
-
-    // (cos, sin) pairs of the lane's last 64 output dims, loaded in one batch
-    float2 orp[4][2];
-    if (rope_t != nullptr) {
+    // (cos, sin) pairs of the lane's output dims when this wave's dims reach the rotated
+    // ones, loaded before the last products
+    const bool rot = rope_t != nullptr && 16 * DPW * (wu + 1) > WD - R;
+    float2 orp[DPW][2];
+    if (rot) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int d = 0; d < DPW; ++d)
 #pragma unroll
-            for (int e = 0; e < 2; ++e) orp[j][e] = rope_pair(rope_t, 16 * (NDN - 4 + j) + 4 * g4 + 2 * e, R);
+            for (int e = 0; e < 2; ++e) orp[d][e] = rope_pair(rope_t, 16 * (DPW * wu + d) + 4 * g4 + 2 * e, R);
     }
-    pv_fence();
-    // ---- epilogue. Each wavefront stages one 16-head block of bf16 output rows in its own
-    // part of the (now idle) tile buffers, so no other wavefront's data is touched.
-    constexpr int OSP = WD + 16;  // staged row pitch (bf16): 1056 bytes spread the banks
-    static_assert(2 * 16 * OSP <= WR * WP, "two wavefronts' staging fits one tile buffer");
-    bf16_t *const ostage = (wu < 2 ? KV0 : KV1) + (wu & 1) * 16 * OSP;
-    // The products computed O^T: lane (l16, g4) holds dims 16nd + 4g4 + r
-    // (r = 0..3, four consecutive dims) of head 16b + l16, and the denominator of that head
-    // in every component of lacc[b], so each lane normalises, rotates back the last R dims
-    // (pairs sit in one lane) and stores 8 bytes per dim block.
+    // denominators of this wave's S^T heads, shared with the waves that hold their outputs
+    float lse_v[HB];
 #pragma unroll
     for (int b = 0; b < HB; ++b) {
-        const int h = head0 + 16 * b + l16;
-        if (single) {
-            const float sk = sink[h] * kLog2e;
-            const float mr = m_ref[b];
-            const float lv = lacc[b][0] + ((sk == -INFINITY) ? 0.f : exp2f(sk - mr));
-            if (lse != nullptr && g4 == 0) {
-                const float mu = (mr == -INFINITY) ? 0.f : mr;
-                lse[(int64_t)t * H + h] = (lv > 0.f) ? (mu + log2f(lv)) * kLn2 : -INFINITY;
-            }
-            const float inv = lv > 0.f ? 1.f / lv : 0.f;
-            const int nd_r = (WD - R) >> 4;
-            // groups of 8 blocks: all 8 are packed before the 8 stores go out, so a store's
-            // data registers are not rewritten while it is still in flight (one block at a
-            // time, every store waited for the one before)
-            constexpr int EG = 8;
+        const float skl = sk[b] * kLog2e;
+        const float mr = m_ref[b];
+        const float lv = lacc[b][0] + ((skl == -INFINITY) ? 0.f : exp2f(skl - mr));
+        const float mu = (mr == -INFINITY) ? 0.f : mr;
+        lse_v[b] = (lv > 0.f) ? (mu + log2f(lv)) * kLn2 : -INFINITY;
+        if (g4 == 0) invs[16 * (HB * wu + b) + l16] = lv > 0.f ? 1.f / lv : 0.f;
+    }
+    if (__ballot(growth > kHeadroom) != 0ull && lane == 0) redo = 1;
+    __syncthreads();
+    const bool abandoned = redo != 0;
+    if (!abandoned) {
+        if (nt > 0) {
+            PvPre pre;
+            pv_pre(((nt - 1) & 3) * TB, (nt - 1) & 1, pre);
+            pv_phase(((nt - 1) & 3) * TB, (nt - 1) & 1, pre, [](auto) __attribute__((always_inline)) {});
+        }
+        pv_fence();
+        if (lse != nullptr && g4 == 0) {
 #pragma unroll
-            for (int ng = 0; ng < NDN; ng += EG) {
-                uint2 pk[EG];
+            for (int b = 0; b < HB; ++b) lse[(int64_t)t * H + head0 + 16 * b + l16] = lse_v[b];
+        }
+        // ---- epilogue. Lane (l16, g4) holds dims 16(DPW w + d) + 4g4 + r (four consecutive
+        // dims) of head 16ob + l16: it normalises them, rotates back the rotated dims (pairs
+        // sit in one lane) and stages 8 bytes per dim block; each head block's 16 x 256-byte
+        // row pieces then go out as four 1 KiB stores. The staging sits in a tile buffer
+        // that no wave reads any more.
+        constexpr int OSP = 16 * DPW + 8;  // staged row pitch (bf16)
+        static_assert(NWV * 16 * OSP <= TB, "the staging of every wave fits one tile buffer");
+        bf16_t *const ostage = KVB + ((nt + 2) & 3) * TB + wu * 16 * OSP;
+        const int nd_r = (WD - R) >> 4;  // first dim block that holds a rotated dim
 #pragma unroll
-                for (int q8 = 0; q8 < EG; ++q8) {
-                    const int nd = ng + q8;
-                    const int d0 = 16 * nd + 4 * g4;
-                    float x[4];
+        for (int ob = 0; ob < OB; ++ob) {
+            const float inv = invs[16 * ob + l16];
+            uint2 pko[DPW];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) x[r] = agpr_read(acc[b][nd][r]) * inv;
-                    // blocks before nd_r hold no rotated dim (a uniform test); within a
-                    // block each pair is checked
-                    if (rope_t != nullptr && nd >= nd_r) {
+            for (int d = 0; d < DPW; ++d) {
+                const int nd = DPW * wu + d;
+                const int d0 = 16 * nd + 4 * g4;
+                float x[4];
 #pragma unroll
-                        for (int e = 0; e < 2; ++e) {
-                            const float2 cp = (nd >= NDN - 4) ? orp[nd >= NDN - 4 ? nd - (NDN - 4) : 0][e]
-                                                              : rope_pair(rope_t, d0 + 2 * e, R);
-                            if (d0 + 2 * e >= WD - R) {
-                                const float x0 = x[2 * e], x1 = x[2 * e + 1];
-                                x[2 * e] = x0 * cp.x + x1 * cp.y;
-                                x[2 * e + 1] = x1 * cp.x - x0 * cp.y;
-                            }
+                for (int r = 0; r < 4; ++r) x[r] = agpr_read(acc[ob][d][r]) * inv;
+                if (rot && nd >= nd_r) {
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        if (d0 + 2 * e >= WD - R) {
+                            const float2 cp = orp[d][e];
+                            const float x0 = x[2 * e], x1 = x[2 * e + 1];
+                            x[2 * e] = x0 * cp.x + x1 * cp.y;
+                            x[2 * e + 1] = x1 * cp.x - x0 * cp.y;
                         }
                     }
-                    pk[q8] = make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
                 }
-#pragma unroll
-                for (int q8 = 0; q8 < EG; ++q8)
-                    *reinterpret_cast<uint2 *>(ostage + l16 * OSP + 16 * (ng + q8) + 4 * g4) = pk[q8];
-                // one group at a time: hoisted reads of later groups would need registers
-                // the accumulators still hold
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            // the block's 16 head rows go out whole: one 1 KiB row per store instruction (a
-            // lane's 8-byte pieces of 16 rows would be 16 partial-line writes per store)
-#pragma unroll
-            for (int hr = 0; hr < 16; ++hr)
-                *reinterpret_cast<uint4 *>(out + ((int64_t)t * H + head0 + 16 * b + hr) * WD + 8 * lane) =
-                    *reinterpret_cast<const uint4 *>(ostage + hr * OSP + 8 * lane);
-        } else {
-            const int64_t pu = ((int64_t)t * nsplit + sp) * H + h;
-            float *pml = part;                                                               // [T][nsplit][H][2]
-            bf16_t *pacc = reinterpret_cast<bf16_t *>(part + (int64_t)T * nsplit * H * 2);  // [T][nsplit][H][D] bf16
-            if (g4 == 0) {
-                pml[pu * 2] = m_ref[b];
-                pml[pu * 2 + 1] = lacc[b][0];
+                pko[d] = make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
             }
 #pragma unroll
-            for (int ng = 0; ng < NDN; ng += 4) {
-                uint2 v[4];
+            for (int d = 0; d < DPW; ++d)
+                *reinterpret_cast<uint2 *>(ostage + l16 * OSP + 16 * d + 4 * g4) = pko[d];
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4)
-                    v[q4] = make_uint2(pack_bf16x2(agpr_read(acc[b][ng + q4][0]), agpr_read(acc[b][ng + q4][1])),
-                                       pack_bf16x2(agpr_read(acc[b][ng + q4][2]), agpr_read(acc[b][ng + q4][3])));
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4)
-                    *reinterpret_cast<uint2 *>(pacc + pu * WD + 16 * (ng + q4) + 4 * g4) = v[q4];
-                __builtin_amdgcn_sched_barrier(0);
+            for (int s = 0; s < 4; ++s) {
+                const int hr = 4 * s + (lane >> 4), cw = lane & 15;
+                *reinterpret_cast<uint4 *>(out + ((int64_t)t * H + hw0 + 16 * ob + hr) * WD + 16 * DPW * wu + 8 * cw) =
+                    *reinterpret_cast<const uint4 *>(ostage + hr * OSP + 8 * cw);
             }
+            // one head block at a time: hoisted reads of later blocks would need registers
+            // the accumulators still hold
+            __builtin_amdgcn_sched_barrier(0);
         }
-    }
-    if (abandoned) {
+    } else {
         // rare: a head's maximum grew past the headroom after the first tile; this wave's
-        // 32 heads are computed again by a plain two-pass routine, which overwrites what the
-        // epilogue above stored (the same wave wrote it, so the stores land in order)
-        unit_fallback(q, sink, c, j0, j1, ratio, sidx, idx_t, N, kv, swa, swa_rows,
-                      rope_cs ? rope_cs + (int64_t)t * R : nullptr, R, scale_log2, t, T, H, head0, nsplit, sp,
-                      out, lse, part);
+        // 32 S^T heads are computed again by a plain two-pass routine (nothing was stored)
+        unit_fallback(q, sink, c, 0, j1, ratio, sidx, idx_t, N, kv, swa, swa_rows, rope_t, R, scale_log2, t, T, H,
+                      head0, 1, 0, out, lse, nullptr);
     }
 }
 
 }  // namespace
 
-// bf16, D = 512, whole 128-head groups, and rows addressable by a 32-bit byte offset within
-// a sequence's region (2^21 rows of 1 KiB)
-bool w32_attn_ok(csa_dtype dt, int H, int D, int64_t N, int swa_rows) {
-    return dt == CSA_BF16 && D == WD && H % WH == 0 && N <= (int64_t{1} << 21) && swa_rows <= (1 << 21);
+// bf16, D = 512, whole 128-head groups, rows addressable by a 32-bit byte offset within a
+// sequence's region (2^21 rows of 1 KiB), and a top-k list that fits the LDS copy
+bool w32_attn_ok(csa_dtype dt, int H, int D, int64_t N, int swa_rows, int ratio, int k) {
+    return dt == CSA_BF16 && D == WD && H % WH == 0 && N <= (int64_t{1} << 21) && swa_rows <= (1 << 21) &&
+           (ratio > 0 || k <= kW32Idx);
 }
 
 int launch_attn_w32(const AttnArgs &a, float sl2, int nsplit, int64_t split_slots, hipStream_t st) {
-    const int64_t U = (int64_t)a.T * nsplit * (a.H / WH);
+    if (nsplit != 1) return fail(CSA_EUNSUPPORTED, "attn_w32_kernel: one split per query only");
+    const int64_t U = (int64_t)a.T * (a.H / WH);
     const int64_t blocks = ((U + 7) / 8) * 8;
     hipLaunchKernelGGL(attn_w32_kernel, dim3((unsigned)blocks), dim3(64 * NWV), 0, st, (const bf16_t *)a.q,
                        (const bf16_t *)a.kv, a.sink, a.idx, a.k, a.ratio, sl2, (const bf16_t *)a.swa, a.swa_pos0,
                        a.swa_rows, a.window, a.q_seq, a.q_pos, a.rope_cs, a.rope_dim, a.T, a.B, a.N, a.H,
-                       (bf16_t *)a.out, a.lse, (float *)a.ws, nsplit, split_slots);
+                       (bf16_t *)a.out, a.lse, split_slots);
     return check_launch("attn_w32_kernel");
 }
 

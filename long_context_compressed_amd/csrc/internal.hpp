@@ -99,7 +99,7 @@ int launch_attn(const AttnArgs &a, hipStream_t st);
 bool wide_attn_ok(csa_dtype dt, int H, int D);
 int launch_attn_wide(const AttnArgs &a, float sl2, int nsplit, int64_t split_slots, hipStream_t st);
 int device_cu_count();
-bool w32_attn_ok(csa_dtype dt, int H, int D, int64_t N, int swa_rows);
+bool w32_attn_ok(csa_dtype dt, int H, int D, int64_t N, int swa_rows, int ratio, int k);
 int launch_attn_w32(const AttnArgs &a, float sl2, int nsplit, int64_t split_slots, hipStream_t st);
 
 }  // namespace csa

@@ -402,6 +402,10 @@ def _attn_inputs(seed, T, H, D, B, N, k, swa_rows, dt, pos, with_rope=True, bad_
     dict(T=2, H=128, D=512, B=2, N=900, k=10, swa=128, dt=torch.bfloat16, pos=[131072, 4000]),
     # one query of 64 heads: 64 split units of 2 tiles each
     dict(T=1, H=64, D=512, B=1, N=5000, k=4000, swa=128, dt=torch.bfloat16, pos=[40000]),
+    # many queries with a top-k list longer than the 128-head kernel's LDS copy (1,024):
+    # they take the 8-wavefront kernel; and one just inside it (ragged last main tile)
+    dict(T=256, H=128, D=512, B=1, N=3000, k=1100, swa=200, dt=torch.bfloat16, pos=None),
+    dict(T=256, H=128, D=512, B=1, N=3000, k=1000, swa=200, dt=torch.bfloat16, pos=None),
 ])
 def test_sparse_attn(csa, orc, case):
     c = dict(case)
