@@ -299,7 +299,9 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
 #pragma unroll
             for (int b = 0; b < HB; ++b) {
 #pragma unroll
-                for (int kk = 0; kk < KKN - 2; ++kk) qf[b][kk] = rope_fragment(qf[b][kk], kk, g4, rope_t, R);
+                for (int kk = 0; kk < KKN - 2; ++kk)
+                    if (32 * (kk + 1) > WD - R)  // (wave-uniform: only fragments that reach the rotated dims)
+                        qf[b][kk] = rope_fragment(qf[b][kk], kk, g4, rope_t, R);
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
                     const float cs[4] = {qr[j][0].x, qr[j][1].x, qr[j][2].x, qr[j][3].x};
@@ -646,12 +648,11 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
         stage_barrier();
         tile_iter(0, std::true_type{});
         for (int i = 1; i < nt; ++i) tile_iter(i, std::false_type{});
-        // the loads of the two tiles past the end (stand-ins) land before anything else
-        // touches LDS
-        __builtin_amdgcn_s_waitcnt(0);
     }
     // (cos, sin) pairs of the lane's output dims when this wave's dims reach the rotated
-    // ones, loaded before the last products
+    // ones, loaded before the last products. (The row loads of the two tiles past the end,
+    // stand-ins, may still be landing in their tile buffers, which nothing below touches;
+    // the kernel waits for them before it ends.)
     const bool rot = rope_t != nullptr && 16 * DPW * (wu + 1) > WD - R;
     float2 orp[DPW][2];
     if (rot) {
@@ -737,6 +738,8 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
         unit_fallback(q, sink, c, 0, j1, ratio, sidx, idx_t, N, kv, swa, swa_rows, rope_t, R, scale_log2, t, T, H,
                       head0, 1, 0, out, lse, nullptr);
     }
+    // no load into this workgroup's LDS may still be in flight when it ends
+    __builtin_amdgcn_s_waitcnt(0);
 }
 
 }  // namespace
