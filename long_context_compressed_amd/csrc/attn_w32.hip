@@ -689,11 +689,13 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
         // ---- epilogue. Lane (l16, g4) holds dims 16(DPW w + d) + 4g4 + r (four consecutive
         // dims) of head 16ob + l16: it normalises them, rotates back the rotated dims (pairs
         // sit in one lane) and stages 8 bytes per dim block; each head block's 16 x 256-byte
-        // row pieces then go out as four 1 KiB stores. The staging sits in a tile buffer
-        // that no wave reads any more.
+        // row pieces then go out as four 1 KiB stores. The staging alternates between two
+        // tile buffers that no wave reads any more (and no row load writes), so a head
+        // block's normalisation overlaps the previous block's LDS round trip and stores.
         constexpr int OSP = 16 * DPW + 8;  // staged row pitch (bf16)
         static_assert(NWV * 16 * OSP <= TB, "the staging of every wave fits one tile buffer");
-        bf16_t *const ostage = KVB + ((nt + 2) & 3) * TB + wu * 16 * OSP;
+        bf16_t *const ostage0 = KVB + ((nt + 2) & 3) * TB + wu * 16 * OSP;
+        bf16_t *const ostage1 = KVB + (nt & 3) * TB + wu * 16 * OSP;
         const int nd_r = (WD - R) >> 4;  // first dim block that holds a rotated dim
 #pragma unroll
         for (int ob = 0; ob < OB; ++ob) {
@@ -719,6 +721,7 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
                 }
                 pko[d] = make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
             }
+            bf16_t *const ostage = (ob & 1) ? ostage1 : ostage0;
 #pragma unroll
             for (int d = 0; d < DPW; ++d)
                 *reinterpret_cast<uint2 *>(ostage + l16 * OSP + 16 * d + 4 * g4) = pko[d];
@@ -728,9 +731,6 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
                 *reinterpret_cast<uint4 *>(out + ((int64_t)t * H + hw0 + 16 * ob + hr) * WD + 16 * DPW * wu + 8 * cw) =
                     *reinterpret_cast<const uint4 *>(ostage + hr * OSP + 8 * cw);
             }
-            // one head block at a time: hoisted reads of later blocks would need registers
-            // the accumulators still hold
-            __builtin_amdgcn_sched_barrier(0);
         }
     } else {
         // rare: a head's maximum grew past the headroom after the first tile; this wave's
