@@ -11,10 +11,11 @@
 //     layout of P; each wavefront turns its S^T into P (online softmax against a reference
 //     maximum fixed by the first tile, so O is never rescaled) and puts its two 16-head
 //     blocks of P into LDS (1 KiB each, lane-linear).
-//   - O^T += V^T P^T: wavefront w owns dims 128w .. 128w+127 of all 128 heads (its 128 x 128
-//     fp32 output block fills the 256 accumulation registers), reads P of every head from
-//     LDS and only its quarter of the V fragments (transposing reads), so each V fragment
-//     feeds eight matrix ops and each P fragment four.
+//   - O^T += V^T P^T (MFMA 32x32x16 bf16): wavefront w owns dims 128w .. 128w+127 of all
+//     128 heads (its 128 x 128 fp32 output block fills the 256 accumulation registers),
+//     reads P of every head from LDS and only its quarter of the V fragments (transposing
+//     reads); each V fragment and each P fragment feeds four matrix ops, and the larger ops
+//     halve the instructions the wavefront issues for this product.
 // Tiles are pipelined over four LDS tile buffers. While tile i's S^T runs, the rows of tile
 // i+2 go from memory straight into LDS (buffer loads with the LDS destination), one row per
 // two of its matrix-op steps; then the products of tile i-1 run with the softmax of tile i
@@ -77,11 +78,12 @@ __device__ __forceinline__ void static_for(F &&f) {
 // source register possibly written by a VALU move gets >= 5 wait states (the s_nop at the
 // head of the first product of each V fragment), and the results are read back only after
 // two s_nop 15 (pv_fence).
-__device__ __forceinline__ void pv_mfma(f32x4 &acc, const bf16x8 a, const bf16x8 b) {
-    asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ void pv_mfma32(f32x16 &acc, const bf16x8 a, const bf16x8 b) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
-__device__ __forceinline__ void pv_mfma_after_valu(f32x4 &acc, const bf16x8 a, const bf16x8 b) {
-    asm volatile("s_nop 4\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+__device__ __forceinline__ void pv_mfma32_after_valu(f32x16 &acc, const bf16x8 a, const bf16x8 b) {
+    asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 // one accumulator read out of its AGPR where it is used (left to itself the compiler copies
 // every accumulator to VGPRs at once, more than there are)
@@ -322,7 +324,9 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
     const bf16x8 zero8 = __builtin_bit_cast(bf16x8, u32x4w{0u, 0u, 0u, 0u});
     float m_ref[HB];
     f32x4 lacc[HB];
-    f32x4 acc[OB][DPW];  // O^T: dims 16(DPW w + d) + 4g4 + r of head 16B + l16 of the workgroup
+    // O^T in 32 x 32 blocks: head block hb (heads 32hb .. 32hb+31 of the workgroup) x dim block db
+    // (dims 128w + 32db ..); lane l holds head 32hb + l % 32, dims 32db + 8(j / 4) + 4(l / 32) + j % 4
+    f32x16 acc[OB / 2][DPW / 2];
 #pragma unroll
     for (int b = 0; b < HB; ++b) {
         lacc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -331,10 +335,10 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
     // zeroed by matrix ops into AGPRs, so the accumulators never pass through VGPRs; the
     // zero operand may have just been written by a VALU move, hence the wait states
 #pragma unroll
-    for (int ob = 0; ob < OB; ++ob)
+    for (int hb = 0; hb < OB / 2; ++hb)
 #pragma unroll
-        for (int d = 0; d < DPW; ++d)
-            asm volatile("s_nop 4\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %1, 0" : "=a"(acc[ob][d]) : "v"(zero8));
+        for (int db = 0; db < DPW / 2; ++db)
+            asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(acc[hb][db]) : "v"(zero8));
 
     // The top-k indices are read once into LDS.
     const int64_t jm = (j1 < c.nmain) ? j1 : c.nmain;  // main slots: [0, jm)
@@ -403,73 +407,69 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
         row_dma(rs, voff, soff, kvb + (uint32_t)(nb + (RPW * wu + r) * WP) * 2u);
     };
 
-    // O^T += V^T P^T for the tile in the buffer at bf16 offset vb, with P from PB[pr]. The
-    // wave's 8 dim blocks go in two halves: the V fragments of a half (two transposing
-    // reads per 16-dim block, in the row order of the S^T C layout) stay in registers while
-    // the P fragments of the eight head blocks stream past, each feeding four products.
-    // The first half's V fragments and the first P fragments are read ahead (pv_pre).
-    // `step(p)` is called after product p (0 .. 63) and, with p = 100 + h, before the first
-    // product of half h: the softmax of the next tile goes there, a few instructions at a
-    // time.
+    // O^T += V^T P^T for the tile in the buffer at bf16 offset vb, with P from PB[pr], in
+    // 32 x 32 x 16 matrix ops: the tile's 32 rows are two k-steps of 16, each row set taken
+    // in the order the S^T C layout hands P over (k-step s: rows 8s + 4kg + 0..3 and
+    // 16 + 8s + 4kg + 0..3 for the lanes of half kg). Per k-step the V fragments of the
+    // wave's four 32-dim blocks (two transposing reads each) stay in registers while the P
+    // fragments of the four 32-head blocks stream past, each feeding four products. P of
+    // 32 heads for one k-step is one 16-byte LDS read per lane: lane l takes the fragment
+    // that S^T lane (l % 16, g4 = 2s + l / 32) of head block 2hb + (l / 16) % 2 wrote.
+    // The first k-step's V fragments and the first P fragments are read ahead (pv_pre).
+    // `step(p)` is called after product p (0 .. 31) and, with p = 100 + s, before the first
+    // product of k-step s: the softmax of the next tile goes there, an instruction at a time.
+    const int kg = lane >> 5;
+    const int pbo = ((lane >> 4) & 1) * 64 + (lane & 15) + 16 * kg;
+    auto vfrag = [&](int vb, int db, int s) __attribute__((always_inline)) -> bf16x8 {
+        const bf16_t *base = KVB + vb + 16 * DPW * wu + 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3) +
+                             ((lane & 15) >> 2) * WP;
+        const bf16x4v lo = __builtin_bit_cast(bf16x4v, ld_tr(base + (8 * s + 4 * kg) * WP));
+        const bf16x4v hi = __builtin_bit_cast(bf16x4v, ld_tr(base + (16 + 8 * s + 4 * kg) * WP));
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    auto pfrag = [&](int pr, int hb, int s) __attribute__((always_inline)) -> bf16x8 {
+        return __builtin_bit_cast(bf16x8, PB[pr][2 * hb * 64 + pbo + 32 * s]);
+    };
     struct PvPre {
-        bf16x4v va[DPW / 2], vb[DPW / 2];
-        bf16x8 pr[PVA];
+        bf16x8 a[DPW / 2];
+        bf16x8 b[PVA];
     };
     auto pv_pre = [&](int vb, int pr, PvPre &P) __attribute__((always_inline)) {
-        const int s4 = l16 >> 2, sc = l16 & 3;
-        const bf16_t *v0 = KVB + vb + (4 * g4 + s4) * WP + 4 * sc + 16 * DPW * wu;
-        const bf16_t *v1 = v0 + 16 * WP;
 #pragma unroll
-        for (int dd = 0; dd < DPW / 2; ++dd) {
-            P.va[dd] = __builtin_bit_cast(bf16x4v, ld_tr(v0 + 16 * dd));
-            P.vb[dd] = __builtin_bit_cast(bf16x4v, ld_tr(v1 + 16 * dd));
-        }
-        const u32x4w *pp = &PB[pr][lane];
+        for (int db = 0; db < DPW / 2; ++db) P.a[db] = vfrag(vb, db, 0);
 #pragma unroll
-        for (int cc = 0; cc < PVA; ++cc) P.pr[cc] = __builtin_bit_cast(bf16x8, pp[cc * 64]);
+        for (int cc = 0; cc < PVA; ++cc) P.b[cc] = pfrag(pr, cc, 0);
     };
     auto pv_phase = [&](int vb, int pr, const PvPre &P, auto &&step) __attribute__((always_inline)) {
-        const int s4 = l16 >> 2, sc = l16 & 3;
-        const bf16_t *v0 = KVB + vb + (4 * g4 + s4) * WP + 4 * sc + 16 * DPW * wu;
-        const bf16_t *v1 = v0 + 16 * WP;
-        const u32x4w *pp = &PB[pr][lane];
-        static_for<0, 2>([&](auto DH) __attribute__((always_inline)) {
-            constexpr int dh = decltype(DH)::value;
-            constexpr int DQ = DPW / 2;
-            bf16x4v va[DQ], vb2[DQ];
+        static_for<0, 2>([&](auto SK) __attribute__((always_inline)) {
+            constexpr int sk2 = decltype(SK)::value;
+            bf16x8 va[DPW / 2];
             bf16x8 pr_[PVA + 1];
-            if constexpr (dh == 0) {
+            if constexpr (sk2 == 0) {
 #pragma unroll
-                for (int dd = 0; dd < DQ; ++dd) {
-                    va[dd] = P.va[dd];
-                    vb2[dd] = P.vb[dd];
-                }
+                for (int db = 0; db < DPW / 2; ++db) va[db] = P.a[db];
 #pragma unroll
-                for (int cc = 0; cc < PVA; ++cc) pr_[cc] = P.pr[cc];
+                for (int cc = 0; cc < PVA; ++cc) pr_[cc] = P.b[cc];
             } else {
 #pragma unroll
-                for (int dd = 0; dd < DQ; ++dd) {
-                    va[dd] = __builtin_bit_cast(bf16x4v, ld_tr(v0 + 16 * (DQ * dh + dd)));
-                    vb2[dd] = __builtin_bit_cast(bf16x4v, ld_tr(v1 + 16 * (DQ * dh + dd)));
-                }
+                for (int db = 0; db < DPW / 2; ++db) va[db] = vfrag(vb, db, 1);
 #pragma unroll
-                for (int cc = 0; cc < PVA; ++cc) pr_[cc] = __builtin_bit_cast(bf16x8, pp[cc * 64]);
+                for (int cc = 0; cc < PVA; ++cc) pr_[cc] = pfrag(pr, cc, 1);
             }
             __builtin_amdgcn_sched_barrier(0);
-            step(std::integral_constant<int, 100 + dh>{});
+            step(std::integral_constant<int, 100 + sk2>{});
             __builtin_amdgcn_sched_barrier(0);
-            static_for<0, OB>([&](auto OBI) __attribute__((always_inline)) {
-                constexpr int ob = decltype(OBI)::value;
-                if constexpr (ob + PVA < OB) pr_[(ob + PVA) % (PVA + 1)] = __builtin_bit_cast(bf16x8, pp[(ob + PVA) * 64]);
+            static_for<0, OB / 2>([&](auto HBI) __attribute__((always_inline)) {
+                constexpr int hb = decltype(HBI)::value;
+                if constexpr (hb + PVA < OB / 2) pr_[(hb + PVA) % (PVA + 1)] = pfrag(pr, hb + PVA, sk2);
                 __builtin_amdgcn_sched_barrier(0);
-                static_for<0, DQ>([&](auto DD) __attribute__((always_inline)) {
-                    constexpr int dd = decltype(DD)::value;
-                    const bf16x8 vf = __builtin_shufflevector(va[dd], vb2[dd], 0, 1, 2, 3, 4, 5, 6, 7);
-                    if constexpr (ob == 0)
-                        pv_mfma_after_valu(acc[ob][DQ * dh + dd], vf, pr_[ob % (PVA + 1)]);
+                static_for<0, DPW / 2>([&](auto DBI) __attribute__((always_inline)) {
+                    constexpr int db = decltype(DBI)::value;
+                    if constexpr (hb == 0)
+                        pv_mfma32_after_valu(acc[hb][db], va[db], pr_[hb % (PVA + 1)]);
                     else
-                        pv_mfma(acc[ob][DQ * dh + dd], vf, pr_[ob % (PVA + 1)]);
-                    step(std::integral_constant<int, 32 * dh + DQ * ob + dd>{});
+                        pv_mfma32(acc[hb][db], va[db], pr_[hb % (PVA + 1)]);
+                    step(std::integral_constant<int, 16 * sk2 + 4 * hb + db>{});
                     __builtin_amdgcn_sched_barrier(0);
                 });
             });
@@ -606,18 +606,18 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
         if constexpr (kFirst) {
             static_for<0, kMicro>([&](auto UI) __attribute__((always_inline)) { sm_micro(UI); });
         } else {
-            // micro-step 0 before the first product, 15-18 while the second half's V
-            // fragments are read, the others after every second product
+            // micro-steps 0-1 before the first product, 16-17 while the second k-step's
+            // fragments are read, the others one after each product
             pv_phase(pb, (i - 1) & 1, pre, [&](auto PI) __attribute__((always_inline)) {
                 constexpr int p = decltype(PI)::value;
                 if constexpr (p == 100) {
                     sm_micro(std::integral_constant<int, 0>{});
+                    sm_micro(std::integral_constant<int, 1>{});
                 } else if constexpr (p == 101) {
-                    static_for<15, 19>([&](auto UI) __attribute__((always_inline)) { sm_micro(UI); });
-                } else if constexpr (p < 28 && (p & 1)) {
-                    sm_micro(std::integral_constant<int, (p + 1) / 2>{});
-                } else if constexpr (p >= 33 && p < 100 && (p & 1) && (p - 33) / 2 + 19 < kMicro) {
-                    sm_micro(std::integral_constant<int, (p - 33) / 2 + 19>{});
+                    sm_micro(std::integral_constant<int, 16>{});
+                    sm_micro(std::integral_constant<int, 17>{});
+                } else if constexpr (p < 14 || (p >= 16 && p < 25)) {
+                    sm_micro(std::integral_constant<int, p + 2>{});
                 }
             });
         }
@@ -654,12 +654,15 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
     // stand-ins, may still be landing in their tile buffers, which nothing below touches;
     // the kernel waits for them before it ends.)
     const bool rot = rope_t != nullptr && 16 * DPW * (wu + 1) > WD - R;
-    float2 orp[DPW][2];
+    float2 orp[DPW / 2][4][2];
     if (rot) {
 #pragma unroll
-        for (int d = 0; d < DPW; ++d)
+        for (int db = 0; db < DPW / 2; ++db)
 #pragma unroll
-            for (int e = 0; e < 2; ++e) orp[d][e] = rope_pair(rope_t, 16 * (DPW * wu + d) + 4 * g4 + 2 * e, R);
+            for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+                for (int e = 0; e < 2; ++e)
+                    orp[db][q4][e] = rope_pair(rope_t, 16 * DPW * wu + 32 * db + 8 * q4 + 4 * kg + 2 * e, R);
     }
     // denominators of this wave's S^T heads, shared with the waves that hold their outputs
     float lse_v[HB];
@@ -686,50 +689,60 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
 #pragma unroll
             for (int b = 0; b < HB; ++b) lse[(int64_t)t * H + head0 + 16 * b + l16] = lse_v[b];
         }
-        // ---- epilogue. Lane (l16, g4) holds dims 16(DPW w + d) + 4g4 + r (four consecutive
-        // dims) of head 16ob + l16: it normalises them, rotates back the rotated dims (pairs
-        // sit in one lane) and stages 8 bytes per dim block; each head block's 16 x 256-byte
-        // row pieces then go out as four 1 KiB stores. The staging alternates between two
-        // tile buffers that no wave reads any more (and no row load writes), so a head
-        // block's normalisation overlaps the previous block's LDS round trip and stores.
-        constexpr int OSP = 16 * DPW + 8;  // staged row pitch (bf16)
-        static_assert(NWV * 16 * OSP <= TB, "the staging of every wave fits one tile buffer");
-        bf16_t *const ostage0 = KVB + ((nt + 2) & 3) * TB + wu * 16 * OSP;
-        bf16_t *const ostage1 = KVB + (nt & 3) * TB + wu * 16 * OSP;
-        const int nd_r = (WD - R) >> 4;  // first dim block that holds a rotated dim
+        // ---- epilogue. Lane l holds, per 32 x 32 block (hb, db), dims 32db + 8q + 4kg + r
+        // (q, r = 0..3: four runs of four consecutive dims) of head 32hb + l % 32: it
+        // normalises them, rotates back the rotated dims (pairs sit in one lane) and stages 8
+        // bytes per run; each head block's 32 x 256-byte row pieces then go out as eight
+        // 1 KiB stores (four whole rows each). Staged rows are 256 bytes, 16-byte chunk c of
+        // row h at chunk c ^ (h % 16), so the 32 rows' writes of one chunk spread over the
+        // banks and the reads stay 16-byte aligned. The staging alternates between two tile
+        // buffers that no wave reads any more (and no row load writes), so a head block's
+        // normalisation overlaps the previous block's LDS round trip and stores.
+        constexpr int OSP = 16 * DPW;  // staged row pitch (bf16): 256 bytes
+        static_assert(NWV * 32 * OSP <= TB, "the staging of every wave fits one tile buffer");
+        bf16_t *const ostage0 = KVB + ((nt + 2) & 3) * TB + wu * 32 * OSP;
+        bf16_t *const ostage1 = KVB + (nt & 3) * TB + wu * 32 * OSP;
+        const int n32 = lane & 31;
 #pragma unroll
-        for (int ob = 0; ob < OB; ++ob) {
-            const float inv = invs[16 * ob + l16];
-            uint2 pko[DPW];
+        for (int hb = 0; hb < OB / 2; ++hb) {
+            const float inv = invs[32 * hb + n32];
+            uint2 pko[DPW / 2][4];
 #pragma unroll
-            for (int d = 0; d < DPW; ++d) {
-                const int nd = DPW * wu + d;
-                const int d0 = 16 * nd + 4 * g4;
-                float x[4];
+            for (int db = 0; db < DPW / 2; ++db) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) x[r] = agpr_read(acc[ob][d][r]) * inv;
-                if (rot && nd >= nd_r) {
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int d0 = 16 * DPW * wu + 32 * db + 8 * q4 + 4 * kg;
+                    float x[4];
 #pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        if (d0 + 2 * e >= WD - R) {
-                            const float2 cp = orp[d][e];
-                            const float x0 = x[2 * e], x1 = x[2 * e + 1];
-                            x[2 * e] = x0 * cp.x + x1 * cp.y;
-                            x[2 * e + 1] = x1 * cp.x - x0 * cp.y;
+                    for (int r = 0; r < 4; ++r) x[r] = agpr_read(acc[hb][db][4 * q4 + r]) * inv;
+                    // blocks below the rotated dims skip the test (a uniform one); within a
+                    // block each pair is checked
+                    if (rot && 16 * DPW * wu + 32 * db + 32 > WD - R) {
+#pragma unroll
+                        for (int e = 0; e < 2; ++e) {
+                            if (d0 + 2 * e >= WD - R) {
+                                const float2 cp = orp[db][q4][e];
+                                const float x0 = x[2 * e], x1 = x[2 * e + 1];
+                                x[2 * e] = x0 * cp.x + x1 * cp.y;
+                                x[2 * e + 1] = x1 * cp.x - x0 * cp.y;
+                            }
                         }
                     }
+                    pko[db][q4] = make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
                 }
-                pko[d] = make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
             }
-            bf16_t *const ostage = (ob & 1) ? ostage1 : ostage0;
+            bf16_t *const ostage = (hb & 1) ? ostage1 : ostage0;
 #pragma unroll
-            for (int d = 0; d < DPW; ++d)
-                *reinterpret_cast<uint2 *>(ostage + l16 * OSP + 16 * d + 4 * g4) = pko[d];
+            for (int db = 0; db < DPW / 2; ++db)
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int hr = 4 * s + (lane >> 4), cw = lane & 15;
-                *reinterpret_cast<uint4 *>(out + ((int64_t)t * H + hw0 + 16 * ob + hr) * WD + 16 * DPW * wu + 8 * cw) =
-                    *reinterpret_cast<const uint4 *>(ostage + hr * OSP + 8 * cw);
+                for (int q4 = 0; q4 < 4; ++q4)
+                    *reinterpret_cast<uint2 *>(ostage + n32 * OSP + 8 * ((4 * db + q4) ^ (n32 & 15)) + 4 * kg) =
+                        pko[db][q4];
+#pragma unroll
+            for (int s2 = 0; s2 < 8; ++s2) {
+                const int hr = 4 * s2 + (lane >> 4), cw = lane & 15;
+                *reinterpret_cast<uint4 *>(out + ((int64_t)t * H + hw0 + 32 * hb + hr) * WD + 16 * DPW * wu + 8 * cw) =
+                    *reinterpret_cast<const uint4 *>(ostage + hr * OSP + 8 * (cw ^ (hr & 15)));
             }
         }
     } else {
