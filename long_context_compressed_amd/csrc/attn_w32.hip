@@ -5,17 +5,18 @@
 //
 // One workgroup of 4 wavefronts (one per SIMD) covers 128 heads of one query. The two
 // products of a 32-row tile are split differently over the wavefronts:
-//   - S^T = K Q^T (rows x heads, MFMA 16x16x32 bf16): wavefront w owns heads 32w .. 32w+31
-//     and all 512 dims, so q^T (32 heads x 512 dims, bf16) stays in 128 registers and every
-//     K fragment read from LDS feeds two matrix ops. The C layout of S^T is the B-operand
-//     layout of P; each wavefront turns its S^T into P (online softmax against a reference
-//     maximum fixed by the first tile, so O is never rescaled) and puts its two 16-head
-//     blocks of P into LDS (1 KiB each, lane-linear).
+//   - S^T = K Q^T (rows x heads, MFMA 32x32x16 bf16): wavefront w owns heads 32w .. 32w+31
+//     and all 512 dims, so q^T (32 heads x 512 dims, bf16) stays in 128 registers; each
+//     lane's 16 scores belong to one head, so a head's maximum needs one lane swap. The C
+//     layout of S^T gives P in the B-operand layout of the next product; each wavefront
+//     turns its S^T into P (online softmax against a reference maximum fixed by the first
+//     tile, so O is never rescaled) and puts it into LDS (two 16-row k-steps, 1 KiB each,
+//     lane-linear).
 //   - O^T += V^T P^T (MFMA 32x32x16 bf16): wavefront w owns dims 128w .. 128w+127 of all
 //     128 heads (its 128 x 128 fp32 output block fills the 256 accumulation registers),
 //     reads P of every head from LDS and only its quarter of the V fragments (transposing
-//     reads); each V fragment and each P fragment feeds four matrix ops, and the larger ops
-//     halve the instructions the wavefront issues for this product.
+//     reads); each V fragment and each P fragment feeds four matrix ops.
+// The 32x32x16 ops (rather than 16x16x32) halve the matrix instructions a wavefront issues.
 // Tiles are pipelined over four LDS tile buffers. While tile i's S^T runs, the rows of tile
 // i+2 go from memory straight into LDS (buffer loads with the LDS destination), one row per
 // two of its matrix-op steps; then the products of tile i-1 run with the softmax of tile i
@@ -53,7 +54,7 @@ static_assert(kW32Idx <= kIdxCache, "the two-pass routine reads the LDS copy bel
 // loads of the tile two ahead) done
 constexpr int kWaitTileAhead = RPW | (7 << 4) | (0 << 8);
 static_assert(NDN % NWV == 0, "the output dims split evenly over the wavefronts");
-constexpr int SDA = 2;            // K fragment chunks read ahead
+constexpr int SDA = 3;            // K fragment chunks (16 dims) read ahead
 constexpr int PVA = 2;            // P fragments read ahead
 constexpr float kHeadroom = 24.f; // log2 growth of a head's maximum the tile loop absorbs
 
@@ -247,7 +248,7 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
     __shared__ int redo;
 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int l16 = lane & 15, g4 = lane >> 4;
+    const int n32 = lane & 31, kg = lane >> 5;  // lane of a 32-wide matrix-op row, and its half
     // XCD-aware placement: units (query, head group) are dealt to the 8 XCDs in contiguous
     // runs, so neighbouring queries (which share SWA rows and summaries) meet in one L2
     const int HGN = H / WH;
@@ -274,42 +275,38 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
             ir[m] = (x < nc0) ? idx[(int64_t)t * k + x] : 0;
         }
     }
-    float sk[HB];
-#pragma unroll
-    for (int b = 0; b < HB; ++b) sk[b] = sink[head0 + 16 * b + l16];
+    const float sk = sink[head0 + n32];  // the sink of this lane's S^T head
 
-    // q^T fragments of both head blocks, for the whole query. Every load is issued first
-    // (they overlap; the (cos, sin) pairs of the last 64 dims included), then the fragments
-    // that hold rotated dims are rotated.
+    // q^T fragments of the wave's 32 heads for the whole query, the B operands of the
+    // 32x32x16 S^T products: chunk kc holds dims 16kc + 8(l / 32) .. +7 of head l % 32.
+    // Every load is issued first (they overlap; the (cos, sin) pairs of the last 64 dims
+    // included), then the chunks that reach the rotated dims are rotated.
+    constexpr int QC = 2 * KKN;  // 16-dim chunks of a head
     const float *rope_t = rope_cs ? rope_cs + (int64_t)t * R : nullptr;
-    bf16x8 qf[HB][KKN];
+    bf16x8 qf[QC];
     {
-        float2 qr[2][4];
+        float2 qr[4][4];
         if (rope_t != nullptr) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) qr[j][e] = rope_pair(rope_t, 32 * (KKN - 2 + j) + 8 * g4 + 2 * e, R);
+                for (int e = 0; e < 4; ++e) qr[j][e] = rope_pair(rope_t, 16 * (QC - 4 + j) + 8 * kg + 2 * e, R);
         }
+        const bf16_t *qrow = q + ((int64_t)t * H + head0 + n32) * WD;
 #pragma unroll
-        for (int b = 0; b < HB; ++b) {
-            const bf16_t *qrow = q + ((int64_t)t * H + head0 + 16 * b + l16) * WD;
-#pragma unroll
-            for (int kk = 0; kk < KKN; ++kk) qf[b][kk] = ld_bf16x8(qrow + 32 * kk + 8 * g4);
-        }
+        for (int kc = 0; kc < QC; ++kc) qf[kc] = ld_bf16x8(qrow + 16 * kc + 8 * kg);
         if (rope_t != nullptr) {
+            // (chunk kc = dims 32(kc / 2) + 8g with g = 2(kc % 2) + kg, the form the rotation helpers take)
 #pragma unroll
-            for (int b = 0; b < HB; ++b) {
+            for (int kc = 0; kc < QC - 4; ++kc)
+                if (16 * (kc + 1) > WD - R)  // (wave-uniform: only chunks that reach the rotated dims)
+                    qf[kc] = rope_fragment(qf[kc], kc >> 1, 2 * (kc & 1) + kg, rope_t, R);
 #pragma unroll
-                for (int kk = 0; kk < KKN - 2; ++kk)
-                    if (32 * (kk + 1) > WD - R)  // (wave-uniform: only fragments that reach the rotated dims)
-                        qf[b][kk] = rope_fragment(qf[b][kk], kk, g4, rope_t, R);
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const float cs[4] = {qr[j][0].x, qr[j][1].x, qr[j][2].x, qr[j][3].x};
-                    const float sn[4] = {qr[j][0].y, qr[j][1].y, qr[j][2].y, qr[j][3].y};
-                    qf[b][KKN - 2 + j] = rope_fragment_cs(qf[b][KKN - 2 + j], KKN - 2 + j, g4, cs, sn, R);
-                }
+            for (int j = 0; j < 4; ++j) {
+                const int kc = QC - 4 + j;
+                const float cs[4] = {qr[j][0].x, qr[j][1].x, qr[j][2].x, qr[j][3].x};
+                const float sn[4] = {qr[j][0].y, qr[j][1].y, qr[j][2].y, qr[j][3].y};
+                qf[kc] = rope_fragment_cs(qf[kc], kc >> 1, 2 * (kc & 1) + kg, cs, sn, R);
             }
         }
     }
@@ -317,21 +314,16 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
     const RowCtx c = row_ctx(t, q_seq, q_pos, B, N, k, ratio, swa, swa_pos0, window);
     const int64_t j1 = (max_slots < c.nslots) ? max_slots : c.nslots;  // slots [0, j1)
 
-    // softmax state of the wavefront's S^T heads: m_ref of head 16b + l16 (replicated over
-    // the 4 lane groups); the denominators in the output layout (head 16b + 4g4 + r in
-    // component r of lacc[b]), accumulated by a matrix op against a ones operand so they sum
-    // the same bf16 weights that enter O. The sink's 2^(sink - m_ref) is added at the end.
+    // softmax state of this lane's S^T head (head0 + l % 32): the reference maximum m_ref,
+    // and the denominator, accumulated by matrix ops against a ones operand (every component
+    // of lacc holds it) so it sums the same bf16 weights that enter O. The sink's
+    // 2^(sink - m_ref) is added at the end.
     const bf16x8 zero8 = __builtin_bit_cast(bf16x8, u32x4w{0u, 0u, 0u, 0u});
-    float m_ref[HB];
-    f32x4 lacc[HB];
+    float m_ref = sk * kLog2e;
+    f32x16 lacc = {};
     // O^T in 32 x 32 blocks: head block hb (heads 32hb .. 32hb+31 of the workgroup) x dim block db
     // (dims 128w + 32db ..); lane l holds head 32hb + l % 32, dims 32db + 8(j / 4) + 4(l / 32) + j % 4
     f32x16 acc[OB / 2][DPW / 2];
-#pragma unroll
-    for (int b = 0; b < HB; ++b) {
-        lacc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-        m_ref[b] = sk[b] * kLog2e;
-    }
     // zeroed by matrix ops into AGPRs, so the accumulators never pass through VGPRs; the
     // zero operand may have just been written by a VALU move, hence the wait states
 #pragma unroll
@@ -376,7 +368,7 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
     // and rows stay below 2^31.
     const int nmain32 = (int)jm, nwin32 = (int)(j1 - jm);
     const int ntm = __builtin_amdgcn_readfirstlane((nmain32 + WR - 1) / WR);  // (wave-uniform)
-    const int lo_rel = (int)(c.lo - c.swa0), n32 = (int)N;
+    const int lo_rel = (int)(c.lo - c.swa0), nkv32 = (int)N;
     auto code_read = [&](int i) __attribute__((always_inline)) -> int {
         const int j = i * WR + (lane & 31);
         if (ratio > 0) return j;
@@ -388,7 +380,7 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
         int row;
         if (i < ntm) {
             row = id;
-            ok = i * WR + r < nmain32 && id >= 0 && id < n32;
+            ok = i * WR + r < nmain32 && id >= 0 && id < nkv32;
         } else {
             const int w = (i - ntm) * WR + r;
             row = lo_rel + w;
@@ -409,26 +401,23 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
 
     // O^T += V^T P^T for the tile in the buffer at bf16 offset vb, with P from PB[pr], in
     // 32 x 32 x 16 matrix ops: the tile's 32 rows are two k-steps of 16, each row set taken
-    // in the order the S^T C layout hands P over (k-step s: rows 8s + 4kg + 0..3 and
-    // 16 + 8s + 4kg + 0..3 for the lanes of half kg). Per k-step the V fragments of the
+    // in the order the S^T C layout hands P over (k-step s: rows 16s + 4kg + 0..3 and
+    // 16s + 8 + 4kg + 0..3 for the lanes of half kg). Per k-step the V fragments of the
     // wave's four 32-dim blocks (two transposing reads each) stay in registers while the P
     // fragments of the four 32-head blocks stream past, each feeding four products. P of
-    // 32 heads for one k-step is one 16-byte LDS read per lane: lane l takes the fragment
-    // that S^T lane (l % 16, g4 = 2s + l / 32) of head block 2hb + (l / 16) % 2 wrote.
+    // 32 heads for one k-step is one 16-byte LDS read per lane, in the order S^T wrote it.
     // The first k-step's V fragments and the first P fragments are read ahead (pv_pre).
     // `step(p)` is called after product p (0 .. 31) and, with p = 100 + s, before the first
     // product of k-step s: the softmax of the next tile goes there, an instruction at a time.
-    const int kg = lane >> 5;
-    const int pbo = ((lane >> 4) & 1) * 64 + (lane & 15) + 16 * kg;
     auto vfrag = [&](int vb, int db, int s) __attribute__((always_inline)) -> bf16x8 {
         const bf16_t *base = KVB + vb + 16 * DPW * wu + 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3) +
                              ((lane & 15) >> 2) * WP;
-        const bf16x4v lo = __builtin_bit_cast(bf16x4v, ld_tr(base + (8 * s + 4 * kg) * WP));
-        const bf16x4v hi = __builtin_bit_cast(bf16x4v, ld_tr(base + (16 + 8 * s + 4 * kg) * WP));
+        const bf16x4v lo = __builtin_bit_cast(bf16x4v, ld_tr(base + (16 * s + 4 * kg) * WP));
+        const bf16x4v hi = __builtin_bit_cast(bf16x4v, ld_tr(base + (16 * s + 8 + 4 * kg) * WP));
         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     };
     auto pfrag = [&](int pr, int hb, int s) __attribute__((always_inline)) -> bf16x8 {
-        return __builtin_bit_cast(bf16x8, PB[pr][2 * hb * 64 + pbo + 32 * s]);
+        return __builtin_bit_cast(bf16x8, PB[pr][(2 * hb + s) * 64 + lane]);
     };
     struct PvPre {
         bf16x8 a[DPW / 2];
@@ -484,7 +473,7 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
     uint32_t v0 = 0u, v1 = 0u, v2 = 0u;  // validity of tiles i, i+1, i+2
     uint32_t oa = 0u;                     // row offsets of tile i+2
     float growth = -INFINITY;  // largest tile maximum above the reference, log2 units
-    float nmu[HB] = {0.f, 0.f};  // -m_ref (0 for an empty reference), fixed after the first tile
+    float nmu = 0.f;             // -m_ref (0 for an empty reference), fixed after the first tile
     auto tile_iter = [&](int i, auto FIRST) __attribute__((always_inline)) {
         constexpr bool kFirst = decltype(FIRST)::value;
         const int cb = (i & 3) * TB, pb = ((i + 3) & 3) * TB, db = ((i + 2) & 3) * TB;
@@ -494,115 +483,108 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
         const int id3 = code_read(i + 3);
         PvPre pre;
 
-        // ---- S^T = K Q^T: each K fragment feeds both head blocks
-        f32x4 sacc[2][HB];
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-            for (int b = 0; b < HB; ++b) sacc[m][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // ---- S^T = K Q^T (rows x the wave's 32 heads) in 32 matrix ops of 16 dims; lane l
+        // reads row l % 32, dims 16kc + 8(l / 32) .. +7 (rows 1,056 bytes apart: the 8 lanes a
+        // 16-byte read serves hit distinct banks)
+        f32x16 sacc = {};
         {
-            bf16x8 ring[SDA + 1][2];
-            const bf16_t *kb = KVB + cb + l16 * WP + g4 * 8;
+            bf16x8 ring[SDA + 1];
+            const bf16_t *kb = KVB + cb + n32 * WP + 8 * kg;
 #pragma unroll
-            for (int cc = 0; cc < SDA; ++cc) {
-                ring[cc][0] = ld_bf16x8(kb + 32 * cc);
-                ring[cc][1] = ld_bf16x8(kb + 16 * WP + 32 * cc);
-            }
+            for (int cc = 0; cc < SDA; ++cc) ring[cc] = ld_bf16x8(kb + 16 * cc);
 #pragma unroll
-            for (int kk = 0; kk < KKN; ++kk) {
-                if (kk + SDA < KKN) {
-                    ring[(kk + SDA) % (SDA + 1)][0] = ld_bf16x8(kb + 32 * (kk + SDA));
-                    ring[(kk + SDA) % (SDA + 1)][1] = ld_bf16x8(kb + 16 * WP + 32 * (kk + SDA));
-                }
-                if (!kFirst && kk == KKN - 3) pv_pre(pb, (i - 1) & 1, pre);
-                if (kk & 1) issue_row(drs, db, kk >> 1, so[kk >> 1]);
+            for (int kc = 0; kc < QC; ++kc) {
+                if (kc + SDA < QC) ring[(kc + SDA) % (SDA + 1)] = ld_bf16x8(kb + 16 * (kc + SDA));
+                if (!kFirst && kc == QC - 5) pv_pre(pb, (i - 1) & 1, pre);
+                if ((kc & 3) == 3) issue_row(drs, db, kc >> 2, so[kc >> 2]);
                 __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int m = 0; m < 2; ++m)
-#pragma unroll
-                    for (int b = 0; b < HB; ++b)
-                        sacc[m][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ring[kk % (SDA + 1)][m], qf[b][kk],
-                                                                             sacc[m][b], 0, 0, 0);
+                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[kc % (SDA + 1)], qf[kc], sacc, 0, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        static_assert(KKN == 2 * RPW, "one row load per two k-chunks");
+        static_assert(QC == 4 * RPW, "one row load per four k-chunks");
         // row offsets of tile i+3
         uint32_t oa3;
         const uint32_t v3 = code_finish(i + 3, id3, oa3);
         // rows without data are masked to -inf; full tiles skip the mask
         if (v0 != 0xffffffffu) {
-            const uint32_t vb = v0 >> (4 * g4);  // bit 16m + r: row 16m + 4g4 + r
+            const uint32_t vb = v0 >> (4 * kg);  // bit 8q + r: row 8q + 4kg + r (component 4q + r)
 #pragma unroll
-            for (int m = 0; m < 2; ++m)
+            for (int q4 = 0; q4 < 4; ++q4)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    if (!((vb >> (16 * m + r)) & 1u)) {
-#pragma unroll
-                        for (int b = 0; b < HB; ++b) sacc[m][b][r] = -INFINITY;
-                    }
+                    if (!((vb >> (8 * q4 + r)) & 1u)) sacc[4 * q4 + r] = -INFINITY;
         }
-        // ---- softmax of this tile in 27 micro-steps of one instruction per head block (each
-        // depends on an earlier one), spread between the matrix ops of the previous tile so
-        // that every dependency has a matrix op to hide behind:
-        // p = 2^(s * scale - m_ref) packed to bf16 in the B-operand layout of P.
-        // v_exp_f32 flushes results below 2^-126 to zero, which only drops weights that no
-        // bf16 sum could hold.
-        float tq[HB][4];
-        float ev[HB][8];
-        uint32_t pk[HB][4];
+        // ---- softmax of this tile in 26 micro-steps of one to four independent instructions
+        // (each depending on an earlier step), spread between the matrix ops of the previous
+        // tile so that every dependency has a matrix op to hide behind:
+        // p = 2^(s * scale - m_ref) packed to bf16, components 8s .. 8s+7 being the B
+        // operand of k-step s of P V. v_exp_f32 flushes results below 2^-126 to zero, which
+        // only drops weights that no bf16 sum could hold.
+        float tq[8];
+        float ev[16];
+        uint32_t pk[8];
         auto sm_micro = [&](auto UI) __attribute__((always_inline)) {
             constexpr int u = decltype(UI)::value;
-#pragma unroll
-            for (int b = 0; b < HB; ++b) {
-                if constexpr (u < 4) {
-                    constexpr int m = u >> 1, r = (u & 1) * 2;
-                    tq[b][u] = fmax2(sacc[m][b][r], sacc[m][b][r + 1]);
-                } else if constexpr (u == 4) {
-                    tq[b][0] = fmax2(tq[b][0], tq[b][1]);
-                } else if constexpr (u == 5) {
-                    tq[b][2] = fmax2(tq[b][2], tq[b][3]);
-                } else if constexpr (u == 6) {
-                    tq[b][0] = fmax2(tq[b][0], tq[b][2]);
-                } else if constexpr (u == 7) {
-                    const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(tq[b][0]), __float_as_uint(tq[b][0]),
-                                                                    false, false);
-                    tq[b][1] = __uint_as_float(x[0]);
-                    tq[b][2] = __uint_as_float(x[1]);
-                } else if constexpr (u == 8) {
-                    tq[b][0] = fmax2(tq[b][1], tq[b][2]);
-                } else if constexpr (u == 9) {
-                    const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(tq[b][0]), __float_as_uint(tq[b][0]),
-                                                                    false, false);
-                    tq[b][1] = __uint_as_float(x[0]);
-                    tq[b][2] = __uint_as_float(x[1]);
-                } else if constexpr (u == 10) {
-                    tq[b][0] = fmax2(tq[b][1], tq[b][2]);
-                } else if constexpr (u == 11) {
-                    // the scale is positive, so the max of the raw scores gives the max logit
-                    const float tmax = tq[b][0] * scale_log2;
-                    if constexpr (kFirst) {
-                        m_ref[b] = fmaxf(m_ref[b], tmax);  // O and the sums are still zero
-                        nmu[b] = (m_ref[b] == -INFINITY) ? 0.f : -m_ref[b];
-                    } else {
-                        growth = fmaxf(growth, tmax - m_ref[b]);
-                    }
-                } else if constexpr (u >= 12 && u <= 20) {
-                    constexpr int q = u - 12;  // exponent of value q-1, argument of value q
-                    if constexpr (q >= 1) ev[b][q - 1] = __builtin_amdgcn_exp2f(ev[b][q - 1]);
-                    if constexpr (q < 8) ev[b][q] = fmaf(sacc[q >> 2][b][q & 3], scale_log2, nmu[b]);
-                } else if constexpr (u >= 21 && u <= 24) {
-                    constexpr int j = u - 21;
-                    pk[b][j] = pack_bf16x2(ev[b][2 * j], ev[b][2 * j + 1]);
-                } else if constexpr (u == 25) {
-                    const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(pk[b][0], pk[b][1], pk[b][2], pk[b][3]));
-                    lacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_bf16x8(), pf, lacc[b], 0, 0, 0);
-                } else if constexpr (u == 26) {
-                    PB[i & 1][(HB * wu + b) * 64 + lane] = u32x4w{pk[b][0], pk[b][1], pk[b][2], pk[b][3]};
+            if constexpr (u < 4) {
+                tq[2 * u] = fmax2(sacc[4 * u], sacc[4 * u + 1]);
+                tq[2 * u + 1] = fmax2(sacc[4 * u + 2], sacc[4 * u + 3]);
+            } else if constexpr (u == 4) {
+                tq[0] = fmax2(tq[0], tq[1]);
+                tq[2] = fmax2(tq[2], tq[3]);
+            } else if constexpr (u == 5) {
+                tq[4] = fmax2(tq[4], tq[5]);
+                tq[6] = fmax2(tq[6], tq[7]);
+            } else if constexpr (u == 6) {
+                tq[0] = fmax2(tq[0], tq[2]);
+                tq[4] = fmax2(tq[4], tq[6]);
+            } else if constexpr (u == 7) {
+                tq[0] = fmax2(tq[0], tq[4]);
+            } else if constexpr (u == 8) {
+                const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(tq[0]), __float_as_uint(tq[0]), false,
+                                                                false);
+                tq[1] = __uint_as_float(x[0]);
+                tq[2] = __uint_as_float(x[1]);
+            } else if constexpr (u == 9) {
+                tq[0] = fmax2(tq[1], tq[2]);
+            } else if constexpr (u == 10) {
+                // the scale is positive, so the max of the raw scores gives the max logit
+                const float tmax = tq[0] * scale_log2;
+                if constexpr (kFirst) {
+                    m_ref = fmaxf(m_ref, tmax);  // O and the sums are still zero
+                    nmu = (m_ref == -INFINITY) ? 0.f : -m_ref;
+                } else {
+                    growth = fmaxf(growth, tmax - m_ref);
                 }
+            } else if constexpr (u >= 11 && u <= 19) {
+                constexpr int q2 = u - 11;  // exponents of values 2q2-2, 2q2-1; arguments of 2q2, 2q2+1
+                if constexpr (q2 >= 1) {
+                    ev[2 * q2 - 2] = __builtin_amdgcn_exp2f(ev[2 * q2 - 2]);
+                    ev[2 * q2 - 1] = __builtin_amdgcn_exp2f(ev[2 * q2 - 1]);
+                }
+                if constexpr (q2 < 8) {
+                    ev[2 * q2] = fmaf(sacc[2 * q2], scale_log2, nmu);
+                    ev[2 * q2 + 1] = fmaf(sacc[2 * q2 + 1], scale_log2, nmu);
+                }
+            } else if constexpr (u >= 20 && u <= 23) {
+                constexpr int j = u - 20;
+                pk[2 * j] = pack_bf16x2(ev[4 * j], ev[4 * j + 1]);
+                pk[2 * j + 1] = pack_bf16x2(ev[4 * j + 2], ev[4 * j + 3]);
+            } else if constexpr (u == 24) {
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const bf16x8 pf = __builtin_bit_cast(
+                        bf16x8, make_uint4(pk[4 * s2], pk[4 * s2 + 1], pk[4 * s2 + 2], pk[4 * s2 + 3]));
+                    lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones_bf16x8(), pf, lacc, 0, 0, 0);
+                }
+            } else if constexpr (u == 25) {
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2)
+                    PB[i & 1][(2 * wu + s2) * 64 + lane] =
+                        u32x4w{pk[4 * s2], pk[4 * s2 + 1], pk[4 * s2 + 2], pk[4 * s2 + 3]};
             }
         };
-        constexpr int kMicro = 27;
+        constexpr int kMicro = 26;
         if constexpr (kFirst) {
             static_for<0, kMicro>([&](auto UI) __attribute__((always_inline)) { sm_micro(UI); });
         } else {
@@ -616,7 +598,7 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
                 } else if constexpr (p == 101) {
                     sm_micro(std::integral_constant<int, 16>{});
                     sm_micro(std::integral_constant<int, 17>{});
-                } else if constexpr (p < 14 || (p >= 16 && p < 25)) {
+                } else if constexpr (p < 14 || (p >= 16 && p < 24)) {
                     sm_micro(std::integral_constant<int, p + 2>{});
                 }
             });
@@ -664,16 +646,14 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
                 for (int e = 0; e < 2; ++e)
                     orp[db][q4][e] = rope_pair(rope_t, 16 * DPW * wu + 32 * db + 8 * q4 + 4 * kg + 2 * e, R);
     }
-    // denominators of this wave's S^T heads, shared with the waves that hold their outputs
-    float lse_v[HB];
-#pragma unroll
-    for (int b = 0; b < HB; ++b) {
-        const float skl = sk[b] * kLog2e;
-        const float mr = m_ref[b];
-        const float lv = lacc[b][0] + ((skl == -INFINITY) ? 0.f : exp2f(skl - mr));
-        const float mu = (mr == -INFINITY) ? 0.f : mr;
-        lse_v[b] = (lv > 0.f) ? (mu + log2f(lv)) * kLn2 : -INFINITY;
-        if (g4 == 0) invs[16 * (HB * wu + b) + l16] = lv > 0.f ? 1.f / lv : 0.f;
+    // denominator of this lane's S^T head, shared with the waves that hold its outputs
+    float lse_v;
+    {
+        const float skl = sk * kLog2e;
+        const float lv = lacc[0] + ((skl == -INFINITY) ? 0.f : exp2f(skl - m_ref));
+        const float mu = (m_ref == -INFINITY) ? 0.f : m_ref;
+        lse_v = (lv > 0.f) ? (mu + log2f(lv)) * kLn2 : -INFINITY;
+        if (kg == 0) invs[32 * wu + n32] = lv > 0.f ? 1.f / lv : 0.f;
     }
     if (__ballot(growth > kHeadroom) != 0ull && lane == 0) redo = 1;
     __syncthreads();
@@ -685,10 +665,7 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
             pv_phase(((nt - 1) & 3) * TB, (nt - 1) & 1, pre, [](auto) __attribute__((always_inline)) {});
         }
         pv_fence();
-        if (lse != nullptr && g4 == 0) {
-#pragma unroll
-            for (int b = 0; b < HB; ++b) lse[(int64_t)t * H + head0 + 16 * b + l16] = lse_v[b];
-        }
+        if (lse != nullptr && kg == 0) lse[(int64_t)t * H + head0 + n32] = lse_v;
         // ---- epilogue. Lane l holds, per 32 x 32 block (hb, db), dims 32db + 8q + 4kg + r
         // (q, r = 0..3: four runs of four consecutive dims) of head 32hb + l % 32: it
         // normalises them, rotates back the rotated dims (pairs sit in one lane) and stages 8
@@ -702,7 +679,6 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
         static_assert(NWV * 32 * OSP <= TB, "the staging of every wave fits one tile buffer");
         bf16_t *const ostage0 = KVB + ((nt + 2) & 3) * TB + wu * 32 * OSP;
         bf16_t *const ostage1 = KVB + (nt & 3) * TB + wu * 32 * OSP;
-        const int n32 = lane & 31;
 #pragma unroll
         for (int hb = 0; hb < OB / 2; ++hb) {
             const float inv = invs[32 * hb + n32];
