@@ -104,6 +104,20 @@ __device__ __forceinline__ i32x4s rows_rsrc(const void *p, uint32_t bytes) {
     return i32x4s{lo, hi, (int)__builtin_amdgcn_readfirstlane(bytes), kBufDword3};
 }
 
+// LDS position of 16-byte chunk g (dims 8g .. 8g+7) of a tile row. Within each 256-byte
+// group (128 dims) the bits (s1, bb, h, j) of g = 8 s1 + 4 bb + 2 h + j move to
+// 8 h + 4 s1 + 2 bb + j: the two 16-dim halves (h) of a 32-dim block then sit 128 bytes
+// apart, so the transposing V reads of the two 16-lane groups of a half fall in disjoint
+// banks; the 8 rows a 16-byte K read serves stay in distinct banks.
+__host__ __device__ constexpr int chunk_pos(int g) {
+    return (g & ~15) | (((g >> 1) & 1) << 3) | (((g >> 3) & 1) << 2) | (((g >> 2) & 1) << 1) | (g & 1);
+}
+// the chunk whose position is p (the inverse permutation)
+__host__ __device__ constexpr int chunk_at(int p) {
+    return (p & ~15) | (((p >> 2) & 1) << 3) | (((p >> 1) & 1) << 2) | (((p >> 3) & 1) << 1) | (p & 1);
+}
+static_assert(chunk_at(chunk_pos(13)) == 13 && chunk_pos(chunk_at(6)) == 6 && chunk_pos(2) == 8, "inverse pair");
+
 // One 1 KiB row from memory straight into LDS: lane i moves bytes 16i .. 16i+15 of the row
 // at `soff` within the resource to LDS byte address dst + 16i. Written as assembly so that
 // the compiler does not track it (it would otherwise wait for these loads before every LDS
@@ -358,7 +372,7 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
                                     swa != nullptr ? (uint32_t)swa_rows * WD * 2 : 0u);
     const uint32_t kvb = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)(const char *)KVB);
-    const uint32_t voff = (uint32_t)lane * 16u;
+    const uint32_t voff = (uint32_t)chunk_at(lane) * 16u;  // lane i fills LDS chunk i of a row
     // Tiles 0 .. ntm-1 hold the main slots (top-k entries or summaries, 32 per tile, the
     // last one padded), tiles ntm .. nt-1 the SWA slots, so the rows of a tile all come from
     // one region. Lane r < 32 describes row r of a tile: its byte offset in the region (row
@@ -410,7 +424,8 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
     // `step(p)` is called after product p (0 .. 31) and, with p = 100 + s, before the first
     // product of k-step s: the softmax of the next tile goes there, an instruction at a time.
     auto vfrag = [&](int vb, int db, int s) __attribute__((always_inline)) -> bf16x8 {
-        const bf16_t *base = KVB + vb + 16 * DPW * wu + 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3) +
+        const bf16_t *base = KVB + vb + 16 * DPW * wu + 32 * (db >> 1) + 16 * (db & 1) + 64 * ((lane >> 4) & 1) +
+                             4 * (lane & 3) +
                              ((lane & 15) >> 2) * WP;
         const bf16x4v lo = __builtin_bit_cast(bf16x4v, ld_tr(base + (16 * s + 4 * kg) * WP));
         const bf16x4v hi = __builtin_bit_cast(bf16x4v, ld_tr(base + (16 * s + 8 + 4 * kg) * WP));
@@ -489,12 +504,12 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
         f32x16 sacc = {};
         {
             bf16x8 ring[SDA + 1];
-            const bf16_t *kb = KVB + cb + n32 * WP + 8 * kg;
+            const bf16_t *kb = KVB + cb + n32 * WP + 8 * kg;  // + 8 chunk_pos(2kc): chunk 2kc + kg
 #pragma unroll
-            for (int cc = 0; cc < SDA; ++cc) ring[cc] = ld_bf16x8(kb + 16 * cc);
+            for (int cc = 0; cc < SDA; ++cc) ring[cc] = ld_bf16x8(kb + 8 * chunk_pos(2 * cc));
 #pragma unroll
             for (int kc = 0; kc < QC; ++kc) {
-                if (kc + SDA < QC) ring[(kc + SDA) % (SDA + 1)] = ld_bf16x8(kb + 16 * (kc + SDA));
+                if (kc + SDA < QC) ring[(kc + SDA) % (SDA + 1)] = ld_bf16x8(kb + 8 * chunk_pos(2 * (kc + SDA)));
                 if (!kFirst && kc == QC - 5) pv_pre(pb, (i - 1) & 1, pre);
                 if ((kc & 3) == 3) issue_row(drs, db, kc >> 2, so[kc >> 2]);
                 __builtin_amdgcn_sched_barrier(0);
