@@ -108,7 +108,8 @@ __device__ __forceinline__ i32x4s rows_rsrc(const void *p, uint32_t bytes) {
 // group (128 dims) the bits (s1, bb, h, j) of g = 8 s1 + 4 bb + 2 h + j move to
 // 8 h + 4 s1 + 2 bb + j: the two 16-dim halves (h) of a 32-dim block then sit 128 bytes
 // apart, so the transposing V reads of the two 16-lane groups of a half fall in disjoint
-// banks; the 8 rows a 16-byte K read serves stay in distinct banks.
+// banks. Rows with bit 3 set also flip bit 0 of the position: a 16-byte read is served 16
+// lanes at a time, and rows r and r + 8 (1,056 bytes x 8 apart) would otherwise share banks.
 __host__ __device__ constexpr int chunk_pos(int g) {
     return (g & ~15) | (((g >> 1) & 1) << 3) | (((g >> 3) & 1) << 2) | (((g >> 2) & 1) << 1) | (g & 1);
 }
@@ -372,7 +373,9 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
                                     swa != nullptr ? (uint32_t)swa_rows * WD * 2 : 0u);
     const uint32_t kvb = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)(const char *)KVB);
-    const uint32_t voff = (uint32_t)chunk_at(lane) * 16u;  // lane i fills LDS chunk i of a row
+    // lane i fills LDS chunk i of a row; rows with bit 3 set (the rows of odd waves) hold
+    // their chunks with bit 0 of the position flipped
+    const uint32_t voff = (uint32_t)chunk_at(lane ^ (wu & 1)) * 16u;
     // Tiles 0 .. ntm-1 hold the main slots (top-k entries or summaries, 32 per tile, the
     // last one padded), tiles ntm .. nt-1 the SWA slots, so the rows of a tile all come from
     // one region. Lane r < 32 describes row r of a tile: its byte offset in the region (row
@@ -428,7 +431,8 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
                              4 * (lane & 3) +
                              ((lane & 15) >> 2) * WP;
         const bf16x4v lo = __builtin_bit_cast(bf16x4v, ld_tr(base + (16 * s + 4 * kg) * WP));
-        const bf16x4v hi = __builtin_bit_cast(bf16x4v, ld_tr(base + (16 * s + 8 + 4 * kg) * WP));
+        // (rows 8..15 of a 16: chunk position bit 0 flipped, i.e. 8 elements over)
+        const bf16x4v hi = __builtin_bit_cast(bf16x4v, ld_tr(base + (16 * s + 8 + 4 * kg) * WP + 8 - 16 * ((lane >> 1) & 1)));
         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     };
     auto pfrag = [&](int pr, int hb, int s) __attribute__((always_inline)) -> bf16x8 {
@@ -504,7 +508,7 @@ attn_w32_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, con
         f32x16 sacc = {};
         {
             bf16x8 ring[SDA + 1];
-            const bf16_t *kb = KVB + cb + n32 * WP + 8 * kg;  // + 8 chunk_pos(2kc): chunk 2kc + kg
+            const bf16_t *kb = KVB + cb + n32 * WP + 8 * (kg ^ ((n32 >> 3) & 1));  // + 8 chunk_pos(2kc)
 #pragma unroll
             for (int cc = 0; cc < SDA; ++cc) ring[cc] = ld_bf16x8(kb + 8 * chunk_pos(2 * cc));
 #pragma unroll
