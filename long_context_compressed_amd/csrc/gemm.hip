@@ -11,9 +11,9 @@
 // One GEMM core serves both: C[m][n] = sum_k A[m][k] B[n][k] (both operands K-contiguous,
 // as activations [rows][K] and weights [out][in] are stored), fp32 accumulation on
 // v_mfma_f32_32x32x16_bf16.
-//   - workgroup tile 64 MI (M) x 128 (N), 2 x 2 wavefronts of 32 MI x 64 (MI x 2 blocks of
-//     32 x 32): MI = 4 for the plain GEMM, MI = 2 for the compressor (its epilogue tile
-//     has to fit LDS);
+//   - workgroup tile 64 MI (M) x 64 WN (N), 2 x WN wavefronts of 32 MI x 64 (MI x 2 blocks
+//     of 32 x 32): MI = 4, WN = 4 (256 x 256, 8 wavefronts) for the plain GEMM, MI = 2,
+//     WN = 2 (128 x 128) for the compressor (its epilogue tile has to fit LDS);
 //   - the K loop runs over 32-wide slices through a ring of LDS stages; slices go from
 //     memory straight into LDS by buffer loads with the LDS destination (16 bytes per
 //     lane), all but one stage ahead of the slice being multiplied;
@@ -33,21 +33,24 @@ namespace {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4g __attribute__((ext_vector_type(4)));
 
-constexpr int BN = 128, BK = 32;
+constexpr int BK = 32;
 constexpr int kRowBytes = BK * 2;                    // one slice row: 64 bytes
 constexpr int kBufWord3 = 0x00020000;                // raw buffer, 32-bit data format
 constexpr uint32_t kOob = 0xFFFFFFF0u;               // an offset past any resource: no access
 
-// Tile shapes: MI 32-row blocks per wavefront in M (the workgroup's 2 x 2 wavefronts cover
-// 64 MI rows x 128 columns), NST LDS stages in the K ring.
-template <int MI, int NST>
+// Tile shapes: MI 32-row blocks per wavefront in M, WN wavefronts in N (the workgroup's
+// 2 x WN wavefronts cover 64 MI rows x 64 WN columns), NST LDS stages in the K ring.
+template <int MI, int NST, int WN = 2>
 struct Tile {
     static constexpr int BM = 64 * MI;
+    static constexpr int BN = 64 * WN;
+    static constexpr int NW = 2 * WN;   // wavefronts
     static constexpr int A_BYTES = BM * kRowBytes;
     static constexpr int B_BYTES = BN * kRowBytes;
     static constexpr int STAGE = A_BYTES + B_BYTES;
     static constexpr int LDS = NST * STAGE;
-    static constexpr int AQ = BM / 64;  // A load instructions per wavefront and slice
+    static constexpr int AQ = BM / (16 * NW);  // A load instructions per wavefront and slice
+    static_assert(AQ * 16 * NW == BM, "the A rows split evenly over the wavefronts");
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint64_t bytes) {
@@ -89,17 +92,17 @@ struct Operand {
     bool has_second;
 };
 
-// The GEMM core: accumulates the 128 x 128 tile for K slices [0, K) into acc (per wave a
-// 64 x 64 block as 2 x 2 32x32 MFMA accumulators). rowA(r) / rowB(r) return the byte
+// The GEMM core: accumulates the BM x BN tile for K slices [0, K) into acc (per wave a
+// 32 MI x 64 block as MI x 2 32x32 MFMA accumulators). rowA(r) / rowB(r) return the byte
 // offset of K element 0 of tile row r in the main resource (or kOob), rowA2(r) in the
 // second A resource (or kOob). K % 32 == 0.
-template <int MI, int NST, bool kSecondA, class RA, class RA2, class RB>
+template <int MI, int NST, int WN, bool kSecondA, class RA, class RA2, class RB>
 __device__ __forceinline__ void gemm_core(char *lds, const Operand &opA, const Operand &opB, int64_t K, RA rowA,
                                           RA2 rowA2, RB rowB, f32x16 (&acc)[MI][2]) {
-    using TL = Tile<MI, NST>;
+    using TL = Tile<MI, NST, WN>;
     constexpr int AQ = TL::AQ;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int wm = w >> 1, wn = w & 1;
+    const int wm = w / WN, wn = w % WN;
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -196,15 +199,16 @@ __device__ __forceinline__ int acc_row(int v, int lane) { return 8 * (v >> 2) + 
 // ---------------------------------------------------------------------------------------
 // plain batched GEMM: C[z][m][n] = sum_k A[z][m][k] B[z][n][k]; C bf16 or fp32
 // ---------------------------------------------------------------------------------------
-template <typename OT, int MI, int NST>
-__global__ void __launch_bounds__(256, 2)
+template <typename OT, int MI, int NST, int WN>
+__global__ void __launch_bounds__(128 * WN)
 gemm_bf16_kernel(const bf16_t *__restrict__ A, int64_t lda, int64_t sA, const bf16_t *__restrict__ Bw,
                  int64_t ldb, int64_t sB, OT *__restrict__ C, int64_t ldc, int64_t sC, int64_t M, int64_t N,
                  int64_t K, int mtiles)
 {
-    __shared__ __attribute__((aligned(16))) char lds[Tile<MI, NST>::LDS];
+    using TL = Tile<MI, NST, WN>;
+    __shared__ __attribute__((aligned(16))) char lds[TL::LDS];
     const int z = blockIdx.z;
-    constexpr int BM = Tile<MI, NST>::BM;
+    constexpr int BM = TL::BM, BN = TL::BN;
     const int64_t m0 = (int64_t)(blockIdx.x % mtiles) * BM;
     const int64_t n0 = (int64_t)(blockIdx.x / mtiles) * BN;
     const bf16_t *Ab = A + (int64_t)z * sA + m0 * lda;
@@ -215,23 +219,39 @@ gemm_bf16_kernel(const bf16_t *__restrict__ A, int64_t lda, int64_t sA, const bf
     ob.main = ob.second = make_rsrc(Bb, (uint64_t)((nr - 1) * ldb + K) * 2);
     oa.has_second = ob.has_second = false;
     f32x16 acc[MI][2];
-    gemm_core<MI, NST, false>(
+    gemm_core<MI, NST, WN, false>(
         lds, oa, ob, K, [&](int r) { return r < mr ? (uint32_t)(r * lda * 2) : kOob; },
         [&](int) { return kOob; }, [&](int r) { return r < nr ? (uint32_t)(r * ldb * 2) : kOob; }, acc);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int wm = w >> 1, wn = w & 1;
+    const int wm = w / WN, wn = w % WN;
     OT *Cb = C + (int64_t)z * sC;
+    const int64_t r0 = m0 + 32 * MI * wm + 4 * (lane >> 5), c0 = n0 + 64 * wn + (lane & 31);
+    if (m0 + BM <= M && n0 + BN <= N) {
+        // whole tile: no bounds tests
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int64_t col = n0 + 64 * wn + 32 * j + (lane & 31);
+            for (int j = 0; j < 2; ++j) {
+                OT *cp = Cb + (r0 + 32 * i) * ldc + c0 + 32 * j;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int64_t row = m0 + 32 * MI * wm + 32 * i + acc_row(v, lane);
-                if (row < M && col < N) elem<OT>::store(Cb, row * ldc + col, acc[i][j][v]);
+                for (int v = 0; v < 16; ++v) elem<OT>::store(cp, (8 * (v >> 2) + (v & 3)) * ldc, acc[i][j][v]);
             }
-        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int64_t col = c0 + 32 * j;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int64_t row = r0 + 32 * i + 8 * (v >> 2) + (v & 3);
+                    if (row < M && col < N) elem<OT>::store(Cb, row * ldc + col, acc[i][j][v]);
+                }
+                // one accumulator block at a time (the scheduler would otherwise convert
+                // every block ahead of its stores and run out of registers)
+                __builtin_amdgcn_sched_barrier(0);
+            }
+    }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -254,6 +274,7 @@ compress_hidden_kernel(const bf16_t *__restrict__ Hs, const bf16_t *__restrict__
     __shared__ __attribute__((aligned(16))) char lds[Tile<2, kCompressStages>::LDS];
     constexpr bool kOv = RATIO == 4;
     constexpr int NP = kOv ? 4 : 2;          // projections
+    constexpr int BN = Tile<2, kCompressStages>::BN;
     constexpr int CW = BN / NP;              // channels per tile
     constexpr int TS = kOv ? 124 : 128;      // tokens per tile step
     constexpr int LEAD = kOv ? 4 : 0;        // rows before the tile's first whole entry
@@ -283,9 +304,9 @@ compress_hidden_kernel(const bf16_t *__restrict__ Hs, const bf16_t *__restrict__
     };
     f32x16 acc[2][2];
     if (kOv && carry != nullptr)
-        gemm_core<2, kCompressStages, true>(lds, oa, ob, d, rowA, rowA2, rowB, acc);
+        gemm_core<2, kCompressStages, 2, true>(lds, oa, ob, d, rowA, rowA2, rowB, acc);
     else
-        gemm_core<2, kCompressStages, false>(lds, oa, ob, d, rowA, rowA2, rowB, acc);
+        gemm_core<2, kCompressStages, 2, false>(lds, oa, ob, d, rowA, rowA2, rowB, acc);
 
     // the fp32 tile into LDS: [128 rows][128 columns]
     constexpr int TP = BN;
@@ -379,9 +400,11 @@ compress_hidden_kernel(const bf16_t *__restrict__ Hs, const bf16_t *__restrict__
 
 // the compressor's ring also holds its fp32 epilogue tile
 constexpr size_t kCompressLds = Tile<2, kCompressStages>::LDS;
-static_assert(Tile<2, kCompressStages>::BM * BN * 4 <= (int)kCompressLds, "the epilogue tile fits the ring");
-// the plain GEMM: 256 x 128 tiles, 3 stages (72 KiB: two workgroups per CU)
-constexpr int kGemmMI = 4, kGemmStages = 3;
+static_assert(Tile<2, kCompressStages>::BM * Tile<2, kCompressStages>::BN * 4 <= (int)kCompressLds,
+              "the epilogue tile fits the ring");
+// the plain GEMM: 256 x 256 tiles of 8 wavefronts, 4 stages (128 KiB: one workgroup per CU,
+// three slices in flight)
+constexpr int kGemmMI = 4, kGemmWN = 4, kGemmStages = 4;
 
 }  // namespace
 
@@ -389,14 +412,14 @@ int launch_gemm_bf16(const bf16_t *A, int64_t lda, int64_t sA, const bf16_t *B, 
                      int64_t ldc, int64_t sC, bool c_f32, int64_t M, int64_t N, int64_t K, int batch,
                      hipStream_t st) {
     if (M == 0 || N == 0 || batch == 0) return CSA_OK;
-    constexpr int BM = Tile<kGemmMI, kGemmStages>::BM;
+    constexpr int BM = Tile<kGemmMI, kGemmStages, kGemmWN>::BM, BN = Tile<kGemmMI, kGemmStages, kGemmWN>::BN;
     const int mtiles = (int)((M + BM - 1) / BM), ntiles = (int)((N + BN - 1) / BN);
     const dim3 grid((unsigned)((int64_t)mtiles * ntiles), 1, (unsigned)batch);
     if (c_f32)
-        hipLaunchKernelGGL((gemm_bf16_kernel<float, kGemmMI, kGemmStages>), grid, dim3(256), 0, st, A, lda, sA,
+        hipLaunchKernelGGL((gemm_bf16_kernel<float, kGemmMI, kGemmStages, kGemmWN>), grid, dim3(128 * kGemmWN), 0, st, A, lda, sA,
                            B, ldb, sB, (float *)C, ldc, sC, M, N, K, mtiles);
     else
-        hipLaunchKernelGGL((gemm_bf16_kernel<bf16_t, kGemmMI, kGemmStages>), grid, dim3(256), 0, st, A, lda,
+        hipLaunchKernelGGL((gemm_bf16_kernel<bf16_t, kGemmMI, kGemmStages, kGemmWN>), grid, dim3(128 * kGemmWN), 0, st, A, lda,
                            sA, B, ldb, sB, (bf16_t *)C, ldc, sC, M, N, K, mtiles);
     return check_launch("gemm_bf16_kernel");
 }
