@@ -33,24 +33,34 @@ namespace {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4g __attribute__((ext_vector_type(4)));
 
-constexpr int BK = 32;
-constexpr int kRowBytes = BK * 2;                    // one slice row: 64 bytes
 constexpr int kBufWord3 = 0x00020000;                // raw buffer, 32-bit data format
 constexpr uint32_t kOob = 0xFFFFFFF0u;               // an offset past any resource: no access
 
 // Tile shapes: MI 32-row blocks per wavefront in M, WN wavefronts in N (the workgroup's
-// 2 x WN wavefronts cover 64 MI rows x 64 WN columns), NST LDS stages in the K ring.
-template <int MI, int NST, int WN = 2>
+// 2 x WN wavefronts cover 64 MI rows x 64 WN columns), NST LDS stages in the K ring, K
+// slices of BK (32 or 64).
+template <int MI, int NST, int WN = 2, int BK_ = 32>
 struct Tile {
+    static constexpr int BK = BK_;
+    static constexpr int ROW = BK * 2;     // bytes of one slice row
+    static constexpr int CPR = BK / 8;     // 16-byte chunks per slice row
+    static constexpr int RPL = 64 / CPR;   // rows per load instruction (1 KiB)
     static constexpr int BM = 64 * MI;
     static constexpr int BN = 64 * WN;
     static constexpr int NW = 2 * WN;   // wavefronts
-    static constexpr int A_BYTES = BM * kRowBytes;
-    static constexpr int B_BYTES = BN * kRowBytes;
+    static constexpr int A_BYTES = BM * ROW;
+    static constexpr int B_BYTES = BN * ROW;
     static constexpr int STAGE = A_BYTES + B_BYTES;
     static constexpr int LDS = NST * STAGE;
-    static constexpr int AQ = BM / (16 * NW);  // A load instructions per wavefront and slice
-    static_assert(AQ * 16 * NW == BM, "the A rows split evenly over the wavefronts");
+    static constexpr int AQ = BM / (RPL * NW);  // A load instructions per wavefront and slice
+    static constexpr int BQ = BN / (RPL * NW);  // B load instructions per wavefront and slice
+    static_assert(BK == 32 || BK == 64, "slices of 32 or 64");
+    static_assert(AQ * RPL * NW == BM && BQ * RPL * NW == BN, "the rows split evenly over the wavefronts");
+    // LDS byte offset of (tile row r, 16-byte chunk c) within one operand tile: chunk c sits
+    // in slot c ^ swz(r), so the 16 rows that one 16-byte read serves together fall in
+    // distinct banks (64-byte rows: (r / 4) % 4; 128-byte rows: (r / 2) % 8)
+    __device__ static __forceinline__ int swz(int r) { return BK == 32 ? (r >> 2) & 3 : (r >> 1) & 7; }
+    __device__ static __forceinline__ int slot_off(int r, int c) { return r * ROW + ((c ^ swz(r)) << 4); }
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint64_t bytes) {
@@ -79,8 +89,6 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// LDS byte offset of (tile row r, 16-byte chunk c) within one operand tile
-__device__ __forceinline__ int slot_off(int r, int c) { return r * kRowBytes + ((c ^ ((r >> 2) & 3)) << 4); }
 
 // Row sources of one operand tile. A lane's load covers tile row r; `off(r, c)` gives the
 // byte offset of 16-byte chunk c of that row's current K slice in `main` (kOob when the row
@@ -96,11 +104,11 @@ struct Operand {
 // 32 MI x 64 block as MI x 2 32x32 MFMA accumulators). rowA(r) / rowB(r) return the byte
 // offset of K element 0 of tile row r in the main resource (or kOob), rowA2(r) in the
 // second A resource (or kOob). K % 32 == 0.
-template <int MI, int NST, int WN, bool kSecondA, class RA, class RA2, class RB>
+template <int MI, int NST, int WN, int BK, bool kSecondA, class RA, class RA2, class RB>
 __device__ __forceinline__ void gemm_core(char *lds, const Operand &opA, const Operand &opB, int64_t K, RA rowA,
                                           RA2 rowA2, RB rowB, f32x16 (&acc)[MI][2]) {
-    using TL = Tile<MI, NST, WN>;
-    constexpr int AQ = TL::AQ;
+    using TL = Tile<MI, NST, WN, BK>;
+    constexpr int AQ = TL::AQ, BQ = TL::BQ, CPR = TL::CPR, RPL = TL::RPL, ROW = TL::ROW;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = w / WN, wn = w % WN;
 #pragma unroll
@@ -108,16 +116,16 @@ __device__ __forceinline__ void gemm_core(char *lds, const Operand &opA, const O
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-    // per load instruction: 16 rows x 4 chunks; lane l: row 16 q' + l / 4, LDS slot l % 4,
-    // which holds chunk (l % 4) ^ ((row / 4) % 4) of the row. Each wavefront loads AQ
-    // instructions' worth of A rows and 2 of B rows per slice.
-    uint32_t offA[AQ], offA2[AQ], offB[2];
+    // per load instruction: RPL rows x CPR chunks; lane l: row RPL q' + l / CPR, LDS slot
+    // l % CPR, which holds chunk (l % CPR) ^ swz(row) of the row. Each wavefront loads AQ
+    // instructions' worth of A rows and BQ of B rows per slice.
+    uint32_t offA[AQ], offA2[AQ], offB[BQ];
     bool useA2[AQ];
-    const int slot = lane & 3;
+    const int slot = lane % CPR;
 #pragma unroll
     for (int q = 0; q < AQ; ++q) {
-        const int r = 16 * (AQ * w + q) + (lane >> 2);
-        const int chunk = slot ^ ((r >> 2) & 3);
+        const int r = RPL * (AQ * w + q) + lane / CPR;
+        const int chunk = slot ^ TL::swz(r);
         const uint32_t a = rowA(r);
         offA[q] = a == kOob ? kOob : a + 16u * chunk;
         useA2[q] = false;
@@ -128,18 +136,18 @@ __device__ __forceinline__ void gemm_core(char *lds, const Operand &opA, const O
         }
     }
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int r = 16 * (2 * w + q) + (lane >> 2);
+    for (int q = 0; q < BQ; ++q) {
+        const int r = RPL * (BQ * w + q) + lane / CPR;
         const uint32_t b = rowB(r);
-        offB[q] = b == kOob ? kOob : b + 16u * (slot ^ ((r >> 2) & 3));
+        offB[q] = b == kOob ? kOob : b + 16u * (slot ^ TL::swz(r));
     }
     const int64_t nk = K / BK;
     auto issue = [&](int64_t ks) __attribute__((always_inline)) {
         char *st = lds + (int)(ks % NST) * TL::STAGE;
-        const uint32_t kb = ks < nk ? (uint32_t)(ks * kRowBytes) : kOob;  // past the end: no access
+        const uint32_t kb = ks < nk ? (uint32_t)(ks * ROW) : kOob;  // past the end: no access
 #pragma unroll
         for (int q = 0; q < AQ; ++q) {
-            char *dst = st + 16 * (AQ * w + q) * kRowBytes;  // the instruction's 1 KiB destination
+            char *dst = st + RPL * (AQ * w + q) * ROW;  // the instruction's 1 KiB destination
             // every lane writes its LDS slot exactly once (a load past a resource's end
             // writes zeros), so a lane whose row comes from the second source takes only
             // that load: the two loads run under complementary lane masks
@@ -149,13 +157,13 @@ __device__ __forceinline__ void gemm_core(char *lds, const Operand &opA, const O
                 lds_load16(opA.main, (offA[q] == kOob || kb == kOob) ? kOob : offA[q] + kb, dst);
         }
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
+        for (int q = 0; q < BQ; ++q)
             lds_load16(opB.main, (offB[q] == kOob || kb == kOob) ? kOob : offB[q] + kb,
-                       st + TL::A_BYTES + 16 * (2 * w + q) * kRowBytes);
+                       st + TL::A_BYTES + RPL * (BQ * w + q) * ROW);
     };
     // loads per slice and wave that always issue (with two A sources one lane mask may be
     // empty and its load skipped: counting the minimum keeps the waits exact-or-stricter)
-    constexpr int kLoadsPerSlice = AQ + 2;
+    constexpr int kLoadsPerSlice = AQ + BQ;
 #pragma unroll
     for (int s = 0; s < NST - 1; ++s) issue(s);
 
@@ -173,13 +181,13 @@ __device__ __forceinline__ void gemm_core(char *lds, const Operand &opA, const O
 #pragma unroll
             for (int i = 0; i < MI; ++i) {
                 const int ra = 32 * MI * wm + 32 * i + fr;
-                af[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4g *>(st + slot_off(ra, 2 * sub + fc)));
+                af[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4g *>(st + TL::slot_off(ra, 2 * sub + fc)));
             }
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const int rb = 64 * wn + 32 * j + fr;
                 bfr[j] = __builtin_bit_cast(
-                    bf16x8, *reinterpret_cast<const u32x4g *>(st + TL::A_BYTES + slot_off(rb, 2 * sub + fc)));
+                    bf16x8, *reinterpret_cast<const u32x4g *>(st + TL::A_BYTES + TL::slot_off(rb, 2 * sub + fc)));
             }
 #pragma unroll
             for (int i = 0; i < MI; ++i)
@@ -199,13 +207,13 @@ __device__ __forceinline__ int acc_row(int v, int lane) { return 8 * (v >> 2) + 
 // ---------------------------------------------------------------------------------------
 // plain batched GEMM: C[z][m][n] = sum_k A[z][m][k] B[z][n][k]; C bf16 or fp32
 // ---------------------------------------------------------------------------------------
-template <typename OT, int MI, int NST, int WN>
+template <typename OT, int MI, int NST, int WN, int BK>
 __global__ void __launch_bounds__(128 * WN)
 gemm_bf16_kernel(const bf16_t *__restrict__ A, int64_t lda, int64_t sA, const bf16_t *__restrict__ Bw,
                  int64_t ldb, int64_t sB, OT *__restrict__ C, int64_t ldc, int64_t sC, int64_t M, int64_t N,
                  int64_t K, int mtiles)
 {
-    using TL = Tile<MI, NST, WN>;
+    using TL = Tile<MI, NST, WN, BK>;
     __shared__ __attribute__((aligned(16))) char lds[TL::LDS];
     const int z = blockIdx.z;
     constexpr int BM = TL::BM, BN = TL::BN;
@@ -219,7 +227,7 @@ gemm_bf16_kernel(const bf16_t *__restrict__ A, int64_t lda, int64_t sA, const bf
     ob.main = ob.second = make_rsrc(Bb, (uint64_t)((nr - 1) * ldb + K) * 2);
     oa.has_second = ob.has_second = false;
     f32x16 acc[MI][2];
-    gemm_core<MI, NST, WN, false>(
+    gemm_core<MI, NST, WN, BK, false>(
         lds, oa, ob, K, [&](int r) { return r < mr ? (uint32_t)(r * lda * 2) : kOob; },
         [&](int) { return kOob; }, [&](int r) { return r < nr ? (uint32_t)(r * ldb * 2) : kOob; }, acc);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -304,9 +312,9 @@ compress_hidden_kernel(const bf16_t *__restrict__ Hs, const bf16_t *__restrict__
     };
     f32x16 acc[2][2];
     if (kOv && carry != nullptr)
-        gemm_core<2, kCompressStages, 2, true>(lds, oa, ob, d, rowA, rowA2, rowB, acc);
+        gemm_core<2, kCompressStages, 2, 32, true>(lds, oa, ob, d, rowA, rowA2, rowB, acc);
     else
-        gemm_core<2, kCompressStages, 2, false>(lds, oa, ob, d, rowA, rowA2, rowB, acc);
+        gemm_core<2, kCompressStages, 2, 32, false>(lds, oa, ob, d, rowA, rowA2, rowB, acc);
 
     // the fp32 tile into LDS: [128 rows][128 columns]
     constexpr int TP = BN;
@@ -402,9 +410,25 @@ compress_hidden_kernel(const bf16_t *__restrict__ Hs, const bf16_t *__restrict__
 constexpr size_t kCompressLds = Tile<2, kCompressStages>::LDS;
 static_assert(Tile<2, kCompressStages>::BM * Tile<2, kCompressStages>::BN * 4 <= (int)kCompressLds,
               "the epilogue tile fits the ring");
-// the plain GEMM: 256 x 256 tiles of 8 wavefronts, 4 stages (128 KiB: one workgroup per CU,
-// three slices in flight)
-constexpr int kGemmMI = 4, kGemmWN = 4, kGemmStages = 4;
+// the plain GEMM: 256 x 256 tiles of 8 wavefronts, one workgroup per CU (128 KiB of LDS):
+// K slices of 64 in 2 stages (one barrier per 32 matrix ops of a wavefront) when K % 64 == 0,
+// else slices of 32 in 4 stages
+constexpr int kGemmMI = 4, kGemmWN = 4;
+
+template <int NST, int BK>
+void launch_gemm_cfg(const bf16_t *A, int64_t lda, int64_t sA, const bf16_t *B, int64_t ldb, int64_t sB, void *C,
+                     int64_t ldc, int64_t sC, bool c_f32, int64_t M, int64_t N, int64_t K, int batch,
+                     hipStream_t st) {
+    using TL = Tile<kGemmMI, NST, kGemmWN, BK>;
+    const int mtiles = (int)((M + TL::BM - 1) / TL::BM), ntiles = (int)((N + TL::BN - 1) / TL::BN);
+    const dim3 grid((unsigned)((int64_t)mtiles * ntiles), 1, (unsigned)batch);
+    if (c_f32)
+        hipLaunchKernelGGL((gemm_bf16_kernel<float, kGemmMI, NST, kGemmWN, BK>), grid, dim3(128 * kGemmWN), 0, st,
+                           A, lda, sA, B, ldb, sB, (float *)C, ldc, sC, M, N, K, mtiles);
+    else
+        hipLaunchKernelGGL((gemm_bf16_kernel<bf16_t, kGemmMI, NST, kGemmWN, BK>), grid, dim3(128 * kGemmWN), 0, st,
+                           A, lda, sA, B, ldb, sB, (bf16_t *)C, ldc, sC, M, N, K, mtiles);
+}
 
 }  // namespace
 
@@ -412,15 +436,10 @@ int launch_gemm_bf16(const bf16_t *A, int64_t lda, int64_t sA, const bf16_t *B, 
                      int64_t ldc, int64_t sC, bool c_f32, int64_t M, int64_t N, int64_t K, int batch,
                      hipStream_t st) {
     if (M == 0 || N == 0 || batch == 0) return CSA_OK;
-    constexpr int BM = Tile<kGemmMI, kGemmStages, kGemmWN>::BM, BN = Tile<kGemmMI, kGemmStages, kGemmWN>::BN;
-    const int mtiles = (int)((M + BM - 1) / BM), ntiles = (int)((N + BN - 1) / BN);
-    const dim3 grid((unsigned)((int64_t)mtiles * ntiles), 1, (unsigned)batch);
-    if (c_f32)
-        hipLaunchKernelGGL((gemm_bf16_kernel<float, kGemmMI, kGemmStages, kGemmWN>), grid, dim3(128 * kGemmWN), 0, st, A, lda, sA,
-                           B, ldb, sB, (float *)C, ldc, sC, M, N, K, mtiles);
+    if (K % 64 == 0)
+        launch_gemm_cfg<2, 64>(A, lda, sA, B, ldb, sB, C, ldc, sC, c_f32, M, N, K, batch, st);
     else
-        hipLaunchKernelGGL((gemm_bf16_kernel<bf16_t, kGemmMI, kGemmStages, kGemmWN>), grid, dim3(128 * kGemmWN), 0, st, A, lda,
-                           sA, B, ldb, sB, (bf16_t *)C, ldc, sC, M, N, K, mtiles);
+        launch_gemm_cfg<4, 32>(A, lda, sA, B, ldb, sB, C, ldc, sC, c_f32, M, N, K, batch, st);
     return check_launch("gemm_bf16_kernel");
 }
 

@@ -83,6 +83,7 @@ def test_compress_hidden_into_cache_and_full_size_sample(csa, orc):
     (300, 128, 512, 16, 96, 320, torch.bfloat16),   # ragged rows, group width and model width
     (130, 64, 512, 1, 200, 0, torch.float32),       # one group, the grouped stage alone (fp32 y)
     (77, 8, 128, 4, 64, 96, torch.float32),
+    (70, 6, 32, 2, 80, 160, torch.bfloat16),        # K of both maps an odd multiple of 32
 ])
 def test_out_proj(csa, orc, T, H, D, G, d_g, dm, odt):
     say("out_proj", T, H, D, G, d_g, dm, odt)
