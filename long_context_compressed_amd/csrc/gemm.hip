@@ -39,9 +39,10 @@ constexpr uint32_t kOob = 0xFFFFFFF0u;               // an offset past any resou
 // Tile shapes: MI 32-row blocks per wavefront in M, WN wavefronts in N (the workgroup's
 // 2 x WN wavefronts cover 64 MI rows x 64 WN columns), NST LDS stages in the K ring, K
 // slices of BK (32 or 64).
-template <int MI, int NST, int WN = 2, int BK_ = 32>
+template <int MI, int NST_, int WN = 2, int BK_ = 32>
 struct Tile {
     static constexpr int BK = BK_;
+    static constexpr int NST = NST_;
     static constexpr int ROW = BK * 2;     // bytes of one slice row
     static constexpr int CPR = BK / 8;     // 16-byte chunks per slice row
     static constexpr int RPL = 64 / CPR;   // rows per load instruction (1 KiB)
@@ -51,7 +52,7 @@ struct Tile {
     static constexpr int A_BYTES = BM * ROW;
     static constexpr int B_BYTES = BN * ROW;
     static constexpr int STAGE = A_BYTES + B_BYTES;
-    static constexpr int LDS = NST * STAGE;
+    static constexpr int LDS = NST_ * STAGE;
     static constexpr int AQ = BM / (RPL * NW);  // A load instructions per wavefront and slice
     static constexpr int BQ = BN / (RPL * NW);  // B load instructions per wavefront and slice
     static_assert(BK == 32 || BK == 64, "slices of 32 or 64");
@@ -271,18 +272,22 @@ gemm_bf16_kernel(const bf16_t *__restrict__ A, int64_t lda, int64_t sA, const bf
 // 32 p + x = channel 32 nt + x of projection p. Tokens before 0 come from the carry rows
 // (the last 4 hidden rows of the previous chunk) or are absent (weight 0).
 // ratio 128: tile rows are the 128 tokens of entry mt; columns 64 channels x (C, Z).
-constexpr int kCompressStages = 4;
+// K slices of 64 in 2 stages when d % 64 == 0, else of 32 in 4 stages (64 KiB either way:
+// two workgroups per CU)
+template <int BK>
+using CompressTile = Tile<2, BK == 64 ? 2 : 4, 2, BK>;
 
-template <int RATIO, typename OT>
+template <int RATIO, typename OT, int BK>
 __global__ void __launch_bounds__(256, 2)
 compress_hidden_kernel(const bf16_t *__restrict__ Hs, const bf16_t *__restrict__ carry, const bf16_t *__restrict__ W,
                        const float *__restrict__ bias, int64_t n, int64_t d, int c, OT *__restrict__ out,
                        int64_t out_bstride, int mtiles, int ntiles)
 {
-    __shared__ __attribute__((aligned(16))) char lds[Tile<2, kCompressStages>::LDS];
+    using TL = CompressTile<BK>;
+    __shared__ __attribute__((aligned(16))) char lds[TL::LDS];
     constexpr bool kOv = RATIO == 4;
     constexpr int NP = kOv ? 4 : 2;          // projections
-    constexpr int BN = Tile<2, kCompressStages>::BN;
+    constexpr int BN = TL::BN;
     constexpr int CW = BN / NP;              // channels per tile
     constexpr int TS = kOv ? 124 : 128;      // tokens per tile step
     constexpr int LEAD = kOv ? 4 : 0;        // rows before the tile's first whole entry
@@ -312,9 +317,9 @@ compress_hidden_kernel(const bf16_t *__restrict__ Hs, const bf16_t *__restrict__
     };
     f32x16 acc[2][2];
     if (kOv && carry != nullptr)
-        gemm_core<2, kCompressStages, 2, 32, true>(lds, oa, ob, d, rowA, rowA2, rowB, acc);
+        gemm_core<2, TL::NST, 2, BK, true>(lds, oa, ob, d, rowA, rowA2, rowB, acc);
     else
-        gemm_core<2, kCompressStages, 2, 32, false>(lds, oa, ob, d, rowA, rowA2, rowB, acc);
+        gemm_core<2, TL::NST, 2, BK, false>(lds, oa, ob, d, rowA, rowA2, rowB, acc);
 
     // the fp32 tile into LDS: [128 rows][128 columns]
     constexpr int TP = BN;
@@ -407,8 +412,8 @@ compress_hidden_kernel(const bf16_t *__restrict__ Hs, const bf16_t *__restrict__
 }
 
 // the compressor's ring also holds its fp32 epilogue tile
-constexpr size_t kCompressLds = Tile<2, kCompressStages>::LDS;
-static_assert(Tile<2, kCompressStages>::BM * Tile<2, kCompressStages>::BN * 4 <= (int)kCompressLds,
+static_assert(CompressTile<32>::BM * CompressTile<32>::BN * 4 <= CompressTile<32>::LDS &&
+                  CompressTile<64>::BM * CompressTile<64>::BN * 4 <= CompressTile<64>::LDS,
               "the epilogue tile fits the ring");
 // the plain GEMM: 256 x 256 tiles of 8 wavefronts, one workgroup per CU (128 KiB of LDS):
 // K slices of 64 in 2 stages (one barrier per 32 matrix ops of a wavefront) when K % 64 == 0,
@@ -443,31 +448,40 @@ int launch_gemm_bf16(const bf16_t *A, int64_t lda, int64_t sA, const bf16_t *B, 
     return check_launch("gemm_bf16_kernel");
 }
 
+template <int BK>
+void launch_compress_cfg(const bf16_t *Hs, const bf16_t *carry, const bf16_t *W, const float *bias, int B, int64_t n,
+                         int64_t d, int c, int ratio, void *out, bool out_f32, int64_t bs, hipStream_t st) {
+    if (ratio == 4) {
+        const int mtiles = (int)((n + 123) / 124), ntiles = (c + 31) / 32;
+        const dim3 grid((unsigned)((int64_t)mtiles * ntiles), 1, (unsigned)B);
+        if (out_f32)
+            hipLaunchKernelGGL((compress_hidden_kernel<4, float, BK>), grid, dim3(256), 0, st, Hs, carry, W, bias,
+                               n, d, c, (float *)out, bs, mtiles, ntiles);
+        else
+            hipLaunchKernelGGL((compress_hidden_kernel<4, bf16_t, BK>), grid, dim3(256), 0, st, Hs, carry, W,
+                               bias, n, d, c, (bf16_t *)out, bs, mtiles, ntiles);
+    } else {
+        const int mtiles = (int)(n / ratio), ntiles = (c + 63) / 64;
+        const dim3 grid((unsigned)((int64_t)mtiles * ntiles), 1, (unsigned)B);
+        if (out_f32)
+            hipLaunchKernelGGL((compress_hidden_kernel<128, float, BK>), grid, dim3(256), 0, st, Hs, carry, W,
+                               bias, n, d, c, (float *)out, bs, mtiles, ntiles);
+        else
+            hipLaunchKernelGGL((compress_hidden_kernel<128, bf16_t, BK>), grid, dim3(256), 0, st, Hs, carry, W,
+                               bias, n, d, c, (bf16_t *)out, bs, mtiles, ntiles);
+    }
+}
+
 int launch_compress_hidden(const bf16_t *Hs, const bf16_t *carry, const bf16_t *W, const float *bias, int B,
                            int64_t n, int64_t d, int c, int ratio, void *out, bool out_f32, int64_t out_bstride,
                            hipStream_t st) {
     const int64_t E = n / ratio;
     if (B == 0 || E == 0) return CSA_OK;
     const int64_t bs = out_bstride ? out_bstride : E * c;
-    if (ratio == 4) {
-        const int mtiles = (int)((n + 123) / 124), ntiles = (c + 31) / 32;
-        const dim3 grid((unsigned)((int64_t)mtiles * ntiles), 1, (unsigned)B);
-        if (out_f32)
-            hipLaunchKernelGGL((compress_hidden_kernel<4, float>), grid, dim3(256), 0, st, Hs, carry, W, bias,
-                               n, d, c, (float *)out, bs, mtiles, ntiles);
-        else
-            hipLaunchKernelGGL((compress_hidden_kernel<4, bf16_t>), grid, dim3(256), 0, st, Hs, carry, W,
-                               bias, n, d, c, (bf16_t *)out, bs, mtiles, ntiles);
-    } else {
-        const int mtiles = (int)E, ntiles = (c + 63) / 64;
-        const dim3 grid((unsigned)((int64_t)mtiles * ntiles), 1, (unsigned)B);
-        if (out_f32)
-            hipLaunchKernelGGL((compress_hidden_kernel<128, float>), grid, dim3(256), 0, st, Hs, carry, W,
-                               bias, n, d, c, (float *)out, bs, mtiles, ntiles);
-        else
-            hipLaunchKernelGGL((compress_hidden_kernel<128, bf16_t>), grid, dim3(256), 0, st, Hs, carry, W,
-                               bias, n, d, c, (bf16_t *)out, bs, mtiles, ntiles);
-    }
+    if (d % 64 == 0)
+        launch_compress_cfg<64>(Hs, carry, W, bias, B, n, d, c, ratio, out, out_f32, bs, st);
+    else
+        launch_compress_cfg<32>(Hs, carry, W, bias, B, n, d, c, ratio, out, out_f32, bs, st);
     return check_launch("compress_hidden_kernel");
 }
 
