@@ -148,36 +148,53 @@ attn_wide_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ kv, co
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(buf + row * WP), 16,
                                                  lane * 16, 0, 0, 0);
     };
-    // (KV8) the wave's compressed rows of a landed tile, expanded to bf16 in place: lanes
-    // 0..27 turn 16 codes each into 32 bytes of bf16 (one scale per lane pair), lanes 28..35
-    // move the 128 bytes of bf16 RoPE dims to dims 448..511. Each row's reads are issued
-    // before its writes (one wavefront: LDS in order), so a row converts where it lies.
+    // (KV8) the wave's compressed rows of a landed tile, expanded to bf16 in place, two rows
+    // at a time (one per half-wavefront). In a half, lanes 0..27 turn 16 codes each into 32
+    // bytes of bf16 (one scale per lane pair) with the scaled conversion (code x 2^e in one
+    // instruction per two codes, exact), lanes 28..31 move 32 of the 128 bytes of bf16 RoPE
+    // dims to dims 448..511. Every read of both rows is issued before the first write (LDS
+    // serves one wavefront in order, and the compiler fence keeps the reads ahead), so a row
+    // converts where it lies.
     auto kv8_expand = [&](bf16_t *buf, uint32_t kvm) {
         if constexpr (KV8) {
+            static_assert(RPW % 2 == 0, "rows are expanded in pairs");
+            const int hh = lane >> 5, l = lane & 31;
+            const bool cv = l < 28;
+            const int off = cv ? 16 * l : 448 + 32 * (l - 28);
 #pragma unroll
-            for (int i = 0; i < RPW; ++i) {
-                const int row = RPW * wu + i;
-                if (!((kvm >> row) & 1u)) continue;
+            for (int i = 0; i < RPW; i += 2) {
+                const int row = RPW * wu + i + hh;
+                const bool act = (kvm >> row) & 1u;
                 uint8_t *rb = reinterpret_cast<uint8_t *>(buf + row * WP);
-                uint4 raw = make_uint4(0u, 0u, 0u, 0u);
-                uint32_t sb = 127u;
-                if (lane < 36) raw = *reinterpret_cast<const uint4 *>(rb + 16 * lane);
-                if (lane < 28) sb = rb[448 + 128 + (lane >> 1)];
-                if (lane < 28) {
-                    const int e = (int)sb - 127;
-                    const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+                const uint4 r0 = *reinterpret_cast<const uint4 *>(rb + off);
+                const uint4 r1 = *reinterpret_cast<const uint4 *>(rb + off + 16);
+                const uint32_t sb = rb[576 + (cv ? (l >> 1) : 0)];
+                asm volatile("" ::: "memory");
+                if (act && cv) {
+                    const uint32_t wd[4] = {r0.x, r0.y, r0.z, r0.w};
                     uint32_t o[8];
+                    if (sb != 0u) {
+                        const float sc = __builtin_bit_cast(float, sb << 23);  // 2^(sb - 127)
 #pragma unroll
-                    for (int qd = 0; qd < 4; ++qd) {
-                        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(wd[qd], false);
-                        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(wd[qd], true);
-                        o[2 * qd] = pack_bf16x2(__builtin_ldexpf(lo[0], e), __builtin_ldexpf(lo[1], e));
-                        o[2 * qd + 1] = pack_bf16x2(__builtin_ldexpf(hi[0], e), __builtin_ldexpf(hi[1], e));
+                        for (int qd = 0; qd < 4; ++qd) {
+                            o[2 * qd] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd[qd], sc, false));
+                            o[2 * qd + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd[qd], sc, true));
+                        }
+                    } else {
+                        // e = -127 (2^-127 is no normal float): decode, then scale
+#pragma unroll
+                        for (int qd = 0; qd < 4; ++qd) {
+                            const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(wd[qd], false);
+                            const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(wd[qd], true);
+                            o[2 * qd] = pack_bf16x2(__builtin_ldexpf(lo[0], -127), __builtin_ldexpf(lo[1], -127));
+                            o[2 * qd + 1] = pack_bf16x2(__builtin_ldexpf(hi[0], -127), __builtin_ldexpf(hi[1], -127));
+                        }
                     }
-                    *reinterpret_cast<uint4 *>(rb + 32 * lane) = make_uint4(o[0], o[1], o[2], o[3]);
-                    *reinterpret_cast<uint4 *>(rb + 32 * lane + 16) = make_uint4(o[4], o[5], o[6], o[7]);
-                } else if (lane < 36) {
-                    *reinterpret_cast<uint4 *>(rb + 896 + 16 * (lane - 28)) = raw;
+                    *reinterpret_cast<uint4 *>(rb + 32 * l) = make_uint4(o[0], o[1], o[2], o[3]);
+                    *reinterpret_cast<uint4 *>(rb + 32 * l + 16) = make_uint4(o[4], o[5], o[6], o[7]);
+                } else if (act) {
+                    *reinterpret_cast<uint4 *>(rb + 896 + 32 * (l - 28)) = r0;
+                    *reinterpret_cast<uint4 *>(rb + 896 + 32 * (l - 28) + 16) = r1;
                 }
             }
         }
