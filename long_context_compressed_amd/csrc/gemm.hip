@@ -14,13 +14,14 @@
 //   - workgroup tile 64 MI (M) x 64 WN (N), 2 x WN wavefronts of 32 MI x 64 (MI x 2 blocks
 //     of 32 x 32): MI = 4, WN = 4 (256 x 256, 8 wavefronts) for the plain GEMM, MI = 2,
 //     WN = 2 (128 x 128) for the compressor (its epilogue tile has to fit LDS);
-//   - the K loop runs over 32-wide slices through a ring of LDS stages; slices go from
-//     memory straight into LDS by buffer loads with the LDS destination (16 bytes per
-//     lane), all but one stage ahead of the slice being multiplied;
-//   - a slice row is 64 bytes = four 16-byte chunks; chunk c of tile row r sits in LDS slot
-//     c ^ ((r / 4) % 4) (the lanes of a load fetch the permuted chunks, so the LDS side
-//     stays one contiguous 1 KiB write per instruction), which spreads the 32 rows of a
-//     fragment read over all banks;
+//   - the K loop runs over 64-wide slices in 2 LDS stages (32-wide slices in 4 stages when
+//     K is an odd multiple of 32); slices go from memory straight into LDS by buffer loads
+//     with the LDS destination (16 bytes per lane), all but one stage ahead of the slice
+//     being multiplied, one barrier per slice;
+//   - a slice row is 128 (64) bytes = eight (four) 16-byte chunks; chunk c of tile row r sits
+//     in LDS slot c ^ ((r / 2) % 8) (c ^ ((r / 4) % 4)) (the lanes of a load fetch the
+//     permuted chunks, so the LDS side stays one contiguous 1 KiB write per instruction),
+//     which spreads the 16 rows that a 16-byte fragment read serves together over all banks;
 //   - rows past the operand's end, and the 4 rows before a sequence's first token when no
 //     carry is given, read as zeros (buffer loads past the resource end return 0).
 #include "common.hpp"
