@@ -148,3 +148,34 @@ def test_decode_step_full_size_kv8(csa, orc):
     del inp, step
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("T,H,B,N,k,pos", [
+    (4, 128, 4, 300, 0, [300 * 128, 300 * 128 + 5, 200 * 128 - 1, 127]),  # HCA decode, rows split
+    (3, 128, 3, 2000, 300, [8000, 8001, 100]),                              # CSA decode
+])
+def test_attn_kv8_smallest_block_scale(csa, orc, T, H, B, N, k, pos):
+    """FP8 rows whose every block scale is 2^-127 (E8M0 byte 0, the one scale that is no
+    normal fp32 number, expanded by a separate decode-then-scale step): the codes stay
+    random, the rows' bf16 RoPE dims and the SWA rows are scaled by 2^-120 and the queries by
+    2^118, so the scores are O(1) and the outputs (about 2^-120) are normal bf16 numbers."""
+    say("attn kv8 e=-127", T, H, B, N, k)
+    q, kv8, swa, sink, q_seq, q_pos, idx, p0, rope = _kv8_attn_inputs(600 + T, T, H, B, N, k, 200, pos)
+    kv8 = kv8.clone()
+    kv8[..., 576:590] = 0
+    rope_dims = kv8[..., 448:576].contiguous().view(torch.bfloat16).float() * 2.0 ** -120
+    kv8[..., 448:576] = rope_dims.to(torch.bfloat16).view(torch.uint8)
+    swa = (swa.float() * 2.0 ** -120).to(torch.bfloat16)
+    q = (q.float() * 2.0 ** 118).to(torch.bfloat16)
+    kvd = orc.kv8_decode(kv8)
+    if k == 0:
+        out, lse = csa.hca_attn(q, kv8, sink, 128, 512 ** -0.5, swa, p0, 128, q_seq, q_pos, rope, 64)
+        torch.cuda.synchronize()
+        ref, rlse = orc.hca_attn(q, kvd, sink, 128, 512 ** -0.5, swa, p0, 128, q_seq, q_pos, rope, 64)
+    else:
+        out, lse = csa.sparse_attn(q, kv8, sink, idx, 512 ** -0.5, swa, p0, 128, q_seq, q_pos, rope, 64)
+        torch.cuda.synchronize()
+        ref, rlse = orc.sparse_attn(q, kvd, sink, idx, 512 ** -0.5, swa, p0, 128, q_seq, q_pos, rope, 64)
+    assert float(torch.as_tensor(ref).abs().max()) < 2.0 ** -100  # the outputs really are that small
+    assert_rel(out, ref, TOL_BF16, "attention over FP8 rows with 2^-127 block scales")
+    assert_rel(lse, rlse, 2e-3, "lse over FP8 rows with 2^-127 block scales")
