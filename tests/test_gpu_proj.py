@@ -84,6 +84,8 @@ def test_compress_hidden_into_cache_and_full_size_sample(csa, orc):
     (130, 64, 512, 1, 200, 0, torch.float32),       # one group, the grouped stage alone (fp32 y)
     (77, 8, 128, 4, 64, 96, torch.float32),
     (70, 6, 32, 2, 80, 160, torch.bfloat16),        # K of both maps an odd multiple of 32
+    (1, 8, 64, 2, 32, 32, torch.bfloat16),          # one token, one tile far from full
+    (513, 4, 128, 1, 257, 0, torch.float32),        # 256-row and 256-column tiles plus one of each
 ])
 def test_out_proj(csa, orc, T, H, D, G, d_g, dm, odt):
     say("out_proj", T, H, D, G, d_g, dm, odt)
