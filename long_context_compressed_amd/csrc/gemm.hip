@@ -421,19 +421,32 @@ static_assert(CompressTile<32>::BM * CompressTile<32>::BN * 4 <= CompressTile<32
 // else slices of 32 in 4 stages
 constexpr int kGemmMI = 4, kGemmWN = 4;
 
-template <int NST, int BK>
+template <int NST, int BK, int WN = kGemmWN>
 void launch_gemm_cfg(const bf16_t *A, int64_t lda, int64_t sA, const bf16_t *B, int64_t ldb, int64_t sB, void *C,
                      int64_t ldc, int64_t sC, bool c_f32, int64_t M, int64_t N, int64_t K, int batch,
                      hipStream_t st) {
-    using TL = Tile<kGemmMI, NST, kGemmWN, BK>;
+    using TL = Tile<kGemmMI, NST, WN, BK>;
     const int mtiles = (int)((M + TL::BM - 1) / TL::BM), ntiles = (int)((N + TL::BN - 1) / TL::BN);
     const dim3 grid((unsigned)((int64_t)mtiles * ntiles), 1, (unsigned)batch);
     if (c_f32)
-        hipLaunchKernelGGL((gemm_bf16_kernel<float, kGemmMI, NST, kGemmWN, BK>), grid, dim3(128 * kGemmWN), 0, st,
-                           A, lda, sA, B, ldb, sB, (float *)C, ldc, sC, M, N, K, mtiles);
+        hipLaunchKernelGGL((gemm_bf16_kernel<float, kGemmMI, NST, WN, BK>), grid, dim3(128 * WN), 0, st, A, lda, sA,
+                           B, ldb, sB, (float *)C, ldc, sC, M, N, K, mtiles);
     else
-        hipLaunchKernelGGL((gemm_bf16_kernel<bf16_t, kGemmMI, NST, kGemmWN, BK>), grid, dim3(128 * kGemmWN), 0, st,
-                           A, lda, sA, B, ldb, sB, (bf16_t *)C, ldc, sC, M, N, K, mtiles);
+        hipLaunchKernelGGL((gemm_bf16_kernel<bf16_t, kGemmMI, NST, WN, BK>), grid, dim3(128 * WN), 0, st, A, lda,
+                           sA, B, ldb, sB, (bf16_t *)C, ldc, sC, M, N, K, mtiles);
+}
+
+// Columns of C that 256 x 256 tiles cover in whole rounds of one workgroup per compute
+// unit; the rest go to a second launch of 256 x 128 tiles, so the last round is not a
+// partial one of full-size tiles (Pro width: 896 tiles = 3.5 rounds become 768 + 256
+// half-size tiles). 0 when the tiles already fill whole rounds or fill less than one.
+inline int64_t gemm_round_columns(int64_t M, int64_t N, int batch) {
+    const int cu = device_cu_count();
+    const int64_t mt = (M + 255) / 256, nt = (N + 255) / 256, per_nt = mt * batch;
+    const int64_t tiles = per_nt * nt;
+    if (cu <= 0 || tiles <= cu || tiles % cu == 0) return 0;
+    const int64_t main_nt = (tiles / cu) * cu / per_nt;
+    return (main_nt >= 1 && main_nt < nt) ? main_nt * 256 : 0;
 }
 
 }  // namespace
@@ -442,9 +455,16 @@ int launch_gemm_bf16(const bf16_t *A, int64_t lda, int64_t sA, const bf16_t *B, 
                      int64_t ldc, int64_t sC, bool c_f32, int64_t M, int64_t N, int64_t K, int batch,
                      hipStream_t st) {
     if (M == 0 || N == 0 || batch == 0) return CSA_OK;
-    if (K % 64 == 0)
-        launch_gemm_cfg<2, 64>(A, lda, sA, B, ldb, sB, C, ldc, sC, c_f32, M, N, K, batch, st);
-    else
+    if (K % 64 == 0) {
+        const int64_t n1 = gemm_round_columns(M, N, batch);
+        if (n1 == 0) {
+            launch_gemm_cfg<2, 64>(A, lda, sA, B, ldb, sB, C, ldc, sC, c_f32, M, N, K, batch, st);
+        } else {
+            launch_gemm_cfg<2, 64>(A, lda, sA, B, ldb, sB, C, ldc, sC, c_f32, M, n1, K, batch, st);
+            void *C2 = c_f32 ? (void *)((float *)C + n1) : (void *)((bf16_t *)C + n1);
+            launch_gemm_cfg<2, 64, 2>(A, lda, sA, B + n1 * ldb, ldb, sB, C2, ldc, sC, c_f32, M, N - n1, K, batch, st);
+        }
+    } else
         launch_gemm_cfg<4, 32>(A, lda, sA, B, ldb, sB, C, ldc, sC, c_f32, M, N, K, batch, st);
     return check_launch("gemm_bf16_kernel");
 }

@@ -86,6 +86,7 @@ def test_compress_hidden_into_cache_and_full_size_sample(csa, orc):
     (70, 6, 32, 2, 80, 160, torch.bfloat16),        # K of both maps an odd multiple of 32
     (1, 8, 64, 2, 32, 32, torch.bfloat16),          # one token, one tile far from full
     (513, 4, 128, 1, 257, 0, torch.float32),        # 256-row and 256-column tiles plus one of each
+    (4096, 8, 64, 2, 64, 5000, torch.bfloat16),     # W_b: 320 tiles, the columns past one round in half-size tiles
 ])
 def test_out_proj(csa, orc, T, H, D, G, d_g, dm, odt):
     say("out_proj", T, H, D, G, d_g, dm, odt)
