@@ -421,18 +421,18 @@ static_assert(CompressTile<32>::BM * CompressTile<32>::BN * 4 <= CompressTile<32
 // else slices of 32 in 4 stages
 constexpr int kGemmMI = 4, kGemmWN = 4;
 
-template <int NST, int BK, int WN = kGemmWN>
+template <int NST, int BK, int WN = kGemmWN, int MI = kGemmMI>
 void launch_gemm_cfg(const bf16_t *A, int64_t lda, int64_t sA, const bf16_t *B, int64_t ldb, int64_t sB, void *C,
                      int64_t ldc, int64_t sC, bool c_f32, int64_t M, int64_t N, int64_t K, int batch,
                      hipStream_t st) {
-    using TL = Tile<kGemmMI, NST, WN, BK>;
+    using TL = Tile<MI, NST, WN, BK>;
     const int mtiles = (int)((M + TL::BM - 1) / TL::BM), ntiles = (int)((N + TL::BN - 1) / TL::BN);
     const dim3 grid((unsigned)((int64_t)mtiles * ntiles), 1, (unsigned)batch);
     if (c_f32)
-        hipLaunchKernelGGL((gemm_bf16_kernel<float, kGemmMI, NST, WN, BK>), grid, dim3(128 * WN), 0, st, A, lda, sA,
+        hipLaunchKernelGGL((gemm_bf16_kernel<float, MI, NST, WN, BK>), grid, dim3(128 * WN), 0, st, A, lda, sA,
                            B, ldb, sB, (float *)C, ldc, sC, M, N, K, mtiles);
     else
-        hipLaunchKernelGGL((gemm_bf16_kernel<bf16_t, kGemmMI, NST, WN, BK>), grid, dim3(128 * WN), 0, st, A, lda,
+        hipLaunchKernelGGL((gemm_bf16_kernel<bf16_t, MI, NST, WN, BK>), grid, dim3(128 * WN), 0, st, A, lda,
                            sA, B, ldb, sB, (bf16_t *)C, ldc, sC, M, N, K, mtiles);
 }
 
