@@ -269,23 +269,30 @@ gemm_bf16_kernel(const bf16_t *__restrict__ A, int64_t lda, int64_t sA, const bf
 // ---------------------------------------------------------------------------------------
 // ratio 4 (overlapped): tile rows 0..127 are tokens t0 - 4 .. t0 + 123 with t0 = 124 * mt,
 // so the tile holds 31 whole entries (entry e: b-rows 4e..4e+3, a-rows 4e+4..4e+7); the
-// tile's columns are 32 channels x the 4 projections (C^a, Z^a, C^b, Z^b), column
-// 32 p + x = channel 32 nt + x of projection p. Tokens before 0 come from the carry rows
+// tile's columns are CW = 64 channels x the 4 projections (C^a, Z^a, C^b, Z^b), column
+// CW p + x = channel CW nt + x of projection p. Tokens before 0 come from the carry rows
 // (the last 4 hidden rows of the previous chunk) or are absent (weight 0).
-// ratio 128: tile rows are the 128 tokens of entry mt; columns 64 channels x (C, Z).
-// K slices of 64 in 2 stages when d % 64 == 0, else of 32 in 4 stages (64 KiB either way:
-// two workgroups per CU)
+// ratio 128: tile rows are the 128 tokens of entry mt; columns 128 channels x (C, Z).
+// K slices of 64 in 2 stages when d % 64 == 0, else of 32 in 4 stages (a 96 KiB ring); the
+// fp32 epilogue tile takes 128 KiB: one workgroup of 8 wavefronts per CU
+constexpr int kCompressWN = 4;  // wavefronts in N: 128 x 256 tiles of 8 wavefronts
 template <int BK>
-using CompressTile = Tile<2, BK == 64 ? 2 : 4, 2, BK>;
+using CompressTile = Tile<2, BK == 64 ? 2 : 4, kCompressWN, BK>;
+// the ring, and after the products the fp32 epilogue tile
+template <int BK>
+constexpr int compress_lds() {
+    using TL = CompressTile<BK>;
+    return TL::LDS > TL::BM * TL::BN * 4 ? TL::LDS : TL::BM * TL::BN * 4;
+}
 
 template <int RATIO, typename OT, int BK>
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(128 * kCompressWN)
 compress_hidden_kernel(const bf16_t *__restrict__ Hs, const bf16_t *__restrict__ carry, const bf16_t *__restrict__ W,
                        const float *__restrict__ bias, int64_t n, int64_t d, int c, OT *__restrict__ out,
                        int64_t out_bstride, int mtiles, int ntiles)
 {
     using TL = CompressTile<BK>;
-    __shared__ __attribute__((aligned(16))) char lds[TL::LDS];
+    __shared__ __attribute__((aligned(16))) char lds[compress_lds<BK>()];
     constexpr bool kOv = RATIO == 4;
     constexpr int NP = kOv ? 4 : 2;          // projections
     constexpr int BN = TL::BN;
@@ -318,16 +325,16 @@ compress_hidden_kernel(const bf16_t *__restrict__ Hs, const bf16_t *__restrict__
     };
     f32x16 acc[2][2];
     if (kOv && carry != nullptr)
-        gemm_core<2, TL::NST, 2, BK, true>(lds, oa, ob, d, rowA, rowA2, rowB, acc);
+        gemm_core<2, TL::NST, kCompressWN, BK, true>(lds, oa, ob, d, rowA, rowA2, rowB, acc);
     else
-        gemm_core<2, TL::NST, 2, BK, false>(lds, oa, ob, d, rowA, rowA2, rowB, acc);
+        gemm_core<2, TL::NST, kCompressWN, BK, false>(lds, oa, ob, d, rowA, rowA2, rowB, acc);
 
-    // the fp32 tile into LDS: [128 rows][128 columns]
+    // the fp32 tile into LDS: [128 rows][256 columns]
     constexpr int TP = BN;
     float *tile = reinterpret_cast<float *>(lds);
     {
         const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-        const int wm = w >> 1, wn = w & 1;
+        const int wm = w / kCompressWN, wn = w % kCompressWN;
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -343,9 +350,9 @@ compress_hidden_kernel(const bf16_t *__restrict__ Hs, const bf16_t *__restrict__
     const int64_t E = n / RATIO;  // whole entries of the chunk
     if constexpr (kOv) {
         // 31 entries x 32 channels, four pairs per thread
-        const int x = tid & 31;
+        const int x = tid % CW;
         const int ch = nt * CW + x;
-        for (int e = tid >> 5; e < NE; e += 8) {
+        for (int e = tid / CW; e < NE; e += 128 * kCompressWN / CW) {
             const int64_t ei = (int64_t)mt * NE + e;
             if (ei >= E || ch >= c) continue;
             float z[8], v[8];
@@ -413,9 +420,7 @@ compress_hidden_kernel(const bf16_t *__restrict__ Hs, const bf16_t *__restrict__
 }
 
 // the compressor's ring also holds its fp32 epilogue tile
-static_assert(CompressTile<32>::BM * CompressTile<32>::BN * 4 <= CompressTile<32>::LDS &&
-                  CompressTile<64>::BM * CompressTile<64>::BN * 4 <= CompressTile<64>::LDS,
-              "the epilogue tile fits the ring");
+static_assert(compress_lds<32>() <= 160 * 1024 && compress_lds<64>() <= 160 * 1024, "one workgroup fits a CU's LDS");
 // the plain GEMM: 256 x 256 tiles of 8 wavefronts, one workgroup per CU (128 KiB of LDS):
 // K slices of 64 in 2 stages (one barrier per 32 matrix ops of a wavefront) when K % 64 == 0,
 // else slices of 32 in 4 stages
@@ -473,22 +478,22 @@ template <int BK>
 void launch_compress_cfg(const bf16_t *Hs, const bf16_t *carry, const bf16_t *W, const float *bias, int B, int64_t n,
                          int64_t d, int c, int ratio, void *out, bool out_f32, int64_t bs, hipStream_t st) {
     if (ratio == 4) {
-        const int mtiles = (int)((n + 123) / 124), ntiles = (c + 31) / 32;
+        const int mtiles = (int)((n + 123) / 124), ntiles = (c + 16 * kCompressWN - 1) / (16 * kCompressWN);
         const dim3 grid((unsigned)((int64_t)mtiles * ntiles), 1, (unsigned)B);
         if (out_f32)
-            hipLaunchKernelGGL((compress_hidden_kernel<4, float, BK>), grid, dim3(256), 0, st, Hs, carry, W, bias,
+            hipLaunchKernelGGL((compress_hidden_kernel<4, float, BK>), grid, dim3(128 * kCompressWN), 0, st, Hs, carry, W, bias,
                                n, d, c, (float *)out, bs, mtiles, ntiles);
         else
-            hipLaunchKernelGGL((compress_hidden_kernel<4, bf16_t, BK>), grid, dim3(256), 0, st, Hs, carry, W,
+            hipLaunchKernelGGL((compress_hidden_kernel<4, bf16_t, BK>), grid, dim3(128 * kCompressWN), 0, st, Hs, carry, W,
                                bias, n, d, c, (bf16_t *)out, bs, mtiles, ntiles);
     } else {
-        const int mtiles = (int)(n / ratio), ntiles = (c + 63) / 64;
+        const int mtiles = (int)(n / ratio), ntiles = (c + 32 * kCompressWN - 1) / (32 * kCompressWN);
         const dim3 grid((unsigned)((int64_t)mtiles * ntiles), 1, (unsigned)B);
         if (out_f32)
-            hipLaunchKernelGGL((compress_hidden_kernel<128, float, BK>), grid, dim3(256), 0, st, Hs, carry, W,
+            hipLaunchKernelGGL((compress_hidden_kernel<128, float, BK>), grid, dim3(128 * kCompressWN), 0, st, Hs, carry, W,
                                bias, n, d, c, (float *)out, bs, mtiles, ntiles);
         else
-            hipLaunchKernelGGL((compress_hidden_kernel<128, bf16_t, BK>), grid, dim3(256), 0, st, Hs, carry, W,
+            hipLaunchKernelGGL((compress_hidden_kernel<128, bf16_t, BK>), grid, dim3(128 * kCompressWN), 0, st, Hs, carry, W,
                                bias, n, d, c, (bf16_t *)out, bs, mtiles, ntiles);
     }
 }
