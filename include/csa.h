@@ -358,7 +358,8 @@ int csa_topk_ids(const float *scores, const int32_t *ids, int T, int64_t M, int 
  * attn_sink: [H] fp32 (not scaled); topk_idxs: [T][k] int32;
  * swa_kv: [B][swa_rows][D] dt or NULL (then window is ignored); swa_pos0: [B] int64;
  * rope_cs: [T][rope_dim/2][2] fp32 or NULL (rope_dim ignored); out: [T][H][D] dt;
- * lse: [T][H] fp32 or NULL; workspace: csa_attn_workspace_bytes(...) bytes.
+ * lse: [T][H] fp32 or NULL; workspace: csa_attn_workspace_bytes(...) bytes, 16-byte aligned
+ *      (CSA_EINVAL otherwise, when the query returns more than 0).
  * Supported: dt F32 | BF16, D <= 1024, D % 64 == 0, rope_dim even and <= D, 0 <= k <= 4096;
  * dt = CSA_KV8: kv rows [B][N][592] bytes in the format of csa_quantize_kv8 (q, swa_kv and
  * out bf16), D = 512 and H a multiple of 64.

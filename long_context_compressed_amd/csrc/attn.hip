@@ -113,73 +113,109 @@ constexpr int MD = 512;      // head dim
 constexpr int MHG = 64;      // heads per workgroup
 constexpr int MTR = 32;      // rows per tile
 
-// log-sum-exp merge of split partials + sink + inverse RoPE; one block per (query, head).
-// Workspace layout: [T][nsplit][H][2] fp32 (m_s, l_s), then [T][nsplit][H][D] bf16 partial
-// sums (each split's unnormalised O, rounded once to bf16: half the bytes of fp32, and the
-// merged output is bf16 anyway). The per-split weights 2^(m_s - M) are formed once in LDS;
-// every thread then streams its two output dims over all splits with independent loads.
-template <typename ET>
-__global__ void __launch_bounds__(256)
+// log-sum-exp merge of split partials + sink + inverse RoPE; one wavefront per (query, head),
+// eight dims per lane. Workspace layout: [T][nsplit][H][2] fp32 (m_s, l_s), then
+// [T][nsplit][H][D] bf16 partial sums (each split's unnormalised O, rounded once to bf16:
+// half the bytes of fp32, and the merged output is bf16 anyway). Lane s holds the weights
+// of splits s, s + 64, s + 128, s + 192; the partial rows are fetched 16 bytes per lane in
+// batches of 32 splits whose loads are all issued before the first is used (the merge is a
+// latency problem: a few MB spread over 256 compute units), and the wave-uniform weight of
+// each split is read out of its lane with readlane into a scalar register.
+__global__ void __launch_bounds__(64)
 attn_merge_kernel(const float *__restrict__ part, const float *__restrict__ sink, int nsplit,
-                  const float *__restrict__ rope_cs, int R, int T, int H, int D,
-                  ET *__restrict__ out, float *__restrict__ lse)
+                  const float *__restrict__ rope_cs, int R, int T, int H,
+                  bf16_t *__restrict__ out, float *__restrict__ lse)
 {
-    __shared__ float fs[256];
-    __shared__ float red[2];
+    constexpr int D = MD;
+    constexpr int MB = 32;  // partial rows in flight per lane
     const int64_t unit = blockIdx.x;
     const int t = (int)(unit / H), g = (int)(unit % H);
-    const float *pml = part;
-    const uint32_t *pacc = reinterpret_cast<const uint32_t *>(part + (int64_t)T * nsplit * H * 2);
+    const int lane = threadIdx.x;
+    const int64_t hs = (int64_t)H * 2;  // stride of one split in the (m, l) array
+    const float *pml = part + ((int64_t)t * nsplit * H + g) * 2;
+    const int64_t vs = (int64_t)H * D / 8;  // stride of one split in 16-byte units
+    const uint4 *pacc = reinterpret_cast<const uint4 *>(part + (int64_t)T * nsplit * H * 2) +
+                        ((int64_t)t * nsplit * H + g) * (D / 8) + lane;
+    float mv[4], lv[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int s = lane + 64 * c;
+        mv[c] = s < nsplit ? pml[s * hs] : -INFINITY;
+        lv[c] = s < nsplit ? pml[s * hs + 1] : 0.f;
+    }
+    uint4 v[MB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) v[i] = i < nsplit ? pacc[i * vs] : make_uint4(0u, 0u, 0u, 0u);
     const float sk = sink[g] * kLog2e;
-    if (threadIdx.x < 64) {
-        // one wavefront forms the global max, the denominator and the split weights
-        const int lane = threadIdx.x;
-        float M = sk;
-        for (int s2 = lane; s2 < nsplit; s2 += 64) M = fmaxf(M, pml[(((int64_t)t * nsplit + s2) * H + g) * 2]);
+    float M = fmaxf(sk, fmaxf(fmaxf(mv[0], mv[1]), fmaxf(mv[2], mv[3])));
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-        const float mu = (M == -INFINITY) ? 0.f : M;
-        float L = 0.f;
-        for (int s2 = lane; s2 < nsplit; s2 += 64) {
-            const int64_t o = (((int64_t)t * nsplit + s2) * H + g) * 2;
-            const float f = exp2f(pml[o] - mu);
-            fs[s2] = f;
-            L += pml[o + 1] * f;
-        }
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    const float mu = (M == -INFINITY) ? 0.f : M;
+    float f[4], L = 0.f;
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
-        L += exp2f(sk - mu);
-        if (lane == 0) {
-            red[0] = mu;
-            red[1] = L;
+    for (int c = 0; c < 4; ++c) {
+        f[c] = exp2f(mv[c] - mu);
+        L += lv[c] * f[c];
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
+    L += exp2f(sk - mu);
+    float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    auto fold = [&](const uint4 &w, float fw) {
+        x[0] = fmaf(lo_bf16(w.x), fw, x[0]);
+        x[1] = fmaf(hi_bf16(w.x), fw, x[1]);
+        x[2] = fmaf(lo_bf16(w.y), fw, x[2]);
+        x[3] = fmaf(hi_bf16(w.y), fw, x[3]);
+        x[4] = fmaf(lo_bf16(w.z), fw, x[4]);
+        x[5] = fmaf(hi_bf16(w.z), fw, x[5]);
+        x[6] = fmaf(lo_bf16(w.w), fw, x[6]);
+        x[7] = fmaf(hi_bf16(w.w), fw, x[7]);
+    };
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+        for (int b = 0; b < 64; b += MB) {
+            const int s0 = 64 * c + b;
+            if (s0 >= nsplit) break;
+            if (s0 > 0) {
+#pragma unroll
+                for (int i = 0; i < MB; ++i)
+                    v[i] = s0 + i < nsplit ? pacc[(s0 + i) * vs] : make_uint4(0u, 0u, 0u, 0u);
+            }
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+                fold(v[i], __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f[c]), b + i)));
         }
     }
-    __syncthreads();
-    const float mu = red[0], L = red[1];
     const float inv = L > 0.f ? 1.f / L : 0.f;
-    for (int d0 = 2 * threadIdx.x; d0 < D; d0 += 2 * blockDim.x) {
-        float x0 = 0.f, x1 = 0.f;
-        const uint32_t *pp = pacc + ((((int64_t)t * nsplit) * H + g) * D + d0) / 2;
-#pragma unroll 8
-        for (int s2 = 0; s2 < nsplit; ++s2) {
-            const uint32_t v = pp[(int64_t)s2 * H * D / 2];
-            x0 = fmaf(lo_bf16(v), fs[s2], x0);
-            x1 = fmaf(hi_bf16(v), fs[s2], x1);
-        }
-        x0 *= inv;
-        x1 *= inv;
-        if (rope_cs != nullptr && d0 >= D - R) {
-            const int p = (d0 - (D - R)) >> 1;
+    const int d0 = 8 * lane;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+        float x0 = x[e] * inv, x1 = x[e + 1] * inv;
+        const int d = d0 + e;
+        if (rope_cs != nullptr && d >= D - R) {
+            const int p = (d - (D - R)) >> 1;
             const float cs = rope_cs[((int64_t)t * (R / 2) + p) * 2], sn = rope_cs[((int64_t)t * (R / 2) + p) * 2 + 1];
             const float y0 = x0 * cs + x1 * sn, y1 = -x0 * sn + x1 * cs;
             x0 = y0;
             x1 = y1;
         }
-        ET *orow = out + ((int64_t)t * H + g) * D;
-        elem<ET>::store(orow, d0, x0);
-        elem<ET>::store(orow, d0 + 1, x1);
+        x[e] = x0;
+        x[e + 1] = x1;
     }
-    if (lse != nullptr && threadIdx.x == 0) lse[(int64_t)t * H + g] = L > 0.f ? (mu + log2f(L)) * kLn2 : -INFINITY;
+    bf16_t *orow = out + ((int64_t)t * H + g) * D + d0;
+    if ((reinterpret_cast<uintptr_t>(out) & 15) == 0) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            w[e] = (uint32_t)f32_to_bf16(x[2 * e]) |
+                   ((uint32_t)f32_to_bf16(x[2 * e + 1]) << 16);
+        *reinterpret_cast<uint4 *>(orow) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) orow[e] = f32_to_bf16(x[e]);
+    }
+    if (lse != nullptr && lane == 0) lse[(int64_t)t * H + g] = L > 0.f ? (mu + log2f(L)) * kLn2 : -INFINITY;
 }
 
 // Row splits per (query, head group): enough workgroups to cover the CUs once, at least
@@ -239,13 +275,14 @@ int launch_attn(const AttnArgs &a, hipStream_t st) {
     const size_t need = attn_workspace_bytes(a.T, a.H, a.D, max_rows);
     if (need > a.ws_bytes || (need > 0 && a.ws == nullptr))
         return fail(CSA_EWORKSPACE, "attention: workspace smaller than csa_attn_workspace_bytes()");
+    if (need > 0 && (reinterpret_cast<uintptr_t>(a.ws) & 15) != 0)
+        return fail(CSA_EINVAL, "attention: workspace must be 16-byte aligned");
     const int64_t tiles = (max_rows + MTR - 1) / MTR;
     const int64_t split_slots = ((tiles + ns - 1) / ns) * MTR;
     const int rc = launch_attn_wide(a, sl2, ns, split_slots, st);
     if (rc != CSA_OK || ns == 1) return rc;
-    hipLaunchKernelGGL(attn_merge_kernel<bf16_t>, dim3((unsigned)((int64_t)a.T * a.H)), dim3(256), 0, st,
-                       (const float *)a.ws, a.sink, ns, a.rope_cs, a.rope_dim, a.T, a.H, a.D, (bf16_t *)a.out,
-                       a.lse);
+    hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)((int64_t)a.T * a.H)), dim3(64), 0, st,
+                       (const float *)a.ws, a.sink, ns, a.rope_cs, a.rope_dim, a.T, a.H, (bf16_t *)a.out, a.lse);
     return check_launch("attn_merge_kernel");
 }
 
