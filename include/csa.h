@@ -167,7 +167,10 @@ int csa_out_proj(const void *o, int T, int H, int D, int G, const void *W_a, int
  * Supported: H_I == 64, D_I == 128 (the indexer of both model sizes), ratio >= 1; per-head
  * keys in F32 | BF16 | MXFP4, shared keys in BF16 (k_heads other than H_I or 1 is
  * CSA_EINVAL, a shared-key dtype other than BF16 CSA_EUNSUPPORTED). T, N may be 0 (nothing
- * is launched).
+ * is launched). MXFP4 per-head keys with B == 1 and T > 16 (a prefill chunk of one
+ * sequence) run as matrix-core tiles of queries x entries over that one key store; every
+ * other MXFP4 case (several sequences, or few queries) streams each query's own keys. Both
+ * give the same scores.
  */
 int csa_index_scores(const void *q_I, const uint8_t *q_I_scale, const float *w,
                      const void *k_I, const uint8_t *k_I_scale,

@@ -165,6 +165,7 @@ __device__ __forceinline__ void fp4_head(const char *lds, uint32_t rs, uint32_t 
     }
 }
 
+// Reads the keys of sequence 0 only: launch_index_mxfp4 dispatches here just when B == 1.
 // second argument: wavefronts per SIMD the register allocation must allow
 __global__ void __launch_bounds__(256, 3)
 index_mxfp4_mfma_kernel(const uint8_t *__restrict__ qI, const uint8_t *__restrict__ qS,
